@@ -1,0 +1,191 @@
+"""CPU oracle of the sparse MoE FFN layer -- TEST INFRASTRUCTURE ONLY.
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It loads ``liboracle.so`` built from ``moe_oracle.c`` (plain
+C, OpenMP, no shared code with the HIP library) and marshals NumPy arrays.
+It never imports the product package.
+
+The arithmetic, and the passages it follows, are described at the top of
+``moe_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+GCC_CMD = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-Wextra", _SRC, "-o", LIB_PATH, "-lm"]
+
+
+def build() -> str:
+    """Compile the oracle library (gcc); returns its path."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = GCC_CMD[:-3] + ["-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError(f"{what} failed with code {rc}")
+
+
+class Oracle:
+    """ctypes view of one build of the oracle library."""
+
+    def __init__(self, lib_path: str = LIB_PATH):
+        if lib_path == LIB_PATH and not os.path.exists(LIB_PATH):
+            build()
+        L = C.CDLL(lib_path)
+        p = C.c_void_p
+        i = C.c_int
+        L.oracle_route.argtypes = [p, p, p, p, i, i, i, i, p, p, p, p]
+        L.oracle_route_from_logits.argtypes = [p, i, i, i, p, p]
+        L.oracle_align.argtypes = [p, i, i, i, p, p, p]
+        L.oracle_forward.argtypes = [p] * 10 + [i] * 6 + [p] * 10
+        for f in (L.oracle_route, L.oracle_route_from_logits, L.oracle_align, L.oracle_forward):
+            f.restype = C.c_int
+        self.lib = L
+        self.path = lib_path
+
+    def route(self, x, w_router, bias, w_sg, k: int) -> Dict[str, np.ndarray]:
+        """Router logits (fp32), top-k ids, renormalised weights (double), shared gate s."""
+        x = _c(x, np.uint16)
+        w_router = _c(w_router, np.uint16)
+        bias = _c(bias, np.float32)
+        w_sg = _c(w_sg, np.uint16)
+        T, H = x.shape
+        E = w_router.shape[0]
+        logits = np.empty((T, E), np.float32)
+        ids = np.empty((T, k), np.int32)
+        w = np.empty((T, k), np.float64)
+        s = np.empty(T, np.float64) if w_sg is not None else None
+        _check(self.lib.oracle_route(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_sg), T, H, E, k,
+                                     _ptr(logits), _ptr(ids), _ptr(w), _ptr(s)), "oracle_route")
+        return {"logits": logits, "ids": ids, "w": w, "s": s}
+
+    def route_from_logits(self, logits, k: int):
+        logits = _c(logits, np.float32)
+        T, E = logits.shape
+        ids = np.empty((T, k), np.int32)
+        w = np.empty((T, k), np.float64)
+        _check(self.lib.oracle_route_from_logits(_ptr(logits), T, E, k, _ptr(ids), _ptr(w)),
+               "oracle_route_from_logits")
+        return ids, w
+
+    def align(self, ids, E: int):
+        """Stable expert grouping: counts[E], offsets[E+1], perm[T*k] (unpadded)."""
+        ids = _c(ids, np.int32)
+        T, k = ids.shape
+        counts = np.empty(E, np.int32)
+        offsets = np.empty(E + 1, np.int32)
+        perm = np.empty(T * k, np.int32)
+        _check(self.lib.oracle_align(_ptr(ids), T, E, k, _ptr(counts), _ptr(offsets), _ptr(perm)),
+               "oracle_align")
+        return counts, offsets, perm
+
+    def forward(self, inp: Dict[str, np.ndarray], k: Optional[int] = None, ids_in=None,
+                want=()) -> Dict[str, np.ndarray]:
+        """Whole layer on the arrays of ``inp`` (keys as produced by the seeded generator).
+
+        ``want`` may name any of "h", "o", "hs", "os" for per-stage outputs.
+        """
+        x = _c(inp["x"], np.uint16)
+        wr = _c(inp["w_router"], np.uint16)
+        bias = _c(inp.get("bias"), np.float32)
+        wg = _c(inp["w_gate"], np.uint16)
+        wu = _c(inp["w_up"], np.uint16)
+        wd = _c(inp["w_down"], np.uint16)
+        sg = _c(inp.get("ws_gate"), np.uint16)
+        su = _c(inp.get("ws_up"), np.uint16)
+        sd = _c(inp.get("ws_down"), np.uint16)
+        wsg = _c(inp.get("w_sg"), np.uint16)
+        T, H = x.shape
+        E, I, _ = wg.shape
+        I_s = 0 if sg is None else sg.shape[0]
+        if k is None:
+            k = inp["wl"].k
+        ids_in = _c(ids_in, np.int32)
+        y = np.empty((T, H), np.float64)
+        ids = np.empty((T, k), np.int32)
+        w = np.empty((T, k), np.float64)
+        s = np.empty(T, np.float64)
+        logits = np.empty((T, E), np.float32)
+        h = np.empty((T * k, I), np.float64) if "h" in want else None
+        o = np.empty((T * k, H), np.float64) if "o" in want else None
+        hs = np.empty((T, I_s), np.float64) if ("hs" in want and I_s) else None
+        os_ = np.empty((T, H), np.float64) if ("os" in want and I_s) else None
+        _check(self.lib.oracle_forward(_ptr(x), _ptr(wr), _ptr(bias), _ptr(wg), _ptr(wu), _ptr(wd),
+                                       _ptr(sg), _ptr(su), _ptr(sd), _ptr(wsg), T, H, E, k, I, I_s,
+                                       _ptr(ids_in), _ptr(y), _ptr(ids), _ptr(w), _ptr(s), _ptr(logits),
+                                       _ptr(h), _ptr(o), _ptr(hs), _ptr(os_)), "oracle_forward")
+        out = {"y": y, "ids": ids, "w": w, "s": s if I_s else None, "logits": logits}
+        if h is not None:
+            out["h"] = h
+        if o is not None:
+            out["o"] = o
+        if hs is not None:
+            out["hs"] = hs
+        if os_ is not None:
+            out["os"] = os_
+        return out
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def route(*a, **kw):
+    return default().route(*a, **kw)
+
+
+def route_from_logits(*a, **kw):
+    return default().route_from_logits(*a, **kw)
+
+
+def align(*a, **kw):
+    return default().align(*a, **kw)
+
+
+def forward(*a, **kw):
+    return default().forward(*a, **kw)
+
+
+def topk_margin(logits: np.ndarray, k: int) -> np.ndarray:
+    """Smallest gap between consecutive sorted logits over ranks 0..k (per token).
+
+    A token whose margin is below a threshold is a near-tie: a different
+    fp32 summation order may legitimately change its selection or order.
+    """
+    lg = np.asarray(logits, np.float64)
+    srt = -np.sort(-lg, axis=1)
+    kk = min(k + 1, lg.shape[1])
+    d = srt[:, : kk - 1] - srt[:, 1:kk]
+    return d.min(axis=1) if d.shape[1] else np.full(lg.shape[0], np.inf)

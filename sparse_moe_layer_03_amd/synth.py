@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs for the sparse MoE FFN layer.
+
+This module only draws numbers.  It holds none of the layer's arithmetic
+(no router, no top-k, no FFN, no combine), so both the oracle's tests and
+the HIP path's tests, the benchmark and the smoke check may take their
+inputs from it without sharing any of the method.
+
+Workloads are named by what they are.  The shapes follow the Qwen3-class
+MoE block that the engine pages run as a selected-expert MoE path
+(guanjiawei.ai "AIMA AMD395 Qwen3.6-35B-A3B", section on the data path;
+kongchang.com "GFX1151 engine", section on the MoE kernel, which defines
+MoE as many expert sub-networks of which only a few are active per step).
+
+Every array that the layer reads in BF16 is returned as ``uint16`` bit
+patterns (round-to-nearest-even from float32 draws); the router bias is
+float32.
+
+Draw order from ``numpy.random.default_rng(seed)`` (PCG64), each tensor
+drawn with ``standard_normal(dtype=float32)`` and scaled by its sigma:
+x, W_router, bias (only if the workload has one), W_gate, W_up, W_down,
+Ws_gate, Ws_up, Ws_down, w_sg (the four shared tensors only when the
+shared expert exists), then, for the skewed workload, the rows that are
+zeroed to force exact ties.
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field, replace
+from typing import Dict, Optional
+
+import numpy as np
+
+WEIGHT_SIGMA = 0.02
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    I_s: int
+    bias: Optional[str] = None  # None | "normal" | "zipf"
+    bias_sigma: float = 1.0
+    zipf_s: float = 1.1
+    tie_frac: float = 0.0  # fraction of tokens given x_t = 0 (exact ties)
+    note: str = field(default="", compare=False)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", T=16, H=256, E=8, k=2, I=128, I_s=0,
+                     note="T=16, hidden 256, 8 experts, top-2, FFN 128, no shared expert"),
+    "decode": Workload("decode", T=1, H=2048, E=256, k=8, I=512, I_s=512,
+                       note="T=1 decode step, hidden 2048, 256 experts, top-8, FFN 512, shared expert 512"),
+    "prefill1k": Workload("prefill1k", T=1024, H=2048, E=256, k=8, I=512, I_s=512,
+                          note="T=1024 short prefill, no router bias (near-uniform load)"),
+    "prefill8k": Workload("prefill8k", T=8192, H=2048, E=256, k=8, I=512, I_s=512,
+                          bias="normal", bias_sigma=1.0,
+                          note="T=8192 long prefill, router bias ~ N(0,1) (uneven load)"),
+    "skew32k": Workload("skew32k", T=32768, H=2048, E=256, k=8, I=512, I_s=512,
+                        bias="zipf", zipf_s=1.1, tie_frac=0.01,
+                        note="T=32768 skewed chunk, Zipf(1.1) expert popularity, 1% exact-tie tokens"),
+}
+
+
+def workload(name: str, **overrides) -> Workload:
+    w = WORKLOADS[name]
+    return replace(w, **overrides) if overrides else w
+
+
+# ---------------------------------------------------------------- bf16 bits
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); finite inputs only."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _draw_bf16(rng: np.random.Generator, shape, sigma: float, chunk: int = 1 << 24) -> np.ndarray:
+    """standard_normal float32 draws scaled by sigma, rounded to bf16 bits.
+
+    Drawn in pieces of ``chunk`` values to bound the float32 temporary; the
+    generator's stream is consumed in the same order as one large draw.
+    """
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        m = min(chunk, n - s)
+        v = rng.standard_normal(m, dtype=np.float32)
+        if sigma != 1.0:
+            v *= np.float32(sigma)
+        out[s:s + m] = f32_to_bf16_bits(v)
+    return out.reshape(shape)
+
+
+def zipf_log_pmf_bias(rng: np.random.Generator, E: int, s: float) -> np.ndarray:
+    """Per-expert bias b_e = ln p(r_e), p(r) = r^-s / sum_r' r'^-s, r_e a seeded permutation of 1..E."""
+    ranks = rng.permutation(E).astype(np.float64) + 1.0
+    norm = np.sum(np.arange(1, E + 1, dtype=np.float64) ** (-s))
+    return (np.log(ranks ** (-s) / norm)).astype(np.float32)
+
+
+def make_inputs(wl, seed: int = 0, **overrides) -> Dict[str, np.ndarray]:
+    """Seeded inputs of workload ``wl`` (a name or a Workload).
+
+    Returns a dict with keys x, w_router, bias, w_gate, w_up, w_down,
+    ws_gate, ws_up, ws_down, w_sg (absent tensors are None) and the
+    workload itself under "wl".
+    """
+    if isinstance(wl, str):
+        wl = workload(wl, **overrides)
+    elif overrides:
+        wl = replace(wl, **overrides)
+    T, H, E, k, I, I_s = wl.T, wl.H, wl.E, wl.k, wl.I, wl.I_s
+    rng = np.random.default_rng(seed)
+    out: Dict[str, object] = {"wl": wl}
+    out["x"] = _draw_bf16(rng, (T, H), 1.0)
+    out["w_router"] = _draw_bf16(rng, (E, H), WEIGHT_SIGMA)
+    if wl.bias == "normal":
+        out["bias"] = (rng.standard_normal(E, dtype=np.float32) * np.float32(wl.bias_sigma)).astype(np.float32)
+    elif wl.bias == "zipf":
+        out["bias"] = zipf_log_pmf_bias(rng, E, wl.zipf_s)
+    else:
+        out["bias"] = None
+    out["w_gate"] = _draw_bf16(rng, (E, I, H), WEIGHT_SIGMA)
+    out["w_up"] = _draw_bf16(rng, (E, I, H), WEIGHT_SIGMA)
+    out["w_down"] = _draw_bf16(rng, (E, H, I), WEIGHT_SIGMA)
+    if I_s > 0:
+        out["ws_gate"] = _draw_bf16(rng, (I_s, H), WEIGHT_SIGMA)
+        out["ws_up"] = _draw_bf16(rng, (I_s, H), WEIGHT_SIGMA)
+        out["ws_down"] = _draw_bf16(rng, (H, I_s), WEIGHT_SIGMA)
+        out["w_sg"] = _draw_bf16(rng, (H,), WEIGHT_SIGMA)
+    else:
+        out["ws_gate"] = out["ws_up"] = out["ws_down"] = out["w_sg"] = None
+    if wl.tie_frac > 0.0:
+        n_tie = int(round(wl.tie_frac * T))
+        rows = np.sort(rng.choice(T, size=n_tie, replace=False)) if n_tie else np.zeros(0, np.int64)
+        out["x"][rows] = 0
+        out["tie_rows"] = rows.astype(np.int64)
+        b = out["bias"]
+        if b is None:
+            b = np.zeros(E, dtype=np.float32)
+            out["bias"] = b
+        # Equal values at the k-th/(k+1)-th boundary and inside the top-k, so
+        # the tokens with x_t = 0 (whose logits are exactly b) need the
+        # lowest-index rule to decide both the set and the order.
+        order = np.lexsort((np.arange(E), -b.astype(np.float64)))
+        if E > k:
+            b[order[k]] = b[order[k - 1]]
+        if k >= 3:
+            b[order[2]] = b[order[1]]
+    else:
+        out["tie_rows"] = np.zeros(0, dtype=np.int64)
+    return out
+
+
+def make_logits(T: int, E: int, seed: int = 0, sigma: float = 0.905, tie_frac: float = 0.01,
+                k: int = 8) -> np.ndarray:
+    """Random fp32 router logits with a share of rows carrying exact ties.
+
+    In a tie row the values at several positions are copied from other
+    positions of the same row (so some of them land on the k/k+1 boundary
+    and inside the top-k), and one position gets -0.0 paired with a +0.0.
+    """
+    rng = np.random.default_rng(seed)
+    lg = (rng.standard_normal((T, E), dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+    n_tie = int(round(tie_frac * T))
+    rows = rng.choice(T, size=n_tie, replace=False) if n_tie else []
+    for r in rows:
+        order = np.lexsort((np.arange(E), -lg[r].astype(np.float64)))
+        kk = min(k, E - 1)
+        if E > kk:
+            lg[r, order[kk]] = lg[r, order[kk - 1]]
+        if kk >= 3:
+            lg[r, order[2]] = lg[r, order[1]]
+        if E >= 4:
+            a, c = rng.choice(E, size=2, replace=False)
+            lg[r, a] = np.float32(-0.0)
+            lg[r, c] = np.float32(0.0)
+    return lg
+
+
+def content_hash(inputs: Dict[str, object]) -> str:
+    h = hashlib.sha256()
+    for key in ("x", "w_router", "bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down", "w_sg"):
+        v = inputs.get(key)
+        h.update(key.encode())
+        if v is not None:
+            h.update(np.ascontiguousarray(v).tobytes())
+    return h.hexdigest()[:16]
