@@ -15,12 +15,15 @@ Every array that the layer reads in BF16 is returned as ``uint16`` bit
 patterns (round-to-nearest-even from float32 draws); the router bias is
 float32.
 
-Draw order from ``numpy.random.default_rng(seed)`` (PCG64), each tensor
-drawn with ``standard_normal(dtype=float32)`` and scaled by its sigma:
-x, W_router, bias (only if the workload has one), W_gate, W_up, W_down,
-Ws_gate, Ws_up, Ws_down, w_sg (the four shared tensors only when the
-shared expert exists), then, for the skewed workload, the rows that are
-zeroed to force exact ties.
+Draws: every tensor has a fixed id (x 0, W_router 1, bias 2, W_gate 3,
+W_up 4, W_down 5, Ws_gate 6, Ws_up 7, Ws_down 8, w_sg 9, tie rows 10,
+Zipf rank permutation 11).  A tensor is flattened row-major and cut into
+blocks of 2**20 values; block b is ``standard_normal(dtype=float32)`` from
+``numpy.random.default_rng([seed, tensor_id, b])`` (PCG64 seeded by a
+SeedSequence over that triple), scaled by the tensor's sigma and rounded to
+bf16.  Blocks are independent, so they are drawn on several threads, and a
+tensor's values do not depend on the shapes of the other tensors (the
+weights of a workload are the same for every token count T).
 """
 from __future__ import annotations
 
@@ -82,20 +85,44 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _draw_bf16(rng: np.random.Generator, shape, sigma: float, chunk: int = 1 << 24) -> np.ndarray:
-    """standard_normal float32 draws scaled by sigma, rounded to bf16 bits.
+BLOCK = 1 << 20
+TENSOR_IDS = {"x": 0, "w_router": 1, "bias": 2, "w_gate": 3, "w_up": 4, "w_down": 5,
+              "ws_gate": 6, "ws_up": 7, "ws_down": 8, "w_sg": 9, "tie_rows": 10, "zipf_perm": 11}
+_POOL = None
 
-    Drawn in pieces of ``chunk`` values to bound the float32 temporary; the
-    generator's stream is consumed in the same order as one large draw.
-    """
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        import concurrent.futures
+        import os
+        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    return _POOL
+
+
+def _rng(seed: int, name: str, block: int = 0) -> np.random.Generator:
+    return np.random.default_rng([seed, TENSOR_IDS[name], block])
+
+
+def _draw_bf16(seed: int, name: str, shape, sigma: float) -> np.ndarray:
+    """Blockwise seeded normal draws scaled by sigma, rounded to bf16 bits."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, chunk):
-        m = min(chunk, n - s)
-        v = rng.standard_normal(m, dtype=np.float32)
+
+    def fill(b):
+        s0 = b * BLOCK
+        m = min(BLOCK, n - s0)
+        v = _rng(seed, name, b).standard_normal(m, dtype=np.float32)
         if sigma != 1.0:
             v *= np.float32(sigma)
-        out[s:s + m] = f32_to_bf16_bits(v)
+        out[s0:s0 + m] = f32_to_bf16_bits(v)
+
+    nb = (n + BLOCK - 1) // BLOCK
+    if nb <= 2:
+        for b in range(nb):
+            fill(b)
+    else:
+        list(_pool().map(fill, range(nb)))
     return out.reshape(shape)
 
 
@@ -118,29 +145,30 @@ def make_inputs(wl, seed: int = 0, **overrides) -> Dict[str, np.ndarray]:
     elif overrides:
         wl = replace(wl, **overrides)
     T, H, E, k, I, I_s = wl.T, wl.H, wl.E, wl.k, wl.I, wl.I_s
-    rng = np.random.default_rng(seed)
     out: Dict[str, object] = {"wl": wl}
-    out["x"] = _draw_bf16(rng, (T, H), 1.0)
-    out["w_router"] = _draw_bf16(rng, (E, H), WEIGHT_SIGMA)
+    out["x"] = _draw_bf16(seed, "x", (T, H), 1.0)
+    out["w_router"] = _draw_bf16(seed, "w_router", (E, H), WEIGHT_SIGMA)
     if wl.bias == "normal":
-        out["bias"] = (rng.standard_normal(E, dtype=np.float32) * np.float32(wl.bias_sigma)).astype(np.float32)
+        out["bias"] = (_rng(seed, "bias").standard_normal(E, dtype=np.float32)
+                       * np.float32(wl.bias_sigma)).astype(np.float32)
     elif wl.bias == "zipf":
-        out["bias"] = zipf_log_pmf_bias(rng, E, wl.zipf_s)
+        out["bias"] = zipf_log_pmf_bias(_rng(seed, "zipf_perm"), E, wl.zipf_s)
     else:
         out["bias"] = None
-    out["w_gate"] = _draw_bf16(rng, (E, I, H), WEIGHT_SIGMA)
-    out["w_up"] = _draw_bf16(rng, (E, I, H), WEIGHT_SIGMA)
-    out["w_down"] = _draw_bf16(rng, (E, H, I), WEIGHT_SIGMA)
+    out["w_gate"] = _draw_bf16(seed, "w_gate", (E, I, H), WEIGHT_SIGMA)
+    out["w_up"] = _draw_bf16(seed, "w_up", (E, I, H), WEIGHT_SIGMA)
+    out["w_down"] = _draw_bf16(seed, "w_down", (E, H, I), WEIGHT_SIGMA)
     if I_s > 0:
-        out["ws_gate"] = _draw_bf16(rng, (I_s, H), WEIGHT_SIGMA)
-        out["ws_up"] = _draw_bf16(rng, (I_s, H), WEIGHT_SIGMA)
-        out["ws_down"] = _draw_bf16(rng, (H, I_s), WEIGHT_SIGMA)
-        out["w_sg"] = _draw_bf16(rng, (H,), WEIGHT_SIGMA)
+        out["ws_gate"] = _draw_bf16(seed, "ws_gate", (I_s, H), WEIGHT_SIGMA)
+        out["ws_up"] = _draw_bf16(seed, "ws_up", (I_s, H), WEIGHT_SIGMA)
+        out["ws_down"] = _draw_bf16(seed, "ws_down", (H, I_s), WEIGHT_SIGMA)
+        out["w_sg"] = _draw_bf16(seed, "w_sg", (H,), WEIGHT_SIGMA)
     else:
         out["ws_gate"] = out["ws_up"] = out["ws_down"] = out["w_sg"] = None
     if wl.tie_frac > 0.0:
         n_tie = int(round(wl.tie_frac * T))
-        rows = np.sort(rng.choice(T, size=n_tie, replace=False)) if n_tie else np.zeros(0, np.int64)
+        rows = (np.sort(_rng(seed, "tie_rows").choice(T, size=n_tie, replace=False)) if n_tie
+                else np.zeros(0, np.int64))
         out["x"][rows] = 0
         out["tie_rows"] = rows.astype(np.int64)
         b = out["bias"]

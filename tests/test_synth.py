@@ -11,11 +11,20 @@ def test_bf16_round_to_nearest_even():
     assert got.tolist() == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 1.0, 3.140625]
 
 
-def test_chunked_draws_match_one_draw():
-    a = synth._draw_bf16(np.random.default_rng(5), (1000, 37), 0.02, chunk=997)
-    b = synth.f32_to_bf16_bits(np.random.default_rng(5).standard_normal(37000, dtype=np.float32)
-                               * np.float32(0.02)).reshape(1000, 37)
-    assert np.array_equal(a, b)
+def test_blockwise_draws():
+    n = synth.BLOCK * 2 + 37
+    a = synth._draw_bf16(5, "w_up", (n,), 0.02)
+    for b in range(3):
+        m = min(synth.BLOCK, n - b * synth.BLOCK)
+        ref = synth.f32_to_bf16_bits(np.random.default_rng([5, synth.TENSOR_IDS["w_up"], b])
+                                     .standard_normal(m, dtype=np.float32) * np.float32(0.02))
+        assert np.array_equal(a[b * synth.BLOCK:b * synth.BLOCK + m], ref)
+
+
+def test_weights_do_not_depend_on_T():
+    a = synth.make_inputs(synth.workload("prefill1k", T=3, E=4), seed=0)
+    b = synth.make_inputs(synth.workload("prefill1k", T=9, E=4), seed=0)
+    assert np.array_equal(a["w_down"], b["w_down"]) and np.array_equal(a["x"], b["x"][:3])
 
 
 def test_deterministic_and_seeded():
