@@ -1,0 +1,262 @@
+"""Benchmark of the sparse MoE FFN layer on one MI355X.
+
+One step = one pass of the whole prefill path (router + top-k, align, grouped
+gate/up GEMM with SwiGLU, grouped down GEMM, combine with the gated shared
+expert) over the 8192-token workload (hidden 2048, 256 experts, top-8, FFN
+512, shared expert 512, router bias ~ N(0,1)); weights and tokens are already
+in HBM when the timed region starts.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Also reported in the same line: the single-token decode path (GB/s against
+HBM), a per-stage time breakdown, the roofline of the dominant kernel
+(grouped gate/up GEMM, timed with HIP events on its launch stream) and the CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at T=8192 (MFMA % of peak); T=1 decode GB/s (% of HBM peak)"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense BF16 MFMA (AMD specification)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(T, H, E, k, I, I_s):
+    """Flops of the layer per call (what the method must compute, no padding)."""
+    routed = 6 * T * k * H * I          # gate, up (2 * 2HI) and down (2HI) per assignment
+    shared = 6 * T * H * I_s
+    router = 2 * T * H * E + 2 * T * H  # logits + shared gate
+    gate_up = 4 * T * H * (k * I + I_s)
+    return routed + shared + router, gate_up
+
+
+def decode_bytes(H, E, k, I, I_s):
+    """Bytes one T=1 call must move: router, shared gate, k experts, shared expert, x, y."""
+    return 2 * (E * H + H + k * 3 * H * I + 3 * H * I_s + H + H)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across prefill steps")
+    ap.add_argument("--decode-steps", type=int, default=64, help="decode calls per captured graph")
+    ap.add_argument("--decode-copies", type=int, default=16, help="weight copies rotated across decode calls")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="oracle sample tokens (0: sized to ~15 s)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_moe_layer_03_amd import moe, synth
+    from sparse_moe_layer_03_amd.layer import DeviceLayer, to_device_bf16
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.lib()
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(0)
+
+    # ------------------------------------------------------------ prefill
+    wl = synth.workload("prefill8k")
+    T, H, E, k, I, I_s = wl.T, wl.H, wl.E, wl.k, wl.I, wl.I_s
+    t0 = time.time()
+    inp = synth.make_inputs(wl, seed=0)
+    log(f"[bench] inputs drawn in {time.time() - t0:.1f}s; uploading")
+    base = DeviceLayer.from_inputs(inp, dev)
+    layers = [base]
+    for _ in range(max(0, args.copies - 1)):
+        c = DeviceLayer.__new__(DeviceLayer)
+        c.__dict__.update(base.__dict__)
+        c.w = {key: (None if v is None else v.clone()) for key, v in base.w.items()}
+        c._ws, c._ws_bytes = base.workspace(T)
+        layers.append(c)
+    x = to_device_bf16(inp["x"], dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws, ws_bytes = base.workspace(T)
+    for c in layers:
+        c._ws, c._ws_bytes = ws, ws_bytes
+    stream = torch.cuda.current_stream()
+
+    flops, gate_up_flops = algorithmic(T, H, E, k, I, I_s)
+    for i in range(args.warmup):
+        layers[i % len(layers)].forward(x, y)
+    torch.cuda.synchronize()
+
+    # timed region 1: the product entry point, K steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        layers[i % len(layers)].forward(x, y)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # timed region 2: the same kernels stage by stage, HIP events around each launch
+    bufs = base.alloc_stage_buffers(T)
+    names = ("route", "align", "gate_up", "down", "combine")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        base.run_stages(x, bufs)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        lay = layers[i % len(layers)]
+        e = evs[i]
+        e[0].record(stream)
+        lay.run_route(x, bufs, with_logits=False)
+        e[1].record(stream)
+        lay.run_align(T, bufs)
+        e[2].record(stream)
+        lay.run_gate_up(x, bufs)
+        e[3].record(stream)
+        lay.run_down(T, bufs)
+        e[4].record(stream)
+        lay.run_combine(T, bufs)
+        e[5].record(stream)
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                for j, n in enumerate(names)}
+    counts = np.bincount(bufs["ids"].cpu().numpy().ravel(), minlength=E)
+    BM = moe.moe_align_tile_rows(T, E, k)
+    padded_rows = int(np.sum(np.ceil(counts / BM) * BM))
+    gu_ms = stage_ms["gate_up"]
+    achieved = gate_up_flops / (gu_ms * 1e-3) / 1e12
+    log(f"[bench] prefill T={T}: {ms:.3f} ms/step ({T / ms * 1e3 / 1e6:.2f} M tok/s); stages "
+        + ", ".join(f"{n} {v * 1e3:.1f}us" for n, v in stage_ms.items()))
+
+    out = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long prefill: T=8192 tokens, hidden 2048, 256 experts, top-8, expert FFN 512, "
+                               "shared expert 512 gated by sigmoid(x.w_sg), router bias ~ N(0,1)",
+                   "T": T, "H": H, "E": E, "k": k, "I": I, "I_s": I_s, "tile_rows": BM,
+                   "weight_copies": len(layers)},
+        "layer_tflops": flops / (ms * 1e-3) / 1e12,
+        "layer_mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "stage_us": {n: v * 1e3 for n, v in stage_ms.items()},
+        "padding_overhead": padded_rows / (T * k) - 1.0,
+        "roofline": {"kernel": "grouped_gemm_gate_up (SwiGLU epilogue, routed + shared tiles)",
+                     "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": gate_up_flops, "avg_launch_us": gu_ms * 1e3},
+        "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+    }
+    del layers, bufs
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- decode
+    if not args.no_decode:
+        dwl = synth.workload("decode")
+        dinp = synth.make_inputs(dwl, seed=0, reuse=inp)
+        dbase = DeviceLayer.from_inputs(dinp, dev)
+        dcopies = [dbase.w]
+        for _ in range(max(0, args.decode_copies - 1)):
+            dcopies.append({key: (None if v is None else v.clone()) for key, v in dbase.w.items()})
+        nx = args.decode_steps
+        xs = to_device_bf16(synth._draw_bf16(1, "x", (nx, H), 1.0), dev)
+        ys = torch.empty((nx, H), dtype=torch.bfloat16, device=dev)
+        dws, dws_bytes = dbase.workspace(1)
+
+        def dstep(i):
+            W = dcopies[i % len(dcopies)]
+            moe.moe_forward(xs[i:i + 1], W["w_router"], None, W["w_gate"], W["w_up"], W["w_down"], W["ws_gate"],
+                            W["ws_up"], W["ws_down"], W["w_sg"], 1, H, E, k, I, I_s, ys[i:i + 1], dws, dws_bytes)
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(nx):
+                dstep(i)
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(nx):
+                dstep(i)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = 5
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for _ in range(reps):
+            g.replay()
+        d1.record()
+        torch.cuda.synchronize()
+        dus = d0.elapsed_time(d1) * 1e3 / (reps * nx)
+        nbytes = decode_bytes(H, E, k, I, I_s)
+        gbs = nbytes / (dus * 1e-6) / 1e9
+        # eager launches (host launch overhead included) for context
+        torch.cuda.synchronize()
+        d0.record()
+        for i in range(nx):
+            dstep(i)
+        d1.record()
+        torch.cuda.synchronize()
+        eager_us = d0.elapsed_time(d1) * 1e3 / nx
+        out["decode"] = {"workload": "decode step: T=1, hidden 2048, 256 experts, top-8, FFN 512, shared expert 512",
+                         "us_per_call": dus, "GB_per_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+                         "bytes_per_call": nbytes, "weight_copies": len(dcopies), "timing": "HIP graph of "
+                         f"{nx} calls, {reps} replays", "eager_us_per_call": eager_us}
+        log(f"[bench] decode: {dus:.2f} us/call, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f}% of HBM); "
+            f"eager {eager_us:.2f} us/call")
+        del dcopies, g
+        torch.cuda.empty_cache()
+
+    # -------------------------------------------------------- cpu baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        sample = args.cpu_sample
+        if sample <= 0:
+            probe = 16
+            sub = dict(inp)
+            sub["x"] = inp["x"][:probe]
+            t1 = time.time()
+            oracle.forward(sub)
+            per_tok = (time.time() - t1) / probe
+            sample = int(min(T, max(probe, 15.0 / max(per_tok, 1e-6))))
+        sub = dict(inp)
+        sub["x"] = inp["x"][:sample]
+        t1 = time.time()
+        oracle.forward(sub)
+        secs = time.time() - t1
+        out["cpu_baseline"] = {"value": sample / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"first {sample} of the {T} tokens of the same workload, whole layer "
+                                         f"(route, align, expert FFNs, shared expert, combine), {secs:.1f} s"}
+        log(f"[bench] cpu oracle: {sample / secs:.1f} tokens/s on {threads} threads ({sample} tokens, {secs:.1f}s)")
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

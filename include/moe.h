@@ -1,0 +1,187 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts FFN layer.
+ *
+ * The layer: a router scores every expert for every token, the k best experts
+ * are kept, each kept expert's SwiGLU FFN is evaluated on only the tokens
+ * routed to it, and the expert outputs are summed with renormalised softmax
+ * weights, plus a sigmoid-gated shared expert.  Sources: kongchang.com
+ * "GFX1151 engine" (section on the MoE kernel: many expert sub-networks,
+ * only a few active per step, sparse routing changes the compute and memory
+ * pattern); guanjiawei.ai "AIMA AMD395 Qwen3.6-35B-A3B" (section on the data
+ * path: the block runs as a selected-expert MoE, i.e. only chosen experts are
+ * computed).  The pages give no formulas; the arithmetic below is the plain
+ * reading of a Qwen3-class MoE block.
+ *
+ * Conventions for every entry point
+ *   - Tensors are DEVICE pointers (HIP device memory), row-major, contiguous,
+ *     16-byte aligned.  BF16 values are passed as uint16_t bit patterns.
+ *   - Weight matrices use the [out, in] convention, so the reduction index is
+ *     contiguous: W_router [E,H], W_gate/W_up [E,I,H], W_down [E,H,I],
+ *     Ws_gate/Ws_up [I_s,H], Ws_down [H,I_s], w_sg [H].
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work and return; nothing is synchronised and no value is read
+ *     back to the host, so a call can be captured in a HIP graph.
+ *   - The caller owns every buffer, including `workspace`.  The library never
+ *     allocates or frees device memory and keeps no state between calls
+ *     except a per-device cached architecture check.
+ *   - Argument errors are reported before anything is enqueued.  No C++
+ *     exception crosses this boundary.  A status other than MOE_OK leaves the
+ *     outputs unspecified; moe_last_error() gives a message (thread-local).
+ *   - T = 0 is a successful no-op.
+ *   - Supported shapes: 1 <= E <= 256, 1 <= k <= min(E, 16), H % 256 == 0,
+ *     I % 128 == 0, I_s % 128 == 0 (I_s = 0: no shared expert), T <= 2^24.
+ *   - Results are deterministic: identical inputs give bitwise-identical
+ *     outputs (no floating-point atomics anywhere).
+ */
+#ifndef MOE355_MOE_H
+#define MOE355_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)        /* a required pointer is NULL                         */
+#define MOE_ERR_SHAPE (-2)       /* unsupported or inconsistent sizes                  */
+#define MOE_ERR_ALIGN (-3)       /* a tensor pointer is not 16-byte aligned            */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace smaller than moe_workspace_size()        */
+#define MOE_ERR_ARCH (-5)        /* the current device is not gfx950 / no device       */
+#define MOE_ERR_HIP (-6)         /* a HIP launch failed; see moe_last_error()          */
+
+/* Name of a status code ("MOE_OK", "MOE_ERR_SHAPE", ...). */
+const char* moe_status_str(int status);
+
+/* Message describing the last error returned on this host thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * Rows per expert tile chosen for T tokens (all experts' rows are padded to a
+ * multiple of it).  Depends only on (T, E, k).
+ */
+int moe_align_tile_rows(int T, int E, int k);
+
+/*
+ * Upper bound of padded rows for T tokens: T*k + min(E, T*k) * (BM - 1),
+ * BM = moe_align_tile_rows(T, E, k).  Sizes `sorted` in moe_align.
+ */
+int64_t moe_align_max_rows(int T, int E, int k);
+
+/* Upper bound of tile-table entries written by moe_align (routed + shared). */
+int64_t moe_align_max_tiles(int T, int E, int k);
+
+/*
+ * Bytes of device workspace moe_forward needs for these sizes (worst-case
+ * padding included).  Returns 0 for unsupported sizes.
+ */
+size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s);
+
+/*
+ * The whole layer:  y = sum_{j<k} w[t,j] * FFN_{ids[t,j]}(x_t) + s_t * FFN_s(x_t)
+ *
+ *   logits[t,e] = sum_h x[t,h] W_router[e,h] (+ router_bias[e]), fp32 accumulation
+ *   ids[t,:]    = the k experts with the largest logits, ordered by
+ *                 (logit descending, expert index ascending) -- exact ties go
+ *                 to the lowest index
+ *   w[t,j]      = softmax(logits[t])[ids[t,j]] / sum_j' softmax(logits[t])[ids[t,j']]
+ *   FFN_e(x)    = W_down[e] (silu(W_gate[e] x) * (W_up[e] x)),  silu(z) = z/(1+e^-z)
+ *   s_t         = sigmoid(x_t . w_sg);  FFN_s uses Ws_gate, Ws_up, Ws_down
+ *
+ * Inputs:  x [T,H] bf16; W_router [E,H] bf16; router_bias [E] fp32 or NULL;
+ *          W_gate, W_up [E,I,H] bf16; W_down [E,H,I] bf16;
+ *          Ws_gate, Ws_up [I_s,H], Ws_down [H,I_s], w_sg [H] bf16 -- all four
+ *          NULL with I_s = 0, or all four set with I_s > 0.
+ * Output:  y [T,H] bf16 (fp32 sum rounded to nearest even).
+ * Workspace: at least moe_workspace_size(T,H,E,k,I,I_s) bytes, 256-byte aligned.
+ * Internally the call runs moe_route, moe_align, moe_grouped_gate_up,
+ * moe_grouped_down and moe_combine (or the single-token decode kernels when
+ * T == 1) on `stream`.
+ */
+int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
+                const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
+                const uint16_t* w_sg, int T, int H, int E, int k, int I, int I_s,
+                uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Router stage: logits (fp32 accumulation of bf16 products), optional bias,
+ * top-k by (logit desc, index asc), renormalised softmax weights, and the
+ * shared-expert gate s = sigmoid(x . w_sg).
+ *   Outputs: ids [T,k] int32, w [T,k] fp32; s [T] fp32 (required iff w_sg is
+ *   given, else ignored); logits [T,E] fp32 (nullable: written when given,
+ *   including the bias).
+ */
+int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
+              const uint16_t* w_sg, int T, int H, int E, int k,
+              int32_t* ids, float* w, float* s, float* logits, void* stream);
+
+/*
+ * Top-k and weights on caller-supplied fp32 logits [T,E] (same selection
+ * rule and weights as moe_route; -0 and +0 compare equal).
+ */
+int moe_route_from_logits(const float* logits, int T, int E, int k,
+                          int32_t* ids, float* w, void* stream);
+
+/*
+ * Expert histogram, prefix scan and stable permutation into padded tiles.
+ *   ids [T,k] int32 (values in [0,E)).  BM = moe_align_tile_rows(T,E,k).
+ *   counts [E]      number of assignments routed to each expert
+ *   pad_off [E+1]   first padded row of each expert; pad_off[E] = total rows
+ *                   (expert e owns rows pad_off[e] .. pad_off[e]+ceil(counts[e]/BM)*BM)
+ *   sorted [moe_align_max_rows]  assignment a = t*k + j held by each padded row,
+ *                   ascending a within an expert; -1 marks a padding row
+ *   inv [T*k]       padded row of each assignment
+ *   tiles [2*moe_align_max_tiles]  (expert, first row) per tile of BM rows:
+ *                   first the routed tiles in expert order, then ceil(T/BM)
+ *                   shared-expert tiles (expert = E, first row = first token)
+ *                   when with_shared != 0
+ *   n_tiles [2]     number of routed tiles, total number of tiles
+ *   scratch         at least moe_align_scratch_size(T,E,k) bytes
+ */
+size_t moe_align_scratch_size(int T, int E, int k);
+int moe_align(const int32_t* ids, int T, int E, int k, int with_shared,
+              int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv,
+              int32_t* tiles, int32_t* n_tiles, void* scratch, size_t scratch_bytes, void* stream);
+
+/*
+ * Grouped gate/up GEMM with fused SwiGLU over the tiles of moe_align:
+ *   for a routed padded row p holding assignment a (token t = a / k) of expert e:
+ *     h[p,i] = bf16( silu(sum_h x[t,h] W_gate[e,i,h]) * sum_h x[t,h] W_up[e,i,h] )
+ *   (padding rows get 0); for every token t when I_s > 0:
+ *     h_s[t,i] = bf16( silu(x_t . Ws_gate[i]) * (x_t . Ws_up[i]) )
+ *   h [moe_align_max_rows, I] bf16, h_s [T, I_s] bf16 (NULL iff I_s == 0).
+ */
+int moe_grouped_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up,
+                        const uint16_t* ws_gate, const uint16_t* ws_up,
+                        const int32_t* sorted, const int32_t* tiles, const int32_t* n_tiles,
+                        int T, int H, int E, int k, int I, int I_s,
+                        uint16_t* h, uint16_t* h_s, void* stream);
+
+/*
+ * Grouped down GEMM over the routed tiles:
+ *   o[p,c] = bf16( sum_i h[p,i] W_down[e,c,i] ) for every non-padding row p.
+ *   o [moe_align_max_rows, H] bf16 (padding rows are not written).
+ */
+int moe_grouped_down(const uint16_t* h, const uint16_t* w_down,
+                     const int32_t* sorted, const int32_t* tiles, const int32_t* n_tiles,
+                     int T, int H, int E, int k, int I, uint16_t* o, void* stream);
+
+/*
+ * Deterministic, atomic-free combine, fused with the shared expert's down
+ * projection when I_s > 0:
+ *   y[t,c] = bf16( (((w[t,0] o[inv[t*k]] + w[t,1] o[inv[t*k+1]]) + ...)
+ *                   + w[t,k-1] o[inv[t*k+k-1]]) + s[t] (sum_i h_s[t,i] Ws_down[c,i]) )
+ *   in fp32, j ascending, then the shared term.
+ *   h_s, ws_down and s are NULL iff I_s == 0.
+ */
+int moe_combine(const uint16_t* o, const int32_t* inv, const float* w,
+                const uint16_t* h_s, const uint16_t* ws_down, const float* s,
+                int T, int H, int k, int I_s, uint16_t* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE355_MOE_H */

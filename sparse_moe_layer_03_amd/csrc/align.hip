@@ -1,0 +1,158 @@
+// Align stage: expert histogram, prefix scan and a stable permutation of the
+// token->expert assignments into per-expert row ranges padded to whole tiles.
+//
+// The layer evaluates each expert's FFN only on the tokens routed to it
+// (guanjiawei.ai "AIMA AMD395 Qwen3.6-35B-A3B", data path: selected-expert
+// MoE); grouping the assignments by expert turns that into one dense GEMM
+// tile sequence per expert (kongchang.com "GFX1151 engine", MoE kernel
+// section: sparse routing changes the access pattern, which this grouping
+// makes regular again).
+//
+// Result (bit-exact, independent of scheduling):
+//   counts[e]   number of assignments a = t*k + j with ids[a] = e
+//   pad_off[e]  sum over e' < e of ceil(counts[e'] / BM) * BM
+//   sorted[pad_off[e] + r] = the r-th assignment of expert e in ascending a;
+//                            -1 for the padding rows of the expert's last tile
+//   inv[a]      the padded row that holds assignment a
+//   tiles       (expert, first row) per BM-row tile, experts ascending, then
+//               the shared-expert tiles (E, first token)
+//
+// Three kernels: per-chunk histograms (LDS integer counters: the counts do
+// not depend on the order of the increments), one workgroup that scans the
+// chunk histograms and the expert totals, and a scatter in which every chunk
+// ranks its assignments in order with wave ballots (no ordering atomics).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int CH = 1024;  // assignments per chunk
+
+__global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                         int32_t* __restrict__ chunk_hist) {
+  __shared__ int32_t hist[kMaxE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * CH;
+  const int a1 = min(a0 + CH, n);
+  for (int a = a0 + tid; a < a1; a += 256) atomicAdd(&hist[ids[a]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) chunk_hist[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Exclusive scan of one value per thread over the 256 threads of a block.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sbuf, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) sbuf[wave] = incl;
+  __syncthreads();
+  int wave_off = 0;
+  for (int w = 0; w < wave; ++w) wave_off += sbuf[w];
+  total = sbuf[0] + sbuf[1] + sbuf[2] + sbuf[3];
+  __syncthreads();
+  return wave_off + incl - v;
+}
+
+__global__ __launch_bounds__(256) void align_scan_kernel(int32_t* __restrict__ chunk_hist, int n_chunks, int T,
+                                                         int E, int BM, int with_shared,
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ pad_off,
+                                                         int32_t* __restrict__ sorted, int32_t* __restrict__ tiles,
+                                                         int32_t* __restrict__ n_tiles) {
+  __shared__ int sbuf[4];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      int hv = chunk_hist[(size_t)c * E + e];
+      chunk_hist[(size_t)c * E + e] = run;  // exclusive offset of chunk c within expert e
+      run += hv;
+    }
+    counts[e] = run;
+  }
+  const int ntile = (e < E) ? (run + BM - 1) / BM : 0;
+  int total_tiles;
+  const int tile_off = block_exclusive_scan(ntile, sbuf, total_tiles);
+  const int rows_off = tile_off * BM;  // padded rows are whole tiles
+  if (e < E) {
+    pad_off[e] = rows_off;
+    for (int i = 0; i < ntile; ++i) {
+      tiles[2 * (tile_off + i)] = e;
+      tiles[2 * (tile_off + i) + 1] = rows_off + i * BM;
+    }
+    for (int r = run; r < ntile * BM; ++r) sorted[rows_off + r] = -1;
+  }
+  if (e == 0) pad_off[E] = total_tiles * BM;
+  const int n_shared = with_shared ? (T + BM - 1) / BM : 0;
+  for (int i = e; i < n_shared; i += 256) {
+    tiles[2 * (total_tiles + i)] = E;
+    tiles[2 * (total_tiles + i) + 1] = i * BM;
+  }
+  if (e == 0) {
+    n_tiles[0] = total_tiles;
+    n_tiles[1] = total_tiles + n_shared;
+  }
+}
+
+__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                            const int32_t* __restrict__ chunk_off,
+                                                            const int32_t* __restrict__ pad_off,
+                                                            int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
+  __shared__ int32_t base[kMaxE];
+  __shared__ int32_t wcnt[4][kMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int a0 = blockIdx.x * CH;
+  const int a1 = min(a0 + CH, n);
+  for (int e = tid; e < E; e += 256) base[e] = pad_off[e] + chunk_off[(size_t)blockIdx.x * E + e];
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int s0 = a0; s0 < a1; s0 += 256) {
+    for (int i = tid; i < 4 * kMaxE; i += 256) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const int a = s0 + tid;
+    const bool valid = a < a1;
+    const int e = valid ? ids[a] : 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    if (!valid) peers = 0;
+    const int rank = __popcll(peers & lt_mask);
+    if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);  // lowest peer reports the group size
+    __syncthreads();
+    if (valid) {
+      int pos = base[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+      sorted[pos] = a;
+      inv[a] = pos;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += 256) base[ee] += wcnt[0][ee] + wcnt[1][ee] + wcnt[2][ee] + wcnt[3][ee];
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int align_num_chunks(int T, int k) { return (int)(((int64_t)T * k + CH - 1) / CH); }
+
+hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BM, int with_shared, int32_t* counts,
+                        int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles, int32_t* n_tiles,
+                        int32_t* scratch, hipStream_t st) {
+  const int n = T * k;
+  const int nc = align_num_chunks(T, k);
+  hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, scratch);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(256), 0, st, scratch, nc, T, E, BM, with_shared, counts,
+                     pad_off, sorted, tiles, n_tiles);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, scratch, pad_off, sorted, inv);
+  return hipGetLastError();
+}
+
+}  // namespace moe

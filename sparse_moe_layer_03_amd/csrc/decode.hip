@@ -1,0 +1,280 @@
+// Single-token (T = 1) decode path of the sparse MoE layer on gfx950.
+//
+// At batch-1 decode the layer is a set of matrix-vector products and is bound
+// by HBM bandwidth: the bytes to move are the router, the k selected experts'
+// weights and the shared expert (guanjiawei.ai "AIMA AMD395 Qwen3.6-35B-A3B",
+// data path: only the selected experts are computed; kongchang.com
+// "GFX1151 engine", MoE kernel section: sparse routing changes the memory
+// access pattern of token generation).  Every weight row is read once, by one
+// wavefront, with 16-byte loads (64 lanes x 16 B = 1 KiB per instruction),
+// and all loads of a wavefront are issued before its reductions.
+//
+//   D1 router + shared expert: wave per router row (logit) and per shared
+//      (gate, up) row pair; one wave for the shared gate s = sigmoid(x.w_sg)
+//   D2 top-k + renormalised weights (one wavefront, same rule as prefill)
+//   D3 gate/up of the k selected experts: wave per (expert, row) pair,
+//      h = silu(g) * u kept in fp32
+//   D4 down projection + combine: wave per output column, k + 1 rows of
+//      W_down / Ws_down, y = sum_j w_j o_j + s o_s in fp32 -> bf16
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+struct DecodeWs {
+  float* logits;  // [E]
+  int32_t* ids;   // [k]
+  float* w;       // [k]
+  float* s;       // [1]
+  float* hs;      // [I_s]
+  float* h;       // [k * I]
+};
+
+constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+DecodeWs carve(void* base, int H, int E, int k, int I, int I_s) {
+  (void)H;
+  char* p = static_cast<char*>(base);
+  DecodeWs d;
+  d.logits = reinterpret_cast<float*>(p);
+  p += align256((size_t)E * 4);
+  d.ids = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)k * 4);
+  d.w = reinterpret_cast<float*>(p);
+  p += align256((size_t)k * 4);
+  d.s = reinterpret_cast<float*>(p);
+  p += 256;
+  d.hs = reinterpret_cast<float*>(p);
+  p += align256((size_t)(I_s > 0 ? I_s : 1) * 4);
+  d.h = reinterpret_cast<float*>(p);
+  return d;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    s += bf16_to_f32((uint16_t)(a[q] & 0xffff)) * bf16_to_f32((uint16_t)(b[q] & 0xffff));
+    s += bf16_to_f32((uint16_t)(a[q] >> 16)) * bf16_to_f32((uint16_t)(b[q] >> 16));
+  }
+  return s;
+}
+
+// x (H bf16) -> LDS as 16-byte chunks; H/8 <= 1024 chunks.
+__device__ __forceinline__ void stage_x(const uint16_t* x, int H, u32x4* sx) {
+  for (int c = threadIdx.x; c < H / 8; c += 256) sx[c] = reinterpret_cast<const u32x4*>(x)[c];
+  __syncthreads();
+}
+
+// Dot products of x with one or two bf16 rows of length H, all loads issued
+// in groups of 4 chunks per lane before the arithmetic.
+__device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* r0, const uint16_t* r1, int H, int lane,
+                                         float& d0, float& d1) {
+  const int nch = H / 8;
+  d0 = 0.0f;
+  d1 = 0.0f;
+  for (int base = 0; base < nch; base += 256) {
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int c = base + q * 64 + lane;
+      if (c < nch) {
+        a[q] = reinterpret_cast<const u32x4*>(r0)[c];
+        if (r1) b[q] = reinterpret_cast<const u32x4*>(r1)[c];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int c = base + q * 64 + lane;
+      if (c < nch) {
+        u32x4 xv = sx[c];
+        d0 += dot8(xv, a[q]);
+        if (r1) d1 += dot8(xv, b[q]);
+      }
+    }
+  }
+  d0 = wave_sum(d0);
+  d1 = wave_sum(d1);
+}
+
+__global__ __launch_bounds__(256) void decode_router_shared_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
+    const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up, const uint16_t* __restrict__ w_sg,
+    int H, int E, int I_s, DecodeWs d) {
+  __shared__ u32x4 sx[1024];
+  stage_x(x, H, sx);
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  float d0, d1;
+  if (row < E) {
+    row_dots(sx, wr + (size_t)row * H, nullptr, H, lane, d0, d1);
+    if (lane == 0) {
+      float v = d0 + (bias ? bias[row] : 0.0f);
+      if (v == 0.0f) v = 0.0f;
+      d.logits[row] = v;
+    }
+  } else if (row < E + I_s) {
+    int i = row - E;
+    row_dots(sx, ws_gate + (size_t)i * H, ws_up + (size_t)i * H, H, lane, d0, d1);
+    if (lane == 0) d.hs[i] = silu(d0) * d1;
+  } else if (row == E + I_s && I_s > 0) {
+    row_dots(sx, w_sg, nullptr, H, lane, d0, d1);
+    if (lane == 0) d.s[0] = 1.0f / (1.0f + expf(-d0));
+  }
+}
+
+__global__ __launch_bounds__(64) void decode_topk_kernel(int E, int k, DecodeWs d) {
+  const int lane = threadIdx.x;
+  float v[4];
+  bool valid[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = lane + 64 * q;
+    valid[q] = e < E;
+    v[q] = valid[q] ? d.logits[e] : 0.0f;
+  }
+  int sel_e = -1;
+  float sel_v = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (valid[q] && (be == 0x7fffffff || v[q] > bv)) {
+        bv = v[q];
+        be = lane + 64 * q;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      float ov = __shfl_xor(bv, off);
+      int oe = __shfl_xor(be, off);
+      bool take = (oe != 0x7fffffff) && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+      if (take) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if (lane == r) {
+      sel_e = be;
+      sel_v = bv;
+    }
+    if ((be & 63) == lane) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q == (be >> 6)) valid[q] = false;
+    }
+  }
+  float m = __shfl(sel_v, 0);
+  float ex = (lane < k) ? expf(sel_v - m) : 0.0f;
+  float sum = 0.0f;
+  for (int r = 0; r < k; ++r) sum += __shfl(ex, r);
+  if (lane < k) {
+    d.ids[lane] = sel_e;
+    d.w[lane] = ex / sum;
+  }
+}
+
+__global__ __launch_bounds__(256) void decode_gate_up_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ w_gate,
+                                                             const uint16_t* __restrict__ w_up, int H, int k, int I,
+                                                             DecodeWs d) {
+  __shared__ u32x4 sx[1024];
+  stage_x(x, H, sx);
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // j * I + i
+  if (row >= k * I) return;
+  const int j = row / I, i = row % I;
+  const int e = d.ids[j];
+  float g, u;
+  row_dots(sx, w_gate + ((size_t)e * I + i) * H, w_up + ((size_t)e * I + i) * H, H, lane, g, u);
+  if (lane == 0) d.h[row] = silu(g) * u;
+}
+
+__global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __restrict__ w_down,
+                                                          const uint16_t* __restrict__ ws_down, int H, int k, int I,
+                                                          int I_s, DecodeWs d, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= H) return;
+  float part[kMaxK + 1];
+#pragma unroll
+  for (int j = 0; j <= kMaxK; ++j) part[j] = 0.0f;
+  int ids[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) ids[j] = (j < k) ? d.ids[j] : 0;
+  // routed rows: W_down[e_j, c, :], chunks of 8 along I
+  for (int base = 0; base < I / 8; base += 64) {
+    const int ch = base + lane;
+    u32x4 wv[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k && ch < I / 8)
+        wv[j] = reinterpret_cast<const u32x4*>(w_down + ((size_t)ids[j] * H + c) * I)[ch];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k && ch < I / 8) {
+        const float4* hp = reinterpret_cast<const float4*>(d.h + (size_t)j * I + ch * 8);
+        float4 h0 = hp[0], h1 = hp[1];
+        float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          part[j] += hv[2 * q] * bf16_to_f32((uint16_t)(wv[j][q] & 0xffff));
+          part[j] += hv[2 * q + 1] * bf16_to_f32((uint16_t)(wv[j][q] >> 16));
+        }
+      }
+    }
+  }
+  if (I_s > 0) {
+    for (int base = 0; base < I_s / 8; base += 64) {
+      const int ch = base + lane;
+      if (ch < I_s / 8) {
+        u32x4 wv = reinterpret_cast<const u32x4*>(ws_down + (size_t)c * I_s)[ch];
+        const float4* hp = reinterpret_cast<const float4*>(d.hs + ch * 8);
+        float4 h0 = hp[0], h1 = hp[1];
+        float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          part[kMaxK] += hv[2 * q] * bf16_to_f32((uint16_t)(wv[q] & 0xffff));
+          part[kMaxK] += hv[2 * q + 1] * bf16_to_f32((uint16_t)(wv[q] >> 16));
+        }
+      }
+    }
+  }
+  float yv = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < k) yv += d.w[j] * wave_sum(part[j]);  // rank order
+  if (I_s > 0) yv += d.s[0] * wave_sum(part[kMaxK]);
+  if (lane == 0) y[c] = f32_to_bf16(yv);
+}
+
+}  // namespace
+
+size_t decode_workspace_size(int H, int E, int k, int I, int I_s) {
+  (void)H;
+  return align256((size_t)E * 4) + 2 * align256((size_t)k * 4) + 256 + align256((size_t)(I_s > 0 ? I_s : 1) * 4) +
+         align256((size_t)k * I * 4);
+}
+
+hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_gate,
+                         const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate,
+                         const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int H, int E,
+                         int k, int I, int I_s, uint16_t* y, void* ws, hipStream_t st) {
+  DecodeWs d = carve(ws, H, E, k, I, I_s);
+  int rows1 = E + I_s + (I_s > 0 ? 1 : 0);
+  hipLaunchKernelGGL(decode_router_shared_kernel, dim3((rows1 + 3) / 4), dim3(256), 0, st, x, w_router, bias,
+                     ws_gate, ws_up, w_sg, H, E, I_s, d);
+  hipLaunchKernelGGL(decode_topk_kernel, dim3(1), dim3(64), 0, st, E, k, d);
+  hipLaunchKernelGGL(decode_gate_up_kernel, dim3((k * I + 3) / 4), dim3(256), 0, st, x, w_gate, w_up, H, k, I, d);
+  hipLaunchKernelGGL(decode_down_kernel, dim3((H + 3) / 4), dim3(256), 0, st, w_down, ws_down, H, k, I, I_s, d, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,325 @@
+// C ABI of libmoe355: argument validation, workspace carving and the order of
+// the stage launches.  Every entry point validates its arguments on the host
+// before any HIP call, so argument errors are reported with nothing enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other.
+int g_arch_state[64];
+
+int check_arch() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_ARCH, "no HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_ARCH, "device index %d out of range", dev);
+  if (g_arch_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(MOE_ERR_ARCH, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_arch_state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    if (g_arch_state[dev] == 2)
+      return fail(MOE_ERR_ARCH, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+  }
+  if (g_arch_state[dev] != 1) return fail(MOE_ERR_ARCH, "device %d is not gfx950", dev);
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int tile_rows_override() {
+  static int v = -1;
+  if (v < 0) {
+    const char* s = getenv("MOE_TILE_ROWS");  // tuning only
+    int r = s ? atoi(s) : 0;
+    v = (r == 32 || r == 64 || r == 128) ? r : 0;
+  }
+  return v;
+}
+
+int check_common_shapes(int T, int H, int E, int k) {
+  if (T < 0 || T > (1 << 24)) return fail(MOE_ERR_SHAPE, "T=%d outside [0, 2^24]", T);
+  if (E < 1 || E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
+  if (k < 1 || k > E || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, min(E, %d)]", k, kMaxK);
+  if (H < 256 || H > 8192 || H % 256 != 0) return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 256 in [256, 8192]", H);
+  return MOE_OK;
+}
+
+int check_ffn_shapes(int I, int I_s) {
+  if (I < 128 || I % 128 != 0) return fail(MOE_ERR_SHAPE, "I=%d must be a positive multiple of 128", I);
+  if (I_s < 0 || I_s % 128 != 0) return fail(MOE_ERR_SHAPE, "I_s=%d must be 0 or a multiple of 128", I_s);
+  return MOE_OK;
+}
+
+struct Layout {
+  int BM;
+  int64_t max_rows, max_tiles_routed, max_tiles_total;
+  size_t off_ids, off_w, off_s, off_counts, off_padoff, off_sorted, off_inv, off_tiles, off_ntiles, off_scratch,
+      off_h, off_hs, off_o, total;
+};
+
+Layout layout(int T, int H, int E, int k, int I, int I_s) {
+  Layout L = {};
+  L.BM = moe_align_tile_rows(T, E, k);
+  L.max_rows = moe_align_max_rows(T, E, k);
+  L.max_tiles_routed = L.max_rows / L.BM;
+  L.max_tiles_total = moe_align_max_tiles(T, E, k);
+  const size_t n = (size_t)T * k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes ? bytes : 1);
+    return at;
+  };
+  L.off_ids = take(n * 4);
+  L.off_w = take(n * 4);
+  L.off_s = take((size_t)T * 4);
+  L.off_counts = take((size_t)E * 4);
+  L.off_padoff = take((size_t)(E + 1) * 4);
+  L.off_sorted = take((size_t)L.max_rows * 4);
+  L.off_inv = take(n * 4);
+  L.off_tiles = take((size_t)L.max_tiles_total * 8);
+  L.off_ntiles = take(8);
+  L.off_scratch = take(moe_align_scratch_size(T, E, k));
+  L.off_h = take((size_t)L.max_rows * I * 2);
+  L.off_hs = take((size_t)T * (I_s > 0 ? I_s : 0) * 2);
+  L.off_o = take((size_t)L.max_rows * H * 2);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_ARCH: return "MOE_ERR_ARCH";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_align_tile_rows(int T, int E, int k) {
+  int ov = tile_rows_override();
+  if (ov) return ov;
+  if (E < 1) return 128;
+  int64_t avg = (int64_t)T * k / E;  // mean rows per expert
+  if (avg >= 192) return 128;
+  if (avg >= 48) return 64;
+  return 32;
+}
+
+int64_t moe_align_max_rows(int T, int E, int k) {
+  int64_t n = (int64_t)T * k;
+  int64_t BM = moe_align_tile_rows(T, E, k);
+  int64_t used = n < E ? n : E;
+  return n + used * (BM - 1);
+}
+
+int64_t moe_align_max_tiles(int T, int E, int k) {
+  int64_t BM = moe_align_tile_rows(T, E, k);
+  return moe_align_max_rows(T, E, k) / BM + (T + BM - 1) / BM;
+}
+
+size_t moe_align_scratch_size(int T, int E, int k) {
+  return (size_t)(align_num_chunks(T, k) > 0 ? align_num_chunks(T, k) : 1) * (size_t)(E > 0 ? E : 1) * 4;
+}
+
+size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s) {
+  if (check_common_shapes(T, H, E, k) != MOE_OK || check_ffn_shapes(I, I_s) != MOE_OK) return 0;
+  if (T <= 1) return decode_workspace_size(H, E, k, I, I_s);
+  return layout(T, H, E, k, I, I_s).total;
+}
+
+int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint16_t* w_sg, int T,
+              int H, int E, int k, int32_t* ids, float* w, float* s, float* logits, void* stream) {
+  int rc = check_common_shapes(T, H, E, k);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if (!x || !w_router || !ids || !w) return fail(MOE_ERR_NULL, "moe_route: x, w_router, ids and w are required");
+  if (w_sg && !s) return fail(MOE_ERR_NULL, "moe_route: s is required when w_sg is given");
+  if (!aligned16(x) || !aligned16(w_router) || (w_sg && !aligned16(w_sg)))
+    return fail(MOE_ERR_ALIGN, "moe_route: bf16 tensors must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  return hip_status(launch_route(x, w_router, router_bias, w_sg, T, H, E, k, ids, w, s, logits, (hipStream_t)stream),
+                    "moe_route");
+}
+
+int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* ids, float* w, void* stream) {
+  if (T < 0 || T > (1 << 24)) return fail(MOE_ERR_SHAPE, "T=%d outside [0, 2^24]", T);
+  if (E < 1 || E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
+  if (k < 1 || k > E || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, min(E, %d)]", k, kMaxK);
+  if (T == 0) return ok();
+  if (!logits || !ids || !w) return fail(MOE_ERR_NULL, "moe_route_from_logits: logits, ids and w are required");
+  int rc = check_arch();
+  if (rc) return rc;
+  return hip_status(launch_route_from_logits(logits, T, E, k, ids, w, (hipStream_t)stream), "moe_route_from_logits");
+}
+
+int moe_align(const int32_t* ids, int T, int E, int k, int with_shared, int32_t* counts, int32_t* pad_off,
+              int32_t* sorted, int32_t* inv, int32_t* tiles, int32_t* n_tiles, void* scratch, size_t scratch_bytes,
+              void* stream) {
+  if (T < 0 || T > (1 << 24)) return fail(MOE_ERR_SHAPE, "T=%d outside [0, 2^24]", T);
+  if (E < 1 || E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
+  if (k < 1 || k > E || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, min(E, %d)]", k, kMaxK);
+  if (T == 0) return ok();
+  if (!ids || !counts || !pad_off || !sorted || !inv || !tiles || !n_tiles || !scratch)
+    return fail(MOE_ERR_NULL, "moe_align: every output and the scratch buffer are required");
+  if (scratch_bytes < moe_align_scratch_size(T, E, k))
+    return fail(MOE_ERR_WORKSPACE, "moe_align: scratch of %zu bytes, %zu needed", scratch_bytes,
+                moe_align_scratch_size(T, E, k));
+  int rc = check_arch();
+  if (rc) return rc;
+  return hip_status(launch_align(ids, T, E, k, moe_align_tile_rows(T, E, k), with_shared, counts, pad_off, sorted,
+                                 inv, tiles, n_tiles, static_cast<int32_t*>(scratch), (hipStream_t)stream),
+                    "moe_align");
+}
+
+int moe_grouped_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* ws_gate,
+                        const uint16_t* ws_up, const int32_t* sorted, const int32_t* tiles, const int32_t* n_tiles,
+                        int T, int H, int E, int k, int I, int I_s, uint16_t* h, uint16_t* h_s, void* stream) {
+  int rc = check_common_shapes(T, H, E, k);
+  if (rc || (rc = check_ffn_shapes(I, I_s))) return rc;
+  if (T == 0) return ok();
+  if (!x || !w_gate || !w_up || !sorted || !tiles || !n_tiles || !h)
+    return fail(MOE_ERR_NULL, "moe_grouped_gate_up: missing pointer");
+  if (I_s > 0 && (!ws_gate || !ws_up || !h_s)) return fail(MOE_ERR_NULL, "moe_grouped_gate_up: shared tensors");
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(h) ||
+      (I_s > 0 && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(h_s))))
+    return fail(MOE_ERR_ALIGN, "moe_grouped_gate_up: tensors must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  const int BM = moe_align_tile_rows(T, E, k);
+  const int64_t max_tiles = moe_align_max_rows(T, E, k) / BM;
+  return hip_status(launch_gate_up(x, w_gate, w_up, ws_gate, ws_up, sorted, tiles, n_tiles, T, H, E, k, I, I_s, BM,
+                                   max_tiles, h, h_s, (hipStream_t)stream),
+                    "moe_grouped_gate_up");
+}
+
+int moe_grouped_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,
+                     const int32_t* n_tiles, int T, int H, int E, int k, int I, uint16_t* o, void* stream) {
+  int rc = check_common_shapes(T, H, E, k);
+  if (rc || (rc = check_ffn_shapes(I, 0))) return rc;
+  if (T == 0) return ok();
+  if (!h || !w_down || !sorted || !tiles || !n_tiles || !o) return fail(MOE_ERR_NULL, "moe_grouped_down: missing pointer");
+  if (!aligned16(h) || !aligned16(w_down) || !aligned16(o))
+    return fail(MOE_ERR_ALIGN, "moe_grouped_down: tensors must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  const int BM = moe_align_tile_rows(T, E, k);
+  const int64_t max_tiles = moe_align_max_rows(T, E, k) / BM;
+  return hip_status(launch_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, BM, max_tiles, o,
+                                (hipStream_t)stream),
+                    "moe_grouped_down");
+}
+
+int moe_combine(const uint16_t* o, const int32_t* inv, const float* w, const uint16_t* h_s, const uint16_t* ws_down,
+                const float* s, int T, int H, int k, int I_s, uint16_t* y, void* stream) {
+  if (T < 0 || T > (1 << 24)) return fail(MOE_ERR_SHAPE, "T=%d outside [0, 2^24]", T);
+  if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
+  if (H < 256 || H > 8192 || H % 256 != 0) return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 256", H);
+  if (I_s < 0 || I_s % 128 != 0) return fail(MOE_ERR_SHAPE, "I_s=%d must be 0 or a multiple of 128", I_s);
+  if (T == 0) return ok();
+  if (!o || !inv || !w || !y) return fail(MOE_ERR_NULL, "moe_combine: missing pointer");
+  if (I_s > 0 && (!h_s || !ws_down || !s)) return fail(MOE_ERR_NULL, "moe_combine: shared tensors");
+  if (I_s == 0 && (h_s || ws_down || s)) return fail(MOE_ERR_SHAPE, "moe_combine: shared tensors given with I_s = 0");
+  if (!aligned16(o) || !aligned16(y) || (I_s > 0 && (!aligned16(h_s) || !aligned16(ws_down))))
+    return fail(MOE_ERR_ALIGN, "moe_combine: tensors must be 16-byte aligned");
+  int rc = check_arch();
+  if (rc) return rc;
+  return hip_status(launch_combine(o, inv, w, h_s, ws_down, s, T, H, k, I_s, y, (hipStream_t)stream), "moe_combine");
+}
+
+int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint16_t* w_gate,
+                const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate, const uint16_t* ws_up,
+                const uint16_t* ws_down, const uint16_t* w_sg, int T, int H, int E, int k, int I, int I_s,
+                uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_common_shapes(T, H, E, k);
+  if (rc || (rc = check_ffn_shapes(I, I_s))) return rc;
+  const int n_shared = (ws_gate != nullptr) + (ws_up != nullptr) + (ws_down != nullptr) + (w_sg != nullptr);
+  if (I_s == 0 && n_shared != 0) return fail(MOE_ERR_SHAPE, "shared-expert tensors given with I_s = 0");
+  if (I_s > 0 && n_shared != 4) return fail(MOE_ERR_NULL, "I_s > 0 needs ws_gate, ws_up, ws_down and w_sg");
+  if (T == 0) return ok();
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !workspace)
+    return fail(MOE_ERR_NULL, "x, w_router, w_gate, w_up, w_down, y and workspace are required");
+  const void* ptrs[] = {x, w_router, w_gate, w_up, w_down, y, ws_gate, ws_up, ws_down, w_sg};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MOE_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const size_t need = moe_workspace_size(T, H, E, k, I, I_s);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if ((rc = check_arch())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+
+  if (T == 1)
+    return hip_status(launch_decode(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg, H,
+                                    E, k, I, I_s, y, workspace, st),
+                      "moe_forward (decode)");
+
+  const Layout L = layout(T, H, E, k, I, I_s);
+  char* base = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(base + L.off_ids);
+  float* w = reinterpret_cast<float*>(base + L.off_w);
+  float* s = reinterpret_cast<float*>(base + L.off_s);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
+  int32_t* pad_off = reinterpret_cast<int32_t*>(base + L.off_padoff);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.off_sorted);
+  int32_t* inv = reinterpret_cast<int32_t*>(base + L.off_inv);
+  int32_t* tiles = reinterpret_cast<int32_t*>(base + L.off_tiles);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(base + L.off_ntiles);
+  int32_t* scratch = reinterpret_cast<int32_t*>(base + L.off_scratch);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + L.off_h);
+  uint16_t* h_s = I_s > 0 ? reinterpret_cast<uint16_t*>(base + L.off_hs) : nullptr;
+  uint16_t* o = reinterpret_cast<uint16_t*>(base + L.off_o);
+
+  hipError_t e = launch_route(x, w_router, router_bias, w_sg, T, H, E, k, ids, w, I_s > 0 ? s : nullptr, nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: route");
+  e = launch_align(ids, T, E, k, L.BM, I_s > 0, counts, pad_off, sorted, inv, tiles, n_tiles, scratch, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: align");
+  e = launch_gate_up(x, w_gate, w_up, ws_gate, ws_up, sorted, tiles, n_tiles, T, H, E, k, I, I_s, L.BM,
+                     L.max_tiles_routed, h, h_s, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: gate_up");
+  e = launch_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, L.BM, L.max_tiles_routed, o, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: down");
+  e = launch_combine(o, inv, w, h_s, ws_down, I_s > 0 ? s : nullptr, T, H, k, I_s, y, st);
+  return hip_status(e, "moe_forward: combine");
+}
+
+}  // extern "C"

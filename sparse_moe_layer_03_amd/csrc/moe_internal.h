@@ -1,0 +1,75 @@
+// Internal declarations shared by the HIP translation units of libmoe355.
+// Nothing here is part of the C ABI (see include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;      // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 16;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Map a linear workgroup id to a work item so that each XCD receives one
+// contiguous run of items (items sharing an expert's weights stay in one
+// XCD's L2).  `n_items` is known only on the device.  Returns -1 when this
+// workgroup has no item.
+__device__ __forceinline__ int xcd_item(int bid, int n_items) {
+  int per = (n_items + kNumXcd - 1) / kNumXcd;
+  int xcd = bid % kNumXcd;
+  int slot = bid / kNumXcd;
+  if (slot >= per) return -1;
+  int item = xcd * per + slot;
+  return item < n_items ? item : -1;
+}
+
+// Host-side launch helpers (defined in the .hip files).
+hipError_t launch_route(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
+                        int T, int H, int E, int k, int32_t* ids, float* w, float* s, float* logits,
+                        hipStream_t st);
+hipError_t launch_route_from_logits(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                                    hipStream_t st);
+hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BM, int with_shared, int32_t* counts,
+                        int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles, int32_t* n_tiles,
+                        int32_t* scratch, hipStream_t st);
+int align_num_chunks(int T, int k);
+hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up,
+                          const uint16_t* ws_gate, const uint16_t* ws_up, const int32_t* sorted,
+                          const int32_t* tiles, const int32_t* n_tiles, int T, int H, int E, int k, int I,
+                          int I_s, int BM, int64_t max_tiles, uint16_t* h, uint16_t* h_s, hipStream_t st);
+hipError_t launch_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,
+                       const int32_t* n_tiles, int T, int H, int E, int k, int I, int BM, int64_t max_tiles,
+                       uint16_t* o, hipStream_t st);
+hipError_t launch_combine(const uint16_t* o, const int32_t* inv, const float* w, const uint16_t* h_s,
+                          const uint16_t* ws_down, const float* s, int T, int H, int k, int I_s, uint16_t* y,
+                          hipStream_t st);
+hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_gate,
+                         const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate,
+                         const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int H, int E,
+                         int k, int I, int I_s, uint16_t* y, void* ws, hipStream_t st);
+size_t decode_workspace_size(int H, int E, int k, int I, int I_s);
+
+}  // namespace moe

@@ -133,12 +133,14 @@ def zipf_log_pmf_bias(rng: np.random.Generator, E: int, s: float) -> np.ndarray:
     return (np.log(ranks ** (-s) / norm)).astype(np.float32)
 
 
-def make_inputs(wl, seed: int = 0, **overrides) -> Dict[str, np.ndarray]:
+def make_inputs(wl, seed: int = 0, reuse: Optional[Dict[str, object]] = None, **overrides) -> Dict[str, np.ndarray]:
     """Seeded inputs of workload ``wl`` (a name or a Workload).
 
     Returns a dict with keys x, w_router, bias, w_gate, w_up, w_down,
     ws_gate, ws_up, ws_down, w_sg (absent tensors are None) and the
-    workload itself under "wl".
+    workload itself under "wl".  ``reuse``: the result of an earlier call
+    with the same seed and layer shapes (H, E, I, I_s); its weight arrays are
+    taken as they are instead of being drawn again (they would be identical).
     """
     if isinstance(wl, str):
         wl = workload(wl, **overrides)
@@ -155,16 +157,24 @@ def make_inputs(wl, seed: int = 0, **overrides) -> Dict[str, np.ndarray]:
         out["bias"] = zipf_log_pmf_bias(_rng(seed, "zipf_perm"), E, wl.zipf_s)
     else:
         out["bias"] = None
-    out["w_gate"] = _draw_bf16(seed, "w_gate", (E, I, H), WEIGHT_SIGMA)
-    out["w_up"] = _draw_bf16(seed, "w_up", (E, I, H), WEIGHT_SIGMA)
-    out["w_down"] = _draw_bf16(seed, "w_down", (E, H, I), WEIGHT_SIGMA)
-    if I_s > 0:
-        out["ws_gate"] = _draw_bf16(seed, "ws_gate", (I_s, H), WEIGHT_SIGMA)
-        out["ws_up"] = _draw_bf16(seed, "ws_up", (I_s, H), WEIGHT_SIGMA)
-        out["ws_down"] = _draw_bf16(seed, "ws_down", (H, I_s), WEIGHT_SIGMA)
-        out["w_sg"] = _draw_bf16(seed, "w_sg", (H,), WEIGHT_SIGMA)
+    if reuse is not None:
+        rw = reuse["wl"]
+        if (reuse.get("seed", seed), rw.H, rw.E, rw.I, rw.I_s) != (seed, H, E, I, I_s):
+            raise ValueError("reuse: weights were drawn for another seed or layer shape")
+        for key in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down", "w_sg"):
+            out[key] = reuse[key]
     else:
-        out["ws_gate"] = out["ws_up"] = out["ws_down"] = out["w_sg"] = None
+        out["w_gate"] = _draw_bf16(seed, "w_gate", (E, I, H), WEIGHT_SIGMA)
+        out["w_up"] = _draw_bf16(seed, "w_up", (E, I, H), WEIGHT_SIGMA)
+        out["w_down"] = _draw_bf16(seed, "w_down", (E, H, I), WEIGHT_SIGMA)
+        if I_s > 0:
+            out["ws_gate"] = _draw_bf16(seed, "ws_gate", (I_s, H), WEIGHT_SIGMA)
+            out["ws_up"] = _draw_bf16(seed, "ws_up", (I_s, H), WEIGHT_SIGMA)
+            out["ws_down"] = _draw_bf16(seed, "ws_down", (H, I_s), WEIGHT_SIGMA)
+            out["w_sg"] = _draw_bf16(seed, "w_sg", (H,), WEIGHT_SIGMA)
+        else:
+            out["ws_gate"] = out["ws_up"] = out["ws_down"] = out["w_sg"] = None
+    out["seed"] = seed
     if wl.tie_frac > 0.0:
         n_tie = int(round(wl.tie_frac * T))
         rows = (np.sort(_rng(seed, "tie_rows").choice(T, size=n_tie, replace=False)) if n_tie

@@ -1,0 +1,111 @@
+"""The C ABI library on the host: it loads, exports every declared symbol,
+and rejects bad arguments before touching the GPU (no compute call here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from sparse_moe_layer_03_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/moe.h but not exported"
+    assert set(names) == set(moe.EXPORTS)
+
+
+def test_status_strings(L):
+    for code, name in ((0, "MOE_OK"), (-1, "MOE_ERR_NULL"), (-2, "MOE_ERR_SHAPE"), (-3, "MOE_ERR_ALIGN"),
+                       (-4, "MOE_ERR_WORKSPACE"), (-5, "MOE_ERR_ARCH"), (-6, "MOE_ERR_HIP")):
+        assert moe.status_str(code) == name
+
+
+def test_tile_rows_policy():
+    assert moe.moe_align_tile_rows(8192, 256, 8) == 128
+    assert moe.moe_align_tile_rows(32768, 256, 8) == 128
+    assert moe.moe_align_tile_rows(1024, 256, 8) == 32
+    assert moe.moe_align_tile_rows(2048, 256, 8) == 64
+    assert moe.moe_align_max_rows(8192, 256, 8) == 8192 * 8 + 256 * 127
+    assert moe.moe_align_max_rows(2, 256, 8) == 16 + 16 * 31
+    assert moe.moe_align_max_tiles(16, 8, 2) == (32 + 8 * 31) // 32 + 1
+
+
+def test_workspace_sizes():
+    big = moe.moe_workspace_size(8192, 2048, 256, 8, 512, 512)
+    small = moe.moe_workspace_size(1024, 2048, 256, 8, 512, 512)
+    dec = moe.moe_workspace_size(1, 2048, 256, 8, 512, 512)
+    assert big > small > dec > 0
+    assert dec < (1 << 20)
+    # h and o of every padded row must fit
+    rows = moe.moe_align_max_rows(8192, 256, 8)
+    assert big >= rows * (512 + 2048) * 2
+    for bad in ((16, 255, 8, 2, 128, 0), (16, 256, 0, 1, 128, 0), (16, 256, 8, 9, 128, 0), (16, 256, 8, 2, 100, 0),
+                (16, 256, 8, 2, 128, 64), (16, 256, 300, 2, 128, 0), (16, 256, 8, 17, 128, 0), (-1, 256, 8, 2, 128, 0)):
+        assert moe.moe_workspace_size(*bad) == 0, bad
+
+
+def fwd(L, x=1 << 12, wr=1 << 12, b=None, wg=1 << 12, wu=1 << 12, wd=1 << 12, sg=None, su=None, sd=None, wsg=None,
+        T=16, H=256, E=8, k=2, I=128, I_s=0, y=1 << 12, ws=1 << 12, nbytes=1 << 40):
+    return L.moe_forward(x, wr, b, wg, wu, wd, sg, su, sd, wsg, T, H, E, k, I, I_s, y, ws, nbytes, None)
+
+
+def test_forward_argument_errors(L):
+    assert fwd(L, T=0) == moe.MOE_OK  # no-op
+    assert fwd(L, x=None) == moe.MOE_ERR_NULL
+    assert fwd(L, y=None) == moe.MOE_ERR_NULL
+    assert fwd(L, ws=None) == moe.MOE_ERR_NULL
+    assert fwd(L, k=9) == moe.MOE_ERR_SHAPE
+    assert fwd(L, k=0) == moe.MOE_ERR_SHAPE
+    assert fwd(L, E=257, k=2) == moe.MOE_ERR_SHAPE
+    assert fwd(L, H=320) == moe.MOE_ERR_SHAPE
+    assert fwd(L, I=96) == moe.MOE_ERR_SHAPE
+    assert fwd(L, T=-3) == moe.MOE_ERR_SHAPE
+    # shared-expert pointers: all or none
+    assert fwd(L, sg=1 << 12) == moe.MOE_ERR_SHAPE
+    assert fwd(L, I_s=128, sg=1 << 12, su=1 << 12, sd=1 << 12) == moe.MOE_ERR_NULL
+    # alignment and workspace size
+    assert fwd(L, x=(1 << 12) + 2) == moe.MOE_ERR_ALIGN
+    assert fwd(L, ws=(1 << 12) + 16) == moe.MOE_ERR_ALIGN
+    assert fwd(L, nbytes=100) == moe.MOE_ERR_WORKSPACE
+    assert "workspace" in moe.last_error()
+
+
+def test_stage_argument_errors(L):
+    p = 1 << 12
+    assert L.moe_route(None, p, None, None, 16, 256, 8, 2, p, p, None, None, None) == moe.MOE_ERR_NULL
+    assert L.moe_route(p, p, None, p, 16, 256, 8, 2, p, p, None, None, None) == moe.MOE_ERR_NULL  # s missing
+    assert L.moe_route(p, p, None, None, 16, 256, 8, 20, p, p, None, None, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_route_from_logits(p, 16, 300, 2, p, p, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_route_from_logits(None, 16, 8, 2, p, p, None) == moe.MOE_ERR_NULL
+    assert L.moe_align(p, 16, 8, 2, 0, p, p, p, p, p, p, p, 1, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_align(p, 16, 8, 2, 0, p, p, None, p, p, p, p, 1 << 20, None) == moe.MOE_ERR_NULL
+    assert L.moe_grouped_gate_up(p, p, p, None, None, p, p, p, 16, 256, 8, 2, 128, 128, p, None, None) == \
+        moe.MOE_ERR_NULL
+    assert L.moe_grouped_down(p, p, p, p, p, 16, 256, 8, 2, 100, p, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_combine(p, p, p, p, None, None, 16, 256, 2, 0, p, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_combine(p, p, p, None, None, None, 16, 256, 2, 0, None, None) == moe.MOE_ERR_NULL
+    for f, args in ((L.moe_route, (p, p, None, None, 0, 256, 8, 2, None, None, None, None, None)),
+                    (L.moe_align, (None, 0, 8, 2, 0, None, None, None, None, None, None, None, 0, None))):
+        assert f(*args) == moe.MOE_OK  # T = 0 is a no-op
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="host without a GPU only")
+def test_valid_call_without_gpu_reports_arch(L):
+    assert fwd(L) == moe.MOE_ERR_ARCH
