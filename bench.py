@@ -60,6 +60,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=0, help="oracle sample tokens (0: sized to ~15 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -173,6 +175,15 @@ def main():
     }
     del layers, bufs
     torch.cuda.empty_cache()
+
+    if args.calib_copy:
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        bcopy = torch.empty_like(a)
+        for _ in range(3):
+            bcopy.copy_(a)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = a.numel() * 4
+        del a, bcopy
 
     # ------------------------------------------------------------- decode
     if not args.no_decode:

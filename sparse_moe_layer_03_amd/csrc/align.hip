@@ -59,7 +59,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sbuf, int& total
   return wave_off + incl - v;
 }
 
-__global__ __launch_bounds__(256) void align_scan_kernel(int32_t* __restrict__ chunk_hist, int n_chunks, int T,
+__global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restrict__ chunk_hist,
+                                                         int32_t* __restrict__ chunk_off, int n_chunks, int T,
                                                          int E, int BM, int with_shared,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ pad_off,
                                                          int32_t* __restrict__ sorted, int32_t* __restrict__ tiles,
@@ -68,10 +69,16 @@ __global__ __launch_bounds__(256) void align_scan_kernel(int32_t* __restrict__ c
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      int hv = chunk_hist[(size_t)c * E + e];
-      chunk_hist[(size_t)c * E + e] = run;  // exclusive offset of chunk c within expert e
-      run += hv;
+    // exclusive offset of every chunk within expert e; loads issued 16 at a time
+    for (int c0 = 0; c0 < n_chunks; c0 += 16) {
+      int hv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) hv[i] = (c0 + i < n_chunks) ? chunk_hist[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (c0 + i < n_chunks) chunk_off[(size_t)(c0 + i) * E + e] = run;
+        run += hv[i];
+      }
     }
     counts[e] = run;
   }
@@ -149,9 +156,10 @@ hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BM, int wit
   const int n = T * k;
   const int nc = align_num_chunks(T, k);
   hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, scratch);
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(256), 0, st, scratch, nc, T, E, BM, with_shared, counts,
-                     pad_off, sorted, tiles, n_tiles);
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, scratch, pad_off, sorted, inv);
+  int32_t* chunk_off = scratch + (size_t)nc * E;
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(256), 0, st, scratch, chunk_off, nc, T, E, BM, with_shared,
+                     counts, pad_off, sorted, tiles, n_tiles);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, chunk_off, pad_off, sorted, inv);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@
 //   D4 down projection + combine: wave per output column, k + 1 rows of
 //      W_down / Ws_down, y = sum_j w_j o_j + s o_s in fp32 -> bf16
 #include "moe_internal.h"
+#include "moe_topk.h"
 
 namespace moe {
 namespace {
@@ -131,53 +132,21 @@ __global__ __launch_bounds__(256) void decode_router_shared_kernel(
 
 __global__ __launch_bounds__(64) void decode_topk_kernel(int E, int k, DecodeWs d) {
   const int lane = threadIdx.x;
-  float v[4];
-  bool valid[4];
+  float v[1][4];
+  bool valid[1][4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     int e = lane + 64 * q;
-    valid[q] = e < E;
-    v[q] = valid[q] ? d.logits[e] : 0.0f;
+    valid[0][q] = e < E;
+    v[0][q] = valid[0][q] ? d.logits[e] : 0.0f;
   }
-  int sel_e = -1;
-  float sel_v = 0.0f;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (valid[q] && (be == 0x7fffffff || v[q] > bv)) {
-        bv = v[q];
-        be = lane + 64 * q;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oe = __shfl_xor(be, off);
-      bool take = (oe != 0x7fffffff) && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (take) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (lane == r) {
-      sel_e = be;
-      sel_v = bv;
-    }
-    if ((be & 63) == lane) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (q == (be >> 6)) valid[q] = false;
-    }
-  }
-  float m = __shfl(sel_v, 0);
-  float ex = (lane < k) ? expf(sel_v - m) : 0.0f;
-  float sum = 0.0f;
-  for (int r = 0; r < k; ++r) sum += __shfl(ex, r);
+  int sel_e[1];
+  float sel_v[1];
+  wave_topk<1>(v, valid, k, lane, sel_e, sel_v);
+  float wt = wave_renorm_weight(sel_v[0], k, lane);
   if (lane < k) {
-    d.ids[lane] = sel_e;
-    d.w[lane] = ex / sum;
+    d.ids[lane] = sel_e[0];
+    d.w[lane] = wt;
   }
 }
 

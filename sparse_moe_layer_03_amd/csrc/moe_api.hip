@@ -6,7 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 using namespace moe;
@@ -63,7 +63,7 @@ int tile_rows_override() {
   if (v < 0) {
     const char* s = getenv("MOE_TILE_ROWS");  // tuning only
     int r = s ? atoi(s) : 0;
-    v = (r == 32 || r == 64 || r == 128) ? r : 0;
+    v = (r == 32 || r == 64 || r == 128 || r == 256) ? r : 0;
   }
   return v;
 }
@@ -161,7 +161,8 @@ int64_t moe_align_max_tiles(int T, int E, int k) {
 }
 
 size_t moe_align_scratch_size(int T, int E, int k) {
-  return (size_t)(align_num_chunks(T, k) > 0 ? align_num_chunks(T, k) : 1) * (size_t)(E > 0 ? E : 1) * 4;
+  // per-chunk histograms, then per-chunk exclusive offsets
+  return 2 * (size_t)(align_num_chunks(T, k) > 0 ? align_num_chunks(T, k) : 1) * (size_t)(E > 0 ? E : 1) * 4;
 }
 
 size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s) {

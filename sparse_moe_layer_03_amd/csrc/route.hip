@@ -15,6 +15,7 @@
 // The logits of the 32 tokens then sit in LDS and each wavefront selects the
 // top-k of 8 tokens with wave-wide arg-max reductions.
 #include "moe_internal.h"
+#include "moe_topk.h"
 
 namespace moe {
 namespace {
@@ -23,55 +24,10 @@ constexpr int RT = 32;       // tokens per workgroup
 constexpr int RBK = 64;      // K columns per LDS stage (128 bytes per row)
 constexpr int RCH = RBK / 8; // 16-byte chunks per row per stage
 
-__device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ (row & 7); }
-
-// Wave-wide selection of the k largest (value desc, index asc).  Lane l holds
-// the values of experts l, l+64, l+128, l+192 (absent ones are invalid).
-// Lane r < k ends with (sel_e, sel_v) of rank r.
-__device__ __forceinline__ void wave_topk(float v[4], bool valid[4], int k, int lane, int& sel_e, float& sel_v) {
-  sel_e = -1;
-  sel_v = 0.0f;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int e = lane + 64 * q;
-      if (valid[q] && (be == 0x7fffffff || v[q] > bv)) {  // ascending e: strict > keeps the lower index
-        bv = v[q];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oe = __shfl_xor(be, off);
-      bool take = (oe != 0x7fffffff) && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (take) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (lane == r) {
-      sel_e = be;
-      sel_v = bv;
-    }
-    if ((be & 63) == lane) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (q == (be >> 6)) valid[q] = false;
-    }
-  }
-}
-
-// Weights of the selected experts: lane r < k holds rank r's logit.
-__device__ __forceinline__ float wave_renorm_weight(float sel_v, int k, int lane) {
-  float m = __shfl(sel_v, 0);
-  float ex = (lane < k) ? expf(sel_v - m) : 0.0f;
-  float sum = 0.0f;
-  for (int r = 0; r < k; ++r) sum += __shfl(ex, r);  // rank order
-  return ex / sum;
-}
+// 16-byte chunk swizzle of a 128-byte LDS row: 8 consecutive rows read at one
+// logical chunk hit 8 distinct bank groups of a 128-byte bank row, and 16
+// consecutive rows 16 distinct groups of a 256-byte one.
+__device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ (((row >> 1) ^ ((row & 1) << 2)) & 7); }
 
 __global__ __launch_bounds__(256) void route_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                                                     const float* __restrict__ bias,
@@ -88,30 +44,33 @@ __global__ __launch_bounds__(256) void route_kernel(const uint16_t* __restrict__
 
   // global -> register assignment
   const int xr = tid >> 3, xc = tid & 7;                     // one x chunk per thread
-  const uint16_t* xrow = (t0 + xr < T) ? x + (size_t)(t0 + xr) * H : nullptr;
+  // Rows past T and router rows past E load row 0 and are zeroed when they
+  // are written to LDS (a select right after a load would stall on it).
+  const bool xok = t0 + xr < T;
+  const uint16_t* xrow = x + (size_t)(xok ? t0 + xr : 0) * H;
   const int nwl = (EP * RCH + 255) / 256;                    // router chunks per thread (<= 8)
   u32x4 px, pw[8];
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
   auto gload = [&](int kb) {
-    px = xrow ? *reinterpret_cast<const u32x4*>(xrow + kb * RBK + xc * 8) : zero;
+    px = *reinterpret_cast<const u32x4*>(xrow + kb * RBK + xc * 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i < nwl) {
         int idx = tid + 256 * i;
         int r = idx >> 3, c = idx & 7;
-        pw[i] = (r < E) ? *reinterpret_cast<const u32x4*>(wr + (size_t)r * H + kb * RBK + c * 8) : zero;
+        pw[i] = *reinterpret_cast<const u32x4*>(wr + (size_t)(r < E ? r : 0) * H + kb * RBK + c * 8);
       }
     }
   };
   auto sstore = [&](int st) {
-    sx[st * RT * RCH + xr * RCH + swz8(xr, xc)] = px;
+    sx[st * RT * RCH + xr * RCH + swz8(xr, xc)] = xok ? px : zero;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i < nwl) {
         int idx = tid + 256 * i;
         int r = idx >> 3, c = idx & 7;
-        if (r < EP) sw[st * EP * RCH + r * RCH + swz8(r, c)] = pw[i];
+        if (r < EP) sw[st * EP * RCH + r * RCH + swz8(r, c)] = (r < E) ? pw[i] : zero;
       }
     }
   };
@@ -187,25 +146,30 @@ __global__ __launch_bounds__(256) void route_kernel(const uint16_t* __restrict__
   if (w_sg && xc == 0 && t0 + xr < T) sout[t0 + xr] = 1.0f / (1.0f + expf(-gpart));
   __syncthreads();
 
-  for (int r = wave * (RT / 4); r < (wave + 1) * (RT / 4); ++r) {
-    int t = t0 + r;
-    if (t >= T) break;
-    float v[4];
-    bool valid[4];
+  constexpr int NT = RT / 4;  // tokens per wave
+  const int r0 = wave * NT;
+  float v[NT][4];
+  bool valid[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       int e = lane + 64 * q;
-      valid[q] = e < E;
-      v[q] = valid[q] ? sl[r * LS + e] : 0.0f;
-      if (logits_out && valid[q]) logits_out[(size_t)t * E + e] = v[q];
+      valid[t][q] = e < E && t0 + r0 + t < T;
+      v[t][q] = valid[t][q] ? sl[(r0 + t) * LS + e] : 0.0f;
+      if (logits_out && valid[t][q]) logits_out[(size_t)(t0 + r0 + t) * E + e] = v[t][q];
     }
-    int sel_e;
-    float sel_v;
-    wave_topk(v, valid, k, lane, sel_e, sel_v);
-    float wt = wave_renorm_weight(sel_v, k, lane);
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = sel_e;
-      wout[(size_t)t * k + lane] = wt;
+  }
+  int sel_e[NT];
+  float sel_v[NT];
+  wave_topk<NT>(v, valid, k, lane, sel_e, sel_v);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tok = t0 + r0 + t;
+    float wt = wave_renorm_weight(sel_v[t], k, lane);
+    if (tok < T && lane < k) {
+      ids[(size_t)tok * k + lane] = sel_e[t];
+      wout[(size_t)tok * k + lane] = wt;
     }
   }
 }
@@ -216,22 +180,22 @@ __global__ __launch_bounds__(256) void topk_from_logits_kernel(const float* __re
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float v[4];
-  bool valid[4];
+  float v[1][4];
+  bool valid[1][4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     int e = lane + 64 * q;
-    valid[q] = e < E;
-    float val = valid[q] ? logits[(size_t)t * E + e] : 0.0f;
+    valid[0][q] = e < E;
+    float val = valid[0][q] ? logits[(size_t)t * E + e] : 0.0f;
     if (val == 0.0f) val = 0.0f;
-    v[q] = val;
+    v[0][q] = val;
   }
-  int sel_e;
-  float sel_v;
-  wave_topk(v, valid, k, lane, sel_e, sel_v);
-  float wt = wave_renorm_weight(sel_v, k, lane);
+  int sel_e[1];
+  float sel_v[1];
+  wave_topk<1>(v, valid, k, lane, sel_e, sel_v);
+  float wt = wave_renorm_weight(sel_v[0], k, lane);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = sel_e;
+    ids[(size_t)t * k + lane] = sel_e[0];
     wout[(size_t)t * k + lane] = wt;
   }
 }

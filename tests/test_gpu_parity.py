@@ -76,7 +76,10 @@ def test_route_generated(torch, full_layer, name, T):
     ids = b["ids"].cpu().numpy()
     G.check_ids(ids, r["ids"], ex, f"route {name}")
     same = np.all(ids == r["ids"], axis=1)
-    np.testing.assert_allclose(b["w"].cpu().numpy()[same], r["w"][same], rtol=0, atol=1e-6)
+    # w_j = exp(l_j - l_0) / sum: a logit error d moves w_j by at most about 2 w_j max|d|
+    dl = np.abs(lg.astype(np.float64) - r["logits"]).max(axis=1, keepdims=True)
+    dw = np.abs(b["w"].cpu().numpy().astype(np.float64) - r["w"])
+    assert np.all((dw <= 1e-6 + 2.0 * dl)[same])
     if wl.I_s:
         np.testing.assert_allclose(b["s"].cpu().numpy()[:Tn], r["s"], rtol=0, atol=1e-6)
     if len(inp.get("tie_rows", ())):
@@ -170,7 +173,7 @@ def test_layer_parity(torch, full_layer, label, case):
     if same.sum() > 0:
         ro = oracle.forward(inp, want=("h",))
         inv = b["inv"].cpu().numpy()
-        h_gpu = G.y_to_f64(b["h"])[inv]
+        h_gpu = G.y_to_f64(b["h"][torch.from_numpy(inv).long().cuda()])  # written rows only
         sel = np.repeat(same, wl.k)
         d = h_gpu[sel] - ro["h"][sel]
         rel = np.linalg.norm(d) / np.linalg.norm(ro["h"][sel])
