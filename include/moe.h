@@ -58,18 +58,27 @@ const char* moe_status_str(int status);
 const char* moe_last_error(void);
 
 /*
- * Rows per expert tile chosen for T tokens (all experts' rows are padded to a
- * multiple of it).  Depends only on (T, E, k).
+ * Tile heights chosen for T tokens.  Every expert's rows are cut into
+ * floor(count / BIG) tiles of BIG rows, and the remainder is padded to whole
+ * tiles of SMALL rows (SMALL divides BIG):
+ *   moe_align_tile_rows        BIG   (128, 64 or 32, from the mean rows per expert)
+ *   moe_align_small_tile_rows  SMALL (BIG / 2 when BIG = 128, else 32)
+ * Depends only on (T, E, k).
  */
 int moe_align_tile_rows(int T, int E, int k);
+int moe_align_small_tile_rows(int T, int E, int k);
 
 /*
- * Upper bound of padded rows for T tokens: T*k + min(E, T*k) * (BM - 1),
- * BM = moe_align_tile_rows(T, E, k).  Sizes `sorted` in moe_align.
+ * Upper bound of padded rows: T*k + min(E, T*k) * (SMALL - 1).  Sizes `sorted`
+ * in moe_align and the rows of h and o.
  */
 int64_t moe_align_max_rows(int T, int E, int k);
 
-/* Upper bound of tile-table entries written by moe_align (routed + shared). */
+/* Capacity of the BIG tile list: floor(T*k / BIG).  The SMALL tiles start at
+ * this entry of the tile table. */
+int64_t moe_align_max_big_tiles(int T, int E, int k);
+
+/* Entries of the tile table: BIG capacity + SMALL capacity. */
 int64_t moe_align_max_tiles(int T, int E, int k);
 
 /*
@@ -95,9 +104,10 @@ size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s);
  *          NULL with I_s = 0, or all four set with I_s > 0.
  * Output:  y [T,H] bf16 (fp32 sum rounded to nearest even).
  * Workspace: at least moe_workspace_size(T,H,E,k,I,I_s) bytes, 256-byte aligned.
- * Internally the call runs moe_route, moe_align, moe_grouped_gate_up,
- * moe_grouped_down and moe_combine (or the single-token decode kernels when
- * T == 1) on `stream`.
+ * Internally the call runs the router GEMM together with the shared expert's
+ * gate/up GEMM, then top-k, align, the routed gate/up and down GEMMs and the
+ * combine (or the single-token decode kernels when T == 1) on `stream`; the
+ * arithmetic of every element is the same as that of the stage entry points.
  */
 int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
@@ -109,9 +119,8 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
  * Router stage: logits (fp32 accumulation of bf16 products), optional bias,
  * top-k by (logit desc, index asc), renormalised softmax weights, and the
  * shared-expert gate s = sigmoid(x . w_sg).
- *   Outputs: ids [T,k] int32, w [T,k] fp32; s [T] fp32 (required iff w_sg is
- *   given, else ignored); logits [T,E] fp32 (nullable: written when given,
- *   including the bias).
+ *   Outputs: logits [T,E] fp32 (required; includes the bias), ids [T,k] int32,
+ *   w [T,k] fp32; s [T] fp32 (required iff w_sg is given, else ignored).
  */
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
               const uint16_t* w_sg, int T, int H, int E, int k,
@@ -126,22 +135,23 @@ int moe_route_from_logits(const float* logits, int T, int E, int k,
 
 /*
  * Expert histogram, prefix scan and stable permutation into padded tiles.
- *   ids [T,k] int32 (values in [0,E)).  BM = moe_align_tile_rows(T,E,k).
+ *   ids [T,k] int32 (values in [0,E)).  BIG, SMALL as moe_align_tile_rows /
+ *   moe_align_small_tile_rows.
  *   counts [E]      number of assignments routed to each expert
  *   pad_off [E+1]   first padded row of each expert; pad_off[E] = total rows
- *                   (expert e owns rows pad_off[e] .. pad_off[e]+ceil(counts[e]/BM)*BM)
+ *                   (expert e owns floor(counts[e]/BIG) BIG tiles, then
+ *                   ceil((counts[e] mod BIG)/SMALL) SMALL tiles)
  *   sorted [moe_align_max_rows]  assignment a = t*k + j held by each padded row,
  *                   ascending a within an expert; -1 marks a padding row
  *   inv [T*k]       padded row of each assignment
- *   tiles [2*moe_align_max_tiles]  (expert, first row) per tile of BM rows:
- *                   first the routed tiles in expert order, then ceil(T/BM)
- *                   shared-expert tiles (expert = E, first row = first token)
- *                   when with_shared != 0
- *   n_tiles [2]     number of routed tiles, total number of tiles
+ *   tiles [2*moe_align_max_tiles]  (expert, first row) per tile: the BIG tiles
+ *                   in expert order from entry 0, the SMALL tiles in expert
+ *                   order from entry moe_align_max_big_tiles
+ *   n_tiles [2]     number of BIG tiles, number of SMALL tiles
  *   scratch         at least moe_align_scratch_size(T,E,k) bytes
  */
 size_t moe_align_scratch_size(int T, int E, int k);
-int moe_align(const int32_t* ids, int T, int E, int k, int with_shared,
+int moe_align(const int32_t* ids, int T, int E, int k,
               int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv,
               int32_t* tiles, int32_t* n_tiles, void* scratch, size_t scratch_bytes, void* stream);
 

@@ -10,12 +10,15 @@
 //
 // Result (bit-exact, independent of scheduling):
 //   counts[e]   number of assignments a = t*k + j with ids[a] = e
-//   pad_off[e]  sum over e' < e of ceil(counts[e'] / BM) * BM
+//   rows of e   floor(counts[e] / BIG) tiles of BIG rows, then the remainder
+//               padded to whole tiles of SMALL rows (SMALL divides BIG)
+//   pad_off[e]  sum of the padded row counts of the experts before e
 //   sorted[pad_off[e] + r] = the r-th assignment of expert e in ascending a;
 //                            -1 for the padding rows of the expert's last tile
 //   inv[a]      the padded row that holds assignment a
-//   tiles       (expert, first row) per BM-row tile, experts ascending, then
-//               the shared-expert tiles (E, first token)
+//   tiles       (expert, first row) of every BIG tile, experts ascending; the
+//               SMALL tiles likewise from entry small_base on
+//   n_tiles     {number of BIG tiles, number of SMALL tiles}
 //
 // Three kernels: per-chunk histograms (LDS integer counters: the counts do
 // not depend on the order of the increments), one workgroup that scans the
@@ -60,8 +63,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sbuf, int& total
 }
 
 __global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restrict__ chunk_hist,
-                                                         int32_t* __restrict__ chunk_off, int n_chunks, int T,
-                                                         int E, int BM, int with_shared,
+                                                         int32_t* __restrict__ chunk_off, int n_chunks, int E,
+                                                         int BIG, int SMALL, int small_base,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ pad_off,
                                                          int32_t* __restrict__ sorted, int32_t* __restrict__ tiles,
                                                          int32_t* __restrict__ n_tiles) {
@@ -82,27 +85,30 @@ __global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restri
     }
     counts[e] = run;
   }
-  const int ntile = (e < E) ? (run + BM - 1) / BM : 0;
-  int total_tiles;
-  const int tile_off = block_exclusive_scan(ntile, sbuf, total_tiles);
-  const int rows_off = tile_off * BM;  // padded rows are whole tiles
+  const int nbig = (e < E) ? run / BIG : 0;
+  const int rem = (e < E) ? run - nbig * BIG : 0;
+  const int nsmall = (rem + SMALL - 1) / SMALL;
+  const int padded = nbig * BIG + nsmall * SMALL;
+  int total_rows, total_big, total_small;
+  const int rows_off = block_exclusive_scan(padded, sbuf, total_rows);
+  const int big_off = block_exclusive_scan(nbig, sbuf, total_big);
+  const int small_off = block_exclusive_scan(nsmall, sbuf, total_small);
   if (e < E) {
     pad_off[e] = rows_off;
-    for (int i = 0; i < ntile; ++i) {
-      tiles[2 * (tile_off + i)] = e;
-      tiles[2 * (tile_off + i) + 1] = rows_off + i * BM;
+    for (int i = 0; i < nbig; ++i) {
+      tiles[2 * (big_off + i)] = e;
+      tiles[2 * (big_off + i) + 1] = rows_off + i * BIG;
     }
-    for (int r = run; r < ntile * BM; ++r) sorted[rows_off + r] = -1;
-  }
-  if (e == 0) pad_off[E] = total_tiles * BM;
-  const int n_shared = with_shared ? (T + BM - 1) / BM : 0;
-  for (int i = e; i < n_shared; i += 256) {
-    tiles[2 * (total_tiles + i)] = E;
-    tiles[2 * (total_tiles + i) + 1] = i * BM;
+    for (int i = 0; i < nsmall; ++i) {
+      tiles[2 * (small_base + small_off + i)] = e;
+      tiles[2 * (small_base + small_off + i) + 1] = rows_off + nbig * BIG + i * SMALL;
+    }
+    for (int r = run; r < padded; ++r) sorted[rows_off + r] = -1;
   }
   if (e == 0) {
-    n_tiles[0] = total_tiles;
-    n_tiles[1] = total_tiles + n_shared;
+    pad_off[E] = total_rows;
+    n_tiles[0] = total_big;
+    n_tiles[1] = total_small;
   }
 }
 
@@ -150,14 +156,14 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
 
 int align_num_chunks(int T, int k) { return (int)(((int64_t)T * k + CH - 1) / CH); }
 
-hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BM, int with_shared, int32_t* counts,
-                        int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles, int32_t* n_tiles,
-                        int32_t* scratch, hipStream_t st) {
+hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
+                        int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
+                        int32_t* n_tiles, int32_t* scratch, hipStream_t st) {
   const int n = T * k;
   const int nc = align_num_chunks(T, k);
   hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, scratch);
   int32_t* chunk_off = scratch + (size_t)nc * E;
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(256), 0, st, scratch, chunk_off, nc, T, E, BM, with_shared,
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(256), 0, st, scratch, chunk_off, nc, E, BIG, SMALL, small_base,
                      counts, pad_off, sorted, tiles, n_tiles);
   hipLaunchKernelGGL(align_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, chunk_off, pad_off, sorted, inv);
   return hipGetLastError();

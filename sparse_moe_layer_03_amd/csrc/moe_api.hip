@@ -58,13 +58,21 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+int env_rows(const char* name) {
+  const char* s = getenv(name);  // tuning only
+  const int r = s ? atoi(s) : 0;
+  return (r == 32 || r == 64 || r == 128) ? r : 0;
+}
+
 int tile_rows_override() {
   static int v = -1;
-  if (v < 0) {
-    const char* s = getenv("MOE_TILE_ROWS");  // tuning only
-    int r = s ? atoi(s) : 0;
-    v = (r == 32 || r == 64 || r == 128 || r == 256) ? r : 0;
-  }
+  if (v < 0) v = env_rows("MOE_TILE_ROWS");
+  return v;
+}
+
+int small_rows_override() {
+  static int v = -1;
+  if (v < 0) v = env_rows("MOE_SMALL_ROWS");
   return v;
 }
 
@@ -83,18 +91,20 @@ int check_ffn_shapes(int I, int I_s) {
 }
 
 struct Layout {
-  int BM;
-  int64_t max_rows, max_tiles_routed, max_tiles_total;
-  size_t off_ids, off_w, off_s, off_counts, off_padoff, off_sorted, off_inv, off_tiles, off_ntiles, off_scratch,
-      off_h, off_hs, off_o, total;
+  int BIG, SMALL;
+  int64_t max_rows, max_big, max_small, max_tiles;
+  size_t off_ids, off_w, off_s, off_logits, off_counts, off_padoff, off_sorted, off_inv, off_tiles, off_ntiles,
+      off_scratch, off_h, off_hs, off_o, total;
 };
 
 Layout layout(int T, int H, int E, int k, int I, int I_s) {
   Layout L = {};
-  L.BM = moe_align_tile_rows(T, E, k);
+  L.BIG = moe_align_tile_rows(T, E, k);
+  L.SMALL = moe_align_small_tile_rows(T, E, k);
   L.max_rows = moe_align_max_rows(T, E, k);
-  L.max_tiles_routed = L.max_rows / L.BM;
-  L.max_tiles_total = moe_align_max_tiles(T, E, k);
+  L.max_big = moe_align_max_big_tiles(T, E, k);
+  L.max_tiles = moe_align_max_tiles(T, E, k);
+  L.max_small = L.max_tiles - L.max_big;
   const size_t n = (size_t)T * k;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -105,11 +115,12 @@ Layout layout(int T, int H, int E, int k, int I, int I_s) {
   L.off_ids = take(n * 4);
   L.off_w = take(n * 4);
   L.off_s = take((size_t)T * 4);
+  L.off_logits = take((size_t)T * E * 4);
   L.off_counts = take((size_t)E * 4);
   L.off_padoff = take((size_t)(E + 1) * 4);
   L.off_sorted = take((size_t)L.max_rows * 4);
   L.off_inv = take(n * 4);
-  L.off_tiles = take((size_t)L.max_tiles_total * 8);
+  L.off_tiles = take((size_t)L.max_tiles * 8);
   L.off_ntiles = take(8);
   L.off_scratch = take(moe_align_scratch_size(T, E, k));
   L.off_h = take((size_t)L.max_rows * I * 2);
@@ -139,25 +150,39 @@ const char* moe_status_str(int status) {
 const char* moe_last_error(void) { return g_err; }
 
 int moe_align_tile_rows(int T, int E, int k) {
-  int ov = tile_rows_override();
+  const int ov = tile_rows_override();
   if (ov) return ov;
-  if (E < 1) return 128;
-  int64_t avg = (int64_t)T * k / E;  // mean rows per expert
-  if (avg >= 192) return 128;
+  if (E < 1) return 32;
+  const int64_t avg = (int64_t)T * k / E;  // mean rows per expert
+  if (avg >= 128) return 128;
   if (avg >= 48) return 64;
   return 32;
 }
 
-int64_t moe_align_max_rows(int T, int E, int k) {
-  int64_t n = (int64_t)T * k;
-  int64_t BM = moe_align_tile_rows(T, E, k);
-  int64_t used = n < E ? n : E;
-  return n + used * (BM - 1);
+int moe_align_small_tile_rows(int T, int E, int k) {
+  const int big = moe_align_tile_rows(T, E, k);
+  const int ov = small_rows_override();
+  if (ov && ov <= big) return ov;
+  return big >= 128 ? big / 2 : 32;
 }
 
+int64_t moe_align_max_rows(int T, int E, int k) {
+  const int64_t n = (int64_t)T * k;
+  const int64_t small = moe_align_small_tile_rows(T, E, k);
+  const int64_t used = n < E ? n : E;
+  return n + used * (small - 1);
+}
+
+int64_t moe_align_max_big_tiles(int T, int E, int k) { return (int64_t)T * k / moe_align_tile_rows(T, E, k); }
+
 int64_t moe_align_max_tiles(int T, int E, int k) {
-  int64_t BM = moe_align_tile_rows(T, E, k);
-  return moe_align_max_rows(T, E, k) / BM + (T + BM - 1) / BM;
+  const int64_t n = (int64_t)T * k;
+  const int64_t big = moe_align_tile_rows(T, E, k), small = moe_align_small_tile_rows(T, E, k);
+  const int64_t used = n < E ? n : E;
+  int64_t max_small = used * (big / small);  // at most big/small SMALL tiles per expert
+  const int64_t bound = (n + used * (small - 1)) / small;
+  if (bound < max_small) max_small = bound;
+  return moe_align_max_big_tiles(T, E, k) + max_small;
 }
 
 size_t moe_align_scratch_size(int T, int E, int k) {
@@ -176,13 +201,16 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_b
   int rc = check_common_shapes(T, H, E, k);
   if (rc) return rc;
   if (T == 0) return ok();
-  if (!x || !w_router || !ids || !w) return fail(MOE_ERR_NULL, "moe_route: x, w_router, ids and w are required");
+  if (!x || !w_router || !ids || !w || !logits)
+    return fail(MOE_ERR_NULL, "moe_route: x, w_router, ids, w and logits are required");
   if (w_sg && !s) return fail(MOE_ERR_NULL, "moe_route: s is required when w_sg is given");
   if (!aligned16(x) || !aligned16(w_router) || (w_sg && !aligned16(w_sg)))
     return fail(MOE_ERR_ALIGN, "moe_route: bf16 tensors must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
-  return hip_status(launch_route(x, w_router, router_bias, w_sg, T, H, E, k, ids, w, s, logits, (hipStream_t)stream),
-                    "moe_route");
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_dense(x, w_router, router_bias, nullptr, nullptr, T, H, E, 0, logits, nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "moe_route: router GEMM");
+  return hip_status(launch_topk(logits, T, E, k, w_sg ? x : nullptr, w_sg, H, ids, w, s, st), "moe_route: top-k");
 }
 
 int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* ids, float* w, void* stream) {
@@ -193,12 +221,12 @@ int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* ids
   if (!logits || !ids || !w) return fail(MOE_ERR_NULL, "moe_route_from_logits: logits, ids and w are required");
   int rc = check_arch();
   if (rc) return rc;
-  return hip_status(launch_route_from_logits(logits, T, E, k, ids, w, (hipStream_t)stream), "moe_route_from_logits");
+  return hip_status(launch_topk(logits, T, E, k, nullptr, nullptr, 0, ids, w, nullptr, (hipStream_t)stream),
+                    "moe_route_from_logits");
 }
 
-int moe_align(const int32_t* ids, int T, int E, int k, int with_shared, int32_t* counts, int32_t* pad_off,
-              int32_t* sorted, int32_t* inv, int32_t* tiles, int32_t* n_tiles, void* scratch, size_t scratch_bytes,
-              void* stream) {
+int moe_align(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* pad_off, int32_t* sorted,
+              int32_t* inv, int32_t* tiles, int32_t* n_tiles, void* scratch, size_t scratch_bytes, void* stream) {
   if (T < 0 || T > (1 << 24)) return fail(MOE_ERR_SHAPE, "T=%d outside [0, 2^24]", T);
   if (E < 1 || E > kMaxE) return fail(MOE_ERR_SHAPE, "E=%d outside [1, %d]", E, kMaxE);
   if (k < 1 || k > E || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, min(E, %d)]", k, kMaxK);
@@ -210,10 +238,35 @@ int moe_align(const int32_t* ids, int T, int E, int k, int with_shared, int32_t*
                 moe_align_scratch_size(T, E, k));
   int rc = check_arch();
   if (rc) return rc;
-  return hip_status(launch_align(ids, T, E, k, moe_align_tile_rows(T, E, k), with_shared, counts, pad_off, sorted,
-                                 inv, tiles, n_tiles, static_cast<int32_t*>(scratch), (hipStream_t)stream),
+  return hip_status(launch_align(ids, T, E, k, moe_align_tile_rows(T, E, k), moe_align_small_tile_rows(T, E, k),
+                                 (int)moe_align_max_big_tiles(T, E, k), counts, pad_off, sorted, inv, tiles, n_tiles,
+                                 static_cast<int32_t*>(scratch), (hipStream_t)stream),
                     "moe_align");
 }
+
+namespace {
+// The routed GEMMs of both tile classes.
+hipError_t launch_routed_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up,
+                                 const int32_t* sorted, const int32_t* tiles, const int32_t* n_tiles, int T, int H,
+                                 int E, int k, int I, uint16_t* h, hipStream_t st) {
+  const int BIG = moe_align_tile_rows(T, E, k), SMALL = moe_align_small_tile_rows(T, E, k);
+  const int64_t max_big = moe_align_max_big_tiles(T, E, k), max_small = moe_align_max_tiles(T, E, k) - max_big;
+  hipError_t e = launch_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, BIG, max_big, h, st);
+  if (e != hipSuccess) return e;
+  return launch_gate_up(x, w_gate, w_up, sorted, tiles + 2 * max_big, n_tiles + 1, T, H, k, I, SMALL, max_small, h,
+                        st);
+}
+
+hipError_t launch_routed_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,
+                              const int32_t* n_tiles, int T, int H, int E, int k, int I, uint16_t* o,
+                              hipStream_t st) {
+  const int BIG = moe_align_tile_rows(T, E, k), SMALL = moe_align_small_tile_rows(T, E, k);
+  const int64_t max_big = moe_align_max_big_tiles(T, E, k), max_small = moe_align_max_tiles(T, E, k) - max_big;
+  hipError_t e = launch_down(h, w_down, sorted, tiles, n_tiles, T, H, k, I, BIG, max_big, o, st);
+  if (e != hipSuccess) return e;
+  return launch_down(h, w_down, sorted, tiles + 2 * max_big, n_tiles + 1, T, H, k, I, SMALL, max_small, o, st);
+}
+}  // namespace
 
 int moe_grouped_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* ws_gate,
                         const uint16_t* ws_up, const int32_t* sorted, const int32_t* tiles, const int32_t* n_tiles,
@@ -228,10 +281,12 @@ int moe_grouped_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_
       (I_s > 0 && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(h_s))))
     return fail(MOE_ERR_ALIGN, "moe_grouped_gate_up: tensors must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
-  const int BM = moe_align_tile_rows(T, E, k);
-  const int64_t max_tiles = moe_align_max_rows(T, E, k) / BM;
-  return hip_status(launch_gate_up(x, w_gate, w_up, ws_gate, ws_up, sorted, tiles, n_tiles, T, H, E, k, I, I_s, BM,
-                                   max_tiles, h, h_s, (hipStream_t)stream),
+  const hipStream_t st = (hipStream_t)stream;
+  if (I_s > 0) {
+    hipError_t e = launch_dense(x, nullptr, nullptr, ws_gate, ws_up, T, H, E, I_s, nullptr, h_s, st);
+    if (e != hipSuccess) return hip_status(e, "moe_grouped_gate_up: shared expert");
+  }
+  return hip_status(launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, E, k, I, h, st),
                     "moe_grouped_gate_up");
 }
 
@@ -244,10 +299,7 @@ int moe_grouped_down(const uint16_t* h, const uint16_t* w_down, const int32_t* s
   if (!aligned16(h) || !aligned16(w_down) || !aligned16(o))
     return fail(MOE_ERR_ALIGN, "moe_grouped_down: tensors must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
-  const int BM = moe_align_tile_rows(T, E, k);
-  const int64_t max_tiles = moe_align_max_rows(T, E, k) / BM;
-  return hip_status(launch_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, BM, max_tiles, o,
-                                (hipStream_t)stream),
+  return hip_status(launch_routed_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, o, (hipStream_t)stream),
                     "moe_grouped_down");
 }
 
@@ -299,6 +351,7 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   int32_t* ids = reinterpret_cast<int32_t*>(base + L.off_ids);
   float* w = reinterpret_cast<float*>(base + L.off_w);
   float* s = reinterpret_cast<float*>(base + L.off_s);
+  float* logits = reinterpret_cast<float*>(base + L.off_logits);
   int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
   int32_t* pad_off = reinterpret_cast<int32_t*>(base + L.off_padoff);
   int32_t* sorted = reinterpret_cast<int32_t*>(base + L.off_sorted);
@@ -310,14 +363,17 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   uint16_t* h_s = I_s > 0 ? reinterpret_cast<uint16_t*>(base + L.off_hs) : nullptr;
   uint16_t* o = reinterpret_cast<uint16_t*>(base + L.off_o);
 
-  hipError_t e = launch_route(x, w_router, router_bias, w_sg, T, H, E, k, ids, w, I_s > 0 ? s : nullptr, nullptr, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: route");
-  e = launch_align(ids, T, E, k, L.BM, I_s > 0, counts, pad_off, sorted, inv, tiles, n_tiles, scratch, st);
+  // router logits and the shared expert's gate/up share one launch (same token rows)
+  hipError_t e = launch_dense(x, w_router, router_bias, ws_gate, ws_up, T, H, E, I_s, logits, h_s, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: router + shared gate/up");
+  e = launch_topk(logits, T, E, k, I_s > 0 ? x : nullptr, w_sg, H, ids, w, I_s > 0 ? s : nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: top-k");
+  e = launch_align(ids, T, E, k, L.BIG, L.SMALL, (int)L.max_big, counts, pad_off, sorted, inv, tiles, n_tiles, scratch,
+                   st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: align");
-  e = launch_gate_up(x, w_gate, w_up, ws_gate, ws_up, sorted, tiles, n_tiles, T, H, E, k, I, I_s, L.BM,
-                     L.max_tiles_routed, h, h_s, st);
+  e = launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, E, k, I, h, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: gate_up");
-  e = launch_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, L.BM, L.max_tiles_routed, o, st);
+  e = launch_routed_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, o, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: down");
   e = launch_combine(o, inv, w, h_s, ws_down, I_s > 0 ? s : nullptr, T, H, k, I_s, y, st);
   return hip_status(e, "moe_forward: combine");

@@ -107,15 +107,15 @@ class DeviceLayer:
             "y": torch.empty((T, s.H), dtype=torch.bfloat16, device=dev),
         }
 
-    def run_route(self, x, b, stream=None, with_logits=True):
+    def run_route(self, x, b, stream=None):
         s = self.shapes
         T = x.shape[0]
         moe.moe_route(x, self.w["w_router"], self.bias, self.w["w_sg"], T, s.H, s.E, s.k, b["ids"], b["w"],
-                      b["s"] if s.I_s else None, b["logits"] if with_logits else None, stream)
+                      b["s"] if s.I_s else None, b["logits"], stream)
 
     def run_align(self, T, b, stream=None):
         s = self.shapes
-        moe.moe_align(b["ids"], T, s.E, s.k, s.I_s > 0, b["counts"], b["pad_off"], b["sorted"], b["inv"],
+        moe.moe_align(b["ids"], T, s.E, s.k, b["counts"], b["pad_off"], b["sorted"], b["inv"],
                       b["tiles"], b["n_tiles"], b["scratch"], b["scratch"].numel(), stream)
 
     def run_gate_up(self, x, b, stream=None):

@@ -24,8 +24,8 @@ MOE_ERR_ARCH = -5
 MOE_ERR_HIP = -6
 
 EXPORTS = (
-    "moe_status_str", "moe_last_error", "moe_align_tile_rows", "moe_align_max_rows", "moe_align_max_tiles",
-    "moe_workspace_size", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
+    "moe_status_str", "moe_last_error", "moe_align_tile_rows", "moe_align_small_tile_rows", "moe_align_max_rows",
+    "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
     "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine",
 )
 
@@ -51,14 +51,16 @@ def lib():
             "moe_status_str": ([i], C.c_char_p),
             "moe_last_error": ([], C.c_char_p),
             "moe_align_tile_rows": ([i, i, i], i),
+            "moe_align_small_tile_rows": ([i, i, i], i),
             "moe_align_max_rows": ([i, i, i], i64),
+            "moe_align_max_big_tiles": ([i, i, i], i64),
             "moe_align_max_tiles": ([i, i, i], i64),
             "moe_workspace_size": ([i, i, i, i, i, i], z),
             "moe_forward": ([p] * 10 + [i] * 6 + [p, p, z, p], i),
             "moe_route": ([p, p, p, p, i, i, i, i, p, p, p, p, p], i),
             "moe_route_from_logits": ([p, i, i, i, p, p, p], i),
             "moe_align_scratch_size": ([i, i, i], z),
-            "moe_align": ([p, i, i, i, i, p, p, p, p, p, p, p, z, p], i),
+            "moe_align": ([p, i, i, i, p, p, p, p, p, p, p, z, p], i),
             "moe_grouped_gate_up": ([p] * 8 + [i] * 6 + [p, p, p], i),
             "moe_grouped_down": ([p] * 5 + [i] * 5 + [p, p], i),
             "moe_combine": ([p] * 6 + [i] * 4 + [p, p], i),
@@ -105,8 +107,16 @@ def moe_align_tile_rows(T: int, E: int, k: int) -> int:
     return lib().moe_align_tile_rows(T, E, k)
 
 
+def moe_align_small_tile_rows(T: int, E: int, k: int) -> int:
+    return lib().moe_align_small_tile_rows(T, E, k)
+
+
 def moe_align_max_rows(T: int, E: int, k: int) -> int:
     return lib().moe_align_max_rows(T, E, k)
+
+
+def moe_align_max_big_tiles(T: int, E: int, k: int) -> int:
+    return lib().moe_align_max_big_tiles(T, E, k)
 
 
 def moe_align_max_tiles(T: int, E: int, k: int) -> int:
@@ -138,9 +148,9 @@ def moe_route_from_logits(logits, T, E, k, ids, w, stream=None):
     _check(lib().moe_route_from_logits(_p(logits), T, E, k, _p(ids), _p(w), _stream(stream)))
 
 
-def moe_align(ids, T, E, k, with_shared, counts, pad_off, sorted_rows, inv, tiles, n_tiles, scratch,
-              scratch_bytes, stream=None):
-    _check(lib().moe_align(_p(ids), T, E, k, int(with_shared), _p(counts), _p(pad_off), _p(sorted_rows),
+def moe_align(ids, T, E, k, counts, pad_off, sorted_rows, inv, tiles, n_tiles, scratch, scratch_bytes,
+              stream=None):
+    _check(lib().moe_align(_p(ids), T, E, k, _p(counts), _p(pad_off), _p(sorted_rows),
                            _p(inv), _p(tiles), _p(n_tiles), _p(scratch), scratch_bytes, _stream(stream)))
 
 

@@ -42,9 +42,38 @@ def test_tile_rows_policy():
     assert moe.moe_align_tile_rows(32768, 256, 8) == 128
     assert moe.moe_align_tile_rows(1024, 256, 8) == 32
     assert moe.moe_align_tile_rows(2048, 256, 8) == 64
-    assert moe.moe_align_max_rows(8192, 256, 8) == 8192 * 8 + 256 * 127
+    assert moe.moe_align_small_tile_rows(8192, 256, 8) == 64
+    for T, E, k in ((2048, 256, 8), (1024, 256, 8), (16, 8, 2), (5, 3, 3)):
+        assert moe.moe_align_small_tile_rows(T, E, k) == 32
+    # padding is at most SMALL - 1 rows per used expert
+    assert moe.moe_align_max_rows(8192, 256, 8) == 8192 * 8 + 256 * 63
     assert moe.moe_align_max_rows(2, 256, 8) == 16 + 16 * 31
-    assert moe.moe_align_max_tiles(16, 8, 2) == (32 + 8 * 31) // 32 + 1
+    assert moe.moe_align_max_big_tiles(8192, 256, 8) == 8192 * 8 // 128
+    # every expert may hold up to BIG/SMALL small tiles, bounded by the padded rows
+    assert moe.moe_align_max_tiles(8192, 256, 8) == 512 + min(256 * 2, (65536 + 256 * 63) // 64)
+    assert moe.moe_align_max_tiles(16, 8, 2) == 1 + min(8, (32 + 8 * 31) // 32)
+
+
+def test_tile_capacity_is_worst_case():
+    """Brute force over small histograms: the capacities bound every possible tiling."""
+    import itertools
+    import numpy as np
+    for E, k, T in ((3, 2, 40), (4, 1, 70), (2, 2, 100)):
+        B, S = moe.moe_align_tile_rows(T, E, k), moe.moe_align_small_tile_rows(T, E, k)
+        n = T * k
+        worst = [0, 0, 0]
+        for c in itertools.product(range(T + 1), repeat=E - 1):
+            last = n - sum(c)
+            if not 0 <= last <= T:
+                continue
+            cnt = np.array(list(c) + [last])
+            nb = cnt // B
+            ns = (cnt - nb * B + S - 1) // S
+            worst = [max(worst[0], int((nb * B + ns * S).sum())), max(worst[1], int(nb.sum())),
+                     max(worst[2], int(nb.sum() + ns.sum()))]
+        assert worst[0] <= moe.moe_align_max_rows(T, E, k)
+        assert worst[1] <= moe.moe_align_max_big_tiles(T, E, k)
+        assert worst[2] <= moe.moe_align_max_tiles(T, E, k)
 
 
 def test_workspace_sizes():
@@ -89,20 +118,21 @@ def test_forward_argument_errors(L):
 
 def test_stage_argument_errors(L):
     p = 1 << 12
-    assert L.moe_route(None, p, None, None, 16, 256, 8, 2, p, p, None, None, None) == moe.MOE_ERR_NULL
-    assert L.moe_route(p, p, None, p, 16, 256, 8, 2, p, p, None, None, None) == moe.MOE_ERR_NULL  # s missing
-    assert L.moe_route(p, p, None, None, 16, 256, 8, 20, p, p, None, None, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_route(None, p, None, None, 16, 256, 8, 2, p, p, None, p, None) == moe.MOE_ERR_NULL
+    assert L.moe_route(p, p, None, None, 16, 256, 8, 2, p, p, None, None, None) == moe.MOE_ERR_NULL  # logits
+    assert L.moe_route(p, p, None, p, 16, 256, 8, 2, p, p, None, p, None) == moe.MOE_ERR_NULL  # s missing
+    assert L.moe_route(p, p, None, None, 16, 256, 8, 20, p, p, None, p, None) == moe.MOE_ERR_SHAPE
     assert L.moe_route_from_logits(p, 16, 300, 2, p, p, None) == moe.MOE_ERR_SHAPE
     assert L.moe_route_from_logits(None, 16, 8, 2, p, p, None) == moe.MOE_ERR_NULL
-    assert L.moe_align(p, 16, 8, 2, 0, p, p, p, p, p, p, p, 1, None) == moe.MOE_ERR_WORKSPACE
-    assert L.moe_align(p, 16, 8, 2, 0, p, p, None, p, p, p, p, 1 << 20, None) == moe.MOE_ERR_NULL
+    assert L.moe_align(p, 16, 8, 2, p, p, p, p, p, p, p, 1, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_align(p, 16, 8, 2, p, p, None, p, p, p, p, 1 << 20, None) == moe.MOE_ERR_NULL
     assert L.moe_grouped_gate_up(p, p, p, None, None, p, p, p, 16, 256, 8, 2, 128, 128, p, None, None) == \
         moe.MOE_ERR_NULL
     assert L.moe_grouped_down(p, p, p, p, p, 16, 256, 8, 2, 100, p, None) == moe.MOE_ERR_SHAPE
     assert L.moe_combine(p, p, p, p, None, None, 16, 256, 2, 0, p, None) == moe.MOE_ERR_SHAPE
     assert L.moe_combine(p, p, p, None, None, None, 16, 256, 2, 0, None, None) == moe.MOE_ERR_NULL
     for f, args in ((L.moe_route, (p, p, None, None, 0, 256, 8, 2, None, None, None, None, None)),
-                    (L.moe_align, (None, 0, 8, 2, 0, None, None, None, None, None, None, None, 0, None))):
+                    (L.moe_align, (None, 0, 8, 2, None, None, None, None, None, None, None, 0, None))):
         assert f(*args) == moe.MOE_OK  # T = 0 is a no-op
 
 

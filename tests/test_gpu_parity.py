@@ -88,29 +88,35 @@ def test_route_generated(torch, full_layer, name, T):
 
 
 # ------------------------------------------------------------------- align
-def _check_align(b, ids, T, E, k, with_shared):
-    BM = moe.moe_align_tile_rows(T, E, k)
+def _check_align(b, ids, T, E, k):
+    """Align outputs vs the oracle's stable grouping and the BIG/SMALL tiling rule."""
+    BIG = moe.moe_align_tile_rows(T, E, k)
+    SMALL = moe.moe_align_small_tile_rows(T, E, k)
+    max_big = moe.moe_align_max_big_tiles(T, E, k)
     counts, offsets, perm = oracle.align(ids, E)
     g_counts = b["counts"].cpu().numpy()
     g_pad = b["pad_off"].cpu().numpy()
     g_sorted = b["sorted"].cpu().numpy()
     g_inv = b["inv"].cpu().numpy()
-    g_tiles = b["tiles"].cpu().numpy()
+    g_tiles = b["tiles"].cpu().numpy().reshape(-1, 2)
     g_nt = b["n_tiles"].cpu().numpy()
     assert np.array_equal(g_counts, counts)
-    padded = ((counts + BM - 1) // BM) * BM
+    nbig = counts // BIG
+    nsmall = (counts - nbig * BIG + SMALL - 1) // SMALL
+    padded = nbig * BIG + nsmall * SMALL
     assert np.array_equal(g_pad, np.concatenate([[0], np.cumsum(padded)]))
+    assert g_pad[E] <= moe.moe_align_max_rows(T, E, k)
     for e in range(E):
         p0 = g_pad[e]
         assert np.array_equal(g_sorted[p0:p0 + counts[e]], perm[offsets[e]:offsets[e + 1]]), f"expert {e}"
         assert np.all(g_sorted[p0 + counts[e]:p0 + padded[e]] == -1)
     assert np.array_equal(g_sorted[g_inv], np.arange(T * k))
-    n_routed = int(padded.sum() // BM)
-    n_shared = (T + BM - 1) // BM if with_shared else 0
-    assert g_nt.tolist() == [n_routed, n_routed + n_shared]
-    exp_tiles = [(e, g_pad[e] + i * BM) for e in range(E) for i in range(padded[e] // BM)]
-    exp_tiles += [(E, i * BM) for i in range(n_shared)]
-    assert g_tiles[:2 * len(exp_tiles)].reshape(-1, 2).tolist() == [list(t) for t in exp_tiles]
+    assert g_nt.tolist() == [int(nbig.sum()), int(nsmall.sum())]
+    assert nbig.sum() <= max_big and nsmall.sum() <= moe.moe_align_max_tiles(T, E, k) - max_big
+    big = [[e, g_pad[e] + i * BIG] for e in range(E) for i in range(nbig[e])]
+    small = [[e, g_pad[e] + nbig[e] * BIG + i * SMALL] for e in range(E) for i in range(nsmall[e])]
+    assert g_tiles[:len(big)].tolist() == big
+    assert g_tiles[max_big:max_big + len(small)].tolist() == small
 
 
 @pytest.mark.parametrize("name,T", [("tiny", None), ("prefill1k", 1024), ("prefill8k", 8192), ("skew32k", 32768)])
@@ -121,11 +127,11 @@ def test_align_exact(torch, full_layer, name, T):
     lay = _layer_for(inp, full_layer)
     x = G.to_dev_x(inp)
     b = lay.alloc_stage_buffers(x.shape[0])
-    lay.run_route(x, b, with_logits=False)
+    lay.run_route(x, b)
     lay.run_align(x.shape[0], b)
     torch.cuda.synchronize()
     wl = inp["wl"]
-    _check_align(b, b["ids"].cpu().numpy(), x.shape[0], wl.E, wl.k, wl.I_s > 0)
+    _check_align(b, b["ids"].cpu().numpy(), x.shape[0], wl.E, wl.k)
 
 
 # -------------------------------------------------------------- whole layer
@@ -157,7 +163,7 @@ def test_layer_parity(torch, full_layer, label, case):
     inp = _inputs_for(case)
     wl = inp["wl"]
     G.say(f"[layer] {label}: T={inp['x'].shape[0]} H={wl.H} E={wl.E} k={wl.k} I={wl.I} I_s={wl.I_s} "
-          f"BM={moe.moe_align_tile_rows(inp['x'].shape[0], wl.E, wl.k)}")
+          f"BIG={moe.moe_align_tile_rows(inp['x'].shape[0], wl.E, wl.k)}")
     lay = _layer_for(inp, full_layer)
     x = G.to_dev_x(inp)
     y = lay.forward(x)
@@ -237,22 +243,23 @@ def crafted_ids(E, k, T, want, seed=5):
     return ids
 
 
-@pytest.mark.parametrize("E,k,T", [(16, 8, 512), (16, 4, 256), (16, 2, 300)])
+@pytest.mark.parametrize("E,k,T", [(24, 8, 512), (16, 4, 256), (16, 2, 300)])
 def test_padded_tile_boundaries(torch, E, k, T):
-    """Crafted loads of 0, 1, BM-1, BM, BM+1 and 2BM+1 rows per expert (the tile edges)."""
-    BM = moe.moe_align_tile_rows(T, E, k)
-    G.say(f"[boundaries] E={E} k={k} T={T} BM={BM}")
+    """Crafted loads at the tile edges: 0, 1, SMALL-1, SMALL, SMALL+1, BIG-1, BIG, BIG+1, 2BIG+1, BIG+SMALL+1."""
+    B = moe.moe_align_tile_rows(T, E, k)
+    S = moe.moe_align_small_tile_rows(T, E, k)
+    G.say(f"[boundaries] E={E} k={k} T={T} BIG={B} SMALL={S}")
     wl = synth.Workload("bnd", T=T, H=256, E=E, k=k, I=128, I_s=128)
     inp = synth.make_inputs(wl, seed=11)
-    ids = crafted_ids(E, k, T, [0, 1, BM - 1, BM, BM + 1, 2 * BM + 1])
+    ids = crafted_ids(E, k, T, [0, 1, S - 1, S, S + 1, B - 1, B, B + 1, 2 * B + 1, B + S + 1])
     r = oracle.forward(inp, ids_in=ids)
     lay = DeviceLayer.from_inputs(inp)
     x = G.to_dev_x(inp)
     b = lay.run_stages(x, ids=torch.from_numpy(ids).cuda(), w=torch.from_numpy(r["w"].astype(np.float32)).cuda(),
                        s=torch.from_numpy(r["s"].astype(np.float32)).cuda())
     torch.cuda.synchronize()
-    _check_align(b, ids, T, E, k, True)
-    G.check_y(G.y_to_f64(b["y"]), r["y"], f"boundaries BM={BM}")
+    _check_align(b, ids, T, E, k)
+    G.check_y(G.y_to_f64(b["y"]), r["y"], f"boundaries BIG={B} SMALL={S}")
 
 
 # ------------------------------------------------------------ determinism
@@ -303,7 +310,7 @@ def test_full_size_sampled(torch, full_layer, name, T):
     x = G.to_dev_x(inp)
     y = lay.forward(x)
     b = lay.alloc_stage_buffers(T)
-    lay.run_route(x, b, with_logits=False)
+    lay.run_route(x, b)
     torch.cuda.synchronize()
     ids = b["ids"].cpu().numpy()
     r = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["w_sg"], wl.k)
