@@ -265,20 +265,24 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        sample = args.cpu_sample
-        if sample <= 0:
-            probe = 16
+        def run_oracle(n):
             sub = dict(inp)
-            sub["x"] = inp["x"][:probe]
+            sub["x"] = inp["x"][:n]
             t1 = time.time()
             oracle.forward(sub)
-            per_tok = (time.time() - t1) / probe
-            sample = int(min(T, max(probe, 15.0 / max(per_tok, 1e-6))))
-        sub = dict(inp)
-        sub["x"] = inp["x"][:sample]
-        t1 = time.time()
-        oracle.forward(sub)
-        secs = time.time() - t1
+            return time.time() - t1
+
+        sample = args.cpu_sample
+        if sample > 0:
+            secs = run_oracle(sample)
+        else:
+            # grow the sample until it takes about 15 s (every thread busy from the first probe)
+            sample, secs = min(T, 8 * threads), 0.0
+            while True:
+                secs = run_oracle(sample)
+                if secs >= 8.0 or sample >= T:
+                    break
+                sample = int(min(T, max(2 * sample, sample * 15.0 / max(secs, 1e-3))))
         out["cpu_baseline"] = {"value": sample / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                                "sample": f"first {sample} of the {T} tokens of the same workload, whole layer "
                                          f"(route, align, expert FFNs, shared expert, combine), {secs:.1f} s"}
