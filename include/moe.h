@@ -58,12 +58,15 @@ const char* moe_status_str(int status);
 const char* moe_last_error(void);
 
 /*
- * Tile heights chosen for T tokens.  Every expert's rows are cut into
- * floor(count / BIG) tiles of BIG rows, and the remainder is padded to whole
- * tiles of SMALL rows (SMALL divides BIG):
- *   moe_align_tile_rows        BIG   (128, 64 or 32, from the mean rows per expert)
- *   moe_align_small_tile_rows  SMALL (BIG / 2 when BIG = 128, else 32)
- * Depends only on (T, E, k).
+ * Tile heights chosen for T tokens.  BIG (moe_align_tile_rows) is 128, 64 or
+ * 32 from the mean rows per expert.  SMALL (moe_align_small_tile_rows) equals
+ * BIG: every expert's rows are cut into ceil(count / BIG) tiles, the last one
+ * padded, and there is one tile list.  The environment variables
+ * MOE_TILE_ROWS and MOE_SMALL_ROWS (32, 64 or 128; read once per process; for
+ * tuning) override BIG and SMALL.  With SMALL < BIG an expert gets
+ * floor(count / BIG) BIG tiles and its remainder is padded to whole SMALL
+ * tiles, listed separately.  Depends only on (T, E, k) and those variables;
+ * the layer's results do not depend on the tiling.
  */
 int moe_align_tile_rows(int T, int E, int k);
 int moe_align_small_tile_rows(int T, int E, int k);
@@ -74,8 +77,9 @@ int moe_align_small_tile_rows(int T, int E, int k);
  */
 int64_t moe_align_max_rows(int T, int E, int k);
 
-/* Capacity of the BIG tile list: floor(T*k / BIG).  The SMALL tiles start at
- * this entry of the tile table. */
+/* Capacity of the BIG tile list: (T*k + min(E, T*k) * (BIG - 1)) / BIG with
+ * one tile class, floor(T*k / BIG) with two.  The SMALL tiles (if any) start
+ * at this entry of the tile table. */
 int64_t moe_align_max_big_tiles(int T, int E, int k);
 
 /* Entries of the tile table: BIG capacity + SMALL capacity. */

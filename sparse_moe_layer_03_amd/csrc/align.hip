@@ -11,7 +11,8 @@
 // Result (bit-exact, independent of scheduling):
 //   counts[e]   number of assignments a = t*k + j with ids[a] = e
 //   rows of e   floor(counts[e] / BIG) tiles of BIG rows, then the remainder
-//               padded to whole tiles of SMALL rows (SMALL divides BIG)
+//               padded to whole tiles of SMALL rows (SMALL divides BIG); with
+//               SMALL == BIG, ceil(counts[e] / BIG) tiles, all in the BIG list
 //   pad_off[e]  sum of the padded row counts of the experts before e
 //   sorted[pad_off[e] + r] = the r-th assignment of expert e in ascending a;
 //                            -1 for the padding rows of the expert's last tile
@@ -85,8 +86,10 @@ __global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restri
     }
     counts[e] = run;
   }
-  const int nbig = (e < E) ? run / BIG : 0;
-  const int rem = (e < E) ? run - nbig * BIG : 0;
+  // one tile class (SMALL == BIG): every tile of the expert, the last one padded, in the BIG list
+  const bool one = SMALL == BIG;
+  const int nbig = (e < E) ? (one ? (run + BIG - 1) / BIG : run / BIG) : 0;
+  const int rem = (e < E && !one) ? run - nbig * BIG : 0;
   const int nsmall = (rem + SMALL - 1) / SMALL;
   const int padded = nbig * BIG + nsmall * SMALL;
   int total_rows, total_big, total_small;

@@ -36,6 +36,8 @@
 //     use them, also across the barrier;
 //   * work items are dealt so that each XCD gets one contiguous run (the
 //     tiles of one expert share that XCD's L2).
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -416,6 +418,20 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
   // fragment reads, then the LDS writes of the next step (their buffer was
   // released by the barrier just passed) and the next global loads, then the
   // MFMAs with the remaining fragment reads one sub-step ahead.
+  // A wave whose first row carries no data has only padding rows (padding
+  // sits at the end of a tile): it still loads and writes its share of the
+  // tiles but issues no fragment reads and no MFMAs, leaving the SIMD's
+  // matrix core to the other workgroup on the CU.
+  bool live;
+  {
+    const int r = wm * C::WTM;
+    if (it.dense) {
+      live = it.row0 + r < p.T;
+    } else {
+      live = p.sorted[it.row0 + r] >= 0;
+    }
+    live = __builtin_amdgcn_readfirstlane((int)live) != 0;
+  }
   const int nk = p.K / BK;
   gload(pa0, pb0, 0);
   gload(pa1, pb1, 1);
@@ -424,36 +440,45 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
   __syncthreads();
   Frag f0, f1;
   bool pending = false;  // f1 holds the last sub-step of the previous K step
-  auto stage = [&](int st, u32x4 (&pa)[NA], u32x4 (&pb)[NB], int next_kb) {
-    read_frags(f0, st, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    sstore(pa, pb, st ^ 1);
-    gload(pa, pb, next_kb);
-    __builtin_amdgcn_sched_barrier(0);
-    if (pending) mma(f1);
+  auto kloop = [&](auto LIVE) {
+    constexpr bool L = decltype(LIVE)::value;
+    auto stage = [&](int st, u32x4 (&pa)[NA], u32x4 (&pb)[NB], int next_kb) {
+      if constexpr (L) read_frags(f0, st, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      sstore(pa, pb, st ^ 1);
+      gload(pa, pb, next_kb);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (L) {
+        if (pending) mma(f1);
 #pragma unroll
-    for (int sub = 1; sub < SUB; ++sub) {
-      if (sub & 1) {
-        read_frags(f1, st, sub);
-        mma(f0);
-      } else {
-        read_frags(f0, st, sub);
-        mma(f1);
+        for (int sub = 1; sub < SUB; ++sub) {
+          if (sub & 1) {
+            read_frags(f1, st, sub);
+            mma(f0);
+          } else {
+            read_frags(f0, st, sub);
+            mma(f1);
+          }
+        }
+        if (SUB % 2 == 0) {
+          pending = true;
+        } else {
+          mma(f0);
+          pending = false;
+        }
       }
-    }
-    if (SUB % 2 == 0) {
-      pending = true;
-    } else {
-      mma(f0);
-      pending = false;
+    };
+    for (int kb = 0; kb < nk; kb += 2) {
+      stage(0, pa1, pb1, min(kb + 3, nk - 1));  // writes step kb+1 -> LDS[1]
+      __syncthreads();
+      stage(1, pa0, pb0, min(kb + 4, nk - 1));  // writes step kb+2 -> LDS[0]
+      __syncthreads();
     }
   };
-  for (int kb = 0; kb < nk; kb += 2) {
-    stage(0, pa1, pb1, min(kb + 3, nk - 1));  // writes step kb+1 -> LDS[1]
-    __syncthreads();
-    stage(1, pa0, pb0, min(kb + 4, nk - 1));  // writes step kb+2 -> LDS[0]
-    __syncthreads();
-  }
+  if (live)
+    kloop(std::true_type{});
+  else
+    kloop(std::false_type{});
   if (pending) mma(f1);
   epilogue<BM, MODE, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
 }

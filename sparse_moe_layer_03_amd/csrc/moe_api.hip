@@ -162,8 +162,7 @@ int moe_align_tile_rows(int T, int E, int k) {
 int moe_align_small_tile_rows(int T, int E, int k) {
   const int big = moe_align_tile_rows(T, E, k);
   const int ov = small_rows_override();
-  if (ov && ov <= big) return ov;
-  return big >= 128 ? big / 2 : 32;
+  return (ov && ov <= big) ? ov : big;  // one tile class unless overridden
 }
 
 int64_t moe_align_max_rows(int T, int E, int k) {
@@ -173,12 +172,19 @@ int64_t moe_align_max_rows(int T, int E, int k) {
   return n + used * (small - 1);
 }
 
-int64_t moe_align_max_big_tiles(int T, int E, int k) { return (int64_t)T * k / moe_align_tile_rows(T, E, k); }
+int64_t moe_align_max_big_tiles(int T, int E, int k) {
+  const int64_t n = (int64_t)T * k;
+  const int64_t big = moe_align_tile_rows(T, E, k), small = moe_align_small_tile_rows(T, E, k);
+  const int64_t used = n < E ? n : E;
+  if (small == big) return (n + used * (big - 1)) / big;  // sum of ceil(count / BIG)
+  return n / big;
+}
 
 int64_t moe_align_max_tiles(int T, int E, int k) {
   const int64_t n = (int64_t)T * k;
   const int64_t big = moe_align_tile_rows(T, E, k), small = moe_align_small_tile_rows(T, E, k);
   const int64_t used = n < E ? n : E;
+  if (small == big) return moe_align_max_big_tiles(T, E, k);
   int64_t max_small = used * (big / small);  // at most big/small SMALL tiles per expert
   const int64_t bound = (n + used * (small - 1)) / small;
   if (bound < max_small) max_small = bound;
@@ -252,7 +258,7 @@ hipError_t launch_routed_gate_up(const uint16_t* x, const uint16_t* w_gate, cons
   const int BIG = moe_align_tile_rows(T, E, k), SMALL = moe_align_small_tile_rows(T, E, k);
   const int64_t max_big = moe_align_max_big_tiles(T, E, k), max_small = moe_align_max_tiles(T, E, k) - max_big;
   hipError_t e = launch_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, BIG, max_big, h, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || SMALL == BIG) return e;
   return launch_gate_up(x, w_gate, w_up, sorted, tiles + 2 * max_big, n_tiles + 1, T, H, k, I, SMALL, max_small, h,
                         st);
 }
@@ -263,7 +269,7 @@ hipError_t launch_routed_down(const uint16_t* h, const uint16_t* w_down, const i
   const int BIG = moe_align_tile_rows(T, E, k), SMALL = moe_align_small_tile_rows(T, E, k);
   const int64_t max_big = moe_align_max_big_tiles(T, E, k), max_small = moe_align_max_tiles(T, E, k) - max_big;
   hipError_t e = launch_down(h, w_down, sorted, tiles, n_tiles, T, H, k, I, BIG, max_big, o, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || SMALL == BIG) return e;
   return launch_down(h, w_down, sorted, tiles + 2 * max_big, n_tiles + 1, T, H, k, I, SMALL, max_small, o, st);
 }
 }  // namespace

@@ -7,6 +7,7 @@ import re
 import pytest
 
 from sparse_moe_layer_03_amd import moe
+from tests.tiling_rule import tiles_per_expert
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
@@ -42,16 +43,16 @@ def test_tile_rows_policy():
     assert moe.moe_align_tile_rows(32768, 256, 8) == 128
     assert moe.moe_align_tile_rows(1024, 256, 8) == 32
     assert moe.moe_align_tile_rows(2048, 256, 8) == 64
-    assert moe.moe_align_small_tile_rows(8192, 256, 8) == 64
-    for T, E, k in ((2048, 256, 8), (1024, 256, 8), (16, 8, 2), (5, 3, 3)):
-        assert moe.moe_align_small_tile_rows(T, E, k) == 32
-    # padding is at most SMALL - 1 rows per used expert
-    assert moe.moe_align_max_rows(8192, 256, 8) == 8192 * 8 + 256 * 63
+    for T, E, k in ((8192, 256, 8), (2048, 256, 8), (1024, 256, 8), (16, 8, 2), (5, 3, 3)):
+        assert moe.moe_align_small_tile_rows(T, E, k) == moe.moe_align_tile_rows(T, E, k)
+    # padding is at most BIG - 1 rows per used expert
+    assert moe.moe_align_max_rows(8192, 256, 8) == 8192 * 8 + 256 * 127
     assert moe.moe_align_max_rows(2, 256, 8) == 16 + 16 * 31
-    assert moe.moe_align_max_big_tiles(8192, 256, 8) == 8192 * 8 // 128
-    # every expert may hold up to BIG/SMALL small tiles, bounded by the padded rows
-    assert moe.moe_align_max_tiles(8192, 256, 8) == 512 + min(256 * 2, (65536 + 256 * 63) // 64)
-    assert moe.moe_align_max_tiles(16, 8, 2) == 1 + min(8, (32 + 8 * 31) // 32)
+    assert moe.moe_align_max_big_tiles(8192, 256, 8) == (65536 + 256 * 127) // 128
+    assert moe.moe_align_max_tiles(8192, 256, 8) == (65536 + 256 * 127) // 128
+    # BIG == SMALL == 32: one tile class, ceil(count / 32) tiles per expert
+    assert moe.moe_align_max_big_tiles(16, 8, 2) == (32 + 8 * 31) // 32
+    assert moe.moe_align_max_tiles(16, 8, 2) == (32 + 8 * 31) // 32
 
 
 def test_tile_capacity_is_worst_case():
@@ -67,8 +68,7 @@ def test_tile_capacity_is_worst_case():
             if not 0 <= last <= T:
                 continue
             cnt = np.array(list(c) + [last])
-            nb = cnt // B
-            ns = (cnt - nb * B + S - 1) // S
+            nb, ns = tiles_per_expert(cnt, B, S)
             worst = [max(worst[0], int((nb * B + ns * S).sum())), max(worst[1], int(nb.sum())),
                      max(worst[2], int(nb.sum() + ns.sum()))]
         assert worst[0] <= moe.moe_align_max_rows(T, E, k)

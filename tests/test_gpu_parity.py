@@ -2,6 +2,9 @@
 
 Run on an MI355X:  python -u -m pytest tests -m gpu -x -v --timeout 300
 """
+import os
+import sys
+
 import numpy as np
 import pytest
 
@@ -9,6 +12,7 @@ import oracle
 from sparse_moe_layer_03_amd import moe, synth
 from sparse_moe_layer_03_amd.layer import DeviceLayer
 from tests import gpu_util as G
+from tests.boundary_case import BOUNDARY_CASES, check_align, run_boundary_case
 
 pytestmark = pytest.mark.gpu
 
@@ -88,37 +92,6 @@ def test_route_generated(torch, full_layer, name, T):
 
 
 # ------------------------------------------------------------------- align
-def _check_align(b, ids, T, E, k):
-    """Align outputs vs the oracle's stable grouping and the BIG/SMALL tiling rule."""
-    BIG = moe.moe_align_tile_rows(T, E, k)
-    SMALL = moe.moe_align_small_tile_rows(T, E, k)
-    max_big = moe.moe_align_max_big_tiles(T, E, k)
-    counts, offsets, perm = oracle.align(ids, E)
-    g_counts = b["counts"].cpu().numpy()
-    g_pad = b["pad_off"].cpu().numpy()
-    g_sorted = b["sorted"].cpu().numpy()
-    g_inv = b["inv"].cpu().numpy()
-    g_tiles = b["tiles"].cpu().numpy().reshape(-1, 2)
-    g_nt = b["n_tiles"].cpu().numpy()
-    assert np.array_equal(g_counts, counts)
-    nbig = counts // BIG
-    nsmall = (counts - nbig * BIG + SMALL - 1) // SMALL
-    padded = nbig * BIG + nsmall * SMALL
-    assert np.array_equal(g_pad, np.concatenate([[0], np.cumsum(padded)]))
-    assert g_pad[E] <= moe.moe_align_max_rows(T, E, k)
-    for e in range(E):
-        p0 = g_pad[e]
-        assert np.array_equal(g_sorted[p0:p0 + counts[e]], perm[offsets[e]:offsets[e + 1]]), f"expert {e}"
-        assert np.all(g_sorted[p0 + counts[e]:p0 + padded[e]] == -1)
-    assert np.array_equal(g_sorted[g_inv], np.arange(T * k))
-    assert g_nt.tolist() == [int(nbig.sum()), int(nsmall.sum())]
-    assert nbig.sum() <= max_big and nsmall.sum() <= moe.moe_align_max_tiles(T, E, k) - max_big
-    big = [[e, g_pad[e] + i * BIG] for e in range(E) for i in range(nbig[e])]
-    small = [[e, g_pad[e] + nbig[e] * BIG + i * SMALL] for e in range(E) for i in range(nsmall[e])]
-    assert g_tiles[:len(big)].tolist() == big
-    assert g_tiles[max_big:max_big + len(small)].tolist() == small
-
-
 @pytest.mark.parametrize("name,T", [("tiny", None), ("prefill1k", 1024), ("prefill8k", 8192), ("skew32k", 32768)])
 def test_align_exact(torch, full_layer, name, T):
     """Align on the GPU's own ids equals the oracle's stable grouping, bit for bit."""
@@ -131,7 +104,7 @@ def test_align_exact(torch, full_layer, name, T):
     lay.run_align(x.shape[0], b)
     torch.cuda.synchronize()
     wl = inp["wl"]
-    _check_align(b, b["ids"].cpu().numpy(), x.shape[0], wl.E, wl.k)
+    check_align(b, b["ids"].cpu().numpy(), x.shape[0], wl.E, wl.k)
 
 
 # -------------------------------------------------------------- whole layer
@@ -220,46 +193,24 @@ def test_decode_with_bias_and_zero_token(torch, full_layer):
 
 
 # ------------------------------------------------------- padded boundaries
-def crafted_ids(E, k, T, want, seed=5):
-    """[T, k] expert ids whose per-expert loads include the counts in ``want``.
-
-    The experts that do not get a wanted count share the remaining T*k slots
-    evenly.  Slots are dealt column by column from the expert-sorted list, so
-    a row never repeats an expert as long as every load is at most T.
-    """
-    rng = np.random.default_rng(seed)
-    order = rng.permutation(E)
-    counts = np.zeros(E, np.int64)
-    for e, c in zip(order[:len(want)], want):
-        counts[e] = c
-    rest_e = order[len(want):]
-    rest = T * k - counts.sum()
-    counts[rest_e] = rest // len(rest_e)
-    counts[rest_e[:rest % len(rest_e)]] += 1
-    assert counts.sum() == T * k and counts.max() <= T
-    slots = np.repeat(np.arange(E), counts)
-    ids = slots.reshape(k, T).T.astype(np.int32)
-    assert all(len(set(row.tolist())) == k for row in ids)
-    return ids
-
-
-@pytest.mark.parametrize("E,k,T", [(24, 8, 512), (16, 4, 256), (16, 2, 300)])
+@pytest.mark.parametrize("E,k,T", BOUNDARY_CASES)
 def test_padded_tile_boundaries(torch, E, k, T):
-    """Crafted loads at the tile edges: 0, 1, SMALL-1, SMALL, SMALL+1, BIG-1, BIG, BIG+1, 2BIG+1, BIG+SMALL+1."""
-    B = moe.moe_align_tile_rows(T, E, k)
-    S = moe.moe_align_small_tile_rows(T, E, k)
-    G.say(f"[boundaries] E={E} k={k} T={T} BIG={B} SMALL={S}")
-    wl = synth.Workload("bnd", T=T, H=256, E=E, k=k, I=128, I_s=128)
-    inp = synth.make_inputs(wl, seed=11)
-    ids = crafted_ids(E, k, T, [0, 1, S - 1, S, S + 1, B - 1, B, B + 1, 2 * B + 1, B + S + 1])
-    r = oracle.forward(inp, ids_in=ids)
-    lay = DeviceLayer.from_inputs(inp)
-    x = G.to_dev_x(inp)
-    b = lay.run_stages(x, ids=torch.from_numpy(ids).cuda(), w=torch.from_numpy(r["w"].astype(np.float32)).cuda(),
-                       s=torch.from_numpy(r["s"].astype(np.float32)).cuda())
-    torch.cuda.synchronize()
-    _check_align(b, ids, T, E, k)
-    G.check_y(G.y_to_f64(b["y"]), r["y"], f"boundaries BIG={B} SMALL={S}")
+    """Crafted loads at the tile edges, one tile class (the default tiling)."""
+    run_boundary_case(E, k, T)
+
+
+@pytest.mark.parametrize("big,small", [(64, 32), (128, 64)])
+def test_padded_tile_boundaries_two_classes(torch, big, small):
+    """The same cases with BIG and SMALL tile lists, in a child process (the tiling is read once per process)."""
+    import subprocess
+    env = dict(os.environ, MOE_TILE_ROWS=str(big), MOE_SMALL_ROWS=str(small))
+    G.say(f"[boundaries] child process with MOE_TILE_ROWS={big} MOE_SMALL_ROWS={small}")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-m", "tests.boundary_case"], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=240)
+    print(r.stdout[-3000:], r.stderr[-3000:], flush=True)
+    assert r.returncode == 0
+    assert r.stdout.count("ok ") == len(BOUNDARY_CASES) and f"BIG={big} SMALL={small}" in r.stdout
 
 
 # ------------------------------------------------------------ determinism
