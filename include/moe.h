@@ -108,10 +108,12 @@ size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s);
  *          NULL with I_s = 0, or all four set with I_s > 0.
  * Output:  y [T,H] bf16 (fp32 sum rounded to nearest even).
  * Workspace: at least moe_workspace_size(T,H,E,k,I,I_s) bytes, 256-byte aligned.
- * Internally the call runs the router GEMM together with the shared expert's
- * gate/up GEMM, then top-k, align, the routed gate/up and down GEMMs and the
- * combine (or the single-token decode kernels when T == 1) on `stream`; the
- * arithmetic of every element is the same as that of the stage entry points.
+ * Internally the call runs the router GEMM, top-k with the shared-expert
+ * gate, align, the gate/up GEMM (routed tiles and the shared expert's token
+ * tiles in one launch), the routed down GEMM and the combine fused with the
+ * shared down projection (or the single-token decode kernels when T == 1) on
+ * `stream`; the arithmetic of every element is the same as that of the stage
+ * entry points.
  */
 int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,

@@ -11,11 +11,13 @@
 //
 //   D1 router + shared expert: wave per router row (logit) and per shared
 //      (gate, up) row pair; one wave for the shared gate s = sigmoid(x.w_sg)
-//   D2 top-k + renormalised weights (one wavefront, same rule as prefill)
-//   D3 gate/up of the k selected experts: wave per (expert, row) pair,
-//      h = silu(g) * u kept in fp32
-//   D4 down projection + combine: wave per output column, k + 1 rows of
+//   D2 top-k + gate/up of the k selected experts: every workgroup ranks the
+//      E logits in LDS (same selection rule and weights as prefill), then a
+//      wave per (expert, row) pair computes h = silu(g) * u in fp32;
+//      workgroup 0 also stores ids and weights for D3
+//   D3 down projection + combine: wave per output column, k + 1 rows of
 //      W_down / Ws_down, y = sum_j w_j o_j + s o_s in fp32 -> bf16
+// Wave sums use DPP row shifts and row broadcasts (no LDS round trips).
 #include "moe_internal.h"
 #include "moe_topk.h"
 
@@ -51,10 +53,19 @@ DecodeWs carve(void* base, int H, int E, int k, int I, int I_s) {
   return d;
 }
 
+// Sum over the 64 lanes: inclusive row sums by DPP row_shr 1, 2, 4, 8, then
+// row_bcast:15 and row_bcast:31 carry the row totals up; lane 63 holds the
+// total, which is returned to every lane.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  const int z = 0;
+  int b = __float_as_int(v);
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x111, 0xf, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x112, 0xf, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x114, 0xf, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x118, 0xf, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x142, 0xa, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(b, 63));
 }
 
 __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
@@ -130,98 +141,159 @@ __global__ __launch_bounds__(256) void decode_router_shared_kernel(
   }
 }
 
-__global__ __launch_bounds__(64) void decode_topk_kernel(int E, int k, DecodeWs d) {
-  const int lane = threadIdx.x;
-  float v[1][4];
-  bool valid[1][4];
+// Top-k of the E logits (wave 0 of the workgroup), results in LDS.
+__device__ __forceinline__ void block_topk(const float* __restrict__ logits, int E, int k, int* sel_e,
+                                           float* sel_w) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    float v[4];
+    bool valid[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int e = lane + 64 * q;
-    valid[0][q] = e < E;
-    v[0][q] = valid[0][q] ? d.logits[e] : 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      valid[q] = e < E;
+      v[q] = valid[q] ? logits[e] : 0.0f;
+    }
+    int se;
+    float sv, w;
+    wave_topk_weights(v, valid, k, lane, se, sv, w);
+    if (lane < k) {
+      sel_e[lane] = se;
+      sel_w[lane] = w;
+    }
   }
-  int sel_e[1];
-  float sel_v[1];
-  wave_topk<1>(v, valid, k, lane, sel_e, sel_v);
-  float wt = wave_renorm_weight(sel_v[0], k, lane);
-  if (lane < k) {
-    d.ids[lane] = sel_e[0];
-    d.w[lane] = wt;
-  }
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void decode_gate_up_kernel(const uint16_t* __restrict__ x,
-                                                             const uint16_t* __restrict__ w_gate,
-                                                             const uint16_t* __restrict__ w_up, int H, int k, int I,
-                                                             DecodeWs d) {
+__global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ w_gate,
+                                                                  const uint16_t* __restrict__ w_up, int H, int E,
+                                                                  int k, int I, DecodeWs d) {
   __shared__ u32x4 sx[1024];
-  stage_x(x, H, sx);
+  __shared__ int sel_e[kMaxK];
+  __shared__ float sel_w[kMaxK];
+  for (int c = threadIdx.x; c < H / 8; c += 256) sx[c] = reinterpret_cast<const u32x4*>(x)[c];
+  block_topk(d.logits, E, k, sel_e, sel_w);
+  if (blockIdx.x == 0 && threadIdx.x < k) {
+    d.ids[threadIdx.x] = sel_e[threadIdx.x];
+    d.w[threadIdx.x] = sel_w[threadIdx.x];
+  }
+  // wave w of workgroup b takes row pairs b*4 + w + q*(4*gridDim.x), q = 0..NR-1;
+  // the NR pairs' loads are all issued before any reduction
+  constexpr int NR = 1;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // j * I + i
-  if (row >= k * I) return;
-  const int j = row / I, i = row % I;
-  const int e = d.ids[j];
-  float g, u;
-  row_dots(sx, w_gate + ((size_t)e * I + i) * H, w_up + ((size_t)e * I + i) * H, H, lane, g, u);
-  if (lane == 0) d.h[row] = silu(g) * u;
-}
-
-__global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __restrict__ w_down,
-                                                          const uint16_t* __restrict__ ws_down, int H, int k, int I,
-                                                          int I_s, DecodeWs d, uint16_t* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (c >= H) return;
-  float part[kMaxK + 1];
+  const int stride = 4 * gridDim.x;
+  const int row0 = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nch = H / 8;  // chunks per weight row; lane handles chunks lane + 64 c
+  float g[NR], u[NR];
 #pragma unroll
-  for (int j = 0; j <= kMaxK; ++j) part[j] = 0.0f;
-  int ids[kMaxK];
+  for (int q = 0; q < NR; ++q) g[q] = u[q] = 0.0f;
+  for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
+    u32x4 a[NR][4], b[NR][4];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) ids[j] = (j < k) ? d.ids[j] : 0;
-  // routed rows: W_down[e_j, c, :], chunks of 8 along I
-  for (int base = 0; base < I / 8; base += 64) {
-    const int ch = base + lane;
-    u32x4 wv[kMaxK];
+    for (int q = 0; q < NR; ++q) {
+      const int row = row0 + q * stride;
+      const int rr = row < k * I ? row : 0;
+      const size_t off = ((size_t)sel_e[rr / I] * I + rr % I) * H;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k && ch < I / 8)
-        wv[j] = reinterpret_cast<const u32x4*>(w_down + ((size_t)ids[j] * H + c) * I)[ch];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k && ch < I / 8) {
-        const float4* hp = reinterpret_cast<const float4*>(d.h + (size_t)j * I + ch * 8);
-        float4 h0 = hp[0], h1 = hp[1];
-        float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          part[j] += hv[2 * q] * bf16_to_f32((uint16_t)(wv[j][q] & 0xffff));
-          part[j] += hv[2 * q + 1] * bf16_to_f32((uint16_t)(wv[j][q] >> 16));
+      for (int c = 0; c < 4; ++c) {
+        const int ch = c0 + lane + 64 * c;
+        if (ch < nch) {
+          a[q][c] = reinterpret_cast<const u32x4*>(w_gate + off)[ch];
+          b[q][c] = reinterpret_cast<const u32x4*>(w_up + off)[ch];
         }
       }
     }
+#pragma unroll
+    for (int q = 0; q < NR; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int ch = c0 + lane + 64 * c;
+        if (ch < nch) {
+          const u32x4 xv = sx[ch];
+          g[q] += dot8(xv, a[q][c]);
+          u[q] += dot8(xv, b[q][c]);
+        }
+      }
   }
+#pragma unroll
+  for (int q = 0; q < NR; ++q) {
+    const int row = row0 + q * stride;
+    const float gs = wave_sum(g[q]), us = wave_sum(u[q]);
+    if (row < k * I && lane == 0) d.h[row] = silu(gs) * us;
+  }
+}
+
+// Wave per CPW output columns: the k + 1 weight rows of the columns are
+// loaded together (I / 8 chunks each), and each h value read serves them all.
+__global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __restrict__ w_down,
+                                                          const uint16_t* __restrict__ ws_down, int H, int k, int I,
+                                                          int I_s, DecodeWs d, uint16_t* __restrict__ y) {
+  constexpr int CPW = 1;
+  const int lane = threadIdx.x & 63;
+  const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * CPW;
+  if (c0 >= H) return;
+  int ids[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) ids[j] = (j < k) ? d.ids[j] : 0;
+  float part[CPW][kMaxK + 1];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int j = 0; j <= kMaxK; ++j) part[c][j] = 0.0f;
+  auto accum = [&](float& acc, const u32x4& wv, const float* hv) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc += hv[2 * q] * bf16_to_f32((uint16_t)(wv[q] & 0xffff));
+      acc += hv[2 * q + 1] * bf16_to_f32((uint16_t)(wv[q] >> 16));
+    }
+  };
+  // shared expert rows (independent of the routing): issued first
   if (I_s > 0) {
     for (int base = 0; base < I_s / 8; base += 64) {
       const int ch = base + lane;
       if (ch < I_s / 8) {
-        u32x4 wv = reinterpret_cast<const u32x4*>(ws_down + (size_t)c * I_s)[ch];
-        const float4* hp = reinterpret_cast<const float4*>(d.hs + ch * 8);
-        float4 h0 = hp[0], h1 = hp[1];
-        float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        u32x4 wv[CPW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          part[kMaxK] += hv[2 * q] * bf16_to_f32((uint16_t)(wv[q] & 0xffff));
-          part[kMaxK] += hv[2 * q + 1] * bf16_to_f32((uint16_t)(wv[q] >> 16));
-        }
+        for (int c = 0; c < CPW; ++c) wv[c] = reinterpret_cast<const u32x4*>(ws_down + (size_t)(c0 + c) * I_s)[ch];
+        const float4* hp = reinterpret_cast<const float4*>(d.hs + ch * 8);
+        const float4 h0 = hp[0], h1 = hp[1];
+        const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) accum(part[c][kMaxK], wv[c], hv);
       }
     }
   }
-  float yv = 0.0f;
+  // routed rows W_down[e_j, c, :], chunks of 8 along I
+  for (int base = 0; base < I / 8; base += 64) {
+    const int ch = base + lane;
+    u32x4 wv[kMaxK][CPW];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    if (j < k) yv += d.w[j] * wave_sum(part[j]);  // rank order
-  if (I_s > 0) yv += d.s[0] * wave_sum(part[kMaxK]);
-  if (lane == 0) y[c] = f32_to_bf16(yv);
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k && ch < I / 8)
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+          wv[j][c] = reinterpret_cast<const u32x4*>(w_down + ((size_t)ids[j] * H + c0 + c) * I)[ch];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k && ch < I / 8) {
+        const float4* hp = reinterpret_cast<const float4*>(d.h + (size_t)j * I + ch * 8);
+        const float4 h0 = hp[0], h1 = hp[1];
+        const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) accum(part[c][j], wv[j][c], hv);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    float yv = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      if (j < k) yv += d.w[j] * wave_sum(part[c][j]);  // rank order
+    if (I_s > 0) yv += d.s[0] * wave_sum(part[c][kMaxK]);
+    if (lane == 0) y[c0 + c] = f32_to_bf16(yv);
+  }
 }
 
 }  // namespace
@@ -240,8 +312,10 @@ hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const floa
   int rows1 = E + I_s + (I_s > 0 ? 1 : 0);
   hipLaunchKernelGGL(decode_router_shared_kernel, dim3((rows1 + 3) / 4), dim3(256), 0, st, x, w_router, bias,
                      ws_gate, ws_up, w_sg, H, E, I_s, d);
-  hipLaunchKernelGGL(decode_topk_kernel, dim3(1), dim3(64), 0, st, E, k, d);
-  hipLaunchKernelGGL(decode_gate_up_kernel, dim3((k * I + 3) / 4), dim3(256), 0, st, x, w_gate, w_up, H, k, I, d);
+  // 4 waves per workgroup, one row pair per wave
+  hipLaunchKernelGGL(decode_topk_gate_up_kernel, dim3((k * I + 3) / 4), dim3(256), 0, st, x, w_gate, w_up, H, E,
+                     k, I, d);
+  // 4 waves per workgroup, one output column per wave (H is a multiple of 256)
   hipLaunchKernelGGL(decode_down_kernel, dim3((H + 3) / 4), dim3(256), 0, st, w_down, ws_down, H, k, I, I_s, d, y);
   return hipGetLastError();
 }

@@ -11,13 +11,12 @@
 // One kernel template, four launch kinds:
 //   GATE_UP         routed tiles.  A = gathered token rows of x, B = 128 rows
 //                   of W_gate and the matching 128 rows of W_up; epilogue
-//                   silu(g) * u -> h (bf16)
+//                   silu(g) * u -> h (bf16).  The shared expert's gate/up over
+//                   all tokens rides in the same launch as extra token tiles
+//                   (epilogue -> h_s).
 //   DOWN            routed tiles.  A = h rows, B = 256 rows of W_down -> o
-//   DENSE           token tiles.  Per tile, the shared expert's gate/up column
-//                   blocks (epilogue silu(g) * u -> h_s) and one router block
-//                   (B = W_router, experts past E zero; epilogue logits + bias
-//                   -> fp32 logits).  Router and shared expert read the same
-//                   token rows, so they share the launch.
+//   ROUTER          token tiles.  B = W_router (experts past E zero);
+//                   epilogue logits + bias -> fp32 logits
 //   SHARED_COMBINE  token tiles.  A = h_s rows, B = 256 rows of Ws_down;
 //                   epilogue is the deterministic combine
 //                   y = sum_j w_j o[inv[t, j]] + s * acc
@@ -45,9 +44,9 @@ namespace {
 
 constexpr int BNB = 256;  // B rows per tile
 
-enum { GATE_UP = 0, DOWN = 1, DENSE = 2, SHARED_COMBINE = 3 };
+enum { GATE_UP = 0, DOWN = 1, ROUTER = 2, SHARED_COMBINE = 3 };
 
-// Kind of one work item (fixed by the launch, except in DENSE launches).
+// Kind of one work item.
 enum { K_GU = 0, K_ROUTER = 1, K_DOWN = 2, K_COMBINE = 3 };
 
 // Wave layout of a BM x 256 tile over 4 wavefronts.
@@ -67,14 +66,14 @@ struct Cfg<32> {
 };
 
 struct GemmParams {
-  const uint16_t* a;    // x (GATE_UP, DENSE), h (DOWN) or h_s (SHARED_COMBINE)
+  const uint16_t* a;    // x (GATE_UP, ROUTER), h (DOWN) or h_s (SHARED_COMBINE)
   int lda;              // elements per A row
   int K;                // reduction length
   const uint16_t* b0;   // routed W_gate / W_down
   const uint16_t* b1;   // routed W_up
   const uint16_t* bs0;  // shared Ws_gate / Ws_down
   const uint16_t* bs1;  // shared Ws_up
-  const uint16_t* br;   // DENSE: W_router (NULL: no router block)
+  const uint16_t* br;   // ROUTER: W_router
   int N;                // routed output columns per expert
   int N_s;              // shared output columns (0: no shared blocks)
   int E;                // experts (router rows)
@@ -89,8 +88,8 @@ struct GemmParams {
   const int32_t* inv;
   const float* w;
   const float* s;
-  const float* bias;  // DENSE router: bias [E] or NULL
-  float* logits;      // DENSE router: logits [T, E]
+  const float* bias;  // ROUTER: bias [E] or NULL
+  float* logits;      // ROUTER: logits [T, E]
 };
 
 // 16-byte chunk swizzles of an LDS row of KCH chunks.  Any 16 consecutive rows
@@ -116,32 +115,37 @@ template <int BM, int MODE>
 __device__ __forceinline__ Item decode_item(const GemmParams& p) {
   Item it;
   it.kind = (MODE == DOWN) ? K_DOWN : (MODE == SHARED_COMBINE) ? K_COMBINE : K_GU;
-  it.dense = (MODE == DENSE || MODE == SHARED_COMBINE);
+  it.dense = (MODE == ROUTER || MODE == SHARED_COMBINE);
   it.expert = 0;
   it.row0 = -1;
   it.nb = 0;
-  int n_items, nb_per;
+  const int n_tok_tiles = (p.T + BM - 1) / BM;
   if (MODE == GATE_UP || MODE == DOWN) {
-    nb_per = (MODE == GATE_UP) ? p.N / 128 : p.N / 256;
-    n_items = p.n_tiles[0] * nb_per;
-  } else if (MODE == DENSE) {
-    nb_per = p.N_s / 128 + (p.br ? 1 : 0);  // shared gate/up blocks, then the router block
-    n_items = ((p.T + BM - 1) / BM) * nb_per;
-  } else {
-    nb_per = p.N_s / 256;
-    n_items = ((p.T + BM - 1) / BM) * nb_per;
+    // routed tiles first; a GATE_UP launch then appends the shared expert's
+    // token tiles (they fill the launch's last, partly idle round)
+    const int nb_per = (MODE == GATE_UP) ? p.N / 128 : p.N / 256;
+    const int n_routed = p.n_tiles[0] * nb_per;
+    const int nb_sh = (MODE == GATE_UP && p.bs0) ? p.N_s / 128 : 0;
+    const int item = xcd_item(blockIdx.x, n_routed + n_tok_tiles * nb_sh);
+    if (item < 0) return it;
+    if (item < n_routed) {
+      const int tile = item / nb_per;
+      it.nb = item % nb_per;
+      it.expert = p.tiles[2 * tile];
+      it.row0 = p.tiles[2 * tile + 1];
+    } else {
+      it.dense = true;
+      it.row0 = ((item - n_routed) / nb_sh) * BM;
+      it.nb = (item - n_routed) % nb_sh;
+    }
+    return it;
   }
-  const int item = xcd_item(blockIdx.x, n_items);
+  const int nb_per = (MODE == ROUTER) ? 1 : p.N_s / 256;
+  const int item = xcd_item(blockIdx.x, n_tok_tiles * nb_per);
   if (item < 0) return it;
-  const int tile = item / nb_per;
+  it.row0 = (item / nb_per) * BM;
   it.nb = item % nb_per;
-  if (it.dense) {
-    it.row0 = tile * BM;
-    if (MODE == DENSE && p.br && it.nb == nb_per - 1) it.kind = K_ROUTER;
-  } else {
-    it.expert = p.tiles[2 * tile];
-    it.row0 = p.tiles[2 * tile + 1];
-  }
+  if (MODE == ROUTER) it.kind = K_ROUTER;
   return it;
 }
 
@@ -168,7 +172,7 @@ __device__ __forceinline__ const uint16_t* a_row(const GemmParams& p, const Item
 template <int MODE>
 __device__ __forceinline__ const uint16_t* b_row(const GemmParams& p, const Item it, int j, bool& ok) {
   ok = true;
-  if (MODE == DENSE && it.kind == K_ROUTER) {
+  if (MODE == ROUTER && it.kind == K_ROUTER) {
     ok = j < p.E;
     return p.br + (size_t)(ok ? j : 0) * p.K;
   }
@@ -263,7 +267,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
         } else {
           *reinterpret_cast<u32x4*>(p.out + (size_t)(it.row0 + r) * p.ldo + it.nb * 128 + col) = pk;
         }
-      } else if (MODE == DENSE && it.kind == K_ROUTER) {
+      } else if (MODE == ROUTER && it.kind == K_ROUTER) {
         const int t = it.row0 + r;
         if (t < p.T) {
 #pragma unroll
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int r = trow + RPP * i;
-      if constexpr (MODE == DENSE)
+      if constexpr (MODE == ROUTER)
         sB[st * BNB * KCH + r * KCH + swz<KCH>(r, chunk)] = ((bmask >> i) & 1u) ? pb[i] : zero;
       else
         sB[st * BNB * KCH + r * KCH + swz<KCH>(r, chunk)] = pb[i];
@@ -521,9 +525,9 @@ hipError_t launch_mode(const GemmParams& p, int64_t max_items, hipStream_t st) {
 #ifndef MOE_GEMM_CFG_32
 #define MOE_GEMM_CFG_32 32, 32, 2
 #endif
-// Token-tile height of the dense (router + shared expert) launches.
-#ifndef MOE_DENSE_BM
-#define MOE_DENSE_BM 128
+// Token-tile height of the router launch.
+#ifndef MOE_ROUTER_BM
+#define MOE_ROUTER_BM 32
 #endif
 
 template <int MODE>
@@ -538,34 +542,28 @@ hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t
 
 }  // namespace
 
-int dense_tile_rows() { return MOE_DENSE_BM; }
-
-hipError_t launch_dense(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* ws_gate,
-                        const uint16_t* ws_up, int T, int H, int E, int I_s, float* logits, uint16_t* h_s,
-                        hipStream_t st) {
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E,
+                         float* logits, hipStream_t st) {
   GemmParams p = {};
   p.a = x;
   p.lda = H;
   p.K = H;
-  p.bs0 = I_s > 0 ? ws_gate : nullptr;
-  p.bs1 = I_s > 0 ? ws_up : nullptr;
   p.br = w_router;
-  p.N_s = I_s;
   p.E = E;
   p.T = T;
   p.k = 1;
-  p.out_s = h_s;
-  p.ldo_s = I_s;
   p.bias = bias;
   p.logits = logits;
-  constexpr int BM = MOE_DENSE_BM;
-  const int64_t items = (int64_t)((T + BM - 1) / BM) * (I_s / 128 + (w_router ? 1 : 0));
-  return launch_bm<DENSE>(BM, p, items, st);
+  // Small token tiles: one 256-column block per tile, so the tile count is
+  // the launch's whole parallelism.
+  constexpr int BM = MOE_ROUTER_BM;
+  return launch_bm<ROUTER>(BM, p, (int64_t)((T + BM - 1) / BM), st);
 }
 
 hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const int32_t* sorted,
                           const int32_t* tiles, const int32_t* n_tiles, int T, int H, int k, int I, int BM,
-                          int64_t max_tiles, uint16_t* h, hipStream_t st) {
+                          int64_t max_tiles, uint16_t* h, const uint16_t* ws_gate, const uint16_t* ws_up, int I_s,
+                          uint16_t* h_s, hipStream_t st) {
   GemmParams p = {};
   p.a = x;
   p.lda = H;
@@ -580,7 +578,15 @@ hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint1
   p.k = k;
   p.out = h;
   p.ldo = I;
-  return launch_bm<GATE_UP>(BM, p, max_tiles * (I / 128), st);
+  if (I_s > 0) {
+    p.bs0 = ws_gate;
+    p.bs1 = ws_up;
+    p.N_s = I_s;
+    p.out_s = h_s;
+    p.ldo_s = I_s;
+  }
+  const int64_t shared_items = I_s > 0 ? (int64_t)((T + BM - 1) / BM) * (I_s / 128) : 0;
+  return launch_bm<GATE_UP>(BM, p, max_tiles * (I / 128) + shared_items, st);
 }
 
 hipError_t launch_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,

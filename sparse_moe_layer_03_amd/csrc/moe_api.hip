@@ -214,7 +214,7 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_b
     return fail(MOE_ERR_ALIGN, "moe_route: bf16 tensors must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
   const hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_dense(x, w_router, router_bias, nullptr, nullptr, T, H, E, 0, logits, nullptr, st);
+  hipError_t e = launch_router(x, w_router, router_bias, T, H, E, logits, st);
   if (e != hipSuccess) return hip_status(e, "moe_route: router GEMM");
   return hip_status(launch_topk(logits, T, E, k, w_sg ? x : nullptr, w_sg, H, ids, w, s, st), "moe_route: top-k");
 }
@@ -254,13 +254,15 @@ namespace {
 // The routed GEMMs of both tile classes.
 hipError_t launch_routed_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up,
                                  const int32_t* sorted, const int32_t* tiles, const int32_t* n_tiles, int T, int H,
-                                 int E, int k, int I, uint16_t* h, hipStream_t st) {
+                                 int E, int k, int I, uint16_t* h, const uint16_t* ws_gate, const uint16_t* ws_up,
+                                 int I_s, uint16_t* h_s, hipStream_t st) {
   const int BIG = moe_align_tile_rows(T, E, k), SMALL = moe_align_small_tile_rows(T, E, k);
   const int64_t max_big = moe_align_max_big_tiles(T, E, k), max_small = moe_align_max_tiles(T, E, k) - max_big;
-  hipError_t e = launch_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, BIG, max_big, h, st);
+  hipError_t e = launch_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, BIG, max_big, h, ws_gate, ws_up,
+                                I_s, h_s, st);
   if (e != hipSuccess || SMALL == BIG) return e;
   return launch_gate_up(x, w_gate, w_up, sorted, tiles + 2 * max_big, n_tiles + 1, T, H, k, I, SMALL, max_small, h,
-                        st);
+                        nullptr, nullptr, 0, nullptr, st);
 }
 
 hipError_t launch_routed_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,
@@ -287,12 +289,8 @@ int moe_grouped_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_
       (I_s > 0 && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(h_s))))
     return fail(MOE_ERR_ALIGN, "moe_grouped_gate_up: tensors must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
-  const hipStream_t st = (hipStream_t)stream;
-  if (I_s > 0) {
-    hipError_t e = launch_dense(x, nullptr, nullptr, ws_gate, ws_up, T, H, E, I_s, nullptr, h_s, st);
-    if (e != hipSuccess) return hip_status(e, "moe_grouped_gate_up: shared expert");
-  }
-  return hip_status(launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, E, k, I, h, st),
+  return hip_status(launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, E, k, I, h, ws_gate, ws_up,
+                                          I_s, h_s, (hipStream_t)stream),
                     "moe_grouped_gate_up");
 }
 
@@ -369,16 +367,15 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   uint16_t* h_s = I_s > 0 ? reinterpret_cast<uint16_t*>(base + L.off_hs) : nullptr;
   uint16_t* o = reinterpret_cast<uint16_t*>(base + L.off_o);
 
-  // router logits and the shared expert's gate/up share one launch (same token rows)
-  hipError_t e = launch_dense(x, w_router, router_bias, ws_gate, ws_up, T, H, E, I_s, logits, h_s, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: router + shared gate/up");
+  hipError_t e = launch_router(x, w_router, router_bias, T, H, E, logits, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: router");
   e = launch_topk(logits, T, E, k, I_s > 0 ? x : nullptr, w_sg, H, ids, w, I_s > 0 ? s : nullptr, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: top-k");
   e = launch_align(ids, T, E, k, L.BIG, L.SMALL, (int)L.max_big, counts, pad_off, sorted, inv, tiles, n_tiles, scratch,
                    st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: align");
-  e = launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, E, k, I, h, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: gate_up");
+  e = launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, E, k, I, h, ws_gate, ws_up, I_s, h_s, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: gate_up (routed + shared)");
   e = launch_routed_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, o, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: down");
   e = launch_combine(o, inv, w, h_s, ws_down, I_s > 0 ? s : nullptr, T, H, k, I_s, y, st);

@@ -47,19 +47,21 @@ __device__ __forceinline__ int xcd_item(int bid, int n_items) {
 }
 
 // Host-side launch helpers (defined in the .hip files).
-hipError_t launch_dense(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* ws_gate,
-                        const uint16_t* ws_up, int T, int H, int E, int I_s, float* logits, uint16_t* h_s,
-                        hipStream_t st);
-int dense_tile_rows();
+// Router GEMM over token tiles: fp32 logits (+ bias, -0 -> +0).
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E,
+                         float* logits, hipStream_t st);
 hipError_t launch_topk(const float* logits, int T, int E, int k, const uint16_t* x, const uint16_t* w_sg, int H,
                        int32_t* ids, float* w, float* s, hipStream_t st);
 hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
                         int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
                         int32_t* n_tiles, int32_t* scratch, hipStream_t st);
 int align_num_chunks(int T, int k);
+// Routed gate/up tiles of one tile list; with I_s > 0 the shared expert's
+// gate/up over all T tokens (tiles of BM tokens) joins the same launch.
 hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const int32_t* sorted,
                           const int32_t* tiles, const int32_t* n_tiles, int T, int H, int k, int I, int BM,
-                          int64_t max_tiles, uint16_t* h, hipStream_t st);
+                          int64_t max_tiles, uint16_t* h, const uint16_t* ws_gate, const uint16_t* ws_up, int I_s,
+                          uint16_t* h_s, hipStream_t st);
 hipError_t launch_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,
                        const int32_t* n_tiles, int T, int H, int k, int I, int BM, int64_t max_tiles, uint16_t* o,
                        hipStream_t st);

@@ -36,22 +36,19 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
       }
     }
   }
-  float v[1][4];
-  bool valid[1][4];
+  float v[4];
+  bool valid[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    int e = lane + 64 * q;
-    valid[0][q] = e < E;
-    float val = valid[0][q] ? logits[(size_t)t * E + e] : 0.0f;
-    if (val == 0.0f) val = 0.0f;
-    v[0][q] = val;
+    const int e = lane + 64 * q;
+    valid[q] = e < E;
+    v[q] = valid[q] ? logits[(size_t)t * E + e] : 0.0f;
   }
-  int sel_e[1];
-  float sel_v[1];
-  wave_topk<1>(v, valid, k, lane, sel_e, sel_v);
-  float wt = wave_renorm_weight(sel_v[0], k, lane);
+  int sel_e;
+  float sel_v, wt;
+  wave_topk_weights(v, valid, k, lane, sel_e, sel_v, wt);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = sel_e[0];
+    ids[(size_t)t * k + lane] = sel_e;
     wout[(size_t)t * k + lane] = wt;
   }
   if (gate) {
