@@ -35,18 +35,76 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_prefill8k_hbm_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 --pmc record
+    (FETCH_SIZE and WRITE_SIZE passes, scaled by a device copy of known size), or None when
+    the record is missing or any source it was taken on has changed since."""
+    import hashlib
+    try:
+        line = [ln for ln in open(TRAFFIC_RECORD) if ln.startswith("traffic-record:")][0]
+        rec = json.loads(line.split(":", 1)[1])
+        for path, digest in rec["sources"].items():
+            if hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16] != digest:
+                return None
+        return rec["traffic_bytes"]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+
+
 def algorithmic(T, H, E, k, I, I_s):
     """Flops of the layer per call (what the method must compute, no padding)."""
     routed = 6 * T * k * H * I          # gate, up (2 * 2HI) and down (2HI) per assignment
     shared = 6 * T * H * I_s
     router = 2 * T * H * E + 2 * T * H  # logits + shared gate
-    routed_gate_up = 4 * T * k * H * I  # the routed gate/up GEMM alone
-    return routed + shared + router, routed_gate_up
+    gate_up = 4 * T * H * (k * I + I_s)  # the gate/up launch: routed tiles + the shared expert's token tiles
+    return routed + shared + router, gate_up
 
 
 def decode_bytes(H, E, k, I, I_s):
     """Bytes one T=1 call must move: router, shared gate, k experts, shared expert, x, y."""
     return 2 * (E * H + H + k * 3 * H * I + 3 * H * I_s + H + H)
+
+
+def kernel_only(args):
+    """The dominant kernel alone (for rocprofv3 --pmc passes): route and align once, then
+    --warmup + --steps launches of the gate/up GEMM (routed and shared tiles, as moe_forward
+    launches it), then a 256 MiB device copy."""
+    import torch
+    from sparse_moe_layer_03_amd import moe, synth
+    from sparse_moe_layer_03_amd.layer import DeviceLayer, to_device_bf16
+    dev = torch.device("cuda:0")
+    wl = synth.workload("prefill8k")
+    T, H, E, k, I, I_s = wl.T, wl.H, wl.E, wl.k, wl.I, wl.I_s
+    inp = synth.make_inputs(wl, seed=0)
+    lay = DeviceLayer.from_inputs(inp, dev)
+    x = to_device_bf16(inp["x"], dev)
+    b = lay.alloc_stage_buffers(T)
+    lay.run_route(x, b)
+    lay.run_align(T, b)
+    W = lay.w
+    def launch():
+        moe.moe_grouped_gate_up(x, W["w_gate"], W["w_up"], W["ws_gate"], W["ws_up"], b["sorted"], b["tiles"],
+                                b["n_tiles"], T, H, E, k, I, I_s, b["h"], b["h_s"])
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    c = torch.empty_like(a)
+    c.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel": "gate/up GEMM (routed + shared tiles)", "workload": "8192 tokens", "launches": args.warmup + args.steps,
+                      "us_per_launch": us, "copy_bytes": a.numel() * 4}), flush=True)
+    return 0
 
 
 def main():
@@ -62,6 +120,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--kernel", choices=["gate_up"], default=None,
+                    help="run only the dominant kernel (routed gate/up GEMM of the 8192-token workload) "
+                         "--steps times, then a 256 MiB device copy: the run that hardware counters are taken on")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -74,6 +135,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
+    if args.kernel:
+        return kernel_only(args)
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(0)
 
@@ -137,19 +200,18 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, n in enumerate(names)}
-    # timed region 3: the dominant kernel alone -- the routed grouped gate/up GEMM (its BIG-tile and
-    # SMALL-tile launches), events on the stream it is launched on
-    W = base.w
+    # timed region 3: the dominant kernel alone -- the gate/up GEMM launch (routed tiles and the
+    # shared expert's token tiles, as moe_forward launches it), events on its launch stream
     gu_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    def routed_gate_up(lay):
-        moe.moe_grouped_gate_up(x, lay.w["w_gate"], lay.w["w_up"], None, None, bufs["sorted"], bufs["tiles"],
-                                bufs["n_tiles"], T, H, E, k, I, 0, bufs["h"], None, stream)
+    def gate_up_launch(lay):
+        moe.moe_grouped_gate_up(x, lay.w["w_gate"], lay.w["w_up"], lay.w["ws_gate"], lay.w["ws_up"], bufs["sorted"],
+                                bufs["tiles"], bufs["n_tiles"], T, H, E, k, I, I_s, bufs["h"], bufs["h_s"], stream)
     for i in range(args.warmup):
-        routed_gate_up(layers[i % len(layers)])
+        gate_up_launch(layers[i % len(layers)])
     torch.cuda.synchronize()
     gu_ev[0].record(stream)
     for i in range(args.steps):
-        routed_gate_up(layers[i % len(layers)])
+        gate_up_launch(layers[i % len(layers)])
     gu_ev[1].record(stream)
     torch.cuda.synchronize()
     gu_ms = gu_ev[0].elapsed_time(gu_ev[1]) / args.steps
@@ -183,9 +245,10 @@ def main():
         "layer_mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stage_us": {n: v * 1e3 for n, v in stage_ms.items()},
         "padding_overhead": padded_rows / (T * k) - 1.0,
-        "roofline": {"kernel": "routed grouped gate/up GEMM with SwiGLU epilogue (BIG + SMALL tile launches)",
+        "roofline": {"kernel": "grouped_gemm_kernel<128, 32, 2, 0>: gate/up GEMM with SwiGLU epilogue, one launch over all "
+                               "expert tiles and the shared expert's token tiles",
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "flops_per_launch": gate_up_flops, "avg_launch_us": gu_ms * 1e3,
                      "padded_rows": padded_rows},
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
@@ -292,4 +355,4 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    sys.exit(main())

@@ -154,7 +154,7 @@ int moe_route_from_logits(const float* logits, int T, int E, int k,
  *                   in expert order from entry 0, the SMALL tiles in expert
  *                   order from entry moe_align_max_big_tiles
  *   n_tiles [2]     number of BIG tiles, number of SMALL tiles
- *   scratch         at least moe_align_scratch_size(T,E,k) bytes
+ *   scratch         at least moe_align_scratch_size(T,E,k) bytes, 16-byte aligned
  */
 size_t moe_align_scratch_size(int T, int E, int k);
 int moe_align(const int32_t* ids, int T, int E, int k,
@@ -177,8 +177,10 @@ int moe_grouped_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_
 
 /*
  * Grouped down GEMM over the routed tiles:
- *   o[p,c] = bf16( sum_i h[p,i] W_down[e,c,i] ) for every non-padding row p.
- *   o [moe_align_max_rows, H] bf16 (padding rows are not written).
+ *   for every non-padding row p holding assignment a = sorted[p]:
+ *     o[a,c] = bf16( sum_i h[p,i] W_down[e,c,i] )
+ *   o [T*k, H] bf16, one row per assignment a = t*k + j (token-major), so a
+ *   token's k expert outputs are contiguous.
  */
 int moe_grouped_down(const uint16_t* h, const uint16_t* w_down,
                      const int32_t* sorted, const int32_t* tiles, const int32_t* n_tiles,
@@ -187,12 +189,12 @@ int moe_grouped_down(const uint16_t* h, const uint16_t* w_down,
 /*
  * Deterministic, atomic-free combine, fused with the shared expert's down
  * projection when I_s > 0:
- *   y[t,c] = bf16( (((w[t,0] o[inv[t*k]] + w[t,1] o[inv[t*k+1]]) + ...)
- *                   + w[t,k-1] o[inv[t*k+k-1]]) + s[t] (sum_i h_s[t,i] Ws_down[c,i]) )
- *   in fp32, j ascending, then the shared term.
+ *   y[t,c] = bf16( (((w[t,0] o[t*k] + w[t,1] o[t*k+1]) + ...)
+ *                   + w[t,k-1] o[t*k+k-1]) + s[t] (sum_i h_s[t,i] Ws_down[c,i]) )
+ *   in fp32, j ascending, then the shared term.  o as moe_grouped_down writes it.
  *   h_s, ws_down and s are NULL iff I_s == 0.
  */
-int moe_combine(const uint16_t* o, const int32_t* inv, const float* w,
+int moe_combine(const uint16_t* o, const float* w,
                 const uint16_t* h_s, const uint16_t* ws_down, const float* s,
                 int T, int H, int k, int I_s, uint16_t* y, void* stream);
 

@@ -32,7 +32,9 @@ namespace {
 
 constexpr int CH = 1024;  // assignments per chunk
 
-__global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int n, int E,
+// chunk_hist[e * nc + c]: assignments of chunk c routed to expert e (expert-major,
+// so the scan reads one expert's chunk counts contiguously)
+__global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int n, int E, int nc,
                                                          int32_t* __restrict__ chunk_hist) {
   __shared__ int32_t hist[kMaxE];
   const int tid = threadIdx.x;
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restri
   const int a1 = min(a0 + CH, n);
   for (int a = a0 + tid; a < a1; a += 256) atomicAdd(&hist[ids[a]], 1);
   __syncthreads();
-  for (int e = tid; e < E; e += 256) chunk_hist[(size_t)blockIdx.x * E + e] = hist[e];
+  for (int e = tid; e < E; e += 256) chunk_hist[(size_t)e * nc + blockIdx.x] = hist[e];
 }
 
 // Exclusive scan of one value per thread over the 256 threads of a block.
@@ -73,20 +75,27 @@ __global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restri
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    // exclusive offset of every chunk within expert e; loads issued 16 at a time
-    for (int c0 = 0; c0 < n_chunks; c0 += 16) {
-      int hv[16];
+    // exclusive offset of every chunk within expert e; the expert's counts are
+    // contiguous (nc is a multiple of 4), read 64 at a time with 16-byte loads
+    const int4* src = reinterpret_cast<const int4*>(chunk_hist + (size_t)e * n_chunks);
+    int4* dst = reinterpret_cast<int4*>(chunk_off + (size_t)e * n_chunks);
+    for (int c0 = 0; c0 < n_chunks / 4; c0 += 16) {
+      int4 hv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) hv[i] = (c0 + i < n_chunks) ? chunk_hist[(size_t)(c0 + i) * E + e] : 0;
+      for (int i = 0; i < 16; ++i) hv[i] = (c0 + i < n_chunks / 4) ? src[c0 + i] : make_int4(0, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (c0 + i < n_chunks) chunk_off[(size_t)(c0 + i) * E + e] = run;
-        run += hv[i];
+        int4 o;
+        o.x = run;
+        o.y = o.x + hv[i].x;
+        o.z = o.y + hv[i].y;
+        o.w = o.z + hv[i].z;
+        run = o.w + hv[i].w;
+        if (c0 + i < n_chunks / 4) dst[c0 + i] = o;
       }
     }
     counts[e] = run;
   }
-  // one tile class (SMALL == BIG): every tile of the expert, the last one padded, in the BIG list
   const bool one = SMALL == BIG;
   const int nbig = (e < E) ? (one ? (run + BIG - 1) / BIG : run / BIG) : 0;
   const int rem = (e < E && !one) ? run - nbig * BIG : 0;
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restri
   }
 }
 
-__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
+__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E, int nc,
                                                             const int32_t* __restrict__ chunk_off,
                                                             const int32_t* __restrict__ pad_off,
                                                             int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int a0 = blockIdx.x * CH;
   const int a1 = min(a0 + CH, n);
-  for (int e = tid; e < E; e += 256) base[e] = pad_off[e] + chunk_off[(size_t)blockIdx.x * E + e];
+  for (int e = tid; e < E; e += 256) base[e] = pad_off[e] + chunk_off[(size_t)e * nc + blockIdx.x];
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int s0 = a0; s0 < a1; s0 += 256) {
     for (int i = tid; i < 4 * kMaxE; i += 256) (&wcnt[0][0])[i] = 0;
@@ -157,18 +166,21 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
 
 }  // namespace
 
-int align_num_chunks(int T, int k) { return (int)(((int64_t)T * k + CH - 1) / CH); }
+// Chunks of CH assignments, rounded up to a multiple of 4 (the scan reads 4
+// chunk counts per 16-byte load; chunks past the end are empty).
+int align_num_chunks(int T, int k) { return (int)((((int64_t)T * k + CH - 1) / CH + 3) / 4 * 4); }
 
 hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
                         int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
                         int32_t* n_tiles, int32_t* scratch, hipStream_t st) {
   const int n = T * k;
   const int nc = align_num_chunks(T, k);
-  hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, scratch);
+  hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, scratch);
   int32_t* chunk_off = scratch + (size_t)nc * E;
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(256), 0, st, scratch, chunk_off, nc, E, BIG, SMALL, small_base,
                      counts, pad_off, sorted, tiles, n_tiles);
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, chunk_off, pad_off, sorted, inv);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, chunk_off, pad_off, sorted,
+                     inv);
   return hipGetLastError();
 }
 

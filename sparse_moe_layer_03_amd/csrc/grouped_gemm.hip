@@ -14,12 +14,13 @@
 //                   silu(g) * u -> h (bf16).  The shared expert's gate/up over
 //                   all tokens rides in the same launch as extra token tiles
 //                   (epilogue -> h_s).
-//   DOWN            routed tiles.  A = h rows, B = 256 rows of W_down -> o
+//   DOWN            routed tiles.  A = h rows, B = 256 rows of W_down -> o,
+//                   stored at the row of the assignment (t*k + j) it holds
 //   ROUTER          token tiles.  B = W_router (experts past E zero);
 //                   epilogue logits + bias -> fp32 logits
 //   SHARED_COMBINE  token tiles.  A = h_s rows, B = 256 rows of Ws_down;
 //                   epilogue is the deterministic combine
-//                   y = sum_j w_j o[inv[t, j]] + s * acc
+//                   y = sum_j w_j o[t*k + j] + s * acc
 //
 // Data movement (256 threads, 4 wavefronts, BM x 256 tile):
 //   * per K step of BK columns the A tile (BM x 2BK bytes) and B tile
@@ -84,8 +85,7 @@ struct GemmParams {
   uint16_t* out;    // h or o
   uint16_t* out_s;  // h_s or y
   int ldo, ldo_s;
-  const uint16_t* o;  // combine inputs
-  const int32_t* inv;
+  const uint16_t* o;  // combine inputs: o rows in assignment order (t*k + j)
   const float* w;
   const float* s;
   const float* bias;  // ROUTER: bias [E] or NULL
@@ -129,6 +129,7 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p) {
     const int item = xcd_item(blockIdx.x, n_routed + n_tok_tiles * nb_sh);
     if (item < 0) return it;
     if (item < n_routed) {
+      // tile major: the column blocks of a tile run together and share its A rows in L2
       const int tile = item / nb_per;
       it.nb = item % nb_per;
       it.expert = p.tiles[2 * tile];
@@ -186,28 +187,25 @@ __device__ __forceinline__ const uint16_t* b_row(const GemmParams& p, const Item
   return (it.dense ? p.bs0 : p.b0 + (size_t)it.expert * p.N * p.K) + col * p.K;
 }
 
-// Weighted sum of token t's k expert rows of o at columns ocol..ocol+7, in
+// Weighted sum of token t's k expert outputs at columns ocol..ocol+7, in
 // rank order j = 0..k-1, fp32: y = ((w_0 o_0 + w_1 o_1) + ...) + w_{k-1} o_{k-1}.
-// The row indices and weights of 8 ranks are read first and their 8 row loads
-// issued together (the loads are independent; only the sum is ordered).
-__device__ __forceinline__ void gather_combine8(const uint16_t* __restrict__ o, const int32_t* __restrict__ inv,
-                                                const float* __restrict__ w, int t, int k, int ldo, int ocol,
-                                                float (&y)[8]) {
+// o holds one row per assignment a = t*k + j, so a token's k rows are
+// contiguous and every load address is known up front; the 8 row loads of a
+// group are issued together (only the sum is ordered).
+__device__ __forceinline__ void gather_combine8(const uint16_t* __restrict__ o, const float* __restrict__ w, int t,
+                                                int k, int ldo, int ocol, float (&y)[8]) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) y[q] = 0.0f;
   const size_t base = (size_t)t * k;
   for (int j0 = 0; j0 < k; j0 += 8) {
-    int row[8];
     float wj[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const bool ok = j0 + q < k;
-      row[q] = inv[base + (ok ? j0 + q : 0)];
-      wj[q] = ok ? w[base + j0 + q] : 0.0f;
-    }
     u32x4 ov[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) ov[q] = *reinterpret_cast<const u32x4*>(o + (size_t)row[q] * ldo + ocol);
+    for (int q = 0; q < 8; ++q) {
+      const int j = (j0 + q < k) ? j0 + q : k - 1;
+      wj[q] = w[base + j];
+      ov[q] = *reinterpret_cast<const u32x4*>(o + (base + j) * ldo + ocol);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (j0 + q < k) {
@@ -253,7 +251,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
       }
     }
     __syncthreads();
-    for (int r = cr; r < BM; r += 32) {
+    for (int r = cr; r < BM && MODE != SHARED_COMBINE; r += 32) {
       const float4 v0 = *reinterpret_cast<const float4*>(sc + r * ESLD + cc);
       const float4 v1 = *reinterpret_cast<const float4*>(sc + r * ESLD + cc + 4);
       float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -281,23 +279,39 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
           }
         }
       } else if (MODE == DOWN) {
-        if (p.sorted[it.row0 + r] >= 0) {
+        const int a = p.sorted[it.row0 + r];  // assignment held by the row; -1 for padding
+        if (a >= 0) {
           const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                             pack_bf16x2(v[6], v[7])};
-          *reinterpret_cast<u32x4*>(p.out + (size_t)(it.row0 + r) * p.ldo + it.nb * 256 + col) = pk;
+          *reinterpret_cast<u32x4*>(p.out + (size_t)a * p.ldo + it.nb * 256 + col) = pk;
         }
-      } else if (MODE == SHARED_COMBINE) {
+      }
+    }
+    if constexpr (MODE == SHARED_COMBINE) {
+      // every row of this thread gathers its k expert rows, then adds s[t]
+      // times the shared expert's output
+      constexpr int RPT = BM / 32;
+      float yv[RPT][8];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int t = it.row0 + cr + 32 * i;
+        gather_combine8(p.o, p.w, t < p.T ? t : p.T - 1, p.k, p.ldo, it.nb * 256 + pass * EPW + cc, yv[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int r = cr + 32 * i;
         const int t = it.row0 + r;
         if (t < p.T) {
-          const int ocol = it.nb * 256 + col;
-          float y[8];
-          gather_combine8(p.o, p.inv, p.w, t, p.k, p.ldo, ocol, y);
+          const float4 v0 = *reinterpret_cast<const float4*>(sc + r * ESLD + cc);
+          const float4 v1 = *reinterpret_cast<const float4*>(sc + r * ESLD + cc + 4);
+          const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
           const float st = p.s[t];
+          float* y = yv[i];
 #pragma unroll
           for (int q = 0; q < 8; ++q) y[q] += st * v[q];
           const u32x4 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
                             pack_bf16x2(y[6], y[7])};
-          *reinterpret_cast<u32x4*>(p.out_s + (size_t)t * p.ldo_s + ocol) = pk;
+          *reinterpret_cast<u32x4*>(p.out_s + (size_t)t * p.ldo_s + it.nb * 256 + pass * EPW + cc) = pk;
         }
       }
     }
@@ -487,17 +501,16 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
   epilogue<BM, MODE, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
 }
 
-// Combine without a shared expert: y[t,c] = sum_j w[t,j] o[inv[t*k+j], c].
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ inv,
-                                                      const float* __restrict__ w, int T, int H, int k,
-                                                      uint16_t* __restrict__ y) {
+// Combine without a shared expert: y[t,c] = sum_j w[t,j] o[t*k+j, c].
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o, const float* __restrict__ w,
+                                                      int T, int H, int k, uint16_t* __restrict__ y) {
   const int per_tok = H / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)T * per_tok) return;
   const int t = (int)(idx / per_tok);
   const int col = (int)(idx % per_tok) * 8;
   float acc[8];
-  gather_combine8(o, inv, w, t, k, H, col, acc);
+  gather_combine8(o, w, t, k, H, col, acc);
   u32x4 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
               pack_bf16x2(acc[6], acc[7])};
   *reinterpret_cast<u32x4*>(y + (size_t)t * H + col) = pk;
@@ -525,17 +538,25 @@ hipError_t launch_mode(const GemmParams& p, int64_t max_items, hipStream_t st) {
 #ifndef MOE_GEMM_CFG_32
 #define MOE_GEMM_CFG_32 32, 32, 2
 #endif
-// Token-tile height of the router launch.
-#ifndef MOE_ROUTER_BM
-#define MOE_ROUTER_BM 32
+// Router launch: (token-tile rows, K step, workgroups per CU).
+#ifndef MOE_ROUTER_CFG
+#define MOE_ROUTER_CFG 32, 64, 2
 #endif
+// Down GEMM with 128-row tiles (K = I is short, so its K step may differ).
+#ifndef MOE_DOWN_CFG_128
+#define MOE_DOWN_CFG_128 MOE_GEMM_CFG_128
+#endif
+
+constexpr int router_rows(int bm, int, int) { return bm; }
 
 template <int MODE>
 hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t st) {
   switch (BM) {
     case 32: return launch_mode<MOE_GEMM_CFG_32, MODE>(p, max_items, st);
     case 64: return launch_mode<MOE_GEMM_CFG_64, MODE>(p, max_items, st);
-    case 128: return launch_mode<MOE_GEMM_CFG_128, MODE>(p, max_items, st);
+    case 128:
+      if constexpr (MODE == DOWN) return launch_mode<MOE_DOWN_CFG_128, MODE>(p, max_items, st);
+      return launch_mode<MOE_GEMM_CFG_128, MODE>(p, max_items, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -556,8 +577,8 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const floa
   p.logits = logits;
   // Small token tiles: one 256-column block per tile, so the tile count is
   // the launch's whole parallelism.
-  constexpr int BM = MOE_ROUTER_BM;
-  return launch_bm<ROUTER>(BM, p, (int64_t)((T + BM - 1) / BM), st);
+  constexpr int BM = router_rows(MOE_ROUTER_CFG);
+  return launch_mode<MOE_ROUTER_CFG, ROUTER>(p, (int64_t)((T + BM - 1) / BM), st);
 }
 
 hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const int32_t* sorted,
@@ -608,12 +629,12 @@ hipError_t launch_down(const uint16_t* h, const uint16_t* w_down, const int32_t*
   return launch_bm<DOWN>(BM, p, max_tiles * (H / 256), st);
 }
 
-hipError_t launch_combine(const uint16_t* o, const int32_t* inv, const float* w, const uint16_t* h_s,
+hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s,
                           const uint16_t* ws_down, const float* s, int T, int H, int k, int I_s, uint16_t* y,
                           hipStream_t st) {
   if (I_s == 0) {
     int64_t n = (int64_t)T * (H / 8);
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, o, inv, w, T, H, k, y);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, o, w, T, H, k, y);
     return hipGetLastError();
   }
   GemmParams p = {};
@@ -628,7 +649,6 @@ hipError_t launch_combine(const uint16_t* o, const int32_t* inv, const float* w,
   p.ldo = H;
   p.ldo_s = H;
   p.o = o;
-  p.inv = inv;
   p.w = w;
   p.s = s;
   constexpr int BM = 128;

@@ -125,7 +125,7 @@ Layout layout(int T, int H, int E, int k, int I, int I_s) {
   L.off_scratch = take(moe_align_scratch_size(T, E, k));
   L.off_h = take((size_t)L.max_rows * I * 2);
   L.off_hs = take((size_t)T * (I_s > 0 ? I_s : 0) * 2);
-  L.off_o = take((size_t)L.max_rows * H * 2);
+  L.off_o = take(n * H * 2);
   L.total = o;
   return L;
 }
@@ -239,6 +239,7 @@ int moe_align(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t*
   if (T == 0) return ok();
   if (!ids || !counts || !pad_off || !sorted || !inv || !tiles || !n_tiles || !scratch)
     return fail(MOE_ERR_NULL, "moe_align: every output and the scratch buffer are required");
+  if (!aligned16(scratch)) return fail(MOE_ERR_ALIGN, "moe_align: scratch must be 16-byte aligned");
   if (scratch_bytes < moe_align_scratch_size(T, E, k))
     return fail(MOE_ERR_WORKSPACE, "moe_align: scratch of %zu bytes, %zu needed", scratch_bytes,
                 moe_align_scratch_size(T, E, k));
@@ -307,21 +308,21 @@ int moe_grouped_down(const uint16_t* h, const uint16_t* w_down, const int32_t* s
                     "moe_grouped_down");
 }
 
-int moe_combine(const uint16_t* o, const int32_t* inv, const float* w, const uint16_t* h_s, const uint16_t* ws_down,
+int moe_combine(const uint16_t* o, const float* w, const uint16_t* h_s, const uint16_t* ws_down,
                 const float* s, int T, int H, int k, int I_s, uint16_t* y, void* stream) {
   if (T < 0 || T > (1 << 24)) return fail(MOE_ERR_SHAPE, "T=%d outside [0, 2^24]", T);
   if (k < 1 || k > kMaxK) return fail(MOE_ERR_SHAPE, "k=%d outside [1, %d]", k, kMaxK);
   if (H < 256 || H > 8192 || H % 256 != 0) return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 256", H);
   if (I_s < 0 || I_s % 128 != 0) return fail(MOE_ERR_SHAPE, "I_s=%d must be 0 or a multiple of 128", I_s);
   if (T == 0) return ok();
-  if (!o || !inv || !w || !y) return fail(MOE_ERR_NULL, "moe_combine: missing pointer");
+  if (!o || !w || !y) return fail(MOE_ERR_NULL, "moe_combine: missing pointer");
   if (I_s > 0 && (!h_s || !ws_down || !s)) return fail(MOE_ERR_NULL, "moe_combine: shared tensors");
   if (I_s == 0 && (h_s || ws_down || s)) return fail(MOE_ERR_SHAPE, "moe_combine: shared tensors given with I_s = 0");
   if (!aligned16(o) || !aligned16(y) || (I_s > 0 && (!aligned16(h_s) || !aligned16(ws_down))))
     return fail(MOE_ERR_ALIGN, "moe_combine: tensors must be 16-byte aligned");
   int rc = check_arch();
   if (rc) return rc;
-  return hip_status(launch_combine(o, inv, w, h_s, ws_down, s, T, H, k, I_s, y, (hipStream_t)stream), "moe_combine");
+  return hip_status(launch_combine(o, w, h_s, ws_down, s, T, H, k, I_s, y, (hipStream_t)stream), "moe_combine");
 }
 
 int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint16_t* w_gate,
@@ -378,7 +379,7 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   if (e != hipSuccess) return hip_status(e, "moe_forward: gate_up (routed + shared)");
   e = launch_routed_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, o, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: down");
-  e = launch_combine(o, inv, w, h_s, ws_down, I_s > 0 ? s : nullptr, T, H, k, I_s, y, st);
+  e = launch_combine(o, w, h_s, ws_down, I_s > 0 ? s : nullptr, T, H, k, I_s, y, st);
   return hip_status(e, "moe_forward: combine");
 }
 

@@ -65,7 +65,7 @@ hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint1
 hipError_t launch_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,
                        const int32_t* n_tiles, int T, int H, int k, int I, int BM, int64_t max_tiles, uint16_t* o,
                        hipStream_t st);
-hipError_t launch_combine(const uint16_t* o, const int32_t* inv, const float* w, const uint16_t* h_s,
+hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s,
                           const uint16_t* ws_down, const float* s, int T, int H, int k, int I_s, uint16_t* y,
                           hipStream_t st);
 hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_gate,

@@ -103,7 +103,7 @@ class DeviceLayer:
             "scratch": torch.empty(moe.moe_align_scratch_size(T, s.E, s.k), dtype=torch.uint8, device=dev),
             "h": torch.empty((max_rows, s.I), dtype=torch.bfloat16, device=dev),
             "h_s": torch.empty((T, s.I_s), dtype=torch.bfloat16, device=dev) if s.I_s else None,
-            "o": torch.empty((max_rows, s.H), dtype=torch.bfloat16, device=dev),
+            "o": torch.empty((T * s.k, s.H), dtype=torch.bfloat16, device=dev),
             "y": torch.empty((T, s.H), dtype=torch.bfloat16, device=dev),
         }
 
@@ -132,7 +132,7 @@ class DeviceLayer:
 
     def run_combine(self, T, b, stream=None):
         s = self.shapes
-        moe.moe_combine(b["o"], b["inv"], b["w"], b["h_s"], self.w["ws_down"], b["s"] if s.I_s else None, T,
+        moe.moe_combine(b["o"], b["w"], b["h_s"], self.w["ws_down"], b["s"] if s.I_s else None, T,
                         s.H, s.k, s.I_s, b["y"], stream)
 
     def run_stages(self, x, b=None, stream=None, ids=None, w=None, s=None):

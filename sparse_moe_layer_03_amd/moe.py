@@ -63,7 +63,7 @@ def lib():
             "moe_align": ([p, i, i, i, p, p, p, p, p, p, p, z, p], i),
             "moe_grouped_gate_up": ([p] * 8 + [i] * 6 + [p, p, p], i),
             "moe_grouped_down": ([p] * 5 + [i] * 5 + [p, p], i),
-            "moe_combine": ([p] * 6 + [i] * 4 + [p, p], i),
+            "moe_combine": ([p] * 5 + [i] * 4 + [p, p], i),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -166,6 +166,6 @@ def moe_grouped_down(h, w_down, sorted_rows, tiles, n_tiles, T, H, E, k, I, o, s
                                   _p(o), _stream(stream)))
 
 
-def moe_combine(o, inv, w, h_s, ws_down, s, T, H, k, I_s, y, stream=None):
-    _check(lib().moe_combine(_p(o), _p(inv), _p(w), _p(h_s), _p(ws_down), _p(s), T, H, k, I_s, _p(y),
+def moe_combine(o, w, h_s, ws_down, s, T, H, k, I_s, y, stream=None):
+    _check(lib().moe_combine(_p(o), _p(w), _p(h_s), _p(ws_down), _p(s), T, H, k, I_s, _p(y),
                              _stream(stream)))

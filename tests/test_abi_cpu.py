@@ -82,9 +82,9 @@ def test_workspace_sizes():
     dec = moe.moe_workspace_size(1, 2048, 256, 8, 512, 512)
     assert big > small > dec > 0
     assert dec < (1 << 20)
-    # h and o of every padded row must fit
+    # h of every padded row and o of every assignment must fit
     rows = moe.moe_align_max_rows(8192, 256, 8)
-    assert big >= rows * (512 + 2048) * 2
+    assert big >= rows * 512 * 2 + 8192 * 8 * 2048 * 2
     for bad in ((16, 255, 8, 2, 128, 0), (16, 256, 0, 1, 128, 0), (16, 256, 8, 9, 128, 0), (16, 256, 8, 2, 100, 0),
                 (16, 256, 8, 2, 128, 64), (16, 256, 300, 2, 128, 0), (16, 256, 8, 17, 128, 0), (-1, 256, 8, 2, 128, 0)):
         assert moe.moe_workspace_size(*bad) == 0, bad
@@ -129,8 +129,8 @@ def test_stage_argument_errors(L):
     assert L.moe_grouped_gate_up(p, p, p, None, None, p, p, p, 16, 256, 8, 2, 128, 128, p, None, None) == \
         moe.MOE_ERR_NULL
     assert L.moe_grouped_down(p, p, p, p, p, 16, 256, 8, 2, 100, p, None) == moe.MOE_ERR_SHAPE
-    assert L.moe_combine(p, p, p, p, None, None, 16, 256, 2, 0, p, None) == moe.MOE_ERR_SHAPE
-    assert L.moe_combine(p, p, p, None, None, None, 16, 256, 2, 0, None, None) == moe.MOE_ERR_NULL
+    assert L.moe_combine(p, p, p, None, None, 16, 256, 2, 0, p, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_combine(p, p, None, None, None, 16, 256, 2, 0, None, None) == moe.MOE_ERR_NULL
     for f, args in ((L.moe_route, (p, p, None, None, 0, 256, 8, 2, None, None, None, None, None)),
                     (L.moe_align, (None, 0, 8, 2, None, None, None, None, None, None, None, 0, None))):
         assert f(*args) == moe.MOE_OK  # T = 0 is a no-op

@@ -147,17 +147,18 @@ def test_layer_parity(torch, full_layer, label, case):
     G.check_y(G.y_to_f64(y), y_ref, label)
     # the staged path runs the same kernels: bitwise identical to moe_forward
     assert torch.equal(b["y"].view(torch.int16), y.view(torch.int16))
-    # stage h: every assignment's hidden row vs the oracle's (same selection only)
+    # stages h (padded rows, reached through inv) and o (one row per
+    # assignment t*k + j): vs the oracle's, for tokens with the same selection
     same = np.all(ids == r["ids"], axis=1)
     if same.sum() > 0:
-        ro = oracle.forward(inp, want=("h",))
+        ro = oracle.forward(inp, want=("h", "o"))
         inv = b["inv"].cpu().numpy()
-        h_gpu = G.y_to_f64(b["h"][torch.from_numpy(inv).long().cuda()])  # written rows only
         sel = np.repeat(same, wl.k)
-        d = h_gpu[sel] - ro["h"][sel]
-        rel = np.linalg.norm(d) / np.linalg.norm(ro["h"][sel])
-        G.say(f"[{label}] h: rel-L2 {rel:.3e}")
-        assert rel < 1e-2
+        for name, got in (("h", G.y_to_f64(b["h"][torch.from_numpy(inv).long().cuda()])), ("o", G.y_to_f64(b["o"]))):
+            d = got[sel] - ro[name][sel]
+            rel = np.linalg.norm(d) / np.linalg.norm(ro[name][sel])
+            G.say(f"[{label}] {name}: rel-L2 {rel:.3e}")
+            assert rel < 1e-2
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
