@@ -24,7 +24,8 @@
 // Three kernels: per-chunk histograms (LDS integer counters: the counts do
 // not depend on the order of the increments), one workgroup that scans the
 // chunk histograms and the expert totals, and a scatter in which every chunk
-// ranks its assignments in order with wave ballots (no ordering atomics).
+// ranks its assignments in order with wave ballots (no ordering atomics) and
+// writes the tile entries and padding rows of a share of the experts.
 #include "moe_internal.h"
 
 namespace moe {
@@ -67,10 +68,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sbuf, int& total
 
 __global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restrict__ chunk_hist,
                                                          int32_t* __restrict__ chunk_off, int n_chunks, int E,
-                                                         int BIG, int SMALL, int small_base,
-                                                         int32_t* __restrict__ counts, int32_t* __restrict__ pad_off,
-                                                         int32_t* __restrict__ sorted, int32_t* __restrict__ tiles,
-                                                         int32_t* __restrict__ n_tiles) {
+                                                         int BIG, int SMALL, int32_t* __restrict__ counts, int32_t* __restrict__ pad_off,
+                                                         int32_t* __restrict__ tile_off, int32_t* __restrict__ n_tiles) {
   __shared__ int sbuf[4];
   const int e = threadIdx.x;
   int run = 0;
@@ -107,15 +106,8 @@ __global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restri
   const int small_off = block_exclusive_scan(nsmall, sbuf, total_small);
   if (e < E) {
     pad_off[e] = rows_off;
-    for (int i = 0; i < nbig; ++i) {
-      tiles[2 * (big_off + i)] = e;
-      tiles[2 * (big_off + i) + 1] = rows_off + i * BIG;
-    }
-    for (int i = 0; i < nsmall; ++i) {
-      tiles[2 * (small_base + small_off + i)] = e;
-      tiles[2 * (small_base + small_off + i) + 1] = rows_off + nbig * BIG + i * SMALL;
-    }
-    for (int r = run; r < padded; ++r) sorted[rows_off + r] = -1;
+    tile_off[e] = big_off;  // first BIG-list entry of expert e
+    tile_off[kMaxE + e] = small_off;
   }
   if (e == 0) {
     pad_off[E] = total_rows;
@@ -124,10 +116,17 @@ __global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restri
   }
 }
 
+// Also writes, for the experts e = blockIdx.x, blockIdx.x + gridDim.x, ...,
+// their tile-table entries and the -1 of their padding rows (all threads of
+// the workgroup share each expert's writes).
 __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E, int nc,
+                                                            int BIG, int SMALL, int small_base,
                                                             const int32_t* __restrict__ chunk_off,
                                                             const int32_t* __restrict__ pad_off,
-                                                            int32_t* __restrict__ sorted, int32_t* __restrict__ inv) {
+                                                            const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ tile_off,
+                                                            int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
+                                                            int32_t* __restrict__ tiles) {
   __shared__ int32_t base[kMaxE];
   __shared__ int32_t wcnt[4][kMaxE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -162,12 +161,31 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
     for (int ee = tid; ee < E; ee += 256) base[ee] += wcnt[0][ee] + wcnt[1][ee] + wcnt[2][ee] + wcnt[3][ee];
     __syncthreads();
   }
+  const bool one = SMALL == BIG;
+  for (int e = blockIdx.x; e < E; e += gridDim.x) {
+    const int run = counts[e];
+    const int nbig = one ? (run + BIG - 1) / BIG : run / BIG;
+    const int nsmall = one ? 0 : (run - nbig * BIG + SMALL - 1) / SMALL;
+    const int padded = nbig * BIG + nsmall * SMALL;
+    const int p0 = pad_off[e], b0 = tile_off[e], s0 = small_base + tile_off[kMaxE + e];
+    for (int i = tid; i < nbig; i += 256) {
+      tiles[2 * (b0 + i)] = e;
+      tiles[2 * (b0 + i) + 1] = p0 + i * BIG;
+    }
+    for (int i = tid; i < nsmall; i += 256) {
+      tiles[2 * (s0 + i)] = e;
+      tiles[2 * (s0 + i) + 1] = p0 + nbig * BIG + i * SMALL;
+    }
+    for (int r = run + tid; r < padded; r += 256) sorted[p0 + r] = -1;
+  }
 }
 
 }  // namespace
 
 // Chunks of CH assignments, rounded up to a multiple of 4 (the scan reads 4
 // chunk counts per 16-byte load; chunks past the end are empty).
+int align_scratch_ints(int T, int E, int k) { return 2 * align_num_chunks(T, k) * E + 2 * kMaxE; }
+
 int align_num_chunks(int T, int k) { return (int)((((int64_t)T * k + CH - 1) / CH + 3) / 4 * 4); }
 
 hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
@@ -175,12 +193,14 @@ hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SM
                         int32_t* n_tiles, int32_t* scratch, hipStream_t st) {
   const int n = T * k;
   const int nc = align_num_chunks(T, k);
-  hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, scratch);
+  int32_t* chunk_hist = scratch;
   int32_t* chunk_off = scratch + (size_t)nc * E;
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(256), 0, st, scratch, chunk_off, nc, E, BIG, SMALL, small_base,
-                     counts, pad_off, sorted, tiles, n_tiles);
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, chunk_off, pad_off, sorted,
-                     inv);
+  int32_t* tile_off = chunk_off + (size_t)nc * E;  // [2][kMaxE]
+  hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, chunk_hist);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(256), 0, st, chunk_hist, chunk_off, nc, E, BIG, SMALL, counts,
+                     pad_off, tile_off, n_tiles);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, BIG, SMALL, small_base, chunk_off,
+                     pad_off, counts, tile_off, sorted, inv, tiles);
   return hipGetLastError();
 }
 

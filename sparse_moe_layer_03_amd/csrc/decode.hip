@@ -53,21 +53,6 @@ DecodeWs carve(void* base, int H, int E, int k, int I, int I_s) {
   return d;
 }
 
-// Sum over the 64 lanes: inclusive row sums by DPP row_shr 1, 2, 4, 8, then
-// row_bcast:15 and row_bcast:31 carry the row totals up; lane 63 holds the
-// total, which is returned to every lane.
-__device__ __forceinline__ float wave_sum(float v) {
-  const int z = 0;
-  int b = __float_as_int(v);
-  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x111, 0xf, 0xf, false)));
-  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x112, 0xf, 0xf, false)));
-  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x114, 0xf, 0xf, false)));
-  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x118, 0xf, 0xf, false)));
-  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x142, 0xa, 0xf, false)));
-  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x143, 0xc, 0xf, false)));
-  return __int_as_float(__builtin_amdgcn_readlane(b, 63));
-}
-
 __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
   float s = 0.0f;
 #pragma unroll

@@ -192,8 +192,9 @@ int64_t moe_align_max_tiles(int T, int E, int k) {
 }
 
 size_t moe_align_scratch_size(int T, int E, int k) {
-  // per-chunk histograms, then per-chunk exclusive offsets
-  return 2 * (size_t)(align_num_chunks(T, k) > 0 ? align_num_chunks(T, k) : 1) * (size_t)(E > 0 ? E : 1) * 4;
+  // per-chunk histograms, per-chunk exclusive offsets, per-expert tile-list offsets
+  if (T < 1 || E < 1 || k < 1) return 256;
+  return (size_t)align_scratch_ints(T, E, k) * 4;
 }
 
 size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s) {

@@ -33,6 +33,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Sum over the 64 lanes: inclusive row sums by DPP row_shr 1, 2, 4, 8, then
+// row_bcast:15 and row_bcast:31 carry the row totals up; lane 63 holds the
+// total, which is returned to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  const int z = 0;
+  int b = __float_as_int(v);
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x111, 0xf, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x112, 0xf, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x114, 0xf, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x118, 0xf, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x142, 0xa, 0xf, false)));
+  b = __float_as_int(__int_as_float(b) + __int_as_float(__builtin_amdgcn_update_dpp(z, b, 0x143, 0xc, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(b, 63));
+}
+
 // Map a linear workgroup id to a work item so that each XCD receives one
 // contiguous run of items (items sharing an expert's weights stay in one
 // XCD's L2).  `n_items` is known only on the device.  Returns -1 when this
@@ -56,6 +71,7 @@ hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SM
                         int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
                         int32_t* n_tiles, int32_t* scratch, hipStream_t st);
 int align_num_chunks(int T, int k);
+int align_scratch_ints(int T, int E, int k);
 // Routed gate/up tiles of one tile list; with I_s > 0 the shared expert's
 // gate/up over all T tokens (tiles of BM tokens) joins the same launch.
 hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const int32_t* sorted,

@@ -72,8 +72,7 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
         g += bf16_to_f32((uint16_t)(a[i] >> 16)) * bf16_to_f32((uint16_t)(b[i] >> 16));
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) g += __shfl_xor(g, off);
+    g = wave_sum(g);
     if (lane == 0) sout[t] = 1.0f / (1.0f + expf(-g));
   }
 }
