@@ -41,10 +41,10 @@ DecodeWs carve(void* base, int H, int E, int k, int I, int I_s) {
   DecodeWs d;
   d.logits = reinterpret_cast<float*>(p);
   p += align256((size_t)E * 4);
-  d.ids = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)k * 4);
+  d.ids = reinterpret_cast<int32_t*>(p);  // 256-byte slot: 64 entries, read 16 at a time
+  p += 256;
   d.w = reinterpret_cast<float*>(p);
-  p += align256((size_t)k * 4);
+  p += 256;
   d.s = reinterpret_cast<float*>(p);
   p += 256;
   d.hs = reinterpret_cast<float*>(p);
@@ -63,36 +63,31 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
   return s;
 }
 
-// x (H bf16) -> LDS as 16-byte chunks; H/8 <= 1024 chunks.
-__device__ __forceinline__ void stage_x(const uint16_t* x, int H, u32x4* sx) {
-  for (int c = threadIdx.x; c < H / 8; c += 256) sx[c] = reinterpret_cast<const u32x4*>(x)[c];
-  __syncthreads();
-}
-
-// Dot products of x with one or two bf16 rows of length H, all loads issued
-// in groups of 4 chunks per lane before the arithmetic.
-__device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* r0, const uint16_t* r1, int H, int lane,
-                                         float& d0, float& d1) {
+// Dot products of x with one or two bf16 rows of length H.  x comes from LDS
+// (sx) when given, else straight from global memory; every load of a group
+// of 4 chunks per lane (x's included) is issued before the arithmetic.
+__device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* xg, const uint16_t* r0, const uint16_t* r1,
+                                         int H, int lane, float& d0, float& d1) {
   const int nch = H / 8;
   d0 = 0.0f;
   d1 = 0.0f;
   for (int base = 0; base < nch; base += 256) {
-    u32x4 a[4], b[4];
+    u32x4 a[4], b[4], xv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       int c = base + q * 64 + lane;
       if (c < nch) {
         a[q] = reinterpret_cast<const u32x4*>(r0)[c];
         if (r1) b[q] = reinterpret_cast<const u32x4*>(r1)[c];
+        xv[q] = sx ? sx[c] : reinterpret_cast<const u32x4*>(xg)[c];
       }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       int c = base + q * 64 + lane;
       if (c < nch) {
-        u32x4 xv = sx[c];
-        d0 += dot8(xv, a[q]);
-        if (r1) d1 += dot8(xv, b[q]);
+        d0 += dot8(xv[q], a[q]);
+        if (r1) d1 += dot8(xv[q], b[q]);
       }
     }
   }
@@ -104,13 +99,11 @@ __global__ __launch_bounds__(256) void decode_router_shared_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
     const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up, const uint16_t* __restrict__ w_sg,
     int H, int E, int I_s, DecodeWs d) {
-  __shared__ u32x4 sx[1024];
-  stage_x(x, H, sx);
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   float d0, d1;
   if (row < E) {
-    row_dots(sx, wr + (size_t)row * H, nullptr, H, lane, d0, d1);
+    row_dots(nullptr, x, wr + (size_t)row * H, nullptr, H, lane, d0, d1);
     if (lane == 0) {
       float v = d0 + (bias ? bias[row] : 0.0f);
       if (v == 0.0f) v = 0.0f;
@@ -118,10 +111,10 @@ __global__ __launch_bounds__(256) void decode_router_shared_kernel(
     }
   } else if (row < E + I_s) {
     int i = row - E;
-    row_dots(sx, ws_gate + (size_t)i * H, ws_up + (size_t)i * H, H, lane, d0, d1);
+    row_dots(nullptr, x, ws_gate + (size_t)i * H, ws_up + (size_t)i * H, H, lane, d0, d1);
     if (lane == 0) d.hs[i] = silu(d0) * d1;
   } else if (row == E + I_s && I_s > 0) {
-    row_dots(sx, w_sg, nullptr, H, lane, d0, d1);
+    row_dots(nullptr, x, w_sg, nullptr, H, lane, d0, d1);
     if (lane == 0) d.s[0] = 1.0f / (1.0f + expf(-d0));
   }
 }
@@ -211,6 +204,7 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
 
 // Wave per CPW output columns: the k + 1 weight rows of the columns are
 // loaded together (I / 8 chunks each), and each h value read serves them all.
+template <int KT>  // k <= KT
 __global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __restrict__ w_down,
                                                           const uint16_t* __restrict__ ws_down, int H, int k, int I,
                                                           int I_s, DecodeWs d, uint16_t* __restrict__ y) {
@@ -218,14 +212,24 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __rest
   const int lane = threadIdx.x & 63;
   const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * CPW;
   if (c0 >= H) return;
-  int ids[kMaxK];
+  // ids and weights: KT entries read with 16-byte loads (their workspace
+  // slots hold 64 entries), entries past k unused
+  int ids[KT];
+  float wsel[KT];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) ids[j] = (j < k) ? d.ids[j] : 0;
-  float part[CPW][kMaxK + 1];
+  for (int q = 0; q < KT / 4; ++q) {
+    const int4 iv = reinterpret_cast<const int4*>(d.ids)[q];
+    const float4 wv = reinterpret_cast<const float4*>(d.w)[q];
+    ids[4 * q] = iv.x, ids[4 * q + 1] = iv.y, ids[4 * q + 2] = iv.z, ids[4 * q + 3] = iv.w;
+    wsel[4 * q] = wv.x, wsel[4 * q + 1] = wv.y, wsel[4 * q + 2] = wv.z, wsel[4 * q + 3] = wv.w;
+  }
+#pragma unroll
+  for (int j = 0; j < KT; ++j) ids[j] = j < k ? ids[j] : 0;  // keep unused rows in range
+  float part[CPW][KT + 1];
 #pragma unroll
   for (int c = 0; c < CPW; ++c)
 #pragma unroll
-    for (int j = 0; j <= kMaxK; ++j) part[c][j] = 0.0f;
+    for (int j = 0; j <= KT; ++j) part[c][j] = 0.0f;
   auto accum = [&](float& acc, const u32x4& wv, const float* hv) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -233,38 +237,46 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __rest
       acc += hv[2 * q + 1] * bf16_to_f32((uint16_t)(wv[q] >> 16));
     }
   };
-  // shared expert rows (independent of the routing): issued first
-  if (I_s > 0) {
-    for (int base = 0; base < I_s / 8; base += 64) {
-      const int ch = base + lane;
-      if (ch < I_s / 8) {
-        u32x4 wv[CPW];
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) wv[c] = reinterpret_cast<const u32x4*>(ws_down + (size_t)(c0 + c) * I_s)[ch];
-        const float4* hp = reinterpret_cast<const float4*>(d.hs + ch * 8);
-        const float4 h0 = hp[0], h1 = hp[1];
-        const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) accum(part[c][kMaxK], wv[c], hv);
-      }
-    }
-  }
-  // routed rows W_down[e_j, c, :], chunks of 8 along I
-  for (int base = 0; base < I / 8; base += 64) {
+  // Per step of 64 chunks: the loads that do not depend on the routing (the
+  // shared row, h_s and every h_j) are issued first, then the k routed rows.
+  const int nI = I / 8, nS = I_s > 0 ? I_s / 8 : 0;
+  const int nmax = nI > nS ? nI : nS;
+  for (int base = 0; base < nmax; base += 64) {
     const int ch = base + lane;
-    u32x4 wv[kMaxK][CPW];
+    const bool okS = ch < nS, okI = ch < nI;
+    u32x4 wsv[CPW];
+    float4 hs0 = {}, hs1 = {};
+    if (okS) {
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k && ch < I / 8)
+      for (int c = 0; c < CPW; ++c) wsv[c] = reinterpret_cast<const u32x4*>(ws_down + (size_t)(c0 + c) * I_s)[ch];
+      const float4* hp = reinterpret_cast<const float4*>(d.hs + ch * 8);
+      hs0 = hp[0];
+      hs1 = hp[1];
+    }
+    float4 h0[KT], h1[KT];
+#pragma unroll
+    for (int j = 0; j < KT; ++j)
+      if (j < k && okI) {
+        const float4* hp = reinterpret_cast<const float4*>(d.h + (size_t)j * I + ch * 8);
+        h0[j] = hp[0];
+        h1[j] = hp[1];
+      }
+    u32x4 wv[KT][CPW];
+#pragma unroll
+    for (int j = 0; j < KT; ++j)
+      if (j < k && okI)
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
           wv[j][c] = reinterpret_cast<const u32x4*>(w_down + ((size_t)ids[j] * H + c0 + c) * I)[ch];
+    if (okS) {
+      const float hv[8] = {hs0.x, hs0.y, hs0.z, hs0.w, hs1.x, hs1.y, hs1.z, hs1.w};
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k && ch < I / 8) {
-        const float4* hp = reinterpret_cast<const float4*>(d.h + (size_t)j * I + ch * 8);
-        const float4 h0 = hp[0], h1 = hp[1];
-        const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      for (int c = 0; c < CPW; ++c) accum(part[c][KT], wsv[c], hv);
+    }
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      if (j < k && okI) {
+        const float hv[8] = {h0[j].x, h0[j].y, h0[j].z, h0[j].w, h1[j].x, h1[j].y, h1[j].z, h1[j].w};
 #pragma unroll
         for (int c = 0; c < CPW; ++c) accum(part[c][j], wv[j][c], hv);
       }
@@ -274,9 +286,9 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __rest
   for (int c = 0; c < CPW; ++c) {
     float yv = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j)
-      if (j < k) yv += d.w[j] * wave_sum(part[c][j]);  // rank order
-    if (I_s > 0) yv += d.s[0] * wave_sum(part[c][kMaxK]);
+    for (int j = 0; j < KT; ++j)
+      if (j < k) yv += wsel[j] * wave_sum(part[c][j]);  // rank order
+    if (I_s > 0) yv += d.s[0] * wave_sum(part[c][KT]);
     if (lane == 0) y[c0 + c] = f32_to_bf16(yv);
   }
 }
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __rest
 
 size_t decode_workspace_size(int H, int E, int k, int I, int I_s) {
   (void)H;
-  return align256((size_t)E * 4) + 2 * align256((size_t)k * 4) + 256 + align256((size_t)(I_s > 0 ? I_s : 1) * 4) +
+  return align256((size_t)E * 4) + 2 * 256 + 256 + align256((size_t)(I_s > 0 ? I_s : 1) * 4) +
          align256((size_t)k * I * 4);
 }
 
@@ -301,7 +313,12 @@ hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const floa
   hipLaunchKernelGGL(decode_topk_gate_up_kernel, dim3((k * I + 3) / 4), dim3(256), 0, st, x, w_gate, w_up, H, E,
                      k, I, d);
   // 4 waves per workgroup, one output column per wave (H is a multiple of 256)
-  hipLaunchKernelGGL(decode_down_kernel, dim3((H + 3) / 4), dim3(256), 0, st, w_down, ws_down, H, k, I, I_s, d, y);
+  if (k <= 8)
+    hipLaunchKernelGGL(decode_down_kernel<8>, dim3((H + 3) / 4), dim3(256), 0, st, w_down, ws_down, H, k, I, I_s, d,
+                       y);
+  else
+    hipLaunchKernelGGL(decode_down_kernel<kMaxK>, dim3((H + 3) / 4), dim3(256), 0, st, w_down, ws_down, H, k, I, I_s,
+                       d, y);
   return hipGetLastError();
 }
 
