@@ -234,6 +234,11 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
   const int ncol = gu ? 128 : 256;
   const int cr = tid >> 3;       // copy-out: row within a 32-row group
   const int cc = (tid & 7) * 8;  // copy-out: first of 8 columns
+  // DOWN: the assignment held by each of this thread's copy-out rows, read
+  // once for all column passes (-1: padding row, not stored)
+  int arow_of[BM / 32];
+#pragma unroll
+  for (int i = 0; i < BM / 32; ++i) arow_of[i] = (MODE == DOWN) ? p.sorted[it.row0 + cr + 32 * i] : 0;
   for (int pass = 0; pass < ncol / EPW; ++pass) {
 #pragma unroll
     for (int m = 0; m < MI; ++m) {
@@ -251,7 +256,9 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
       }
     }
     __syncthreads();
-    for (int r = cr; r < BM && MODE != SHARED_COMBINE; r += 32) {
+#pragma unroll
+    for (int i = 0; i < (MODE == SHARED_COMBINE ? 0 : BM / 32); ++i) {
+      const int r = cr + 32 * i;
       const float4 v0 = *reinterpret_cast<const float4*>(sc + r * ESLD + cc);
       const float4 v1 = *reinterpret_cast<const float4*>(sc + r * ESLD + cc + 4);
       float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -279,7 +286,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
           }
         }
       } else if (MODE == DOWN) {
-        const int a = p.sorted[it.row0 + r];  // assignment held by the row; -1 for padding
+        const int a = arow_of[i];
         if (a >= 0) {
           const u32x4 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                             pack_bf16x2(v[6], v[7])};

@@ -22,7 +22,15 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  // gate loads first, so they overlap the selection
+  float v[4];
+  bool valid[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    valid[q] = e < E;
+    v[q] = valid[q] ? logits[(size_t)t * E + e] : 0.0f;
+  }
+  // gate loads after the logits: the selection waits only for the logits
   u32x4 xv[4], gv[4];
   const int nch = H / 8;
   const bool gate = x != nullptr && w_sg != nullptr;
@@ -35,14 +43,6 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(const float* __restrict_
         gv[q] = reinterpret_cast<const u32x4*>(w_sg)[c];
       }
     }
-  }
-  float v[4];
-  bool valid[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    valid[q] = e < E;
-    v[q] = valid[q] ? logits[(size_t)t * E + e] : 0.0f;
   }
   int sel_e;
   float sel_v, wt;
