@@ -17,7 +17,8 @@
 //   DOWN            routed tiles.  A = h rows, B = 256 rows of W_down -> o,
 //                   stored at the row of the assignment (t*k + j) it holds
 //   ROUTER          token tiles.  B = W_router (experts past E zero);
-//                   epilogue logits + bias -> fp32 logits
+//                   epilogue logits + bias -> fp32 logits; the shared-expert
+//                   gate x . w_sg accumulates from the A tiles in LDS
 //   SHARED_COMBINE  token tiles.  A = h_s rows, B = 256 rows of Ws_down;
 //                   epilogue is the deterministic combine
 //                   y = sum_j w_j o[t*k + j] + s * acc
@@ -88,8 +89,10 @@ struct GemmParams {
   const uint16_t* o;  // combine inputs: o rows in assignment order (t*k + j)
   const float* w;
   const float* s;
-  const float* bias;  // ROUTER: bias [E] or NULL
-  float* logits;      // ROUTER: logits [T, E]
+  const float* bias;     // ROUTER: bias [E] or NULL
+  float* logits;         // ROUTER: logits [T, E]
+  const uint16_t* w_sg;  // ROUTER: shared-expert gate vector [K] or NULL
+  float* gate_s;         // ROUTER: s = sigmoid(x . w_sg) [T] (when w_sg is given)
 };
 
 // 16-byte chunk swizzles of an LDS row of KCH chunks.  Any 16 consecutive rows
@@ -219,12 +222,35 @@ __device__ __forceinline__ void gather_combine8(const uint16_t* __restrict__ o, 
   }
 }
 
+// Sum of the 8 bf16 products of two 16-byte chunks, fp32.
+__device__ __forceinline__ float dot8_bf16(const u32x4& a, const u32x4& b) {
+  float r = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r += bf16_to_f32((uint16_t)(a[q] & 0xffff)) * bf16_to_f32((uint16_t)(b[q] & 0xffff));
+    r += bf16_to_f32((uint16_t)(a[q] >> 16)) * bf16_to_f32((uint16_t)(b[q] >> 16));
+  }
+  return r;
+}
+
 constexpr int EPW = 64;        // epilogue staging: columns per pass
 constexpr int ESLD = EPW + 4;  // fp32 row stride of the staging tile
 
 // Epilogue: accumulators -> fp32 LDS staging 64 columns at a time -> stores.
 // Wave layout: rows wm*WTM + m*32 + (MFMA row), tile columns bb[j] + (lane&31).
 // Gate/up items pair column block j (gate) with j + NJ/2 (up).
+// Router gate: the partial dot products x . w_sg (one per thread, KCH threads
+// per token row, consecutive lanes of one wave) are summed and
+// s = sigmoid(sum) stored.
+template <int BM, int KCH>
+__device__ __forceinline__ void router_gate(const GemmParams& p, const Item it, float gacc) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int off = 1; off < KCH; off <<= 1) gacc += __shfl_xor(gacc, off);
+  const int t = it.row0 + tid / KCH;
+  if (tid % KCH == 0 && t < p.T) p.gate_s[t] = 1.0f / (1.0f + expf(-gacc));
+}
+
 template <int BM, int MODE, int MI, int NJ, int WTM>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32x16 (&acc)[MI][NJ], int wm,
                                          const int (&bb)[NJ], unsigned char* smem) {
@@ -465,9 +491,17 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
   __syncthreads();
   Frag f0, f1;
   bool pending = false;  // f1 holds the last sub-step of the previous K step
+  // ROUTER: partial x . w_sg of the shared-expert gate from the A tile in LDS:
+  // thread t takes row t / KCH, 16-byte chunk t % KCH of every K step
+  float gacc = 0.0f;
+  static_assert(MODE != ROUTER || BM * KCH == 256, "router gate needs one A chunk per thread");
   auto kloop = [&](auto LIVE) {
     constexpr bool L = decltype(LIVE)::value;
-    auto stage = [&](int st, u32x4 (&pa)[NA], u32x4 (&pb)[NB], int next_kb) {
+    auto stage = [&](int st, u32x4 (&pa)[NA], u32x4 (&pb)[NB], int next_kb, int ks) {
+      u32x4 gv = {0u, 0u, 0u, 0u};
+      if constexpr (MODE == ROUTER) {
+        if (p.w_sg) gv = *reinterpret_cast<const u32x4*>(p.w_sg + ks * BK + (tid % KCH) * 8);
+      }
       if constexpr (L) read_frags(f0, st, 0);
       __builtin_amdgcn_sched_barrier(0);
       sstore(pa, pb, st ^ 1);
@@ -492,11 +526,17 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
           pending = false;
         }
       }
+      if constexpr (MODE == ROUTER) {
+        if (p.w_sg) {
+          const int r = tid / KCH, c = tid % KCH;
+          gacc += dot8_bf16(sA[st * BM * KCH + r * KCH + swz<KCH>(r, c)], gv);
+        }
+      }
     };
     for (int kb = 0; kb < nk; kb += 2) {
-      stage(0, pa1, pb1, min(kb + 3, nk - 1));  // writes step kb+1 -> LDS[1]
+      stage(0, pa1, pb1, min(kb + 3, nk - 1), kb);  // step kb from LDS[0]; writes step kb+1 -> LDS[1]
       __syncthreads();
-      stage(1, pa0, pb0, min(kb + 4, nk - 1));  // writes step kb+2 -> LDS[0]
+      stage(1, pa0, pb0, min(kb + 4, nk - 1), kb + 1);  // step kb+1 from LDS[1]; writes step kb+2 -> LDS[0]
       __syncthreads();
     }
   };
@@ -505,6 +545,9 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
   else
     kloop(std::false_type{});
   if (pending) mma(f1);
+  if constexpr (MODE == ROUTER) {
+    if (p.w_sg) router_gate<BM, KCH>(p, it, gacc);
+  }
   epilogue<BM, MODE, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
 }
 
@@ -570,8 +613,8 @@ hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t
 
 }  // namespace
 
-hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E,
-                         float* logits, hipStream_t st) {
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg, int T,
+                         int H, int E, float* logits, float* s, hipStream_t st) {
   GemmParams p = {};
   p.a = x;
   p.lda = H;
@@ -582,6 +625,8 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const floa
   p.k = 1;
   p.bias = bias;
   p.logits = logits;
+  p.w_sg = w_sg;
+  p.gate_s = s;
   // Small token tiles: one 256-column block per tile, so the tile count is
   // the launch's whole parallelism.
   constexpr int BM = router_rows(MOE_ROUTER_CFG);

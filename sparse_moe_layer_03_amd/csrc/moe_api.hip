@@ -215,9 +215,9 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_b
     return fail(MOE_ERR_ALIGN, "moe_route: bf16 tensors must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
   const hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_router(x, w_router, router_bias, T, H, E, logits, st);
+  hipError_t e = launch_router(x, w_router, router_bias, w_sg, T, H, E, logits, s, st);
   if (e != hipSuccess) return hip_status(e, "moe_route: router GEMM");
-  return hip_status(launch_topk(logits, T, E, k, w_sg ? x : nullptr, w_sg, H, ids, w, s, st), "moe_route: top-k");
+  return hip_status(launch_topk(logits, T, E, k, ids, w, st), "moe_route: top-k");
 }
 
 int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* ids, float* w, void* stream) {
@@ -228,8 +228,7 @@ int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* ids
   if (!logits || !ids || !w) return fail(MOE_ERR_NULL, "moe_route_from_logits: logits, ids and w are required");
   int rc = check_arch();
   if (rc) return rc;
-  return hip_status(launch_topk(logits, T, E, k, nullptr, nullptr, 0, ids, w, nullptr, (hipStream_t)stream),
-                    "moe_route_from_logits");
+  return hip_status(launch_topk(logits, T, E, k, ids, w, (hipStream_t)stream), "moe_route_from_logits");
 }
 
 int moe_align(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t* pad_off, int32_t* sorted,
@@ -369,9 +368,10 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   uint16_t* h_s = I_s > 0 ? reinterpret_cast<uint16_t*>(base + L.off_hs) : nullptr;
   uint16_t* o = reinterpret_cast<uint16_t*>(base + L.off_o);
 
-  hipError_t e = launch_router(x, w_router, router_bias, T, H, E, logits, st);
+  hipError_t e =
+      launch_router(x, w_router, router_bias, I_s > 0 ? w_sg : nullptr, T, H, E, logits, I_s > 0 ? s : nullptr, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: router");
-  e = launch_topk(logits, T, E, k, I_s > 0 ? x : nullptr, w_sg, H, ids, w, I_s > 0 ? s : nullptr, st);
+  e = launch_topk(logits, T, E, k, ids, w, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: top-k");
   e = launch_align(ids, T, E, k, L.BIG, L.SMALL, (int)L.max_big, counts, pad_off, sorted, inv, tiles, n_tiles, scratch,
                    st);

@@ -62,11 +62,12 @@ __device__ __forceinline__ int xcd_item(int bid, int n_items) {
 }
 
 // Host-side launch helpers (defined in the .hip files).
-// Router GEMM over token tiles: fp32 logits (+ bias, -0 -> +0).
-hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E,
-                         float* logits, hipStream_t st);
-hipError_t launch_topk(const float* logits, int T, int E, int k, const uint16_t* x, const uint16_t* w_sg, int H,
-                       int32_t* ids, float* w, float* s, hipStream_t st);
+// Router GEMM over token tiles: fp32 logits (+ bias, -0 -> +0) and, when w_sg
+// is given, the shared-expert gate s = sigmoid(x . w_sg) from the same x tiles.
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg, int T,
+                         int H, int E, float* logits, float* s, hipStream_t st);
+// Top-k ids and renormalised weights from fp32 logits [T, E].
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
                         int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
                         int32_t* n_tiles, int32_t* scratch, hipStream_t st);

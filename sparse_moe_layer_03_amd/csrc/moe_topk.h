@@ -39,66 +39,99 @@ __device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
   lo = take ? ol : lo;
 }
 
-// Maximum 64-bit key over the wave, returned to every lane (uniform).
-__device__ __forceinline__ void wave_max_key(uint32_t hi, uint32_t lo, uint32_t& mhi, uint32_t& mlo) {
-  // inclusive maxima within rows of 16 lanes, then rows 1 and 3 take the
-  // previous row's maximum, then rows 2 and 3 take row 1's: lane 63 holds it
-  dpp_max_step<0x111, 0xf>(hi, lo);
-  dpp_max_step<0x112, 0xf>(hi, lo);
-  dpp_max_step<0x114, 0xf>(hi, lo);
-  dpp_max_step<0x118, 0xf>(hi, lo);
-  dpp_max_step<0x142, 0xa>(hi, lo);
-  dpp_max_step<0x143, 0xc>(hi, lo);
-  mhi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
-  mlo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+// Top-k of up to 256 logits held 4 per lane (lane l: experts l, l+64, l+128,
+// l+192; absent experts invalid), for NT tokens at once: their selection
+// rounds are independent, so the DPP chains interleave.  Lane r < k ends
+// with rank r's expert in sel_e[t] and logit in sel_v[t], and w[t] returns
+// rank r's weight in lane r:
+//   w_r = exp(l_r - l_0) / sum_{r' < k} exp(l_r' - l_0), the sum in rank order.
+template <int NT>
+__device__ __forceinline__ void wave_topk_weights_n(const float (&v)[NT][4], const bool (&valid)[NT][4], int k,
+                                                    int lane, int (&sel_e)[NT], float (&sel_v)[NT], float (&w)[NT]) {
+  uint32_t kh[NT][4], kl[NT][4];
+  float m[NT], sum[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float x = v[t][q];
+      if (x == 0.0f) x = 0.0f;  // -0 -> +0
+      kh[t][q] = valid[t][q] ? float_order_key(x) : 0u;
+      kl[t][q] = valid[t][q] ? ~(uint32_t)(lane + 64 * q) : 0u;
+    }
+    sel_e[t] = -1;
+    sel_v[t] = 0.0f;
+    m[t] = 0.0f;
+    sum[t] = 0.0f;
+  }
+  for (int r = 0; r < k; ++r) {
+    uint32_t bh[NT], bl[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {  // this lane's best remaining key
+      bh[t] = kh[t][0];
+      bl[t] = kl[t][0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
+        const bool take = (kh[t][q] > bh[t]) || (kh[t][q] == bh[t] && kl[t][q] > bl[t]);
+        bh[t] = take ? kh[t][q] : bh[t];
+        bl[t] = take ? kl[t][q] : bl[t];
+      }
+    }
+    // wave maxima: inclusive maxima within rows of 16 lanes, then rows 1 and
+    // 3 take the previous row's, then rows 2 and 3 take row 1's (lane 63)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dpp_max_step<0x111, 0xf>(bh[t], bl[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dpp_max_step<0x112, 0xf>(bh[t], bl[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dpp_max_step<0x114, 0xf>(bh[t], bl[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dpp_max_step<0x118, 0xf>(bh[t], bl[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dpp_max_step<0x142, 0xa>(bh[t], bl[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dpp_max_step<0x143, 0xc>(bh[t], bl[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t mh = (uint32_t)__builtin_amdgcn_readlane((int)bh[t], 63);
+      const uint32_t ml = (uint32_t)__builtin_amdgcn_readlane((int)bl[t], 63);
+      // the winning key is a valid one (k <= number of valid experts); the
+      // clamp only keeps an index in range should that ever not hold
+      const int e = min(max((int)~ml, 0), 255);
+      const float val = float_from_order_key(mh);
+      if (lane == r) {
+        sel_e[t] = e;
+        sel_v[t] = val;
+      }
+      if ((e & 63) == lane) {  // the owner drops the selected key
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q == (e >> 6)) kh[t][q] = kl[t][q] = 0u;
+      }
+      if (r == 0) m[t] = val;
+      sum[t] += expf(val - m[t]);  // uniform, rank order
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) w[t] = (lane < k) ? expf(sel_v[t] - m[t]) / sum[t] : 0.0f;
 }
 
-// Top-k of up to 256 logits held 4 per lane (lane l: experts l, l+64, l+128,
-// l+192; absent experts invalid).  Lane r < k ends with rank r's expert in
-// sel_e and logit in sel_v; w returns rank r's weight in lane r:
-//   w_r = exp(l_r - l_0) / sum_{r' < k} exp(l_r' - l_0), the sum in rank order.
+// One token.
 __device__ __forceinline__ void wave_topk_weights(const float (&v)[4], const bool (&valid)[4], int k, int lane,
                                                   int& sel_e, float& sel_v, float& w) {
-  uint32_t kh[4], kl[4];
+  float vv[1][4];
+  bool ok[1][4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    float x = v[q];
-    if (x == 0.0f) x = 0.0f;  // -0 -> +0
-    kh[q] = valid[q] ? float_order_key(x) : 0u;
-    kl[q] = valid[q] ? ~(uint32_t)(lane + 64 * q) : 0u;
+    vv[0][q] = v[q];
+    ok[0][q] = valid[q];
   }
-  sel_e = -1;
-  sel_v = 0.0f;
-  float m = 0.0f, sum = 0.0f;
-  for (int r = 0; r < k; ++r) {
-    // this lane's best remaining key
-    uint32_t bh = kh[0], bl = kl[0];
-#pragma unroll
-    for (int q = 1; q < 4; ++q) {
-      const bool take = (kh[q] > bh) || (kh[q] == bh && kl[q] > bl);
-      bh = take ? kh[q] : bh;
-      bl = take ? kl[q] : bl;
-    }
-    uint32_t mh, ml;
-    wave_max_key(bh, bl, mh, ml);
-    // the winning key is a valid one (k <= number of valid experts); the
-    // clamp only keeps an index in range should that ever not hold
-    const int e = min(max((int)~ml, 0), 255);
-    const float val = float_from_order_key(mh);
-    if (lane == r) {
-      sel_e = e;
-      sel_v = val;
-    }
-    // the owner drops the selected key
-    if ((e & 63) == lane) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (q == (e >> 6)) kh[q] = kl[q] = 0u;
-    }
-    if (r == 0) m = val;
-    sum += expf(val - m);  // uniform, rank order
-  }
-  w = (lane < k) ? expf(sel_v - m) / sum : 0.0f;
+  int e[1];
+  float sv[1], ww[1];
+  wave_topk_weights_n<1>(vv, ok, k, lane, e, sv, ww);
+  sel_e = e[0];
+  sel_v = sv[0];
+  w = ww[0];
 }
 
 }  // namespace moe
