@@ -112,8 +112,13 @@ SMALL = synth.Workload("small", T=200, H=512, E=16, k=4, I=256, I_s=128, bias="n
 SMALL_BM128 = synth.Workload("small128", T=700, H=256, E=16, k=6, I=128, I_s=128)
 SMALL_BM32 = synth.Workload("small32", T=45, H=256, E=12, k=3, I=384, I_s=0)
 
+WIDE = synth.Workload("wide", T=96, H=4096, E=32, k=4, I=256, I_s=256, bias="normal", bias_sigma=0.5)
+K16 = synth.Workload("k16", T=70, H=512, E=32, k=16, I=256, I_s=128)
+
 LAYER_CASES = [
     ("tiny", dict(wl="tiny")),
+    ("wide-H4096", dict(wl=WIDE)),
+    ("k16", dict(wl=K16)),
     ("small-bm64", dict(wl=SMALL)),
     ("small-bm128", dict(wl=SMALL_BM128)),
     ("small-bm32", dict(wl=SMALL_BM32)),
@@ -176,6 +181,28 @@ def test_decode_parity(torch, full_layer, seed):
     if ex[0]:
         pytest.skip("near-tie token")
     G.check_y(G.y_to_f64(y), r["y"], f"decode seed {seed}")
+
+
+DECODE_SHAPES = [
+    ("k16-shared", synth.Workload("d16", T=1, H=512, E=32, k=16, I=256, I_s=128)),
+    ("k9-noshared", synth.Workload("d9", T=1, H=256, E=12, k=9, I=384, I_s=0)),
+    ("wide-H4096", synth.Workload("dwide", T=1, H=4096, E=64, k=4, I=640, I_s=256, bias="normal")),
+    ("k1", synth.Workload("d1", T=1, H=256, E=8, k=1, I=128, I_s=128)),
+]
+
+
+@pytest.mark.parametrize("label,wl", DECODE_SHAPES, ids=[c[0] for c in DECODE_SHAPES])
+def test_decode_shapes(torch, label, wl):
+    """Decode kernels at other shapes: k above 8 (the wide top-k template), no shared expert, H above
+    2048 (several chunk groups per row), I not a multiple of 512, k = 1."""
+    G.say(f"[decode-shape] {label}")
+    inp = synth.make_inputs(wl, seed=4)  # seed 4: the token's top-k margin is >= 4e-3 for every shape here
+    lay = DeviceLayer.from_inputs(inp)
+    y = lay.forward(G.to_dev_x(inp))
+    torch.cuda.synchronize()
+    r = oracle.forward(inp)
+    assert not G.excluded_tokens(r["logits"], wl.k)[0]
+    G.check_y(G.y_to_f64(y), r["y"], f"decode {label}")
 
 
 def test_decode_with_bias_and_zero_token(torch, full_layer):
