@@ -9,12 +9,13 @@
 // wavefront, with 16-byte loads (64 lanes x 16 B = 1 KiB per instruction),
 // and all loads of a wavefront are issued before its reductions.
 //
-//   D1 router + shared expert: wave per router row (logit) and per shared
-//      (gate, up) row pair; one wave for the shared gate s = sigmoid(x.w_sg)
-//   D2 top-k + gate/up of the k selected experts: every workgroup ranks the
-//      E logits in LDS (same selection rule and weights as prefill), then a
-//      wave per (expert, row) pair computes h = silu(g) * u in fp32;
-//      workgroup 0 also stores ids and weights for D3
+//   D1 router: wave per router row (logit); one wave for the shared gate
+//      s = sigmoid(x.w_sg)
+//   D2 top-k + gate/up: in every workgroup, wave 0 selects the k experts from
+//      the E logits (same rule and weights as prefill) while waves 1..3
+//      compute the shared expert's gate/up rows; then a wave per (expert,
+//      row) pair computes h = silu(g) * u in fp32; workgroup 0 also stores
+//      ids and weights for D3
 //   D3 down projection + combine: wave per output column, k + 1 rows of
 //      W_down / Ws_down, y = sum_j w_j o_j + s o_s in fp32 -> bf16
 // Wave sums use DPP row shifts and row broadcasts (no LDS round trips).
@@ -95,10 +96,11 @@ __device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* xg, co
   d1 = wave_sum(d1);
 }
 
-__global__ __launch_bounds__(256) void decode_router_shared_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
-    const uint16_t* __restrict__ ws_gate, const uint16_t* __restrict__ ws_up, const uint16_t* __restrict__ w_sg,
-    int H, int E, int I_s, DecodeWs d) {
+__global__ __launch_bounds__(256) void decode_router_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wr,
+                                                            const float* __restrict__ bias,
+                                                            const uint16_t* __restrict__ w_sg, int H, int E,
+                                                            DecodeWs d) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   float d0, d1;
@@ -109,17 +111,14 @@ __global__ __launch_bounds__(256) void decode_router_shared_kernel(
       if (v == 0.0f) v = 0.0f;
       d.logits[row] = v;
     }
-  } else if (row < E + I_s) {
-    int i = row - E;
-    row_dots(nullptr, x, ws_gate + (size_t)i * H, ws_up + (size_t)i * H, H, lane, d0, d1);
-    if (lane == 0) d.hs[i] = silu(d0) * d1;
-  } else if (row == E + I_s && I_s > 0) {
+  } else if (row == E && w_sg) {
     row_dots(nullptr, x, w_sg, nullptr, H, lane, d0, d1);
     if (lane == 0) d.s[0] = 1.0f / (1.0f + expf(-d0));
   }
 }
 
-// Top-k of the E logits (wave 0 of the workgroup), results in LDS.
+// Top-k of the E logits by wave 0 of the workgroup, results in LDS (the
+// caller synchronises the workgroup before reading them).
 __device__ __forceinline__ void block_topk(const float* __restrict__ logits, int E, int k, int* sel_e,
                                            float* sel_w) {
   const int lane = threadIdx.x & 63;
@@ -140,18 +139,31 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ logits, int
       sel_w[lane] = w;
     }
   }
-  __syncthreads();
 }
 
+// While wave 0 selects the experts, waves 1..3 compute the shared expert's
+// gate/up rows (they do not depend on the routing): row i = silu(g) * u -> h_s.
 __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t* __restrict__ x,
                                                                   const uint16_t* __restrict__ w_gate,
-                                                                  const uint16_t* __restrict__ w_up, int H, int E,
-                                                                  int k, int I, DecodeWs d) {
+                                                                  const uint16_t* __restrict__ w_up,
+                                                                  const uint16_t* __restrict__ ws_gate,
+                                                                  const uint16_t* __restrict__ ws_up, int H, int E,
+                                                                  int k, int I, int I_s, DecodeWs d) {
   __shared__ u32x4 sx[1024];
   __shared__ int sel_e[kMaxK];
   __shared__ float sel_w[kMaxK];
   for (int c = threadIdx.x; c < H / 8; c += 256) sx[c] = reinterpret_cast<const u32x4*>(x)[c];
-  block_topk(d.logits, E, k, sel_e, sel_w);
+  const int wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    block_topk(d.logits, E, k, sel_e, sel_w);
+  } else {
+    for (int i = blockIdx.x * 3 + wave - 1; i < I_s; i += 3 * gridDim.x) {
+      float g, u;
+      row_dots(nullptr, x, ws_gate + (size_t)i * H, ws_up + (size_t)i * H, H, threadIdx.x & 63, g, u);
+      if ((threadIdx.x & 63) == 0) d.hs[i] = silu(g) * u;
+    }
+  }
+  __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x < k) {
     d.ids[threadIdx.x] = sel_e[threadIdx.x];
     d.w[threadIdx.x] = sel_w[threadIdx.x];
@@ -306,12 +318,12 @@ hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const floa
                          const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int H, int E,
                          int k, int I, int I_s, uint16_t* y, void* ws, hipStream_t st) {
   DecodeWs d = carve(ws, H, E, k, I, I_s);
-  int rows1 = E + I_s + (I_s > 0 ? 1 : 0);
-  hipLaunchKernelGGL(decode_router_shared_kernel, dim3((rows1 + 3) / 4), dim3(256), 0, st, x, w_router, bias,
-                     ws_gate, ws_up, w_sg, H, E, I_s, d);
-  // 4 waves per workgroup, one row pair per wave
-  hipLaunchKernelGGL(decode_topk_gate_up_kernel, dim3((k * I + 3) / 4), dim3(256), 0, st, x, w_gate, w_up, H, E,
-                     k, I, d);
+  const int rows1 = E + (I_s > 0 ? 1 : 0);
+  hipLaunchKernelGGL(decode_router_kernel, dim3((rows1 + 3) / 4), dim3(256), 0, st, x, w_router, bias,
+                     I_s > 0 ? w_sg : nullptr, H, E, d);
+  // 4 waves per workgroup, one routed row pair per wave; waves 1..3 also take the shared rows
+  hipLaunchKernelGGL(decode_topk_gate_up_kernel, dim3((k * I + 3) / 4), dim3(256), 0, st, x, w_gate, w_up, ws_gate,
+                     ws_up, H, E, k, I, I_s, d);
   // 4 waves per workgroup, one output column per wave (H is a multiple of 256)
   if (k <= 8)
     hipLaunchKernelGGL(decode_down_kernel<8>, dim3((H + 3) / 4), dim3(256), 0, st, w_down, ws_down, H, k, I, I_s, d,
