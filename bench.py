@@ -38,20 +38,30 @@ def log(msg):
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_prefill8k_hbm_traffic.md")
 
 
-def measured_traffic():
+def measured_traffic(kernel):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 --pmc record
     (FETCH_SIZE and WRITE_SIZE passes, scaled by a device copy of known size), or None when
-    the record is missing or any source it was taken on has changed since."""
+    the record is missing, was taken on another kernel, or any source it was taken on has
+    changed since."""
     import hashlib
     try:
         line = [ln for ln in open(TRAFFIC_RECORD) if ln.startswith("traffic-record:")][0]
         rec = json.loads(line.split(":", 1)[1])
+        if rec["kernel"] != kernel:
+            return None
         for path, digest in rec["sources"].items():
             if hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16] != digest:
                 return None
         return rec["traffic_bytes"]
     except (OSError, IndexError, KeyError, ValueError):
         return None
+
+
+def gate_up_kernel_name(tile_rows):
+    """The kernel that runs the gate/up launch for a tile height (as rocprofv3 names it)."""
+    if tile_rows == 256:
+        return "grouped_gemm_dma_kernel<0>"
+    return f"grouped_gemm_kernel<{tile_rows}, 32, 2, 0>"
 
 
 def algorithmic(T, H, E, k, I, I_s):
@@ -245,10 +255,10 @@ def main():
         "layer_mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stage_us": {n: v * 1e3 for n, v in stage_ms.items()},
         "padding_overhead": padded_rows / (T * k) - 1.0,
-        "roofline": {"kernel": "grouped_gemm_kernel<128, 32, 2, 0>: gate/up GEMM with SwiGLU epilogue, one launch over all "
+        "roofline": {"kernel": gate_up_kernel_name(BIG) + ": gate/up GEMM with SwiGLU epilogue, one launch over all "
                                "expert tiles and the shared expert's token tiles",
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(gate_up_kernel_name(BIG)),
                      "flops_per_launch": gate_up_flops, "avg_launch_us": gu_ms * 1e3,
                      "padded_rows": padded_rows},
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),

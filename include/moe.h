@@ -58,12 +58,12 @@ const char* moe_status_str(int status);
 const char* moe_last_error(void);
 
 /*
- * Tile heights chosen for T tokens.  BIG (moe_align_tile_rows) is 128, 64 or
- * 32 from the mean rows per expert.  SMALL (moe_align_small_tile_rows) equals
- * BIG: every expert's rows are cut into ceil(count / BIG) tiles, the last one
- * padded, and there is one tile list.  The environment variables
- * MOE_TILE_ROWS and MOE_SMALL_ROWS (32, 64 or 128; read once per process; for
- * tuning) override BIG and SMALL.  With SMALL < BIG an expert gets
+ * Tile heights chosen for T tokens.  BIG (moe_align_tile_rows) is 256, 128,
+ * 64 or 32 from the mean rows per expert T*k/E (>= 192, >= 128, >= 48, less).
+ * SMALL (moe_align_small_tile_rows) equals BIG: every expert's rows are cut
+ * into ceil(count / BIG) tiles, the last one padded, and there is one tile
+ * list.  The environment variables MOE_TILE_ROWS and MOE_SMALL_ROWS (32, 64,
+ * 128 or 256; read once per process; for tuning) override BIG and SMALL.  With SMALL < BIG an expert gets
  * floor(count / BIG) BIG tiles and its remainder is padded to whole SMALL
  * tiles, listed separately.  Depends only on (T, E, k) and those variables;
  * the layer's results do not depend on the tiling.

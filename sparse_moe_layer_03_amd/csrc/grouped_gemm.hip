@@ -4,11 +4,16 @@
 // (guanjiawei.ai "AIMA AMD395 Qwen3.6-35B-A3B", data path: selected-expert
 // MoE; kongchang.com "GFX1151 engine", MoE kernel section: the prefill gain
 // came from a rewritten MoE kernel).  After the align stage every expert owns
-// a run of padded rows cut into tiles; one workgroup computes one (tile,
+// a run of padded rows cut into tiles; a workgroup computes a (tile,
 // 256-column block) item as a dense BF16 GEMM on v_mfma_f32_32x32x16_bf16
-// with fp32 accumulation.
+// with fp32 accumulation.  Every output element sums its K products in the
+// same order (16-column MFMA steps, ascending) whatever the tile height, so
+// results do not depend on the tiling.
 //
-// One kernel template, four launch kinds:
+// Two kernels: grouped_gemm_kernel for tiles of 32 to 128 rows (below) and
+// the persistent 256-row grouped_gemm_dma_kernel for the routed gate/up and
+// down GEMMs of large token counts (described where it is defined).
+// grouped_gemm_kernel has four launch kinds:
 //   GATE_UP         routed tiles.  A = gathered token rows of x, B = 128 rows
 //                   of W_gate and the matching 128 rows of W_up; epilogue
 //                   silu(g) * u -> h (bf16).  The shared expert's gate/up over
@@ -23,7 +28,8 @@
 //                   epilogue is the deterministic combine
 //                   y = sum_j w_j o[t*k + j] + s * acc
 //
-// Data movement (256 threads, 4 wavefronts, BM x 256 tile):
+// Data movement of the BM <= 128 kernel (256 threads, 4 wavefronts, BM x 256
+// tile; the 256-row kernel is described where it is defined):
 //   * per K step of BK columns the A tile (BM x 2BK bytes) and B tile
 //     (256 x 2BK bytes) are loaded with 16-byte global loads into registers
 //     two steps ahead (two register sets), then written to one of two LDS
@@ -51,20 +57,25 @@ enum { GATE_UP = 0, DOWN = 1, ROUTER = 2, SHARED_COMBINE = 3 };
 // Kind of one work item.
 enum { K_GU = 0, K_ROUTER = 1, K_DOWN = 2, K_COMBINE = 3 };
 
-// Wave layout of a BM x 256 tile over 4 wavefronts.
+// Wave layout of a BM x 256 tile: NT threads, WAVES_M x WAVES_N wavefronts of
+// WTM x WTN outputs each (MI x NJ blocks of 32 x 32).
 template <int BM>
 struct Cfg;
 template <>
+struct Cfg<256> {
+  static constexpr int NT = 512, WAVES_M = 4, WTM = 64, MI = 2, WAVES_N = 2, WTN = 128, NJ = 4;
+};
+template <>
 struct Cfg<128> {
-  static constexpr int WAVES_M = 2, WTM = 64, MI = 2, WAVES_N = 2, WTN = 128, NJ = 4;
+  static constexpr int NT = 256, WAVES_M = 2, WTM = 64, MI = 2, WAVES_N = 2, WTN = 128, NJ = 4;
 };
 template <>
 struct Cfg<64> {
-  static constexpr int WAVES_M = 1, WTM = 64, MI = 2, WAVES_N = 4, WTN = 64, NJ = 2;
+  static constexpr int NT = 256, WAVES_M = 1, WTM = 64, MI = 2, WAVES_N = 4, WTN = 64, NJ = 2;
 };
 template <>
 struct Cfg<32> {
-  static constexpr int WAVES_M = 1, WTM = 32, MI = 1, WAVES_N = 4, WTN = 64, NJ = 2;
+  static constexpr int NT = 256, WAVES_M = 1, WTM = 32, MI = 1, WAVES_N = 4, WTN = 64, NJ = 2;
 };
 
 struct GemmParams {
@@ -114,6 +125,41 @@ struct Item {
   int nb;    // column block
 };
 
+// Routed launches (GATE_UP, DOWN): item count and item by index.  Routed
+// tiles come first, tile major (the column blocks of a tile run together and
+// share its A rows in L2); a GATE_UP launch then appends the shared expert's
+// token tiles (they fill the launch's last, partly idle round).
+struct RoutedItems {
+  int n_routed, nb_per, nb_sh, total;
+};
+template <int BM, int MODE>
+__device__ __forceinline__ RoutedItems routed_items(const GemmParams& p) {
+  RoutedItems r;
+  r.nb_per = (MODE == GATE_UP) ? p.N / 128 : p.N / 256;
+  r.n_routed = p.n_tiles[0] * r.nb_per;
+  r.nb_sh = (MODE == GATE_UP && p.bs0) ? p.N_s / 128 : 0;
+  r.total = r.n_routed + ((p.T + BM - 1) / BM) * r.nb_sh;
+  return r;
+}
+template <int BM, int MODE>
+__device__ __forceinline__ Item routed_item_at(const GemmParams& p, const RoutedItems& r, int item) {
+  Item it;
+  it.kind = (MODE == DOWN) ? K_DOWN : K_GU;
+  it.expert = 0;
+  if (item < r.n_routed) {
+    const int tile = item / r.nb_per;
+    it.dense = false;
+    it.nb = item % r.nb_per;
+    it.expert = p.tiles[2 * tile];
+    it.row0 = p.tiles[2 * tile + 1];
+  } else {
+    it.dense = true;
+    it.row0 = ((item - r.n_routed) / r.nb_sh) * BM;
+    it.nb = (item - r.n_routed) % r.nb_sh;
+  }
+  return it;
+}
+
 template <int BM, int MODE>
 __device__ __forceinline__ Item decode_item(const GemmParams& p) {
   Item it;
@@ -124,25 +170,10 @@ __device__ __forceinline__ Item decode_item(const GemmParams& p) {
   it.nb = 0;
   const int n_tok_tiles = (p.T + BM - 1) / BM;
   if (MODE == GATE_UP || MODE == DOWN) {
-    // routed tiles first; a GATE_UP launch then appends the shared expert's
-    // token tiles (they fill the launch's last, partly idle round)
-    const int nb_per = (MODE == GATE_UP) ? p.N / 128 : p.N / 256;
-    const int n_routed = p.n_tiles[0] * nb_per;
-    const int nb_sh = (MODE == GATE_UP && p.bs0) ? p.N_s / 128 : 0;
-    const int item = xcd_item(blockIdx.x, n_routed + n_tok_tiles * nb_sh);
+    const RoutedItems r = routed_items<BM, MODE>(p);
+    const int item = xcd_item(blockIdx.x, r.total);
     if (item < 0) return it;
-    if (item < n_routed) {
-      // tile major: the column blocks of a tile run together and share its A rows in L2
-      const int tile = item / nb_per;
-      it.nb = item % nb_per;
-      it.expert = p.tiles[2 * tile];
-      it.row0 = p.tiles[2 * tile + 1];
-    } else {
-      it.dense = true;
-      it.row0 = ((item - n_routed) / nb_sh) * BM;
-      it.nb = (item - n_routed) % nb_sh;
-    }
-    return it;
+    return routed_item_at<BM, MODE>(p, r, item);
   }
   const int nb_per = (MODE == ROUTER) ? 1 : p.N_s / 256;
   const int item = xcd_item(blockIdx.x, n_tok_tiles * nb_per);
@@ -251,20 +282,22 @@ __device__ __forceinline__ void router_gate(const GemmParams& p, const Item it, 
   if (tid % KCH == 0 && t < p.T) p.gate_s[t] = 1.0f / (1.0f + expf(-gacc));
 }
 
-template <int BM, int MODE, int MI, int NJ, int WTM>
+template <int BM, int NT, int MODE, int MI, int NJ, int WTM>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32x16 (&acc)[MI][NJ], int wm,
                                          const int (&bb)[NJ], unsigned char* smem) {
+  constexpr int RG = NT / 8;    // copy-out: rows per group
+  constexpr int RPT = BM / RG;  // copy-out: rows per thread
   const int tid = threadIdx.x, lane = tid & 63;
   float* sc = reinterpret_cast<float*>(smem);  // [BM][ESLD]
   const bool gu = it.kind == K_GU;
   const int ncol = gu ? 128 : 256;
-  const int cr = tid >> 3;       // copy-out: row within a 32-row group
+  const int cr = tid >> 3;       // copy-out: row within a group of RG rows
   const int cc = (tid & 7) * 8;  // copy-out: first of 8 columns
   // DOWN: the assignment held by each of this thread's copy-out rows, read
   // once for all column passes (-1: padding row, not stored)
-  int arow_of[BM / 32];
+  int arow_of[RPT];
 #pragma unroll
-  for (int i = 0; i < BM / 32; ++i) arow_of[i] = (MODE == DOWN) ? p.sorted[it.row0 + cr + 32 * i] : 0;
+  for (int i = 0; i < RPT; ++i) arow_of[i] = (MODE == DOWN) ? p.sorted[it.row0 + cr + RG * i] : 0;
   for (int pass = 0; pass < ncol / EPW; ++pass) {
 #pragma unroll
     for (int m = 0; m < MI; ++m) {
@@ -283,8 +316,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < (MODE == SHARED_COMBINE ? 0 : BM / 32); ++i) {
-      const int r = cr + 32 * i;
+    for (int i = 0; i < (MODE == SHARED_COMBINE ? 0 : RPT); ++i) {
+      const int r = cr + RG * i;
       const float4 v0 = *reinterpret_cast<const float4*>(sc + r * ESLD + cc);
       const float4 v1 = *reinterpret_cast<const float4*>(sc + r * ESLD + cc + 4);
       float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -323,16 +356,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
     if constexpr (MODE == SHARED_COMBINE) {
       // every row of this thread gathers its k expert rows, then adds s[t]
       // times the shared expert's output
-      constexpr int RPT = BM / 32;
       float yv[RPT][8];
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const int t = it.row0 + cr + 32 * i;
+        const int t = it.row0 + cr + RG * i;
         gather_combine8(p.o, p.w, t < p.T ? t : p.T - 1, p.k, p.ldo, it.nb * 256 + pass * EPW + cc, yv[i]);
       }
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        const int r = cr + 32 * i;
+        const int r = cr + RG * i;
         const int t = it.row0 + r;
         if (t < p.T) {
           const float4 v0 = *reinterpret_cast<const float4*>(sc + r * ESLD + cc);
@@ -361,10 +393,10 @@ constexpr size_t lds_bytes() {
 
 // BM x 256 tile, K steps of BK columns, OCC workgroups per CU (register budget).
 template <int BM, int BK, int OCC, int MODE>
-__global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmParams p) {
   using C = Cfg<BM>;
   constexpr int KCH = BK / 8;               // 16-byte chunks per row per K step
-  constexpr int RPP = 256 / KCH;            // rows covered by one pass of 256 threads
+  constexpr int RPP = C::NT / KCH;          // rows covered by one pass of the NT threads
   constexpr int NA = (BM + RPP - 1) / RPP;  // A chunks per thread per K step
   constexpr int NB = BNB / RPP;             // B chunks per thread per K step
   constexpr int SUB = BK / 16;              // MFMA K sub-steps per K step
@@ -494,7 +526,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
   // ROUTER: partial x . w_sg of the shared-expert gate from the A tile in LDS:
   // thread t takes row t / KCH, 16-byte chunk t % KCH of every K step
   float gacc = 0.0f;
-  static_assert(MODE != ROUTER || BM * KCH == 256, "router gate needs one A chunk per thread");
+  static_assert(MODE != ROUTER || BM * KCH == C::NT, "router gate needs one A chunk per thread");
   auto kloop = [&](auto LIVE) {
     constexpr bool L = decltype(LIVE)::value;
     auto stage = [&](int st, u32x4 (&pa)[NA], u32x4 (&pb)[NB], int next_kb, int ks) {
@@ -548,7 +580,262 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_kernel(GemmParams p) {
   if constexpr (MODE == ROUTER) {
     if (p.w_sg) router_gate<BM, KCH>(p, it, gacc);
   }
-  epilogue<BM, MODE, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
+  epilogue<BM, C::NT, MODE, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
+}
+
+// 256 x 256 tiles for the routed gate/up and down GEMMs.  512 threads (8
+// wavefronts of 64 x 128 outputs), one workgroup per CU, persistent: the
+// workgroups of an XCD walk that XCD's contiguous run of items together.
+//   * A and B rows arrive by direct-to-LDS loads (global_load_lds_dwordx4):
+//     no staging registers and no LDS stores; a K step is 64 columns, so
+//     every row load is one whole 128-byte line;
+//   * two 64 KB stages: the loads of step k + 1 are in flight while step k
+//     is computed, and the last step of an item overlaps the first loads of
+//     the next item, which also run under the epilogue;
+//   * the epilogue stages bf16 results in the stage that the last K step
+//     used (free once its fragments are read), so it never waits for or
+//     disturbs the loads of the next item;
+//   * A row groups of only padding are not loaded: their LDS rows hold
+//     finite values of earlier data and feed only output rows that are not
+//     stored (a row of A reaches only the same row of the product).
+constexpr int DBM = 256, DNT = 512, DBK = 64, DKCH = DBK / 8;
+constexpr int DRPI = 64 / DKCH;                    // rows filled by one load instruction (64 lanes x 16 B)
+constexpr int DNQ = 32 / DRPI;                     // load instructions per wave per operand per K step
+constexpr int DSTAGE = (DBM + BNB) * DKCH;         // 16-byte chunks per stage (A rows, then B rows)
+constexpr size_t DLDS = 2 * (size_t)DSTAGE * 16;   // 128 KB
+constexpr int DESB = 72;                           // bf16 row stride of the epilogue staging tile
+
+// One direct-to-LDS load: 16 bytes per lane from src into LDS at
+// lds_base + 16 * lane (lds_base wave-uniform, in M0).  Inline assembly, so
+// that the compiler's wait-count pass does not order later LDS reads behind
+// it; the K loop waits for it explicitly before the barrier that publishes
+// the stage.  (The compiler's own waits for its loads only grow stronger
+// from loads it does not see: vector-memory counts complete in issue order.)
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
+               : "memory", "m0");
+}
+
+// wait until every vector-memory access of this wave has completed
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
+
+// Per-item state of the persistent kernel.
+struct DmaItem {
+  Item it;
+  const uint16_t* asrc[DNQ];  // this lane's A source of load q (K step 0)
+  const uint16_t* bbase;      // this wave's B rows: bbase + the item-independent lane offsets
+  uint32_t aon;               // bit q: A group q holds a data row
+  bool live;                  // this wave's 64 rows hold data
+};
+
+template <int MODE>
+__device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, int wave, int wm, int lane) {
+  DmaItem d;
+  d.it = it;
+  d.aon = 0;
+  // load q of wave w fills rows w*32 + q*8 .. +7 of the A (or B) part of a
+  // stage: lane l -> row w*32 + q*8 + l/8, LDS slot l%8, which holds logical
+  // chunk swz(row, l%8) (the swizzle is its own inverse)
+#pragma unroll
+  for (int q = 0; q < DNQ; ++q) {
+    const int r = wave * 32 + q * DRPI + lane / DKCH;
+    const int ch = swz<DKCH>(r, lane % DKCH);
+    bool ok;
+    d.asrc[q] = a_row<MODE>(p, it, r, ok) + ch * 8;
+    d.aon |= (__builtin_amdgcn_readfirstlane(ok ? 1 : 0) ? 1u : 0u) << q;  // lane 0 holds the group's first row
+  }
+  // B rows w*32 .. w*32+31: gate/up items take gate rows in waves 0-3 and up
+  // rows in waves 4-7 (the same 128 intermediate columns)
+  if (MODE == GATE_UP) {
+    const uint16_t* g = it.dense ? p.bs0 : p.b0 + (size_t)it.expert * p.N * p.K;
+    const uint16_t* u = it.dense ? p.bs1 : p.b1 + (size_t)it.expert * p.N * p.K;
+    d.bbase = (wave < 4 ? g : u) + (size_t)it.nb * 128 * p.K;
+  } else {
+    d.bbase = (it.dense ? p.bs0 : p.b0 + (size_t)it.expert * p.N * p.K) + (size_t)it.nb * 256 * p.K;
+  }
+  const int r = wm * 64;
+  const bool lv = it.dense ? (it.row0 + r < p.T) : (p.sorted[it.row0 + r] >= 0);
+  d.live = __builtin_amdgcn_readfirstlane((int)lv) != 0;
+  return d;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) {
+  static_assert(MODE == GATE_UP || MODE == DOWN, "routed GEMMs only");
+  using C = Cfg<DBM>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+
+  // this workgroup's items: slot s of its XCD takes items first, first + nslot, ...
+  const RoutedItems ri = routed_items<DBM, MODE>(p);
+  const int per = (ri.total + kNumXcd - 1) / kNumXcd;
+  const int nslot = (int)gridDim.x / kNumXcd;
+  const int xcd = (int)blockIdx.x % kNumXcd;
+  const int first = xcd * per + (int)blockIdx.x / kNumXcd;
+  const int last = min(ri.total, (xcd + 1) * per);
+  if (first >= last) return;
+
+  u32x4* sm = reinterpret_cast<u32x4*>(smem);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  // A groups that are never loaded must not hold arbitrary bits on the first item
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int i = tid; i < 2 * DSTAGE; i += DNT) sm[i] = zero;
+  __syncthreads();
+
+  // element offset of this lane's B source of load q from the wave's bbase
+  uint32_t boff[DNQ];
+#pragma unroll
+  for (int q = 0; q < DNQ; ++q) {
+    const int r = wave * 32 + q * DRPI + lane / DKCH;
+    boff[q] = (uint32_t)((MODE == GATE_UP ? (r & 127) : r) * p.K + swz<DKCH>(r, lane % DKCH) * 8);
+  }
+  auto issue = [&](const DmaItem& d, int st, int kb) {
+    const uint32_t base = lds0 + (uint32_t)st * DSTAGE * 16;
+#pragma unroll
+    for (int q = 0; q < DNQ; ++q)
+      if ((d.aon >> q) & 1u) dma16(d.asrc[q] + kb * DBK, base + (uint32_t)(wave * 32 + q * DRPI) * DKCH * 16);
+#pragma unroll
+    for (int q = 0; q < DNQ; ++q)
+      dma16(d.bbase + boff[q] + kb * DBK, base + (uint32_t)(DBM + wave * 32 + q * DRPI) * DKCH * 16);
+  };
+  int bb[C::NJ];
+  {
+    constexpr int half = C::NJ / 2;
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j)
+      bb[j] = (MODE == GATE_UP) ? (j < half ? wn * half * 32 + j * 32 : 128 + wn * half * 32 + (j - half) * 32)
+                                : wn * C::WTN + j * 32;
+  }
+  struct Frag {
+    bf16x8 a[C::MI], b[C::NJ];
+  };
+  auto read_frags = [&](Frag& f, int st, int sub) {
+    const u32x4* cA = sm + st * DSTAGE;
+    const u32x4* cB = cA + DBM * DKCH;
+    const int c = 2 * sub + (lane >> 5);
+#pragma unroll
+    for (int m = 0; m < C::MI; ++m) {
+      const int r = wm * C::WTM + m * 32 + (lane & 31);
+      f.a[m] = __builtin_bit_cast(bf16x8, cA[r * DKCH + swz<DKCH>(r, c)]);
+    }
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) {
+      const int r = bb[j] + (lane & 31);
+      f.b[j] = __builtin_bit_cast(bf16x8, cB[r * DKCH + swz<DKCH>(r, c)]);
+    }
+  };
+  f32x16 acc[C::MI][C::NJ];
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int m = 0; m < C::MI; ++m)
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j)
+        acc[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
+  };
+
+  constexpr int SUB = DBK / 16;
+  const int nk = p.K / DBK;  // even: K is a multiple of 128
+  DmaItem cur = dma_item<MODE>(p, routed_item_at<DBM, MODE>(p, ri, first), wave, wm, lane);
+  issue(cur, 0, 0);
+  for (int item = first; item < last; item += nslot) {
+    const int nxt = item + nslot;
+    const bool has_next = nxt < last;
+    DmaItem next = cur;
+    if (has_next) next = dma_item<MODE>(p, routed_item_at<DBM, MODE>(p, ri, nxt), wave, wm, lane);
+#pragma unroll
+    for (int m = 0; m < C::MI; ++m)
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[m][j][q] = 0.0f;
+    // K loop: wait for this wave's loads of step kb, barrier (everyone's have
+    // landed and everyone has finished reading the other stage), then load
+    // step kb + 1 (or the next item's step 0) into the other stage and
+    // compute step kb.  The last sub-step's fragments are read before the
+    // barrier and their MFMAs issued after it.
+    Frag f0, f1;
+    bool pending = false;
+    for (int kb = 0; kb < nk; ++kb) {
+      const int st = kb & 1;
+      wait_vm0();
+      __syncthreads();
+      if (kb + 1 < nk)
+        issue(cur, st ^ 1, kb + 1);
+      else if (has_next)
+        issue(next, 0, 0);
+      if (cur.live) {
+        read_frags(f0, st, 0);
+        if (pending) mma(f1);
+#pragma unroll
+        for (int sub = 1; sub < SUB; ++sub) {
+          if (sub & 1) {
+            read_frags(f1, st, sub);
+            mma(f0);
+          } else {
+            read_frags(f0, st, sub);
+            mma(f1);
+          }
+        }
+        pending = true;
+      }
+    }
+    if (pending) mma(f1);
+    __syncthreads();  // every fragment read of stage 1 has completed
+
+    // Epilogue through stage 1 (bf16 [256][DESB]), 64 output columns a pass:
+    // gate/up items store silu(g) * u -> h (or h_s), down items store rows
+    // of o at their assignment.
+    uint16_t* es = reinterpret_cast<uint16_t*>(smem) + (size_t)DSTAGE * 8;
+    const Item& it = cur.it;
+    const int cr = tid >> 3, cc = (tid & 7) * 8;
+    constexpr int RG = DNT / 8, RPT = DBM / RG;
+    const int ncol = (MODE == GATE_UP) ? 128 : 256;
+    // DOWN: the assignment held by each copy-out row (-1: padding, not stored)
+    int arow[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) arow[i] = (MODE == DOWN) ? p.sorted[it.row0 + cr + RG * i] : 0;
+    for (int pass = 0; pass < ncol / EPW; ++pass) {
+#pragma unroll
+      for (int m = 0; m < C::MI; ++m) {
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j) {
+          if (MODE == GATE_UP && j >= C::NJ / 2) continue;
+          const int col = bb[j] + (lane & 31) - pass * EPW;
+          if (col >= 0 && col < EPW) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int row = wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+              const float v = (MODE == GATE_UP) ? silu(acc[m][j][q]) * acc[m][(j + C::NJ / 2) % C::NJ][q]
+                                                : acc[m][j][q];
+              es[row * DESB + col] = f32_to_bf16(v);
+            }
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int r = cr + RG * i;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(es + r * DESB + cc);
+        const int col = pass * EPW + cc;
+        if (MODE == GATE_UP) {
+          if (it.dense) {
+            const int t = it.row0 + r;
+            if (t < p.T) *reinterpret_cast<u32x4*>(p.out_s + (size_t)t * p.ldo_s + it.nb * 128 + col) = v;
+          } else {
+            *reinterpret_cast<u32x4*>(p.out + (size_t)(it.row0 + r) * p.ldo + it.nb * 128 + col) = v;
+          }
+        } else {
+          const int a = arow[i];
+          if (a >= 0) *reinterpret_cast<u32x4*>(p.out + (size_t)a * p.ldo + it.nb * 256 + col) = v;
+        }
+      }
+      __syncthreads();
+    }
+    cur = next;
+  }
 }
 
 // Combine without a shared expert: y[t,c] = sum_j w[t,j] o[t*k+j, c].
@@ -574,7 +861,25 @@ hipError_t launch_mode(const GemmParams& p, int64_t max_items, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<BM, BK, OCC, MODE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BK, OCC, MODE>), dim3((unsigned)grid), dim3(256), lds, st, p);
+  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BK, OCC, MODE>), dim3((unsigned)grid), dim3(Cfg<BM>::NT), lds, st, p);
+  return hipGetLastError();
+}
+
+// Persistent launch: one workgroup per CU (at most one per item).
+template <int MODE>
+hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st) {
+  if (max_items <= 0) return hipSuccess;
+  if (p.K % (2 * DBK) != 0) return hipErrorInvalidValue;
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  int64_t grid = n_cu < max_items ? n_cu : max_items;
+  grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
+  e = hipFuncSetAttribute((const void*)grouped_gemm_dma_kernel<MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)DLDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE>), dim3((unsigned)grid), dim3(DNT), DLDS, st, p);
   return hipGetLastError();
 }
 
@@ -607,6 +912,9 @@ hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t
     case 128:
       if constexpr (MODE == DOWN) return launch_mode<MOE_DOWN_CFG_128, MODE>(p, max_items, st);
       return launch_mode<MOE_GEMM_CFG_128, MODE>(p, max_items, st);
+    case 256:
+      if constexpr (MODE == GATE_UP || MODE == DOWN) return launch_dma<MODE>(p, max_items, st);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -58,10 +58,15 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Mean rows per expert from which 256-row tiles are used.
+#ifndef MOE_TILE256_MIN_MEAN
+#define MOE_TILE256_MIN_MEAN 192
+#endif
+
 int env_rows(const char* name) {
   const char* s = getenv(name);  // tuning only
   const int r = s ? atoi(s) : 0;
-  return (r == 32 || r == 64 || r == 128) ? r : 0;
+  return (r == 32 || r == 64 || r == 128 || r == 256) ? r : 0;
 }
 
 int tile_rows_override() {
@@ -154,6 +159,7 @@ int moe_align_tile_rows(int T, int E, int k) {
   if (ov) return ov;
   if (E < 1) return 32;
   const int64_t avg = (int64_t)T * k / E;  // mean rows per expert
+  if (avg >= MOE_TILE256_MIN_MEAN) return 256;
   if (avg >= 128) return 128;
   if (avg >= 48) return 64;
   return 32;

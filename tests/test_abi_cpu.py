@@ -39,17 +39,22 @@ def test_status_strings(L):
 
 
 def test_tile_rows_policy():
-    assert moe.moe_align_tile_rows(8192, 256, 8) == 128
-    assert moe.moe_align_tile_rows(32768, 256, 8) == 128
+    # mean rows per expert T*k/E: >= 192 -> 256, >= 128 -> 128, >= 48 -> 64, else 32
+    assert moe.moe_align_tile_rows(8192, 256, 8) == 256
+    assert moe.moe_align_tile_rows(32768, 256, 8) == 256
+    assert moe.moe_align_tile_rows(6144, 256, 8) == 256
+    assert moe.moe_align_tile_rows(6143, 256, 8) == 128
+    assert moe.moe_align_tile_rows(4096, 256, 8) == 128
     assert moe.moe_align_tile_rows(1024, 256, 8) == 32
     assert moe.moe_align_tile_rows(2048, 256, 8) == 64
-    for T, E, k in ((8192, 256, 8), (2048, 256, 8), (1024, 256, 8), (16, 8, 2), (5, 3, 3)):
+    for T, E, k in ((8192, 256, 8), (4096, 256, 8), (2048, 256, 8), (1024, 256, 8), (16, 8, 2), (5, 3, 3)):
         assert moe.moe_align_small_tile_rows(T, E, k) == moe.moe_align_tile_rows(T, E, k)
     # padding is at most BIG - 1 rows per used expert
-    assert moe.moe_align_max_rows(8192, 256, 8) == 8192 * 8 + 256 * 127
+    assert moe.moe_align_max_rows(8192, 256, 8) == 8192 * 8 + 256 * 255
+    assert moe.moe_align_max_rows(4096, 256, 8) == 4096 * 8 + 256 * 127
     assert moe.moe_align_max_rows(2, 256, 8) == 16 + 16 * 31
-    assert moe.moe_align_max_big_tiles(8192, 256, 8) == (65536 + 256 * 127) // 128
-    assert moe.moe_align_max_tiles(8192, 256, 8) == (65536 + 256 * 127) // 128
+    assert moe.moe_align_max_big_tiles(8192, 256, 8) == (65536 + 256 * 255) // 256
+    assert moe.moe_align_max_tiles(8192, 256, 8) == (65536 + 256 * 255) // 256
     # BIG == SMALL == 32: one tile class, ceil(count / 32) tiles per expert
     assert moe.moe_align_max_big_tiles(16, 8, 2) == (32 + 8 * 31) // 32
     assert moe.moe_align_max_tiles(16, 8, 2) == (32 + 8 * 31) // 32
