@@ -227,9 +227,10 @@ def test_padded_tile_boundaries(torch, E, k, T):
     run_boundary_case(E, k, T)
 
 
-@pytest.mark.parametrize("big,small", [(64, 32), (128, 64)])
-def test_padded_tile_boundaries_two_classes(torch, big, small):
-    """The same cases with BIG and SMALL tile lists, in a child process (the tiling is read once per process)."""
+@pytest.mark.parametrize("big,small", [(64, 32), (128, 64), (256, 256), (256, 64)])
+def test_padded_tile_boundaries_other_tilings(torch, big, small):
+    """The same cases under another tiling, in a child process (the tiling is read once per process):
+    BIG and SMALL tile lists, and the persistent 256-row kernel alone and beside 64-row remainder tiles."""
     import subprocess
     env = dict(os.environ, MOE_TILE_ROWS=str(big), MOE_SMALL_ROWS=str(small))
     G.say(f"[boundaries] child process with MOE_TILE_ROWS={big} MOE_SMALL_ROWS={small}")
