@@ -220,6 +220,56 @@ def test_decode_with_bias_and_zero_token(torch, full_layer):
     assert torch.count_nonzero(y0.view(torch.int16)).item() == 0
 
 
+def test_decode_repeated_calls(torch, full_layer):
+    """Many single-token calls on one workspace, each with its own token: every call matches the oracle."""
+    inp = G.inputs("decode", 1, seed=0)
+    lay = _layer_for(inp, full_layer)
+    n = 24
+    xs = synth._draw_bf16(300, "x", (n, 2048), 1.0)
+    ys = []
+    for i in range(n):
+        sub = dict(inp)
+        sub["x"] = xs[i:i + 1]
+        ys.append(lay.forward(G.to_dev_x(sub)))
+    torch.cuda.synchronize()
+    checked = 0
+    for i in range(0, n, 3):
+        sub = dict(inp)
+        sub["x"] = xs[i:i + 1]
+        r = oracle.forward(sub)
+        if G.excluded_tokens(r["logits"], 8)[0]:
+            continue
+        G.check_y(G.y_to_f64(ys[i]), r["y"], f"decode call {i}")
+        checked += 1
+    assert checked >= 4
+
+
+def test_decode_graph_replay(torch, full_layer):
+    """Single-token calls captured in a HIP graph: every replay equals the eager results bit for bit."""
+    inp = G.inputs("decode", 1, seed=0)
+    lay = _layer_for(inp, full_layer)
+    n = 8
+    xs = G.to_dev_x({"x": synth._draw_bf16(400, "x", (n, 2048), 1.0)})
+    eager = torch.stack([lay.forward(xs[i:i + 1])[0] for i in range(n)])
+    ys = torch.empty((n, 2048), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n):
+            lay.forward(xs[i:i + 1], y=ys[i:i + 1])
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            lay.forward(xs[i:i + 1], y=ys[i:i + 1])
+    for rep in range(3):
+        ys.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (xs.float() * 2).sum().item()  # eager work between replays
+        assert torch.equal(ys.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+
+
 # ------------------------------------------------------- padded boundaries
 @pytest.mark.parametrize("E,k,T", BOUNDARY_CASES)
 def test_padded_tile_boundaries(torch, E, k, T):
