@@ -6,11 +6,10 @@
 // the full softmax renormalised over the selection (guanjiawei.ai "AIMA
 // AMD395 Qwen3.6-35B-A3B", data path: only the selected experts run).
 //
-// Each logit becomes one exact 64-bit key: the high word is the float's bits
-// mapped to an unsigned integer of the same order, the low word the bitwise
-// complement of the expert index, so a larger key is a larger logit or, for
-// equal logits, a lower index.  Keys are unique; a selection round is one
-// wave-wide maximum, reduced with DPP row shifts and row broadcasts.
+// Each logit becomes a 32-bit key: the float's bits mapped to an unsigned
+// integer of the same order.  A selection round is one wave-wide maximum of
+// the keys (DPP row shifts and row broadcasts) followed by ballots that find
+// the lowest expert index holding it.
 #pragma once
 
 #include "moe_internal.h"
@@ -28,27 +27,35 @@ __device__ __forceinline__ float float_from_order_key(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-// One DPP step of a 64-bit maximum: (hi, lo) = max((hi, lo), lane-moved (hi, lo)).
-// Lanes without a source read 0, the smallest key.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
-  const uint32_t oh = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, ROW_MASK, 0xf, false);
-  const uint32_t ol = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, ROW_MASK, 0xf, false);
-  const bool take = (oh > hi) || (oh == hi && ol > lo);
-  hi = take ? oh : hi;
-  lo = take ? ol : lo;
+// Maximum over the 64 lanes of a 32-bit unsigned value: inclusive maxima
+// within rows of 16 lanes by DPP row_shr 1, 2, 4, 8, then row_bcast:15 and
+// row_bcast:31 carry them up; lane 63 holds the result, returned uniform.
+// Lanes without a DPP source read 0, the smallest value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Top-k of up to 256 logits held 4 per lane (lane l: experts l, l+64, l+128,
 // l+192; absent experts invalid), for NT tokens at once: their selection
-// rounds are independent, so the DPP chains interleave.  Lane r < k ends
-// with rank r's expert in sel_e[t] and logit in sel_v[t], and w[t] returns
-// rank r's weight in lane r:
+// rounds are independent, so their instruction chains interleave.  A round
+// takes the wave maximum of the 32-bit order keys, then the lowest expert
+// index holding that key: slot q covers indices 64 q .. 64 q + 63, so the
+// first slot whose ballot of "key == maximum" is not empty, and its lowest
+// lane, give it.  Keys are equal exactly when the logits are, so the order is
+// (logit desc, index asc) with no approximation.  Lane r < k ends with rank
+// r's expert in sel_e[t] and logit in sel_v[t], and w[t] returns rank r's
+// weight in lane r:
 //   w_r = exp(l_r - l_0) / sum_{r' < k} exp(l_r' - l_0), the sum in rank order.
 template <int NT>
 __device__ __forceinline__ void wave_topk_weights_n(const float (&v)[NT][4], const bool (&valid)[NT][4], int k,
                                                     int lane, int (&sel_e)[NT], float (&sel_v)[NT], float (&w)[NT]) {
-  uint32_t kh[NT][4], kl[NT][4];
+  uint32_t key[NT][4];
   float m[NT], sum[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -56,8 +63,7 @@ __device__ __forceinline__ void wave_topk_weights_n(const float (&v)[NT][4], con
     for (int q = 0; q < 4; ++q) {
       float x = v[t][q];
       if (x == 0.0f) x = 0.0f;  // -0 -> +0
-      kh[t][q] = valid[t][q] ? float_order_key(x) : 0u;
-      kl[t][q] = valid[t][q] ? ~(uint32_t)(lane + 64 * q) : 0u;
+      key[t][q] = valid[t][q] ? float_order_key(x) : 0u;  // 0: below every finite logit
     }
     sel_e[t] = -1;
     sel_v[t] = 0.0f;
@@ -65,40 +71,20 @@ __device__ __forceinline__ void wave_topk_weights_n(const float (&v)[NT][4], con
     sum[t] = 0.0f;
   }
   for (int r = 0; r < k; ++r) {
-    uint32_t bh[NT], bl[NT];
+    uint32_t mk[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {  // this lane's best remaining key
-      bh[t] = kh[t][0];
-      bl[t] = kl[t][0];
+    for (int t = 0; t < NT; ++t) mk[t] = max(max(key[t][0], key[t][1]), max(key[t][2], key[t][3]));
 #pragma unroll
-      for (int q = 1; q < 4; ++q) {
-        const bool take = (kh[t][q] > bh[t]) || (kh[t][q] == bh[t] && kl[t][q] > bl[t]);
-        bh[t] = take ? kh[t][q] : bh[t];
-        bl[t] = take ? kl[t][q] : bl[t];
-      }
-    }
-    // wave maxima: inclusive maxima within rows of 16 lanes, then rows 1 and
-    // 3 take the previous row's, then rows 2 and 3 take row 1's (lane 63)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) dpp_max_step<0x111, 0xf>(bh[t], bl[t]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) dpp_max_step<0x112, 0xf>(bh[t], bl[t]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) dpp_max_step<0x114, 0xf>(bh[t], bl[t]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) dpp_max_step<0x118, 0xf>(bh[t], bl[t]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) dpp_max_step<0x142, 0xa>(bh[t], bl[t]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) dpp_max_step<0x143, 0xc>(bh[t], bl[t]);
+    for (int t = 0; t < NT; ++t) mk[t] = wave_max_u32(mk[t]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const uint32_t mh = (uint32_t)__builtin_amdgcn_readlane((int)bh[t], 63);
-      const uint32_t ml = (uint32_t)__builtin_amdgcn_readlane((int)bl[t], 63);
-      // the winning key is a valid one (k <= number of valid experts); the
-      // clamp only keeps an index in range should that ever not hold
-      const int e = min(max((int)~ml, 0), 255);
-      const float val = float_from_order_key(mh);
+      const uint64_t b0 = __ballot(key[t][0] == mk[t]), b1 = __ballot(key[t][1] == mk[t]);
+      const uint64_t b2 = __ballot(key[t][2] == mk[t]), b3 = __ballot(key[t][3] == mk[t]);
+      // the maximum is held by a valid key (k <= number of valid experts), so
+      // one ballot is not empty
+      const int e = b0 ? __builtin_ctzll(b0)
+                       : b1 ? 64 + __builtin_ctzll(b1) : b2 ? 128 + __builtin_ctzll(b2) : 192 + __builtin_ctzll(b3 | (1ull << 63));
+      const float val = float_from_order_key(mk[t]);
       if (lane == r) {
         sel_e[t] = e;
         sel_v[t] = val;
@@ -106,7 +92,7 @@ __device__ __forceinline__ void wave_topk_weights_n(const float (&v)[NT][4], con
       if ((e & 63) == lane) {  // the owner drops the selected key
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (q == (e >> 6)) kh[t][q] = kl[t][q] = 0u;
+          if (q == (e >> 6)) key[t][q] = 0u;
       }
       if (r == 0) m[t] = val;
       sum[t] += expf(val - m[t]);  // uniform, rank order
