@@ -124,9 +124,11 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
 /*
  * Router stage: logits (fp32 accumulation of bf16 products), optional bias,
  * top-k by (logit desc, index asc), renormalised softmax weights, and the
- * shared-expert gate s = sigmoid(x . w_sg).
- *   Outputs: logits [T,E] fp32 (required; includes the bias), ids [T,k] int32,
- *   w [T,k] fp32; s [T] fp32 (required iff w_sg is given, else ignored).
+ * shared-expert gate s = sigmoid(x . w_sg), in one launch (the selection
+ * reads the logits from on-chip memory).
+ *   Outputs: ids [T,k] int32, w [T,k] fp32; logits [T,E] fp32 (includes the
+ *   bias; NULL: not stored); s [T] fp32 (required iff w_sg is given, else
+ *   ignored).
  */
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
               const uint16_t* w_sg, int T, int H, int E, int k,

@@ -22,8 +22,10 @@
 //   DOWN            routed tiles.  A = h rows, B = 256 rows of W_down -> o,
 //                   stored at the row of the assignment (t*k + j) it holds
 //   ROUTER          token tiles.  B = W_router (experts past E zero);
-//                   epilogue logits + bias -> fp32 logits; the shared-expert
-//                   gate x . w_sg accumulates from the A tiles in LDS
+//                   epilogue: logits + bias in LDS (and to the optional fp32
+//                   logits output), then top-k and the renormalised weights
+//                   per token from LDS; the shared-expert gate x . w_sg
+//                   accumulates from the A tiles in LDS
 //   SHARED_COMBINE  token tiles.  A = h_s rows, B = 256 rows of Ws_down;
 //                   epilogue is the deterministic combine
 //                   y = sum_j w_j o[t*k + j] + s * acc
@@ -46,6 +48,7 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "moe_topk.h"
 
 namespace moe {
 namespace {
@@ -104,6 +107,8 @@ struct GemmParams {
   float* logits;         // ROUTER: logits [T, E]
   const uint16_t* w_sg;  // ROUTER: shared-expert gate vector [K] or NULL
   float* gate_s;         // ROUTER: s = sigmoid(x . w_sg) [T] (when w_sg is given)
+  int32_t* ids;          // ROUTER: top-k experts [T, k]
+  float* wts;            // ROUTER: their renormalised weights [T, k]
 };
 
 // 16-byte chunk swizzles of an LDS row of KCH chunks.  Any 16 consecutive rows
@@ -282,6 +287,65 @@ __device__ __forceinline__ void router_gate(const GemmParams& p, const Item it, 
   if (tid % KCH == 0 && t < p.T) p.gate_s[t] = 1.0f / (1.0f + expf(-gacc));
 }
 
+// Router epilogue: the tile holds all E logits of its BM tokens.  They go to
+// LDS ([BM][RLD] fp32, bias added, -0 -> +0), to the logits output when one
+// is given, and each wave selects the top k of BM / waves tokens from LDS
+// (the selection rule and weights of moe_topk.h), NTK tokens interleaved.
+constexpr int RLD = 256 + 8;  // row stride: the two lane halves of an MFMA store hit disjoint banks
+template <int BM, int NT, int MI, int NJ, int WTM>
+__device__ __forceinline__ void router_epilogue(const GemmParams& p, const Item it, f32x16 (&acc)[MI][NJ], int wm,
+                                                const int (&bb)[NJ], unsigned char* smem) {
+  constexpr int NW = NT / 64, NTK = 4;
+  static_assert(BM % (NW * NTK) == 0, "tokens per wave");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* sl = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int m = 0; m < MI; ++m)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = bb[j] + (lane & 31);
+      const float b = (p.bias && col < p.E) ? p.bias[col] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = wm * WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        float v = acc[m][j][q] + b;
+        if (v == 0.0f) v = 0.0f;  // -0 -> +0
+        sl[row * RLD + col] = v;
+      }
+    }
+  __syncthreads();
+  const int nrow = min(BM, p.T - it.row0);
+  if (p.logits) {
+    // rows of E logits are contiguous in the output: element i of the tile is
+    // at (row0 * E + i)
+    float* out = p.logits + (size_t)it.row0 * p.E;
+    for (int i = tid; i < nrow * p.E; i += NT) out[i] = sl[(i / p.E) * RLD + i % p.E];
+  }
+  for (int r0 = wave * NTK; r0 < BM; r0 += NW * NTK) {
+    float v[NTK][4];
+    bool valid[NTK][4];
+#pragma unroll
+    for (int t = 0; t < NTK; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        valid[t][q] = e < p.E;
+        v[t][q] = sl[(r0 + t) * RLD + e];
+      }
+    int se[NTK];
+    float sv[NTK], w[NTK];
+    wave_topk_weights_n<NTK>(v, valid, p.k, lane, se, sv, w);
+#pragma unroll
+    for (int t = 0; t < NTK; ++t) {
+      const int tok = it.row0 + r0 + t;
+      if (r0 + t < nrow && lane < p.k) {
+        p.ids[(size_t)tok * p.k + lane] = se[t];
+        p.wts[(size_t)tok * p.k + lane] = w[t];
+      }
+    }
+  }
+}
+
 template <int BM, int NT, int MODE, int MI, int NJ, int WTM>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32x16 (&acc)[MI][NJ], int wm,
                                          const int (&bb)[NJ], unsigned char* smem) {
@@ -384,10 +448,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
   }
 }
 
-template <int BM, int BK>
+template <int BM, int BK, int MODE>
 constexpr size_t lds_bytes() {
   size_t stages = 2 * (size_t)(BM + BNB) * (BK / 8) * 16;
-  size_t epi = (size_t)BM * ESLD * 4;
+  size_t epi = (size_t)BM * (MODE == ROUTER ? RLD : ESLD) * 4;
   return stages > epi ? stages : epi;
 }
 
@@ -579,8 +643,10 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
   if (pending) mma(f1);
   if constexpr (MODE == ROUTER) {
     if (p.w_sg) router_gate<BM, KCH>(p, it, gacc);
+    router_epilogue<BM, C::NT, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
+  } else {
+    epilogue<BM, C::NT, MODE, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
   }
-  epilogue<BM, C::NT, MODE, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
 }
 
 // 256 x 256 tiles for the routed gate/up and down GEMMs.  512 threads (8
@@ -857,7 +923,7 @@ template <int BM, int BK, int OCC, int MODE>
 hipError_t launch_mode(const GemmParams& p, int64_t max_items, hipStream_t st) {
   const int64_t grid = ((max_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid <= 0) return hipSuccess;
-  constexpr size_t lds = lds_bytes<BM, BK>();
+  constexpr size_t lds = lds_bytes<BM, BK, MODE>();
   hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<BM, BK, OCC, MODE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -922,7 +988,7 @@ hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t
 }  // namespace
 
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg, int T,
-                         int H, int E, float* logits, float* s, hipStream_t st) {
+                         int H, int E, int k, float* logits, float* s, int32_t* ids, float* w, hipStream_t st) {
   GemmParams p = {};
   p.a = x;
   p.lda = H;
@@ -930,11 +996,13 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const floa
   p.br = w_router;
   p.E = E;
   p.T = T;
-  p.k = 1;
+  p.k = k;
   p.bias = bias;
   p.logits = logits;
   p.w_sg = w_sg;
   p.gate_s = s;
+  p.ids = ids;
+  p.wts = w;
   // Small token tiles: one 256-column block per tile, so the tile count is
   // the launch's whole parallelism.
   constexpr int BM = router_rows(MOE_ROUTER_CFG);

@@ -98,7 +98,7 @@ int check_ffn_shapes(int I, int I_s) {
 struct Layout {
   int BIG, SMALL;
   int64_t max_rows, max_big, max_small, max_tiles;
-  size_t off_ids, off_w, off_s, off_logits, off_counts, off_padoff, off_sorted, off_inv, off_tiles, off_ntiles,
+  size_t off_ids, off_w, off_s, off_counts, off_padoff, off_sorted, off_inv, off_tiles, off_ntiles,
       off_scratch, off_h, off_hs, off_o, total;
 };
 
@@ -120,7 +120,6 @@ Layout layout(int T, int H, int E, int k, int I, int I_s) {
   L.off_ids = take(n * 4);
   L.off_w = take(n * 4);
   L.off_s = take((size_t)T * 4);
-  L.off_logits = take((size_t)T * E * 4);
   L.off_counts = take((size_t)E * 4);
   L.off_padoff = take((size_t)(E + 1) * 4);
   L.off_sorted = take((size_t)L.max_rows * 4);
@@ -214,16 +213,14 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_b
   int rc = check_common_shapes(T, H, E, k);
   if (rc) return rc;
   if (T == 0) return ok();
-  if (!x || !w_router || !ids || !w || !logits)
-    return fail(MOE_ERR_NULL, "moe_route: x, w_router, ids, w and logits are required");
+  if (!x || !w_router || !ids || !w) return fail(MOE_ERR_NULL, "moe_route: x, w_router, ids and w are required");
   if (w_sg && !s) return fail(MOE_ERR_NULL, "moe_route: s is required when w_sg is given");
   if (!aligned16(x) || !aligned16(w_router) || (w_sg && !aligned16(w_sg)))
     return fail(MOE_ERR_ALIGN, "moe_route: bf16 tensors must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
   const hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_router(x, w_router, router_bias, w_sg, T, H, E, logits, s, st);
-  if (e != hipSuccess) return hip_status(e, "moe_route: router GEMM");
-  return hip_status(launch_topk(logits, T, E, k, ids, w, st), "moe_route: top-k");
+  return hip_status(launch_router(x, w_router, router_bias, w_sg, T, H, E, k, logits, s, ids, w, st),
+                    "moe_route: router GEMM with top-k");
 }
 
 int moe_route_from_logits(const float* logits, int T, int E, int k, int32_t* ids, float* w, void* stream) {
@@ -362,7 +359,6 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   int32_t* ids = reinterpret_cast<int32_t*>(base + L.off_ids);
   float* w = reinterpret_cast<float*>(base + L.off_w);
   float* s = reinterpret_cast<float*>(base + L.off_s);
-  float* logits = reinterpret_cast<float*>(base + L.off_logits);
   int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
   int32_t* pad_off = reinterpret_cast<int32_t*>(base + L.off_padoff);
   int32_t* sorted = reinterpret_cast<int32_t*>(base + L.off_sorted);
@@ -374,11 +370,10 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   uint16_t* h_s = I_s > 0 ? reinterpret_cast<uint16_t*>(base + L.off_hs) : nullptr;
   uint16_t* o = reinterpret_cast<uint16_t*>(base + L.off_o);
 
-  hipError_t e =
-      launch_router(x, w_router, router_bias, I_s > 0 ? w_sg : nullptr, T, H, E, logits, I_s > 0 ? s : nullptr, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: router");
-  e = launch_topk(logits, T, E, k, ids, w, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: top-k");
+  // logits stay in LDS: the router launch selects the experts itself
+  hipError_t e = launch_router(x, w_router, router_bias, I_s > 0 ? w_sg : nullptr, T, H, E, k, nullptr,
+                               I_s > 0 ? s : nullptr, ids, w, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: router with top-k");
   e = launch_align(ids, T, E, k, L.BIG, L.SMALL, (int)L.max_big, counts, pad_off, sorted, inv, tiles, n_tiles, scratch,
                    st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: align");

@@ -62,10 +62,12 @@ __device__ __forceinline__ int xcd_item(int bid, int n_items) {
 }
 
 // Host-side launch helpers (defined in the .hip files).
-// Router GEMM over token tiles: fp32 logits (+ bias, -0 -> +0) and, when w_sg
-// is given, the shared-expert gate s = sigmoid(x . w_sg) from the same x tiles.
+// Router GEMM over token tiles: fp32 logits (+ bias, -0 -> +0; stored when
+// logits is not NULL), the top-k ids and renormalised weights of every token
+// and, when w_sg is given, the shared-expert gate s = sigmoid(x . w_sg) from
+// the same x tiles.
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg, int T,
-                         int H, int E, float* logits, float* s, hipStream_t st);
+                         int H, int E, int k, float* logits, float* s, int32_t* ids, float* w, hipStream_t st);
 // Top-k ids and renormalised weights from fp32 logits [T, E].
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,

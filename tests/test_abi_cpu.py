@@ -124,7 +124,7 @@ def test_forward_argument_errors(L):
 def test_stage_argument_errors(L):
     p = 1 << 12
     assert L.moe_route(None, p, None, None, 16, 256, 8, 2, p, p, None, p, None) == moe.MOE_ERR_NULL
-    assert L.moe_route(p, p, None, None, 16, 256, 8, 2, p, p, None, None, None) == moe.MOE_ERR_NULL  # logits
+    assert L.moe_route(p, p, None, None, 16, 256, 8, 2, None, p, None, p, None) == moe.MOE_ERR_NULL  # ids
     assert L.moe_route(p, p, None, p, 16, 256, 8, 2, p, p, None, p, None) == moe.MOE_ERR_NULL  # s missing
     assert L.moe_route(p, p, None, None, 16, 256, 8, 20, p, p, None, p, None) == moe.MOE_ERR_SHAPE
     assert L.moe_route_from_logits(p, 16, 300, 2, p, p, None) == moe.MOE_ERR_SHAPE
