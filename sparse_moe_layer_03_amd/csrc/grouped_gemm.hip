@@ -658,9 +658,14 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
 //   * two 64 KB stages: the loads of step k + 1 are in flight while step k
 //     is computed, and the last step of an item overlaps the first loads of
 //     the next item, which also run under the epilogue;
-//   * the epilogue stages bf16 results in the stage that the last K step
-//     used (free once its fragments are read), so it never waits for or
-//     disturbs the loads of the next item;
+//   * gate/up MFMAs produce transposed output blocks, so every lane holds
+//     runs of 4 consecutive output columns of one row and the epilogue
+//     stores them as 8-byte writes straight from the accumulators (no LDS
+//     staging, no barrier); down items (rows of o are 4 KB apart) stage
+//     bf16 results in the stage that the last K step used and store 128-byte
+//     row segments; either way the next item's first loads are in flight;
+//   * the rows the epilogue stores to are read at item setup, so the
+//     epilogue issues no load that would wait behind those loads;
 //   * A row groups of only padding are not loaded: their LDS rows hold
 //     finite values of earlier data and feed only output rows that are not
 //     stored (a row of A reaches only the same row of the product).
@@ -669,7 +674,8 @@ constexpr int DRPI = 64 / DKCH;                    // rows filled by one load in
 constexpr int DNQ = 32 / DRPI;                     // load instructions per wave per operand per K step
 constexpr int DSTAGE = (DBM + BNB) * DKCH;         // 16-byte chunks per stage (A rows, then B rows)
 constexpr size_t DLDS = 2 * (size_t)DSTAGE * 16;   // 128 KB
-constexpr int DESB = 72;                           // bf16 row stride of the epilogue staging tile
+constexpr int DESB = 72;                           // bf16 row stride of the down epilogue's staging tile
+static_assert((size_t)DBM * DESB * 2 + DBM * 4 <= (size_t)DSTAGE * 16, "down epilogue staging fits in one stage");
 
 // One direct-to-LDS load: 16 bytes per lane from src into LDS at
 // lds_base + 16 * lane (lds_base wave-uniform, in M0).  Inline assembly, so
@@ -692,6 +698,7 @@ struct DmaItem {
   const uint16_t* bbase;      // this wave's B rows: bbase + the item-independent lane offsets
   uint32_t aon;               // bit q: A group q holds a data row
   bool live;                  // this wave's 64 rows hold data
+  int orow[2];                // this lane's epilogue rows (m = 0, 1): assignment (down), or >= 0 if stored
 };
 
 template <int MODE>
@@ -722,6 +729,13 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
   const int r = wm * 64;
   const bool lv = it.dense ? (it.row0 + r < p.T) : (p.sorted[it.row0 + r] >= 0);
   d.live = __builtin_amdgcn_readfirstlane((int)lv) != 0;
+  // the epilogue's rows, read here so that the epilogue issues no load (a
+  // load there would wait behind the next item's loads already in flight)
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int rr = r + m * 32 + (lane & 31);
+    d.orow[m] = it.dense ? (it.row0 + rr < p.T ? it.row0 + rr : -1) : p.sorted[it.row0 + rr];
+  }
   return d;
 }
 
@@ -792,13 +806,19 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       f.b[j] = __builtin_bit_cast(bf16x8, cB[r * DKCH + swz<DKCH>(r, c)]);
     }
   };
+  // Gate/up items compute transposed blocks (the weight fragment is the
+  // MFMA's first operand): lane l then holds output row (l & 31) and, for
+  // q = 4 g + i, output column 8 g + 4 (l >> 5) + i -- four consecutive
+  // columns of one row per group g.  Down items keep the plain layout (lane l
+  // holds column l & 31 of rows 8 (q >> 2) + 4 (l >> 5) + (q & 3)).
   f32x16 acc[C::MI][C::NJ];
   auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int m = 0; m < C::MI; ++m)
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j)
-        acc[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
+        acc[m][j] = (MODE == GATE_UP) ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0)
+                                      : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
   };
 
   constexpr int SUB = DBK / 16;
@@ -848,57 +868,79 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       }
     }
     if (pending) mma(f1);
-    __syncthreads();  // every fragment read of stage 1 has completed
 
-    // Epilogue through stage 1 (bf16 [256][DESB]), 64 output columns a pass:
-    // gate/up items store silu(g) * u -> h (or h_s), down items store rows
-    // of o at their assignment.
-    uint16_t* es = reinterpret_cast<uint16_t*>(smem) + (size_t)DSTAGE * 8;
     const Item& it = cur.it;
-    const int cr = tid >> 3, cc = (tid & 7) * 8;
-    constexpr int RG = DNT / 8, RPT = DBM / RG;
-    const int ncol = (MODE == GATE_UP) ? 128 : 256;
-    // DOWN: the assignment held by each copy-out row (-1: padding, not stored)
-    int arow[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) arow[i] = (MODE == DOWN) ? p.sorted[it.row0 + cr + RG * i] : 0;
-    for (int pass = 0; pass < ncol / EPW; ++pass) {
+    if constexpr (MODE == GATE_UP) {
+      // Epilogue straight from the accumulators: per (m, j) block and group
+      // g each lane stores 4 bf16 (8 bytes) of its row, silu(g) * u -> h (or
+      // h_s for the shared expert's token tiles); the two lane halves cover
+      // 16 contiguous bytes of a row.  Padding rows are not stored: a row of
+      // A reaches only the same row of the product, so whatever a padding
+      // row of h holds stays in padding rows of o.
+      const int lr = lane & 31, lh = lane >> 5;
+      static_assert(C::MI == 2, "two epilogue rows per lane");
 #pragma unroll
       for (int m = 0; m < C::MI; ++m) {
+        const int r = wm * C::WTM + m * 32 + lr;  // tile row
+        const int o = cur.orow[m];                // token (shared tiles) or assignment; < 0: padding
+        if (o >= 0) {
+          uint16_t* orow = it.dense ? p.out_s + (size_t)o * p.ldo_s + it.nb * 128
+                                    : p.out + (size_t)(it.row0 + r) * p.ldo + it.nb * 128;
 #pragma unroll
-        for (int j = 0; j < C::NJ; ++j) {
-          if (MODE == GATE_UP && j >= C::NJ / 2) continue;
-          const int col = bb[j] + (lane & 31) - pass * EPW;
-          if (col >= 0 && col < EPW) {
+          for (int j = 0; j < C::NJ / 2; ++j) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int row = wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-              const float v = (MODE == GATE_UP) ? silu(acc[m][j][q]) * acc[m][(j + C::NJ / 2) % C::NJ][q]
-                                                : acc[m][j][q];
-              es[row * DESB + col] = f32_to_bf16(v);
+            for (int g = 0; g < 4; ++g) {
+              float v[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = silu(acc[m][j][4 * g + i]) * acc[m][j + C::NJ / 2][4 * g + i];
+              const uint2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+              *reinterpret_cast<uint2*>(orow + bb[j] + 8 * g + 4 * lh) = pk;
             }
           }
         }
       }
-      __syncthreads();
+    } else {
+      // Down: rows of o are 4 KB apart, so the results are staged in LDS
+      // (bf16 [256][DESB], the stage the last K step used, free once its
+      // fragments are read) and stored as 128-byte row segments, 64 output
+      // columns a pass.
+      __syncthreads();  // every fragment read of that stage has completed
+      uint16_t* es = reinterpret_cast<uint16_t*>(smem) + (size_t)((nk - 1) & 1) * DSTAGE * 8;
+      const int cr = tid >> 3, cc = (tid & 7) * 8;
+      constexpr int RG = DNT / 8, RPT = DBM / RG;
+      // the assignment of each copy-out row (-1: padding, not stored), read
+      // from the item's prefetched rows through LDS
+      int* srow = reinterpret_cast<int*>(es + DBM * DESB);
+      if (lane < 32)
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int r = cr + RG * i;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(es + r * DESB + cc);
-        const int col = pass * EPW + cc;
-        if (MODE == GATE_UP) {
-          if (it.dense) {
-            const int t = it.row0 + r;
-            if (t < p.T) *reinterpret_cast<u32x4*>(p.out_s + (size_t)t * p.ldo_s + it.nb * 128 + col) = v;
-          } else {
-            *reinterpret_cast<u32x4*>(p.out + (size_t)(it.row0 + r) * p.ldo + it.nb * 128 + col) = v;
+        for (int m = 0; m < C::MI; ++m)
+          if (wn == 0) srow[wm * C::WTM + m * 32 + lane] = cur.orow[m];
+      for (int pass = 0; pass < 256 / EPW; ++pass) {
+#pragma unroll
+        for (int m = 0; m < C::MI; ++m) {
+#pragma unroll
+          for (int j = 0; j < C::NJ; ++j) {
+            const int col = bb[j] + (lane & 31) - pass * EPW;
+            if (col >= 0 && col < EPW) {
+#pragma unroll
+              for (int q = 0; q < 16; ++q) {
+                const int row = wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                es[row * DESB + col] = f32_to_bf16(acc[m][j][q]);
+              }
+            }
           }
-        } else {
-          const int a = arow[i];
-          if (a >= 0) *reinterpret_cast<u32x4*>(p.out + (size_t)a * p.ldo + it.nb * 256 + col) = v;
         }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const int r = cr + RG * i;
+          const int a = srow[r];
+          if (a >= 0)
+            *reinterpret_cast<u32x4*>(p.out + (size_t)a * p.ldo + it.nb * 256 + pass * EPW + cc) =
+                *reinterpret_cast<const u32x4*>(es + r * DESB + cc);
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
     cur = next;
   }
