@@ -120,8 +120,9 @@ def kernel_only(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    # the clock settles after a few dozen steps of sustained MFMA work: untimed warm-up steps
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across prefill steps")
     ap.add_argument("--decode-steps", type=int, default=64, help="decode calls per captured graph")
     ap.add_argument("--decode-copies", type=int, default=16, help="weight copies rotated across decode calls")
