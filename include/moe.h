@@ -92,6 +92,14 @@ int64_t moe_align_max_tiles(int T, int E, int k);
 size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s);
 
 /*
+ * Byte offset, within a workspace passed to moe_forward with these shapes, of
+ * the expert ids [T,k] int32 (rank order) that the call selected; they stay
+ * there until the workspace is reused.  For routing statistics and checks.
+ * 0 for unsupported shapes (as moe_workspace_size).
+ */
+size_t moe_forward_ids_offset(int T, int H, int E, int k, int I, int I_s);
+
+/*
  * The whole layer:  y = sum_{j<k} w[t,j] * FFN_{ids[t,j]}(x_t) + s_t * FFN_s(x_t)
  *
  *   logits[t,e] = sum_h x[t,h] W_router[e,h] (+ router_bias[e]), fp32 accumulation
@@ -108,13 +116,18 @@ size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s);
  *          NULL with I_s = 0, or all four set with I_s > 0.
  * Output:  y [T,H] bf16 (fp32 sum rounded to nearest even).
  * Workspace: at least moe_workspace_size(T,H,E,k,I,I_s) bytes, 256-byte aligned.
- * Internally the call runs the router GEMM, top-k with the shared-expert
- * gate, align, the gate/up GEMM (routed tiles and the shared expert's token
- * tiles in one launch), the routed down GEMM and the combine fused with the
- * shared down projection (or the single-token decode kernels when T == 1) on
- * `stream`; the arithmetic of every element is the same as that of the stage
- * entry points.
+ * Internally, for T > MOE_SMALL_BATCH_MAX_T, the call runs the router GEMM
+ * with the shared-expert gate and top-k, align, the gate/up GEMM (routed tiles
+ * and the shared expert's token tiles in one launch), the routed down GEMM and
+ * the combine fused with the shared down projection on `stream`; the
+ * arithmetic of every element is the same as that of the stage entry points.
+ * With T == 1 it runs the single-token kernels, and with
+ * 2 <= T <= MOE_SMALL_BATCH_MAX_T the small-batch kernels (each touched
+ * expert's weight rows read once and applied to all of its tokens; h and the
+ * expert outputs kept in fp32, the combine in the same rank order).  The
+ * selection rule is the same on every path.
  */
+#define MOE_SMALL_BATCH_MAX_T 32
 int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                 const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,

@@ -307,6 +307,8 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __rest
 
 }  // namespace
 
+size_t decode_ids_offset(int E) { return align256((size_t)E * 4); }  // after the logits, as carve() lays them out
+
 size_t decode_workspace_size(int H, int E, int k, int I, int I_s) {
   (void)H;
   return align256((size_t)E * 4) + 2 * 256 + 256 + align256((size_t)(I_s > 0 ? I_s : 1) * 4) +

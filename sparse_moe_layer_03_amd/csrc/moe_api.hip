@@ -205,7 +205,15 @@ size_t moe_align_scratch_size(int T, int E, int k) {
 size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s) {
   if (check_common_shapes(T, H, E, k) != MOE_OK || check_ffn_shapes(I, I_s) != MOE_OK) return 0;
   if (T <= 1) return decode_workspace_size(H, E, k, I, I_s);
+  if (T <= kSmallMaxT) return small_batch_workspace_size(T, H, E, k, I, I_s);
   return layout(T, H, E, k, I, I_s).total;
+}
+
+size_t moe_forward_ids_offset(int T, int H, int E, int k, int I, int I_s) {
+  if (moe_workspace_size(T, H, E, k, I, I_s) == 0) return 0;
+  if (T <= 1) return decode_ids_offset(E);
+  if (T <= kSmallMaxT) return small_batch_ids_offset(T, E);
+  return layout(T, H, E, k, I, I_s).off_ids;
 }
 
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint16_t* w_sg, int T,
@@ -353,6 +361,11 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
     return hip_status(launch_decode(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg, H,
                                     E, k, I, I_s, y, workspace, st),
                       "moe_forward (decode)");
+
+  if (T <= kSmallMaxT)
+    return hip_status(launch_small_batch(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg,
+                                         T, H, E, k, I, I_s, y, workspace, st),
+                      "moe_forward (small batch)");
 
   const Layout L = layout(T, H, E, k, I, I_s);
   char* base = static_cast<char*>(workspace);

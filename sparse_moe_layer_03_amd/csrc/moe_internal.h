@@ -17,6 +17,7 @@ constexpr int kWave = 64;
 constexpr int kNumXcd = 8;      // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 16;
+constexpr int kSmallMaxT = 32;  // moe_forward takes the small-batch path for 2 <= T <= kSmallMaxT
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
@@ -92,5 +93,14 @@ hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const floa
                          const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int H, int E,
                          int k, int I, int I_s, uint16_t* y, void* ws, hipStream_t st);
 size_t decode_workspace_size(int H, int E, int k, int I, int I_s);
+// Small-batch path (2 <= T <= kSmallMaxT): router, selection and plan, gate/up
+// and down over the touched experts' weight rows, combine.
+hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_gate,
+                              const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate,
+                              const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int T, int H,
+                              int E, int k, int I, int I_s, uint16_t* y, void* ws, hipStream_t st);
+size_t small_batch_workspace_size(int T, int H, int E, int k, int I, int I_s);
+size_t small_batch_ids_offset(int T, int E);
+size_t decode_ids_offset(int E);
 
 }  // namespace moe

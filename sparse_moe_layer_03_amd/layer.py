@@ -81,6 +81,14 @@ class DeviceLayer:
                         W["ws_down"], W["w_sg"], T, s.H, s.E, s.k, s.I, s.I_s, y, ws, nbytes, stream)
         return y
 
+    def forward_ids(self, T: int):
+        """The expert ids [T, k] (int32, rank order) the last forward of T tokens selected, read back
+        from the workspace."""
+        import torch
+        s = self.shapes
+        off = moe.moe_forward_ids_offset(T, s.H, s.E, s.k, s.I, s.I_s)
+        return self._ws[off:off + T * s.k * 4].view(torch.int32).view(T, s.k)
+
     # ---------------------------------------------------------------- stages
     def alloc_stage_buffers(self, T: int):
         import torch

@@ -22,10 +22,11 @@ MOE_ERR_ALIGN = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_ARCH = -5
 MOE_ERR_HIP = -6
+SMALL_BATCH_MAX_T = 32  # MOE_SMALL_BATCH_MAX_T: moe_forward's small-batch path covers 2 <= T <= this
 
 EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_align_tile_rows", "moe_align_small_tile_rows", "moe_align_max_rows",
-    "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
+    "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward_ids_offset", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
     "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine",
 )
 
@@ -56,6 +57,7 @@ def lib():
             "moe_align_max_big_tiles": ([i, i, i], i64),
             "moe_align_max_tiles": ([i, i, i], i64),
             "moe_workspace_size": ([i, i, i, i, i, i], z),
+            "moe_forward_ids_offset": ([i, i, i, i, i, i], z),
             "moe_forward": ([p] * 10 + [i] * 6 + [p, p, z, p], i),
             "moe_route": ([p, p, p, p, i, i, i, i, p, p, p, p, p], i),
             "moe_route_from_logits": ([p, i, i, i, p, p, p], i),
@@ -125,6 +127,10 @@ def moe_align_max_tiles(T: int, E: int, k: int) -> int:
 
 def moe_workspace_size(T: int, H: int, E: int, k: int, I: int, I_s: int) -> int:
     return lib().moe_workspace_size(T, H, E, k, I, I_s)
+
+
+def moe_forward_ids_offset(T: int, H: int, E: int, k: int, I: int, I_s: int) -> int:
+    return lib().moe_forward_ids_offset(T, H, E, k, I, I_s)
 
 
 def moe_align_scratch_size(T: int, E: int, k: int) -> int:
