@@ -332,6 +332,54 @@ def main():
                          f"{nx} calls, {reps} replays", "eager_us_per_call": eager_us}
         log(f"[bench] decode: {dus:.2f} us/call, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f}% of HBM); "
             f"eager {eager_us:.2f} us/call")
+        # small batches (the small-batch kernels): bytes = router + the touched experts of each call
+        # (counted from the call's own selection) + the shared expert + x + y
+        sb = {}
+        for Tb in (2, 8, 32):
+            ncall = 16
+            xb = to_device_bf16(synth._draw_bf16(2, "x", (ncall * Tb, H), 1.0), dev)
+            yb = torch.empty((ncall * Tb, H), dtype=torch.bfloat16, device=dev)
+            bws, bws_bytes = dbase.workspace(Tb)
+            ids_off = moe.moe_forward_ids_offset(Tb, H, E, k, I, I_s)
+
+            def bstep(i, Tb=Tb, xb=xb, yb=yb, bws=bws, bws_bytes=bws_bytes):
+                W = dcopies[i % len(dcopies)]
+                moe.moe_forward(xb[i * Tb:(i + 1) * Tb], W["w_router"], None, W["w_gate"], W["w_up"], W["w_down"],
+                                W["ws_gate"], W["ws_up"], W["ws_down"], W["w_sg"], Tb, H, E, k, I, I_s,
+                                yb[i * Tb:(i + 1) * Tb], bws, bws_bytes)
+            touched = []
+            for i in range(ncall):
+                bstep(i)
+                torch.cuda.synchronize()
+                ids_i = bws[ids_off:ids_off + Tb * k * 4].view(torch.int32).cpu().numpy()
+                touched.append(len(np.unique(ids_i)))
+            sbytes = float(np.mean([2 * (E * H + H + n * 3 * H * I + 3 * H * I_s + 2 * Tb * H) for n in touched]))
+            s2 = torch.cuda.Stream()
+            s2.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s2):
+                for i in range(ncall):
+                    bstep(i)
+            torch.cuda.current_stream().wait_stream(s2)
+            gb = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gb):
+                for i in range(ncall):
+                    bstep(i)
+            gb.replay()
+            torch.cuda.synchronize()
+            d0.record()
+            for _ in range(reps):
+                gb.replay()
+            d1.record()
+            torch.cuda.synchronize()
+            bus = d0.elapsed_time(d1) * 1e3 / (reps * ncall)
+            sb[str(Tb)] = {"us_per_call": bus, "tokens_per_s": Tb / (bus * 1e-6), "touched_experts": float(np.mean(touched)),
+                           "bytes_per_call": sbytes, "GB_per_s": sbytes / (bus * 1e-6) / 1e9,
+                           "hbm_frac": sbytes / (bus * 1e-6) / 1e9 / PEAK_HBM_GBS}
+            del gb
+            log(f"[bench] small batch T={Tb}: {bus:.1f} us/call, {sb[str(Tb)]['GB_per_s']:.0f} GB/s")
+        out["small_batch"] = {"workload": "2, 8 and 32 tokens per call, decode-config shapes, no router bias",
+                              "timing": f"HIP graph of 16 calls over {len(dcopies)} weight copies, {reps} replays",
+                              "per_T": sb}
         del dcopies, g
         torch.cuda.empty_cache()
 
