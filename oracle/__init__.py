@@ -64,7 +64,10 @@ class Oracle:
         L.oracle_route_from_logits.argtypes = [p, i, i, i, p, p]
         L.oracle_align.argtypes = [p, i, i, i, p, p, p]
         L.oracle_forward.argtypes = [p] * 10 + [i] * 6 + [p] * 10
-        for f in (L.oracle_route, L.oracle_route_from_logits, L.oracle_align, L.oracle_forward):
+        L.oracle_forward_fp8.argtypes = [p] * 16 + [i] * 6 + [p] * 10
+        L.oracle_e4m3_decode.argtypes = [p, C.c_long, p]
+        for f in (L.oracle_route, L.oracle_route_from_logits, L.oracle_align, L.oracle_forward,
+                  L.oracle_forward_fp8, L.oracle_e4m3_decode):
             f.restype = C.c_int
         self.lib = L
         self.path = lib_path
@@ -105,21 +108,31 @@ class Oracle:
                "oracle_align")
         return counts, offsets, perm
 
+    def e4m3_decode(self, codes) -> np.ndarray:
+        """Values (float64) of OCP FP8 E4M3 codes; NaN for the NaN codes."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(codes.shape, np.float64)
+        _check(self.lib.oracle_e4m3_decode(_ptr(codes), codes.size, _ptr(out)), "oracle_e4m3_decode")
+        return out
+
     def forward(self, inp: Dict[str, np.ndarray], k: Optional[int] = None, ids_in=None,
-                want=()) -> Dict[str, np.ndarray]:
+                want=(), fp8: bool = False) -> Dict[str, np.ndarray]:
         """Whole layer on the arrays of ``inp`` (keys as produced by the seeded generator).
 
         ``want`` may name any of "h", "o", "hs", "os" for per-stage outputs.
+        ``fp8``: take the expert weights from the ``*_fp8`` codes and
+        ``*_scale`` row scales of ``inp`` instead of the BF16 arrays.
         """
         x = _c(inp["x"], np.uint16)
         wr = _c(inp["w_router"], np.uint16)
         bias = _c(inp.get("bias"), np.float32)
-        wg = _c(inp["w_gate"], np.uint16)
-        wu = _c(inp["w_up"], np.uint16)
-        wd = _c(inp["w_down"], np.uint16)
-        sg = _c(inp.get("ws_gate"), np.uint16)
-        su = _c(inp.get("ws_up"), np.uint16)
-        sd = _c(inp.get("ws_down"), np.uint16)
+        sfx = "_fp8" if fp8 else ""
+        wg = _c(inp["w_gate" + sfx], np.uint8 if fp8 else np.uint16)
+        wu = _c(inp["w_up" + sfx], np.uint8 if fp8 else np.uint16)
+        wd = _c(inp["w_down" + sfx], np.uint8 if fp8 else np.uint16)
+        sg = _c(inp.get("ws_gate" + sfx), np.uint8 if fp8 else np.uint16)
+        su = _c(inp.get("ws_up" + sfx), np.uint8 if fp8 else np.uint16)
+        sd = _c(inp.get("ws_down" + sfx), np.uint8 if fp8 else np.uint16)
         wsg = _c(inp.get("w_sg"), np.uint16)
         T, H = x.shape
         E, I, _ = wg.shape
@@ -136,10 +149,19 @@ class Oracle:
         o = np.empty((T * k, H), np.float64) if "o" in want else None
         hs = np.empty((T, I_s), np.float64) if ("hs" in want and I_s) else None
         os_ = np.empty((T, H), np.float64) if ("os" in want and I_s) else None
-        _check(self.lib.oracle_forward(_ptr(x), _ptr(wr), _ptr(bias), _ptr(wg), _ptr(wu), _ptr(wd),
-                                       _ptr(sg), _ptr(su), _ptr(sd), _ptr(wsg), T, H, E, k, I, I_s,
-                                       _ptr(ids_in), _ptr(y), _ptr(ids), _ptr(w), _ptr(s), _ptr(logits),
-                                       _ptr(h), _ptr(o), _ptr(hs), _ptr(os_)), "oracle_forward")
+        tail = (_ptr(ids_in), _ptr(y), _ptr(ids), _ptr(w), _ptr(s), _ptr(logits),
+                _ptr(h), _ptr(o), _ptr(hs), _ptr(os_))
+        if fp8:
+            codes = (wg, wu, wd, sg, su, sd)
+            scales = [_c(inp.get(key + "_scale"), np.float32)
+                      for key in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
+            mats = [a for pair in zip(codes, scales) for a in pair]
+            _check(self.lib.oracle_forward_fp8(_ptr(x), _ptr(wr), _ptr(bias), *[_ptr(a) for a in mats], _ptr(wsg),
+                                               T, H, E, k, I, I_s, *tail), "oracle_forward_fp8")
+        else:
+            _check(self.lib.oracle_forward(_ptr(x), _ptr(wr), _ptr(bias), _ptr(wg), _ptr(wu), _ptr(wd),
+                                           _ptr(sg), _ptr(su), _ptr(sd), _ptr(wsg), T, H, E, k, I, I_s, *tail),
+                   "oracle_forward")
         out = {"y": y, "ids": ids, "w": w, "s": s if I_s else None, "logits": logits}
         if h is not None:
             out["h"] = h
@@ -176,6 +198,10 @@ def align(*a, **kw):
 
 def forward(*a, **kw):
     return default().forward(*a, **kw)
+
+
+def e4m3_decode(*a, **kw):
+    return default().e4m3_decode(*a, **kw)
 
 
 def topk_margin(logits: np.ndarray, k: int) -> np.ndarray:

@@ -33,6 +33,15 @@
  * decision (softmax, renormalisation, gate, FFN, combine) is computed in
  * IEEE double.  BF16 inputs are widened exactly (bits << 16).
  *
+ * FP8 expert weights (oracle_forward_fp8): kongchang.com "GFX1151 engine"
+ * (section on the two weight formats) says the HuggingFace-native format
+ * carries 8-bit floating-point quantised weights and that FP8 loses very
+ * little precision; it gives no encoding or scale layout.  Read here as the
+ * OCP FP8 E4M3 encoding with one fp32 scale per output row of every expert
+ * matrix: W[r][c] = scale[r] * e4m3(code[r][c]).  The router and w_sg stay
+ * BF16.  Dequantised weights are exact in double (4 + 24 significant bits),
+ * so the layer's arithmetic is otherwise the BF16 one.
+ *
  * Parallelism: OpenMP over tokens (routing) and over assignments (FFN).
  * Every output element is computed by exactly one thread with a fixed
  * operation order, so results do not depend on the thread count.
@@ -88,6 +97,63 @@ static double dot_bf16_f64(const uint16_t* a, const uint16_t* b, int n) {
     double acc = 0.0;
     for (int i = 0; i < n; ++i) acc += (double)bf16_to_f32(a[i]) * (double)bf16_to_f32(b[i]);
     return acc;
+}
+
+/* OCP FP8 E4M3 ("e4m3fn"): bit 7 sign, bits 6..3 biased exponent (bias 7),
+ * bits 2..0 mantissa.  Exponent field 0: subnormal, m/8 * 2^(1-7).
+ * Otherwise (1 + m/8) * 2^(e-7).  S.1111.111 is NaN; no infinities, so the
+ * largest finite magnitude is 1.75 * 2^8 = 448. */
+static double e4m3_value(uint8_t code) {
+    int sgn = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = e == 0 ? ldexp((double)m / 8.0, 1 - 7) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -mag : mag;
+}
+
+/* Decoded values of n codes (NaN for the two NaN codes). */
+int oracle_e4m3_decode(const uint8_t* codes, long n, double* out) {
+    if (n < 0) return ORC_ERR_SHAPE;
+    if (n > 0 && (!codes || !out)) return ORC_ERR_NULL;
+    for (long i = 0; i < n; ++i) out[i] = e4m3_value(codes[i]);
+    return ORC_OK;
+}
+
+static int all_finite_e4m3(const uint8_t* p, size_t n) {
+    if (!p) return 1;
+    for (size_t i = 0; i < n; ++i)
+        if ((p[i] & 0x7Fu) == 0x7Fu) return 0;
+    return 1;
+}
+
+/* One expert-weight operand: BF16 bits, or E4M3 codes with a scale per row. */
+typedef struct {
+    const uint16_t* bf;
+    const uint8_t* q;
+    const float* scale;
+} wmat;
+
+static int wmat_set(wmat m) { return m.bf != NULL || (m.q != NULL && m.scale != NULL); }
+
+static int wmat_finite(wmat m, size_t rows, size_t cols) {
+    if (m.bf) return all_finite_bf16(m.bf, rows * cols);
+    return all_finite_e4m3(m.q, rows * cols) && all_finite_f32(m.scale, rows);
+}
+
+/* Dot product, in double and ascending index, of a BF16 row x with row r
+ * (length n) of an expert operand. */
+static double dot_row_f64(const uint16_t* x, wmat m, size_t r, int n) {
+    if (m.bf) return dot_bf16_f64(x, m.bf + r * (size_t)n, n);
+    const uint8_t* q = m.q + r * (size_t)n;
+    const double sc = (double)m.scale[r];
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i) acc += (double)bf16_to_f32(x[i]) * (sc * e4m3_value(q[i]));
+    return acc;
+}
+
+/* Element (r, c) of an expert operand with rows of length n, as a double. */
+static double wmat_at(wmat m, size_t r, size_t c, int n) {
+    if (m.bf) return (double)bf16_to_f32(m.bf[r * (size_t)n + c]);
+    return (double)m.scale[r] * e4m3_value(m.q[r * (size_t)n + c]);
 }
 
 /* Steps 2-3 for one token: select k experts by (logit desc, index asc) and
@@ -222,53 +288,41 @@ int oracle_align(const int32_t* ids, int T, int E, int k, int32_t* counts, int32
     return ORC_OK;
 }
 
-/* SwiGLU hidden of one token under one expert's gate/up matrices [I,H]. */
-static void swiglu_hidden(const uint16_t* xt, const uint16_t* wg, const uint16_t* wu, int H, int I, double* hid) {
+/* SwiGLU hidden of one token under one expert's gate/up matrices [I,H],
+ * rows row0 .. row0+I-1 of the operands. */
+static void swiglu_hidden(const uint16_t* xt, wmat wg, wmat wu, size_t row0, int H, int I, double* hid) {
     for (int i = 0; i < I; ++i) {
-        double g = dot_bf16_f64(xt, wg + (size_t)i * H, H);
-        double u = dot_bf16_f64(xt, wu + (size_t)i * H, H);
+        double g = dot_row_f64(xt, wg, row0 + (size_t)i, H);
+        double u = dot_row_f64(xt, wu, row0 + (size_t)i, H);
         hid[i] = silu(g) * u;
     }
 }
 
-/* Down projection o[H] = Wd[H,I] . hid[I]. */
-static void swiglu_down(const double* hid, const uint16_t* wd, int H, int I, double* o) {
+/* Down projection o[H] = Wd[H,I] . hid[I], rows row0 .. row0+H-1 of wd. */
+static void swiglu_down(const double* hid, wmat wd, size_t row0, int H, int I, double* o) {
     for (int c = 0; c < H; ++c) {
-        const uint16_t* row = wd + (size_t)c * I;
         double acc = 0.0;
-        for (int i = 0; i < I; ++i) acc += hid[i] * (double)bf16_to_f32(row[i]);
+        for (int i = 0; i < I; ++i) acc += hid[i] * wmat_at(wd, row0 + (size_t)c, (size_t)i, I);
         o[c] = acc;
     }
 }
 
-/*
- * The whole layer.
- *   Inputs as in oracle_route plus w_gate/w_up [E,I,H], w_down [E,H,I],
- *   ws_gate/ws_up [I_s,H], ws_down [H,I_s], w_sg [H] (the shared four all
- *   NULL with I_s == 0, or all set).
- *   ids_in [T,k] (nullable): when given, routing selection is replaced by
- *   these ids and the weights are the renormalised softmax probabilities of
- *   these ids (used to evaluate a token under another side's selection).
- *   y [T,H] double (out).
- *   Optional outputs (nullable): ids_out [T,k], w_out [T,k] double,
- *   s_out [T] double, logits_out [T,E] fp32, h_out [T*k, I] double (hidden
- *   of assignment a), o_out [T*k, H] double, hs_out [T, I_s], os_out [T, H].
- */
-int oracle_forward(const uint16_t* x, const uint16_t* w_router, const float* bias,
-                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
-                   const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg,
-                   int T, int H, int E, int k, int I, int I_s,
-                   const int32_t* ids_in, double* y,
-                   int32_t* ids_out, double* w_out, double* s_out, float* logits_out,
-                   double* h_out, double* o_out, double* hs_out, double* os_out) {
+/* The whole layer with expert operands given as BF16 or as FP8 codes with
+ * per-row scales; oracle_forward and oracle_forward_fp8 below marshal into it. */
+static int forward_impl(const uint16_t* x, const uint16_t* w_router, const float* bias, wmat w_gate, wmat w_up,
+                        wmat w_down, wmat ws_gate, wmat ws_up, wmat ws_down, const uint16_t* w_sg, int T, int H,
+                        int E, int k, int I, int I_s, const int32_t* ids_in, double* y, int32_t* ids_out,
+                        double* w_out, double* s_out, float* logits_out, double* h_out, double* o_out,
+                        double* hs_out, double* os_out) {
     if (T < 0 || H < 1 || E < 1 || k < 1 || k > E || I < 1 || I_s < 0) return ORC_ERR_SHAPE;
-    int n_shared = (ws_gate != NULL) + (ws_up != NULL) + (ws_down != NULL) + (w_sg != NULL);
+    int n_shared = wmat_set(ws_gate) + wmat_set(ws_up) + wmat_set(ws_down) + (w_sg != NULL);
     if ((I_s == 0 && n_shared != 0) || (I_s > 0 && n_shared != 4)) return ORC_ERR_SHAPE;
     if (T == 0) return ORC_OK;
-    if (!x || !w_router || !w_gate || !w_up || !w_down || !y) return ORC_ERR_NULL;
-    if (!all_finite_bf16(w_gate, (size_t)E * I * H) || !all_finite_bf16(w_up, (size_t)E * I * H) ||
-        !all_finite_bf16(w_down, (size_t)E * H * I) || !all_finite_bf16(ws_gate, ws_gate ? (size_t)I_s * H : 0) ||
-        !all_finite_bf16(ws_up, ws_up ? (size_t)I_s * H : 0) || !all_finite_bf16(ws_down, ws_down ? (size_t)H * I_s : 0))
+    if (!x || !w_router || !wmat_set(w_gate) || !wmat_set(w_up) || !wmat_set(w_down) || !y) return ORC_ERR_NULL;
+    if (!wmat_finite(w_gate, (size_t)E * I, (size_t)H) || !wmat_finite(w_up, (size_t)E * I, (size_t)H) ||
+        !wmat_finite(w_down, (size_t)E * H, (size_t)I) ||
+        (I_s > 0 && (!wmat_finite(ws_gate, (size_t)I_s, (size_t)H) || !wmat_finite(ws_up, (size_t)I_s, (size_t)H) ||
+                     !wmat_finite(ws_down, (size_t)H, (size_t)I_s))))
         return ORC_ERR_NONFINITE;
 
     size_t nA = (size_t)T * k;
@@ -330,18 +384,18 @@ int oracle_forward(const uint16_t* x, const uint16_t* w_router, const float* bia
                 int e = ids[a];
                 int t = a / k;
                 const uint16_t* xt = x + (size_t)t * H;
-                swiglu_hidden(xt, w_gate + (size_t)e * I * H, w_up + (size_t)e * I * H, H, I, hid);
+                swiglu_hidden(xt, w_gate, w_up, (size_t)e * I, H, I, hid);
                 if (h_out) memcpy(h_out + (size_t)a * I, hid, sizeof(double) * (size_t)I);
-                swiglu_down(hid, w_down + (size_t)e * H * I, H, I, o + (size_t)a * H);
+                swiglu_down(hid, w_down, (size_t)e * H, H, I, o + (size_t)a * H);
             }
             /* 6: shared expert over every token */
             if (I_s > 0) {
 #pragma omp for schedule(dynamic, 4)
                 for (int t = 0; t < T; ++t) {
                     const uint16_t* xt = x + (size_t)t * H;
-                    swiglu_hidden(xt, ws_gate, ws_up, H, I_s, hid);
+                    swiglu_hidden(xt, ws_gate, ws_up, 0, H, I_s, hid);
                     if (hs_out) memcpy(hs_out + (size_t)t * I_s, hid, sizeof(double) * (size_t)I_s);
-                    swiglu_down(hid, ws_down, H, I_s, os + (size_t)t * H);
+                    swiglu_down(hid, ws_down, 0, H, I_s, os + (size_t)t * H);
                 }
             }
         }
@@ -379,4 +433,52 @@ done:
     free(o);
     free(os);
     return err;
+}
+
+/*
+ * The whole layer.
+ *   Inputs as in oracle_route plus w_gate/w_up [E,I,H], w_down [E,H,I],
+ *   ws_gate/ws_up [I_s,H], ws_down [H,I_s], w_sg [H] (the shared four all
+ *   NULL with I_s == 0, or all set).
+ *   ids_in [T,k] (nullable): when given, routing selection is replaced by
+ *   these ids and the weights are the renormalised softmax probabilities of
+ *   these ids (used to evaluate a token under another side's selection).
+ *   y [T,H] double (out).
+ *   Optional outputs (nullable): ids_out [T,k], w_out [T,k] double,
+ *   s_out [T] double, logits_out [T,E] fp32, h_out [T*k, I] double (hidden
+ *   of assignment a), o_out [T*k, H] double, hs_out [T, I_s], os_out [T, H].
+ */
+int oracle_forward(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                   const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg,
+                   int T, int H, int E, int k, int I, int I_s,
+                   const int32_t* ids_in, double* y,
+                   int32_t* ids_out, double* w_out, double* s_out, float* logits_out,
+                   double* h_out, double* o_out, double* hs_out, double* os_out) {
+    wmat g = {w_gate, NULL, NULL}, u = {w_up, NULL, NULL}, d = {w_down, NULL, NULL};
+    wmat sg = {ws_gate, NULL, NULL}, su = {ws_up, NULL, NULL}, sd = {ws_down, NULL, NULL};
+    return forward_impl(x, w_router, bias, g, u, d, sg, su, sd, w_sg, T, H, E, k, I, I_s, ids_in, y, ids_out, w_out,
+                        s_out, logits_out, h_out, o_out, hs_out, os_out);
+}
+
+/*
+ * The whole layer with FP8 expert weights (routed and shared): E4M3 codes
+ * q_* in the shapes of the BF16 matrices above, and fp32 scales, one per
+ * output row: sc_gate/sc_up [E,I], sc_down [E,H], ssc_gate/ssc_up [I_s],
+ * ssc_down [H].  Router, bias, w_sg and every output as in oracle_forward.
+ * A NaN code or a non-finite scale gives ORC_ERR_NONFINITE.
+ */
+int oracle_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                       const uint8_t* q_gate, const float* sc_gate, const uint8_t* q_up, const float* sc_up,
+                       const uint8_t* q_down, const float* sc_down,
+                       const uint8_t* qs_gate, const float* ssc_gate, const uint8_t* qs_up, const float* ssc_up,
+                       const uint8_t* qs_down, const float* ssc_down, const uint16_t* w_sg,
+                       int T, int H, int E, int k, int I, int I_s,
+                       const int32_t* ids_in, double* y,
+                       int32_t* ids_out, double* w_out, double* s_out, float* logits_out,
+                       double* h_out, double* o_out, double* hs_out, double* os_out) {
+    wmat g = {NULL, q_gate, sc_gate}, u = {NULL, q_up, sc_up}, d = {NULL, q_down, sc_down};
+    wmat sg = {NULL, qs_gate, ssc_gate}, su = {NULL, qs_up, ssc_up}, sd = {NULL, qs_down, ssc_down};
+    return forward_impl(x, w_router, bias, g, u, d, sg, su, sd, w_sg, T, H, E, k, I, I_s, ids_in, y, ids_out, w_out,
+                        s_out, logits_out, h_out, o_out, hs_out, os_out);
 }

@@ -224,6 +224,38 @@ def make_logits(T: int, E: int, seed: int = 0, sigma: float = 0.905, tie_frac: f
     return lg
 
 
+FP8_KEYS = ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+E4M3_MAX = 448.0
+
+
+def add_fp8_weights(inp: Dict[str, object]) -> Dict[str, object]:
+    """Add FP8 copies of the expert weights of ``inp`` (a make_inputs result).
+
+    For every expert matrix key K in FP8_KEYS that is present, adds
+    ``K + "_fp8"`` (uint8 E4M3 codes, same shape) and ``K + "_scale"``
+    (float32, one per output row, shape = the matrix shape without its last
+    axis).  The scale of a row is its largest magnitude / 448 (1 for an
+    all-zero row); the codes are torch's float32 -> float8_e4m3fn cast of
+    the bf16 values divided by the row's scale, clamped to +-448 first.
+    Returns a new dict; the BF16 arrays stay as they are.
+    """
+    import torch
+
+    out = dict(inp)
+    for key in FP8_KEYS:
+        w = inp.get(key)
+        if w is None:
+            out[key + "_fp8"] = out[key + "_scale"] = None
+            continue
+        v = torch.from_numpy(bf16_bits_to_f32(w))
+        amax = v.abs().amax(dim=-1)
+        scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).to(torch.float32)
+        q = (v / scale.unsqueeze(-1)).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        out[key + "_fp8"] = q.view(torch.uint8).numpy().copy()
+        out[key + "_scale"] = scale.numpy().copy()
+    return out
+
+
 def content_hash(inputs: Dict[str, object]) -> str:
     h = hashlib.sha256()
     for key in ("x", "w_router", "bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down", "w_sg"):

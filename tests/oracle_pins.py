@@ -16,7 +16,11 @@ when the oracle disagrees with what the mathematics fixes:
 * exact special values (x_t = 0, w_sg = 0, k = 1, all-equal logits);
 * the fp32 rounding bound of the router sum;
 * align invariants checked against NumPy's stable sort;
-* equivariances (token permutation, expert relabelling) and exact scaling.
+* equivariances (token permutation, expert relabelling) and exact scaling;
+* FP8 expert weights: the E4M3 decoder against the values the OCP FP8
+  definition fixes and against torch's float8_e4m3fn cast for all 256
+  codes; the FP8 layer against the BF16 layer on the same (exactly
+  representable) dequantised weights, and against the dense mixture.
 
 The same functions run against deliberately mutated builds of the oracle
 (tests/test_oracle_mutants.py) to show that each planted mistake trips at
@@ -62,8 +66,22 @@ def _inputs(seed=1, bias=None, **kw):
     return inp
 
 
+def _e4m3_torch(codes):
+    """float64 values of E4M3 codes by torch's float8_e4m3fn -> float32 cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float32).numpy().astype(F64)
+
+
+def _wf(inp, key, fp8):
+    """float64 expert matrix ``key``: bf16 values, or codes * row scale."""
+    if fp8:
+        return _e4m3_torch(inp[key + "_fp8"]) * inp[key + "_scale"].astype(F64)[..., None]
+    return _f(inp[key])
+
+
 # ------------------------------------------------------------ dense mixture
-def dense_gated_mixture(inp, k):
+def dense_gated_mixture(inp, k, fp8=False):
     """float64 dense evaluation: every expert on every token, then the gate."""
     x = _f(inp["x"])
     wr = _f(inp["w_router"])
@@ -81,15 +99,15 @@ def dense_gated_mixture(inp, k):
     p = p / p.sum(axis=1, keepdims=True)
     G = np.where(sel, p, 0.0)
     G = G / G.sum(axis=1, keepdims=True)
-    wg, wu, wd = _f(inp["w_gate"]), _f(inp["w_up"]), _f(inp["w_down"])
+    wg, wu, wd = _wf(inp, "w_gate", fp8), _wf(inp, "w_up", fp8), _wf(inp, "w_down", fp8)
     y = np.zeros((T, x.shape[1]), F64)
     for e in range(E):
         he = _silu(x @ wg[e].T) * (x @ wu[e].T)
         y += G[:, e:e + 1] * (he @ wd[e].T)
     if inp.get("ws_gate") is not None:
         s = 1.0 / (1.0 + np.exp(-(x @ _f(inp["w_sg"]))))
-        hs = _silu(x @ _f(inp["ws_gate"]).T) * (x @ _f(inp["ws_up"]).T)
-        y += s[:, None] * (hs @ _f(inp["ws_down"]).T)
+        hs = _silu(x @ _wf(inp, "ws_gate", fp8).T) * (x @ _wf(inp, "ws_up", fp8).T)
+        y += s[:, None] * (hs @ _wf(inp, "ws_down", fp8).T)
     ids = np.argsort(np.where(sel, rank, E + 1), axis=1, kind="stable")[:, :k]
     margin = np.sort(logits, axis=1)[:, ::-1]
     gaps = (margin[:, :min(k + 1, E) - 1] - margin[:, 1:min(k + 1, E)]).min(axis=1) if E > 1 else np.full(T, np.inf)
@@ -352,6 +370,78 @@ def pin_stage_outputs(orc):
     hs = _silu(x @ _f(inp["ws_gate"]).T) * (x @ _f(inp["ws_up"]).T)
     assert _rel_l2(r["hs"], hs) < 1e-12
     assert _rel_l2(r["os"], hs @ _f(inp["ws_down"]).T) < 1e-12
+
+
+# -------------------------------------------------------------- FP8 weights
+def pin_e4m3_all_codes(orc):
+    """E4M3 decoder: the values the OCP FP8 definition fixes, and torch's cast for every code."""
+    codes = np.arange(256, dtype=np.uint8)
+    v = orc.e4m3_decode(codes)
+    ref = _e4m3_torch(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(v), nan) and nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(v[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(v[~nan]), np.signbit(ref[~nan]))
+    fixed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3C: 1.5,
+             0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, val in fixed.items():
+        assert v[c] == val, (hex(c), v[c], val)
+    assert v[0x80] == 0.0 and math.copysign(1.0, v[0x80]) == -1.0
+    # magnitudes rise strictly with the code; the sign bit mirrors them
+    assert np.all(np.diff(v[:0x7F]) > 0) and np.array_equal(v[0x80:0xFF], -v[:0x7F])
+
+
+def _fp8_inputs(seed, pow2_scales, **kw):
+    """Tiny layer with FP8 expert weights (random non-NaN codes)."""
+    inp = _inputs(seed=seed, **kw)
+    rng = np.random.default_rng(seed + 100)
+    for key in synth.FP8_KEYS:
+        if inp.get(key) is None:
+            inp[key + "_fp8"] = inp[key + "_scale"] = None
+            continue
+        shape = inp[key].shape
+        codes = rng.integers(0, 0x7F, size=shape, dtype=np.uint8)  # magnitude codes 0..0x7E
+        codes |= (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+        if pow2_scales:
+            scale = np.ldexp(1.0, rng.integers(-12, -6, size=shape[:-1])).astype(np.float32)
+        else:
+            scale = (rng.uniform(0.5, 2.0, size=shape[:-1]) * 2.0 ** -9).astype(np.float32)
+        inp[key + "_fp8"], inp[key + "_scale"] = codes, scale
+    return inp
+
+
+def pin_fp8_matches_bf16_on_exact_weights(orc):
+    """With power-of-two row scales, code * scale is exact in bf16: the FP8 layer equals the BF16 layer bitwise."""
+    for kw in (dict(), dict(I_s=16, E=6, k=3)):
+        inp = _fp8_inputs(30, True, **kw)
+        bf = dict(inp)
+        for key in synth.FP8_KEYS:
+            if inp.get(key) is None:
+                continue
+            w = _wf(inp, key, True)
+            bits = synth.f32_to_bf16_bits(w.astype(np.float32))
+            assert np.array_equal(synth.bf16_bits_to_f32(bits).astype(F64), w)  # exactly representable
+            bf[key] = bits
+        r8 = orc.forward(inp, fp8=True, want=("h", "o"))
+        r16 = orc.forward(bf, want=("h", "o"))
+        for name in ("y", "h", "o", "w", "ids"):
+            assert np.array_equal(r8[name], r16[name]), name
+
+
+def pin_fp8_dense_mixture(orc):
+    """FP8 layer with arbitrary row scales == dense gated mixture on the dequantised weights."""
+    inp = synth.add_fp8_weights(_inputs(seed=31, I_s=16))
+    inp["bias"] = (np.random.default_rng(32).standard_normal(8) * 0.5).astype(np.float32)
+    y_ref, ids_ref, _, gaps = dense_gated_mixture(inp, inp["wl"].k, fp8=True)
+    r = orc.forward(inp, fp8=True)
+    clear = gaps > 1e-4
+    assert clear.sum() >= 0.8 * len(clear)
+    assert np.array_equal(r["ids"][clear], ids_ref[clear])
+    assert _rel_l2(r["y"][clear], y_ref[clear]) < 1e-6  # fp32 vs float64 router logits
+    np.testing.assert_allclose(r["y"][clear], y_ref[clear], rtol=0, atol=1e-7)
+    # the FP8 copy is close to the BF16 layer it was made from (a check of the generator)
+    r16 = orc.forward(inp)
+    assert _rel_l2(r["y"][clear], r16["y"][clear]) < 0.1
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -36,8 +36,14 @@ MUTANTS = {
     "shared_gate_dropped": ("if (I_s > 0) acc = acc + s[t] * os[(size_t)t * H + c];",
                             "if (I_s > 0) acc = acc + os[(size_t)t * H + c];"),
     "shared_gate_sign": ("s[t] = 1.0 / (1.0 + exp(-c));", "s[t] = 1.0 / (1.0 + exp(c));"),
-    "down_transposed": ("acc += hid[i] * (double)bf16_to_f32(row[i]);",
-                        "acc += hid[i] * (double)bf16_to_f32(wd[((size_t)i * H + c) % ((size_t)H * I)]);"),
+    "down_transposed": ("acc += hid[i] * wmat_at(wd, row0 + (size_t)c, (size_t)i, I);",
+                        "acc += hid[i] * wmat_at(wd, row0 + ((size_t)i * H + c) / I % H, ((size_t)i * H + c) % I, I);"),
+    "e4m3_exponent_bias": ("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    "e4m3_subnormal_as_normal": ("ldexp((double)m / 8.0, 1 - 7)", "ldexp(1.0 + (double)m / 8.0, 0 - 7)"),
+    "e4m3_sign_dropped": ("return sgn ? -mag : mag;", "return mag;"),
+    "fp8_scale_by_column": ("acc += (double)bf16_to_f32(x[i]) * (sc * e4m3_value(q[i]));",
+                            "acc += (double)bf16_to_f32(x[i]) * ((double)m.scale[i % 8] * e4m3_value(q[i]));"),
+    "fp8_down_scale_by_column": ("return (double)m.scale[r] * e4m3_value", "return (double)m.scale[c] * e4m3_value"),
     "align_not_stable": ("for (size_t a = 0; a < n; ++a) {\n        int e = ids[a];",
                          "for (size_t a = n; a-- > 0;) {\n        int e = ids[a];"),
     "logit_dot_stride": ("float v = dot_bf16_f32(xt, w_router + (size_t)e * H, H);",
