@@ -129,6 +129,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=0, help="oracle sample tokens (0: sized to ~15 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight calls")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--kernel", choices=["gate_up"], default=None,
@@ -332,38 +333,19 @@ def main():
                          f"{nx} calls, {reps} replays", "eager_us_per_call": eager_us}
         log(f"[bench] decode: {dus:.2f} us/call, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS * 100:.1f}% of HBM); "
             f"eager {eager_us:.2f} us/call")
-        # small batches (the small-batch kernels): bytes = router + the touched experts of each call
-        # (counted from the call's own selection) + the shared expert + x + y
-        sb = {}
-        for Tb in (2, 8, 32):
-            ncall = 16
-            xb = to_device_bf16(synth._draw_bf16(2, "x", (ncall * Tb, H), 1.0), dev)
-            yb = torch.empty((ncall * Tb, H), dtype=torch.bfloat16, device=dev)
-            bws, bws_bytes = dbase.workspace(Tb)
-            ids_off = moe.moe_forward_ids_offset(Tb, H, E, k, I, I_s)
 
-            def bstep(i, Tb=Tb, xb=xb, yb=yb, bws=bws, bws_bytes=bws_bytes):
-                W = dcopies[i % len(dcopies)]
-                moe.moe_forward(xb[i * Tb:(i + 1) * Tb], W["w_router"], None, W["w_gate"], W["w_up"], W["w_down"],
-                                W["ws_gate"], W["ws_up"], W["ws_down"], W["w_sg"], Tb, H, E, k, I, I_s,
-                                yb[i * Tb:(i + 1) * Tb], bws, bws_bytes)
-            touched = []
-            for i in range(ncall):
-                bstep(i)
-                torch.cuda.synchronize()
-                ids_i = bws[ids_off:ids_off + Tb * k * 4].view(torch.int32).cpu().numpy()
-                touched.append(len(np.unique(ids_i)))
-            sbytes = float(np.mean([2 * (E * H + H + n * 3 * H * I + 3 * H * I_s + 2 * Tb * H) for n in touched]))
+        def graph_us(step, ncall):
+            """Average µs per call of step(0..ncall-1) captured in one HIP graph, over `reps` replays."""
             s2 = torch.cuda.Stream()
             s2.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(s2):
                 for i in range(ncall):
-                    bstep(i)
+                    step(i)
             torch.cuda.current_stream().wait_stream(s2)
             gb = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gb):
                 for i in range(ncall):
-                    bstep(i)
+                    step(i)
             gb.replay()
             torch.cuda.synchronize()
             d0.record()
@@ -371,17 +353,90 @@ def main():
                 gb.replay()
             d1.record()
             torch.cuda.synchronize()
-            bus = d0.elapsed_time(d1) * 1e3 / (reps * ncall)
+            del gb
+            return d0.elapsed_time(d1) * 1e3 / (reps * ncall)
+
+        def touched_experts(step, Tb, ws, ncall):
+            ids_off = moe.moe_forward_ids_offset(Tb, H, E, k, I, I_s)
+            out_n = []
+            for i in range(ncall):
+                step(i)
+                torch.cuda.synchronize()
+                out_n.append(len(np.unique(ws[ids_off:ids_off + Tb * k * 4].view(torch.int32).cpu().numpy())))
+            return out_n
+
+        # small batches (the small-batch kernels): bytes = router + the touched experts of each call
+        # (counted from the call's own selection) + the shared expert + x + y
+        sb = {}
+        ncall = 16
+        for Tb in (2, 8, 32):
+            xb = to_device_bf16(synth._draw_bf16(2, "x", (ncall * Tb, H), 1.0), dev)
+            yb = torch.empty((ncall * Tb, H), dtype=torch.bfloat16, device=dev)
+            bws, bws_bytes = dbase.workspace(Tb)
+
+            def bstep(i, Tb=Tb, xb=xb, yb=yb, bws=bws, bws_bytes=bws_bytes):
+                W = dcopies[i % len(dcopies)]
+                moe.moe_forward(xb[i * Tb:(i + 1) * Tb], W["w_router"], None, W["w_gate"], W["w_up"], W["w_down"],
+                                W["ws_gate"], W["ws_up"], W["ws_down"], W["w_sg"], Tb, H, E, k, I, I_s,
+                                yb[i * Tb:(i + 1) * Tb], bws, bws_bytes)
+            touched = touched_experts(bstep, Tb, bws, ncall)
+            sbytes = float(np.mean([2 * (E * H + H + n * 3 * H * I + 3 * H * I_s + 2 * Tb * H) for n in touched]))
+            bus = graph_us(bstep, ncall)
             sb[str(Tb)] = {"us_per_call": bus, "tokens_per_s": Tb / (bus * 1e-6), "touched_experts": float(np.mean(touched)),
                            "bytes_per_call": sbytes, "GB_per_s": sbytes / (bus * 1e-6) / 1e9,
                            "hbm_frac": sbytes / (bus * 1e-6) / 1e9 / PEAK_HBM_GBS}
-            del gb
             log(f"[bench] small batch T={Tb}: {bus:.1f} us/call, {sb[str(Tb)]['GB_per_s']:.0f} GB/s")
         out["small_batch"] = {"workload": "2, 8 and 32 tokens per call, decode-config shapes, no router bias",
                               "timing": f"HIP graph of 16 calls over {len(dcopies)} weight copies, {reps} replays",
                               "per_T": sb}
         del dcopies, g
         torch.cuda.empty_cache()
+
+        # FP8 expert weights (E4M3 codes, one fp32 scale per output row): T = 1, 2, 8, 32.
+        # bytes = router (bf16) + per touched expert 3*H*I code bytes and (2*I + H) scales
+        # + the shared expert likewise + x + y
+        if not args.no_fp8:
+            t0 = time.time()
+            q = synth.add_fp8_weights(dinp)
+            log(f"[bench] FP8 weights made in {time.time() - t0:.1f}s")
+            qbase = DeviceLayer.from_inputs(q, dev, fp8=True)
+            qcopies = [qbase.q]
+            for _ in range(max(0, args.decode_copies - 1)):
+                qcopies.append({key: (None if v is None else v.clone()) for key, v in qbase.q.items()})
+            Wr, Wsg = qbase.w["w_router"], qbase.w["w_sg"]
+
+            def fp8_bytes(n_touched, Tb):
+                per_e = 3 * H * I + 4 * (2 * I + H)
+                shared = 3 * H * I_s + 4 * (2 * I_s + H)
+                return 2 * (E * H + H) + n_touched * per_e + shared + 2 * 2 * Tb * H
+
+            f8 = {}
+            for Tb in (1, 2, 8, 32):
+                nc = nx if Tb == 1 else ncall
+                xb = to_device_bf16(synth._draw_bf16(1 if Tb == 1 else 2, "x", (nc * Tb, H), 1.0), dev)
+                yb = torch.empty((nc * Tb, H), dtype=torch.bfloat16, device=dev)
+                qws, qws_bytes = qbase.workspace(Tb)
+
+                def qstep(i, Tb=Tb, xb=xb, yb=yb, qws=qws, qws_bytes=qws_bytes):
+                    Q = qcopies[i % len(qcopies)]
+                    moe.moe_forward_fp8(xb[i * Tb:(i + 1) * Tb], Wr, None, Q["w_gate"], Q["w_gate_scale"],
+                                        Q["w_up"], Q["w_up_scale"], Q["w_down"], Q["w_down_scale"], Q["ws_gate"],
+                                        Q["ws_gate_scale"], Q["ws_up"], Q["ws_up_scale"], Q["ws_down"],
+                                        Q["ws_down_scale"], Wsg, Tb, H, E, k, I, I_s, yb[i * Tb:(i + 1) * Tb],
+                                        qws, qws_bytes)
+                touched = [k] * nc if Tb == 1 else touched_experts(qstep, Tb, qws, nc)
+                qb = float(np.mean([fp8_bytes(n, Tb) for n in touched]))
+                qus = graph_us(qstep, nc)
+                f8[str(Tb)] = {"us_per_call": qus, "tokens_per_s": Tb / (qus * 1e-6),
+                               "touched_experts": float(np.mean(touched)), "bytes_per_call": qb,
+                               "GB_per_s": qb / (qus * 1e-6) / 1e9, "hbm_frac": qb / (qus * 1e-6) / 1e9 / PEAK_HBM_GBS}
+                log(f"[bench] FP8 weights T={Tb}: {qus:.1f} us/call, {f8[str(Tb)]['GB_per_s']:.0f} GB/s")
+            out["fp8"] = {"workload": "1, 2, 8 and 32 tokens per call, decode-config shapes, expert weights as OCP "
+                                      "FP8 E4M3 with one fp32 scale per output row, no router bias",
+                          "timing": f"HIP graph of {nx} (T=1) or 16 calls over {len(qcopies)} weight copies, "
+                                    f"{reps} replays", "per_T": f8}
+            del qcopies, qbase
+            torch.cuda.empty_cache()
 
     # -------------------------------------------------------- cpu baseline
     if not args.no_cpu_baseline:

@@ -135,6 +135,46 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
                 uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * The whole layer with FP8 expert weights.  kongchang.com "GFX1151 engine"
+ * (section on the two weight formats) describes a HuggingFace-native format
+ * whose weights are FP8-quantised, for speed and a smaller memory footprint.
+ * Encoding: OCP FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent 0 is subnormal; S.1111.111 is NaN; no infinities; largest
+ * magnitude 448), one fp32 scale per output row of every expert matrix:
+ *     W[r][c] = scale[r] * e4m3(code[r][c])
+ * Same arithmetic and outputs as moe_forward on the dequantised weights (the
+ * dot products run over the codes in fp32 and the row scale multiplies each
+ * dot product).  The router (W_router, router_bias) and w_sg stay bf16/fp32.
+ *
+ * Inputs:  q_gate, q_up [E,I,H] and q_down [E,H,I] uint8 codes with scales
+ *          sc_gate, sc_up [E,I] and sc_down [E,H] fp32; shared expert
+ *          qs_gate, qs_up [I_s,H], qs_down [H,I_s] with ssc_gate, ssc_up
+ *          [I_s] and ssc_down [H] -- these six and w_sg all NULL with I_s = 0,
+ *          or all set; everything else as in moe_forward.
+ * Workspace: moe_workspace_size(T,H,E,k,I,I_s) bytes, 256-byte aligned;
+ *          moe_forward_ids_offset() locates the selected ids as for moe_forward.
+ * Sizes: 1 <= T <= MOE_FP8_MAX_T (the single-token and small-batch kernels,
+ *          where reading the weights bounds the step); larger T gives
+ *          MOE_ERR_SHAPE.  Codes that are NaN give NaN outputs (not checked).
+ */
+#define MOE_FP8_MAX_T 32
+int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
+                    const uint8_t* q_gate, const float* sc_gate, const uint8_t* q_up, const float* sc_up,
+                    const uint8_t* q_down, const float* sc_down,
+                    const uint8_t* qs_gate, const float* ssc_gate, const uint8_t* qs_up, const float* ssc_up,
+                    const uint8_t* qs_down, const float* ssc_down, const uint16_t* w_sg,
+                    int T, int H, int E, int k, int I, int I_s,
+                    uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * out[i] = value of the E4M3 code codes[i] (as defined for moe_forward_fp8),
+ * computed with the same device conversion the FP8 kernels use; NaN codes
+ * give NaN.  codes [n] uint8 and out [n] fp32, device pointers, 16-byte
+ * aligned; n >= 0 (0: no-op).  For checking the conversion.
+ */
+int moe_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream);
+
+/*
  * Router stage: logits (fp32 accumulation of bf16 products), optional bias,
  * top-k by (logit desc, index asc), renormalised softmax weights, and the
  * shared-expert gate s = sigmoid(x . w_sg), in one launch (the selection

@@ -19,6 +19,12 @@
 //   D3 down projection + combine: wave per output column, k + 1 rows of
 //      W_down / Ws_down, y = sum_j w_j o_j + s o_s in fp32 -> bf16
 // Wave sums use DPP row shifts and row broadcasts (no LDS round trips).
+//
+// The expert matrices may be FP8 E4M3 codes with one fp32 scale per output
+// row (kongchang.com "GFX1151 engine", section on the two weight formats:
+// FP8-quantised weights for speed and memory): then every weight load moves
+// 8 bytes for the same 8 values, the codes are converted to fp32 in
+// registers, and the row's scale multiplies the row's dot product.
 #include "moe_internal.h"
 #include "moe_topk.h"
 
@@ -54,32 +60,40 @@ DecodeWs carve(void* base, int H, int E, int k, int I, int I_s) {
   return d;
 }
 
-__device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
+// Dot product of 8 bf16 x values with 8 weights (bf16 or E4M3 codes).
+template <class W>
+__device__ __forceinline__ float dot8(u32x4 a, const W& b) {
+  float f[8];
+  chunk_to_f32(b, f);
   float s = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    s += bf16_to_f32((uint16_t)(a[q] & 0xffff)) * bf16_to_f32((uint16_t)(b[q] & 0xffff));
-    s += bf16_to_f32((uint16_t)(a[q] >> 16)) * bf16_to_f32((uint16_t)(b[q] >> 16));
+    s += bf16_to_f32((uint16_t)(a[q] & 0xffff)) * f[2 * q];
+    s += bf16_to_f32((uint16_t)(a[q] >> 16)) * f[2 * q + 1];
   }
   return s;
 }
 
-// Dot products of x with one or two bf16 rows of length H.  x comes from LDS
-// (sx) when given, else straight from global memory; every load of a group
-// of 4 chunks per lane (x's included) is issued before the arithmetic.
-__device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* xg, const uint16_t* r0, const uint16_t* r1,
-                                         int H, int lane, float& d0, float& d1) {
+// Dot products of x with one or two weight rows of length H (bf16, or E4M3
+// codes with Q; unscaled).  x comes from LDS (sx) when given, else straight
+// from global memory; every load of a group of 4 chunks per lane (x's
+// included) is issued before the arithmetic.
+template <bool Q>
+__device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* xg, const void* r0, const void* r1, int H,
+                                         int lane, float& d0, float& d1) {
+  typedef wchunk_t<Q> WC;
   const int nch = H / 8;
   d0 = 0.0f;
   d1 = 0.0f;
   for (int base = 0; base < nch; base += 256) {
-    u32x4 a[4], b[4], xv[4];
+    WC a[4], b[4];
+    u32x4 xv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       int c = base + q * 64 + lane;
       if (c < nch) {
-        a[q] = reinterpret_cast<const u32x4*>(r0)[c];
-        if (r1) b[q] = reinterpret_cast<const u32x4*>(r1)[c];
+        a[q] = reinterpret_cast<const WC*>(r0)[c];
+        if (r1) b[q] = reinterpret_cast<const WC*>(r1)[c];
         xv[q] = sx ? sx[c] : reinterpret_cast<const u32x4*>(xg)[c];
       }
     }
@@ -105,14 +119,14 @@ __global__ __launch_bounds__(256) void decode_router_kernel(const uint16_t* __re
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   float d0, d1;
   if (row < E) {
-    row_dots(nullptr, x, wr + (size_t)row * H, nullptr, H, lane, d0, d1);
+    row_dots<false>(nullptr, x, wr + (size_t)row * H, nullptr, H, lane, d0, d1);
     if (lane == 0) {
       float v = d0 + (bias ? bias[row] : 0.0f);
       if (v == 0.0f) v = 0.0f;
       d.logits[row] = v;
     }
   } else if (row == E && w_sg) {
-    row_dots(nullptr, x, w_sg, nullptr, H, lane, d0, d1);
+    row_dots<false>(nullptr, x, w_sg, nullptr, H, lane, d0, d1);
     if (lane == 0) d.s[0] = 1.0f / (1.0f + expf(-d0));
   }
 }
@@ -143,12 +157,11 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ logits, int
 
 // While wave 0 selects the experts, waves 1..3 compute the shared expert's
 // gate/up rows (they do not depend on the routing): row i = silu(g) * u -> h_s.
-__global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t* __restrict__ x,
-                                                                  const uint16_t* __restrict__ w_gate,
-                                                                  const uint16_t* __restrict__ w_up,
-                                                                  const uint16_t* __restrict__ ws_gate,
-                                                                  const uint16_t* __restrict__ ws_up, int H, int E,
-                                                                  int k, int I, int I_s, DecodeWs d) {
+template <bool Q>
+__global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t* __restrict__ x, ExpertWeights W,
+                                                                  int H, int E, int k, int I, int I_s, DecodeWs d) {
+  typedef wchunk_t<Q> WC;
+  typedef welem_t<Q> WE;
   __shared__ u32x4 sx[1024];
   __shared__ int sel_e[kMaxK];
   __shared__ float sel_w[kMaxK];
@@ -157,9 +170,15 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
   if (wave == 0) {
     block_topk(d.logits, E, k, sel_e, sel_w);
   } else {
+    const WE* sg = static_cast<const WE*>(W.s_gate);
+    const WE* su = static_cast<const WE*>(W.s_up);
     for (int i = blockIdx.x * 3 + wave - 1; i < I_s; i += 3 * gridDim.x) {
       float g, u;
-      row_dots(nullptr, x, ws_gate + (size_t)i * H, ws_up + (size_t)i * H, H, threadIdx.x & 63, g, u);
+      row_dots<Q>(nullptr, x, sg + (size_t)i * H, su + (size_t)i * H, H, threadIdx.x & 63, g, u);
+      if (Q) {
+        g *= W.ssc_gate[i];
+        u *= W.ssc_up[i];
+      }
       if ((threadIdx.x & 63) == 0) d.hs[i] = silu(g) * u;
     }
   }
@@ -168,62 +187,56 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
     d.ids[threadIdx.x] = sel_e[threadIdx.x];
     d.w[threadIdx.x] = sel_w[threadIdx.x];
   }
-  // wave w of workgroup b takes row pairs b*4 + w + q*(4*gridDim.x), q = 0..NR-1;
-  // the NR pairs' loads are all issued before any reduction
-  constexpr int NR = 1;
+  // wave w of workgroup b takes row pair b*4 + w; its loads are all issued
+  // before any reduction
   const int lane = threadIdx.x & 63;
-  const int stride = 4 * gridDim.x;
-  const int row0 = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nch = H / 8;  // chunks per weight row; lane handles chunks lane + 64 c
-  float g[NR], u[NR];
-#pragma unroll
-  for (int q = 0; q < NR; ++q) g[q] = u[q] = 0.0f;
+  const int rr = row < k * I ? row : 0;
+  const size_t rix = (size_t)sel_e[rr / I] * I + rr % I;  // row of W_gate / W_up
+  const WC* gp = reinterpret_cast<const WC*>(static_cast<const WE*>(W.gate) + rix * H);
+  const WC* up = reinterpret_cast<const WC*>(static_cast<const WE*>(W.up) + rix * H);
+  float g = 0.0f, u = 0.0f;
   for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
-    u32x4 a[NR][4], b[NR][4];
+    WC a[4], b[4];
 #pragma unroll
-    for (int q = 0; q < NR; ++q) {
-      const int row = row0 + q * stride;
-      const int rr = row < k * I ? row : 0;
-      const size_t off = ((size_t)sel_e[rr / I] * I + rr % I) * H;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int ch = c0 + lane + 64 * c;
-        if (ch < nch) {
-          a[q][c] = reinterpret_cast<const u32x4*>(w_gate + off)[ch];
-          b[q][c] = reinterpret_cast<const u32x4*>(w_up + off)[ch];
-        }
+    for (int c = 0; c < 4; ++c) {
+      const int ch = c0 + lane + 64 * c;
+      if (ch < nch) {
+        a[c] = gp[ch];
+        b[c] = up[ch];
       }
     }
 #pragma unroll
-    for (int q = 0; q < NR; ++q)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int ch = c0 + lane + 64 * c;
-        if (ch < nch) {
-          const u32x4 xv = sx[ch];
-          g[q] += dot8(xv, a[q][c]);
-          u[q] += dot8(xv, b[q][c]);
-        }
+    for (int c = 0; c < 4; ++c) {
+      const int ch = c0 + lane + 64 * c;
+      if (ch < nch) {
+        const u32x4 xv = sx[ch];
+        g += dot8(xv, a[c]);
+        u += dot8(xv, b[c]);
       }
+    }
   }
-#pragma unroll
-  for (int q = 0; q < NR; ++q) {
-    const int row = row0 + q * stride;
-    const float gs = wave_sum(g[q]), us = wave_sum(u[q]);
-    if (row < k * I && lane == 0) d.h[row] = silu(gs) * us;
+  float gs = wave_sum(g), us = wave_sum(u);
+  if (Q) {
+    gs *= W.sc_gate[rix];
+    us *= W.sc_up[rix];
   }
+  if (row < k * I && lane == 0) d.h[row] = silu(gs) * us;
 }
 
-// Wave per CPW output columns: the k + 1 weight rows of the columns are
-// loaded together (I / 8 chunks each), and each h value read serves them all.
-template <int KT>  // k <= KT
-__global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __restrict__ w_down,
-                                                          const uint16_t* __restrict__ ws_down, int H, int k, int I,
-                                                          int I_s, DecodeWs d, uint16_t* __restrict__ y) {
-  constexpr int CPW = 1;
+// Wave per output column: the k + 1 weight rows of the column are loaded
+// together (I / 8 chunks each), and each h value read serves them all.
+template <int KT, bool Q>  // k <= KT
+__global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H, int k, int I, int I_s, DecodeWs d,
+                                                          uint16_t* __restrict__ y) {
+  typedef wchunk_t<Q> WC;
+  typedef welem_t<Q> WE;
   const int lane = threadIdx.x & 63;
-  const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * CPW;
+  const int c0 = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (c0 >= H) return;
+  const WE* wd = static_cast<const WE*>(W.down);
+  const WE* wsd = static_cast<const WE*>(W.s_down);
   // ids and weights: KT entries read with 16-byte loads (their workspace
   // slots hold 64 entries), entries past k unused
   int ids[KT];
@@ -237,17 +250,14 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __rest
   }
 #pragma unroll
   for (int j = 0; j < KT; ++j) ids[j] = j < k ? ids[j] : 0;  // keep unused rows in range
-  float part[CPW][KT + 1];
+  float part[KT + 1];
 #pragma unroll
-  for (int c = 0; c < CPW; ++c)
+  for (int j = 0; j <= KT; ++j) part[j] = 0.0f;
+  auto accum = [&](float& acc, const WC& wv, const float* hv) {
+    float f[8];
+    chunk_to_f32(wv, f);
 #pragma unroll
-    for (int j = 0; j <= KT; ++j) part[c][j] = 0.0f;
-  auto accum = [&](float& acc, const u32x4& wv, const float* hv) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc += hv[2 * q] * bf16_to_f32((uint16_t)(wv[q] & 0xffff));
-      acc += hv[2 * q + 1] * bf16_to_f32((uint16_t)(wv[q] >> 16));
-    }
+    for (int q = 0; q < 8; ++q) acc += hv[q] * f[q];
   };
   // Per step of 64 chunks: the loads that do not depend on the routing (the
   // shared row, h_s and every h_j) are issued first, then the k routed rows.
@@ -256,11 +266,10 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __rest
   for (int base = 0; base < nmax; base += 64) {
     const int ch = base + lane;
     const bool okS = ch < nS, okI = ch < nI;
-    u32x4 wsv[CPW];
+    WC wsv;
     float4 hs0 = {}, hs1 = {};
     if (okS) {
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) wsv[c] = reinterpret_cast<const u32x4*>(ws_down + (size_t)(c0 + c) * I_s)[ch];
+      wsv = reinterpret_cast<const WC*>(wsd + (size_t)c0 * I_s)[ch];
       const float4* hp = reinterpret_cast<const float4*>(d.hs + ch * 8);
       hs0 = hp[0];
       hs1 = hp[1];
@@ -273,36 +282,71 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const uint16_t* __rest
         h0[j] = hp[0];
         h1[j] = hp[1];
       }
-    u32x4 wv[KT][CPW];
+    WC wv[KT];
 #pragma unroll
     for (int j = 0; j < KT; ++j)
-      if (j < k && okI)
-#pragma unroll
-        for (int c = 0; c < CPW; ++c)
-          wv[j][c] = reinterpret_cast<const u32x4*>(w_down + ((size_t)ids[j] * H + c0 + c) * I)[ch];
+      if (j < k && okI) wv[j] = reinterpret_cast<const WC*>(wd + ((size_t)ids[j] * H + c0) * I)[ch];
     if (okS) {
       const float hv[8] = {hs0.x, hs0.y, hs0.z, hs0.w, hs1.x, hs1.y, hs1.z, hs1.w};
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) accum(part[c][KT], wsv[c], hv);
+      accum(part[KT], wsv, hv);
     }
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
       if (j < k && okI) {
         const float hv[8] = {h0[j].x, h0[j].y, h0[j].z, h0[j].w, h1[j].x, h1[j].y, h1[j].z, h1[j].w};
-#pragma unroll
-        for (int c = 0; c < CPW; ++c) accum(part[c][j], wv[j][c], hv);
+        accum(part[j], wv[j], hv);
       }
     }
   }
+  float yv = 0.0f;
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    float yv = 0.0f;
-#pragma unroll
-    for (int j = 0; j < KT; ++j)
-      if (j < k) yv += wsel[j] * wave_sum(part[c][j]);  // rank order
-    if (I_s > 0) yv += d.s[0] * wave_sum(part[c][KT]);
-    if (lane == 0) y[c0 + c] = f32_to_bf16(yv);
+  for (int j = 0; j < KT; ++j)
+    if (j < k) {
+      float oj = wave_sum(part[j]);
+      if (Q) oj *= W.sc_down[(size_t)ids[j] * H + c0];
+      yv += wsel[j] * oj;  // rank order
+    }
+  if (I_s > 0) {
+    float os = wave_sum(part[KT]);
+    if (Q) os *= W.ssc_down[c0];
+    yv += d.s[0] * os;
   }
+  if (lane == 0) y[c0] = f32_to_bf16(yv);
+}
+
+__global__ __launch_bounds__(256) void e4m3_to_f32_kernel(const uint8_t* __restrict__ codes, float* __restrict__ out,
+                                                          int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  if (i + 8 <= n) {
+    float f[8];
+    chunk_to_f32(*reinterpret_cast<const u32x2*>(codes + i), f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) out[i + q] = f[q];
+  } else {
+    for (int64_t j = i; j < n; ++j) {  // tail: one code at a time, in the low byte
+      float f[8];
+      chunk_to_f32(u32x2{(uint32_t)codes[j], 0u}, f);
+      out[j] = f[0];
+    }
+  }
+}
+
+template <bool Q>
+void launch_decode_t(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
+                     const ExpertWeights& W, int H, int E, int k, int I, int I_s, uint16_t* y, DecodeWs d,
+                     hipStream_t st) {
+  const int rows1 = E + (I_s > 0 ? 1 : 0);
+  hipLaunchKernelGGL(decode_router_kernel, dim3((rows1 + 3) / 4), dim3(256), 0, st, x, w_router, bias,
+                     I_s > 0 ? w_sg : nullptr, H, E, d);
+  // 4 waves per workgroup, one routed row pair per wave; waves 1..3 also take the shared rows
+  hipLaunchKernelGGL(decode_topk_gate_up_kernel<Q>, dim3((k * I + 3) / 4), dim3(256), 0, st, x, W, H, E, k, I, I_s,
+                     d);
+  // 4 waves per workgroup, one output column per wave (H is a multiple of 256)
+  if (k <= 8)
+    hipLaunchKernelGGL((decode_down_kernel<8, Q>), dim3((H + 3) / 4), dim3(256), 0, st, W, H, k, I, I_s, d, y);
+  else
+    hipLaunchKernelGGL((decode_down_kernel<kMaxK, Q>), dim3((H + 3) / 4), dim3(256), 0, st, W, H, k, I, I_s, d, y);
 }
 
 }  // namespace
@@ -315,24 +359,21 @@ size_t decode_workspace_size(int H, int E, int k, int I, int I_s) {
          align256((size_t)k * I * 4);
 }
 
-hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_gate,
-                         const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate,
-                         const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int H, int E,
-                         int k, int I, int I_s, uint16_t* y, void* ws, hipStream_t st) {
+hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
+                         const ExpertWeights& W, int H, int E, int k, int I, int I_s, uint16_t* y, void* ws,
+                         hipStream_t st) {
   DecodeWs d = carve(ws, H, E, k, I, I_s);
-  const int rows1 = E + (I_s > 0 ? 1 : 0);
-  hipLaunchKernelGGL(decode_router_kernel, dim3((rows1 + 3) / 4), dim3(256), 0, st, x, w_router, bias,
-                     I_s > 0 ? w_sg : nullptr, H, E, d);
-  // 4 waves per workgroup, one routed row pair per wave; waves 1..3 also take the shared rows
-  hipLaunchKernelGGL(decode_topk_gate_up_kernel, dim3((k * I + 3) / 4), dim3(256), 0, st, x, w_gate, w_up, ws_gate,
-                     ws_up, H, E, k, I, I_s, d);
-  // 4 waves per workgroup, one output column per wave (H is a multiple of 256)
-  if (k <= 8)
-    hipLaunchKernelGGL(decode_down_kernel<8>, dim3((H + 3) / 4), dim3(256), 0, st, w_down, ws_down, H, k, I, I_s, d,
-                       y);
+  if (W.fp8)
+    launch_decode_t<true>(x, w_router, bias, w_sg, W, H, E, k, I, I_s, y, d, st);
   else
-    hipLaunchKernelGGL(decode_down_kernel<kMaxK>, dim3((H + 3) / 4), dim3(256), 0, st, w_down, ws_down, H, k, I, I_s,
-                       d, y);
+    launch_decode_t<false>(x, w_router, bias, w_sg, W, H, E, k, I, I_s, y, d, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 2047) / 2048;
+  hipLaunchKernelGGL(e4m3_to_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, codes, out, n);
   return hipGetLastError();
 }
 

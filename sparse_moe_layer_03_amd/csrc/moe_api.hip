@@ -357,15 +357,15 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   if ((rc = check_arch())) return rc;
   hipStream_t st = (hipStream_t)stream;
 
-  if (T == 1)
-    return hip_status(launch_decode(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg, H,
-                                    E, k, I, I_s, y, workspace, st),
-                      "moe_forward (decode)");
-
-  if (T <= kSmallMaxT)
-    return hip_status(launch_small_batch(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg,
-                                         T, H, E, k, I, I_s, y, workspace, st),
+  if (T <= kSmallMaxT) {
+    const ExpertWeights W = {w_gate,  w_up,    w_down,  ws_gate, ws_up,   ws_down, nullptr,
+                             nullptr, nullptr, nullptr, nullptr, nullptr, false};
+    if (T == 1)
+      return hip_status(launch_decode(x, w_router, router_bias, w_sg, W, H, E, k, I, I_s, y, workspace, st),
+                        "moe_forward (decode)");
+    return hip_status(launch_small_batch(x, w_router, router_bias, w_sg, W, T, H, E, k, I, I_s, y, workspace, st),
                       "moe_forward (small batch)");
+  }
 
   const Layout L = layout(T, H, E, k, I, I_s);
   char* base = static_cast<char*>(workspace);
@@ -396,6 +396,54 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   if (e != hipSuccess) return hip_status(e, "moe_forward: down");
   e = launch_combine(o, w, h_s, ws_down, I_s > 0 ? s : nullptr, T, H, k, I_s, y, st);
   return hip_status(e, "moe_forward: combine");
+}
+
+int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint8_t* q_gate,
+                    const float* sc_gate, const uint8_t* q_up, const float* sc_up, const uint8_t* q_down,
+                    const float* sc_down, const uint8_t* qs_gate, const float* ssc_gate, const uint8_t* qs_up,
+                    const float* ssc_up, const uint8_t* qs_down, const float* ssc_down, const uint16_t* w_sg, int T,
+                    int H, int E, int k, int I, int I_s, uint16_t* y, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_common_shapes(T, H, E, k);
+  if (rc || (rc = check_ffn_shapes(I, I_s))) return rc;
+  if (T > MOE_FP8_MAX_T)
+    return fail(MOE_ERR_SHAPE, "moe_forward_fp8: T=%d; FP8 expert weights are supported for T <= %d", T,
+                MOE_FP8_MAX_T);
+  const int n_shared = (qs_gate != nullptr) + (ssc_gate != nullptr) + (qs_up != nullptr) + (ssc_up != nullptr) +
+                       (qs_down != nullptr) + (ssc_down != nullptr) + (w_sg != nullptr);
+  if (I_s == 0 && n_shared != 0) return fail(MOE_ERR_SHAPE, "moe_forward_fp8: shared-expert tensors given with I_s = 0");
+  if (I_s > 0 && n_shared != 7)
+    return fail(MOE_ERR_NULL, "moe_forward_fp8: I_s > 0 needs qs_*, ssc_* (gate, up, down) and w_sg");
+  if (T == 0) return ok();
+  if (!x || !w_router || !q_gate || !sc_gate || !q_up || !sc_up || !q_down || !sc_down || !y || !workspace)
+    return fail(MOE_ERR_NULL, "moe_forward_fp8: x, w_router, q_*/sc_* (gate, up, down), y and workspace are required");
+  const void* ptrs[] = {x,       w_router, q_gate, sc_gate, q_up,     sc_up,  q_down,   sc_down, y,
+                        qs_gate, ssc_gate, qs_up,  ssc_up,  qs_down, ssc_down, w_sg};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MOE_ERR_ALIGN, "moe_forward_fp8: tensor pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MOE_ERR_ALIGN, "moe_forward_fp8: workspace must be 256-byte aligned");
+  const size_t need = moe_workspace_size(T, H, E, k, I, I_s);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if ((rc = check_arch())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const ExpertWeights W = {q_gate,  q_up,   q_down,  qs_gate,  qs_up,  qs_down, sc_gate,
+                           sc_up,   sc_down, ssc_gate, ssc_up, ssc_down, true};
+  if (T == 1)
+    return hip_status(launch_decode(x, w_router, router_bias, w_sg, W, H, E, k, I, I_s, y, workspace, st),
+                      "moe_forward_fp8 (decode)");
+  return hip_status(launch_small_batch(x, w_router, router_bias, w_sg, W, T, H, E, k, I, I_s, y, workspace, st),
+                    "moe_forward_fp8 (small batch)");
+}
+
+int moe_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream) {
+  if (n < 0) return fail(MOE_ERR_SHAPE, "moe_e4m3_to_f32: n=%lld < 0", (long long)n);
+  if (n == 0) return ok();
+  if (!codes || !out) return fail(MOE_ERR_NULL, "moe_e4m3_to_f32: codes and out are required");
+  if (!aligned16(codes) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "moe_e4m3_to_f32: pointers must be 16-byte aligned");
+  int rc = check_arch();
+  if (rc) return rc;
+  return hip_status(launch_e4m3_to_f32(codes, out, n, (hipStream_t)stream), "moe_e4m3_to_f32");
 }
 
 }  // extern "C"

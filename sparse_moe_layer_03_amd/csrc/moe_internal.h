@@ -6,12 +6,16 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;      // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
@@ -30,6 +34,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Eight consecutive weights of one row as one load: 16 bytes of BF16, or 8
+// bytes of FP8 E4M3 codes (Q).
+template <bool Q> struct WChunk { typedef u32x4 type; };
+template <> struct WChunk<true> { typedef u32x2 type; };
+template <bool Q> using wchunk_t = typename WChunk<Q>::type;
+template <bool Q> using welem_t = typename std::conditional<Q, uint8_t, uint16_t>::type;
+
+__device__ __forceinline__ void chunk_to_f32(const u32x4& w, float* f) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = bf16_to_f32((uint16_t)(w[q] & 0xffff));
+    f[2 * q + 1] = bf16_to_f32((uint16_t)(w[q] >> 16));
+  }
+}
+
+// OCP FP8 E4M3 codes (lowest byte first) to fp32 with the gfx950 conversion
+// instruction, two codes per instruction; exact (every E4M3 value is an fp32).
+__device__ __forceinline__ void chunk_to_f32(const u32x2& w, float* f) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
+    f[4 * q] = lo[0];
+    f[4 * q + 1] = lo[1];
+    f[4 * q + 2] = hi[0];
+    f[4 * q + 3] = hi[1];
+  }
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
@@ -62,6 +95,17 @@ __device__ __forceinline__ int xcd_item(int bid, int n_items) {
   return item < n_items ? item : -1;
 }
 
+// Expert weights as the single-token and small-batch kernels take them: BF16
+// matrices (fp8 false; scale pointers unused), or OCP FP8 E4M3 codes with one
+// fp32 scale per output row (fp8 true).  Routed gate/up [E,I,H] with scales
+// [E,I], down [E,H,I] with scales [E,H]; shared gate/up [I_s,H] with scales
+// [I_s], down [H,I_s] with scales [H].
+struct ExpertWeights {
+  const void *gate, *up, *down, *s_gate, *s_up, *s_down;
+  const float *sc_gate, *sc_up, *sc_down, *ssc_gate, *ssc_up, *ssc_down;
+  bool fp8;
+};
+
 // Host-side launch helpers (defined in the .hip files).
 // Router GEMM over token tiles: fp32 logits (+ bias, -0 -> +0; stored when
 // logits is not NULL), the top-k ids and renormalised weights of every token
@@ -88,17 +132,17 @@ hipError_t launch_down(const uint16_t* h, const uint16_t* w_down, const int32_t*
 hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s,
                           const uint16_t* ws_down, const float* s, int T, int H, int k, int I_s, uint16_t* y,
                           hipStream_t st);
-hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_gate,
-                         const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate,
-                         const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int H, int E,
-                         int k, int I, int I_s, uint16_t* y, void* ws, hipStream_t st);
+hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
+                         const ExpertWeights& W, int H, int E, int k, int I, int I_s, uint16_t* y, void* ws,
+                         hipStream_t st);
 size_t decode_workspace_size(int H, int E, int k, int I, int I_s);
 // Small-batch path (2 <= T <= kSmallMaxT): router, selection and plan, gate/up
 // and down over the touched experts' weight rows, combine.
-hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_gate,
-                              const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate,
-                              const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int T, int H,
-                              int E, int k, int I, int I_s, uint16_t* y, void* ws, hipStream_t st);
+hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
+                              const ExpertWeights& W, int T, int H, int E, int k, int I, int I_s, uint16_t* y,
+                              void* ws, hipStream_t st);
+// E4M3 codes to fp32 with the conversion the FP8 kernels use.
+hipError_t launch_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n, hipStream_t st);
 size_t small_batch_workspace_size(int T, int H, int E, int k, int I, int I_s);
 size_t small_batch_ids_offset(int T, int E);
 size_t decode_ids_offset(int E);

@@ -18,6 +18,9 @@
 //   S4 down: (touched expert, block of 64 output columns) per workgroup:
 //      o[a][c] = h[a] . W_down[e][c] in fp32 (shared: o_s[t][c])
 //   S5 combine: y[t][c] = sum_j w[t][j] o[t*k+j][c] (j ascending) + s[t] o_s[t][c]
+// With FP8 E4M3 expert weights (one fp32 scale per output row) the weight
+// loads move 8 bytes per 8 values, the codes are converted in registers and
+// the row's scale multiplies each dot product.
 #include "moe_internal.h"
 #include "moe_topk.h"
 
@@ -76,21 +79,27 @@ size_t small_ws_bytes(int T, int H, int E, int k, int I, int I_s) {
   return total;
 }
 
-__device__ __forceinline__ float sb_dot8(const u32x4& a, const u32x4& b) {
+// 8 bf16 x values . 8 weights (bf16, or E4M3 codes), ascending.
+template <class W>
+__device__ __forceinline__ float sb_dot8(const u32x4& a, const W& b) {
+  float f[8];
+  chunk_to_f32(b, f);
   float s = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    s += bf16_to_f32((uint16_t)(a[q] & 0xffff)) * bf16_to_f32((uint16_t)(b[q] & 0xffff));
-    s += bf16_to_f32((uint16_t)(a[q] >> 16)) * bf16_to_f32((uint16_t)(b[q] >> 16));
+    s += bf16_to_f32((uint16_t)(a[q] & 0xffff)) * f[2 * q];
+    s += bf16_to_f32((uint16_t)(a[q] >> 16)) * f[2 * q + 1];
   }
   return s;
 }
 
-__device__ __forceinline__ float dot8_f32w(const float4& h0, const float4& h1, const u32x4& wv) {
-  return h0.x * bf16_to_f32((uint16_t)(wv[0] & 0xffff)) + h0.y * bf16_to_f32((uint16_t)(wv[0] >> 16)) +
-         h0.z * bf16_to_f32((uint16_t)(wv[1] & 0xffff)) + h0.w * bf16_to_f32((uint16_t)(wv[1] >> 16)) +
-         h1.x * bf16_to_f32((uint16_t)(wv[2] & 0xffff)) + h1.y * bf16_to_f32((uint16_t)(wv[2] >> 16)) +
-         h1.z * bf16_to_f32((uint16_t)(wv[3] & 0xffff)) + h1.w * bf16_to_f32((uint16_t)(wv[3] >> 16));
+// 8 fp32 h values . 8 weights (bf16, or E4M3 codes).
+template <class W>
+__device__ __forceinline__ float dot8_f32w(const float4& h0, const float4& h1, const W& wv) {
+  float f[8];
+  chunk_to_f32(wv, f);
+  return h0.x * f[0] + h0.y * f[1] + h0.z * f[2] + h0.w * f[3] + h1.x * f[4] + h1.y * f[5] + h1.z * f[6] +
+         h1.w * f[7];
 }
 
 constexpr int TB = 16;  // tokens (or assignments) staged in LDS at a time
@@ -272,12 +281,11 @@ __global__ __launch_bounds__(1024) void sb_select_kernel(int T, int E, int k, Sm
 // staged in LDS (2048 columns at a time).  Slot u == n_u is the shared expert
 // over all T tokens when I_s > 0.
 constexpr int GP = 2, GR = 4 * GP, GT = 16;
-__global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restrict__ x,
-                                                         const uint16_t* __restrict__ wg,
-                                                         const uint16_t* __restrict__ wu,
-                                                         const uint16_t* __restrict__ wsg,
-                                                         const uint16_t* __restrict__ wsu, int T, int H, int E,
-                                                         int k, int I, int I_s, SmallWs d) {
+template <bool Q>
+__global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restrict__ x, ExpertWeights W, int T,
+                                                         int H, int E, int k, int I, int I_s, SmallWs d) {
+  typedef wchunk_t<Q> WC;
+  typedef welem_t<Q> WE;
   __shared__ u32x4 sx[GT * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nu = d.plan[0];
@@ -291,8 +299,15 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
   const int e = shared ? 0 : rec[0], off = shared ? 0 : rec[1], cnt = shared ? T : rec[2];
   // assignment q of the expert (shared expert: token q)
   auto asg_at = [&](int q) { return shared ? q : (q < TBR ? rec[4 + q] : d.asg[off + q]); };
-  const uint16_t* g0 = shared ? wsg + (size_t)i0 * H : wg + ((size_t)e * I + i0) * H;
-  const uint16_t* u0 = shared ? wsu + (size_t)i0 * H : wu + ((size_t)e * I + i0) * H;
+  const size_t r0 = shared ? (size_t)i0 : (size_t)e * I + i0;  // first of the wave's GP rows
+  const WE* g0 = static_cast<const WE*>(shared ? W.s_gate : W.gate) + r0 * H;
+  const WE* u0 = static_cast<const WE*>(shared ? W.s_up : W.up) + r0 * H;
+  float scg[GP], scu[GP];
+#pragma unroll
+  for (int p = 0; p < GP; ++p) {
+    scg[p] = Q ? (shared ? W.ssc_gate : W.sc_gate)[r0 + p] : 1.0f;
+    scu[p] = Q ? (shared ? W.ssc_up : W.sc_up)[r0 + p] : 1.0f;
+  }
   const int nch = H / 8;
   for (int q0 = 0; q0 < cnt; q0 += GT) {
     const int nt = min(GT, cnt - q0);
@@ -302,14 +317,14 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
 #pragma unroll
       for (int t = 0; t < GT; ++t) ag[p][t] = au[p][t] = 0.0f;
     for (int base = 0; base < nch; base += 256) {
-      u32x4 gv[GP][4], uv[GP][4];
+      WC gv[GP][4], uv[GP][4];
 #pragma unroll
       for (int p = 0; p < GP; ++p)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const int c = min(base + c4 * 64 + lane, nch - 1);
-          gv[p][c4] = reinterpret_cast<const u32x4*>(g0 + (size_t)p * H)[c];
-          uv[p][c4] = reinterpret_cast<const u32x4*>(u0 + (size_t)p * H)[c];
+          gv[p][c4] = reinterpret_cast<const WC*>(g0 + (size_t)p * H)[c];
+          uv[p][c4] = reinterpret_cast<const WC*>(u0 + (size_t)p * H)[c];
         }
       __syncthreads();
       stage_x<GT>(sx, x, H, base, nt, [&](int t) { return shared ? q0 + t : asg_at(q0 + t) / k; });
@@ -317,7 +332,7 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
       for (int p = 0; p < GP; ++p)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
-          if (base + c4 * 64 + lane >= nch) gv[p][c4] = uv[p][c4] = u32x4{0u, 0u, 0u, 0u};
+          if (base + c4 * 64 + lane >= nch) gv[p][c4] = uv[p][c4] = WC{};
 #pragma unroll
       for (int t = 0; t < GT; ++t) {
         if (t < nt) {  // uniform
@@ -338,7 +353,11 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
       if (t < nt) {
 #pragma unroll
         for (int p = 0; p < GP; ++p) {
-          const float gs = wave_sum(ag[p][t]), us = wave_sum(au[p][t]);
+          float gs = wave_sum(ag[p][t]), us = wave_sum(au[p][t]);
+          if (Q) {
+            gs *= scg[p];
+            us *= scu[p];
+          }
           if (lane == 0) {
             if (shared)
               d.hs[(size_t)(q0 + t) * I_s + i0 + p] = silu(gs) * us;
@@ -356,9 +375,11 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
 // reduction chunks j * 4 + l % 4 (four adjacent lanes read 64 contiguous
 // bytes of a row); the four partial sums of a column meet in two DPP steps.
 // h rows of the expert's assignments (fp32) are staged in LDS, 16 at a time.
-__global__ __launch_bounds__(256) void sb_down_kernel(const uint16_t* __restrict__ wd,
-                                                      const uint16_t* __restrict__ wsd, int T, int H, int E, int k,
-                                                      int I, int I_s, SmallWs d) {
+template <bool Q>
+__global__ __launch_bounds__(256) void sb_down_kernel(ExpertWeights W, int T, int H, int E, int k, int I, int I_s,
+                                                      SmallWs d) {
+  typedef wchunk_t<Q> WC;
+  typedef welem_t<Q> WE;
   __shared__ float4 shh[TB * 128];  // 16 rows of up to 512 fp32 reduction values
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nu = d.plan[0];
@@ -370,13 +391,15 @@ __global__ __launch_bounds__(256) void sb_down_kernel(const uint16_t* __restrict
   const int32_t* rec = d.plan + kRec0 + (shared ? 0 : u) * kRecInts;
   const int e = shared ? 0 : rec[0], off = shared ? 0 : rec[1], cnt = shared ? T : rec[2];
   auto asg_at = [&](int q) { return shared ? q : (q < TBR ? rec[4 + q] : d.asg[off + q]); };
-  const uint16_t* wrow = shared ? wsd + (size_t)col * I_s : wd + ((size_t)e * H + col) * I;
+  const size_t wr = shared ? (size_t)col : (size_t)e * H + col;  // row of W_down / Ws_down
+  const WE* wrow = static_cast<const WE*>(shared ? W.s_down : W.down) + wr * K;
+  const float sc = Q ? (shared ? W.ssc_down : W.sc_down)[wr] : 1.0f;
   const int nch = K / 8;
   for (int kb = 0; kb < nch; kb += 64) {  // reduction blocks of 512 values
     const int nb = min(64, nch - kb);        // chunks in this block (a multiple of 16)
-    u32x4 wv[16];
+    WC wv[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) wv[j] = reinterpret_cast<const u32x4*>(wrow)[kb + min(j * 4 + (lane & 3), nb - 1)];
+    for (int j = 0; j < 16; ++j) wv[j] = reinterpret_cast<const WC*>(wrow)[kb + min(j * 4 + (lane & 3), nb - 1)];
     for (int q0 = 0; q0 < cnt; q0 += TB) {
       const int nt = min(TB, cnt - q0);
       __syncthreads();
@@ -408,6 +431,7 @@ __global__ __launch_bounds__(256) void sb_down_kernel(const uint16_t* __restrict
         // permutes, so every lane of the quad holds the total
         part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0xB1, 0xf, 0xf, false));  // [1,0,3,2]
         part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x4E, 0xf, 0xf, false));  // [2,3,0,1]
+        if (Q) part *= sc;
         if ((lane & 3) == 0) {
           const int a = asg_at(q0 + t);
           float* out = (shared ? d.os : d.o) + (size_t)a * H + col;
@@ -442,10 +466,9 @@ size_t small_batch_workspace_size(int T, int H, int E, int k, int I, int I_s) {
   return small_ws_bytes(T, H, E, k, I, I_s);
 }
 
-hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_gate,
-                              const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate,
-                              const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int T, int H,
-                              int E, int k, int I, int I_s, uint16_t* y, void* ws, hipStream_t st) {
+hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
+                              const ExpertWeights& W, int T, int H, int E, int k, int I, int I_s, uint16_t* y,
+                              void* ws, hipStream_t st) {
   if (T < 1 || T > kSmallMaxT) return hipErrorInvalidValue;
   SmallWs d = carve_small(ws, T, H, E, k, I, I_s);
   const int rows1 = E + (I_s > 0 ? 1 : 0);
@@ -455,9 +478,14 @@ hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const
   // expert slots: at most min(E, T*k) touched experts, plus the shared expert
   const int max_u = (T * k < E ? T * k : E) + (I_s > 0 ? 1 : 0);
   const int nrow = I > I_s ? I : I_s;
-  hipLaunchKernelGGL(sb_gate_up_kernel, dim3((nrow + GR - 1) / GR, max_u), dim3(256), 0, st, x, w_gate, w_up, ws_gate,
-                     ws_up, T, H, E, k, I, I_s, d);
-  hipLaunchKernelGGL(sb_down_kernel, dim3(H / 64, max_u), dim3(256), 0, st, w_down, ws_down, T, H, E, k, I, I_s, d);
+  const dim3 g_gu((nrow + GR - 1) / GR, max_u), g_dn(H / 64, max_u);
+  if (W.fp8) {
+    hipLaunchKernelGGL(sb_gate_up_kernel<true>, g_gu, dim3(256), 0, st, x, W, T, H, E, k, I, I_s, d);
+    hipLaunchKernelGGL(sb_down_kernel<true>, g_dn, dim3(256), 0, st, W, T, H, E, k, I, I_s, d);
+  } else {
+    hipLaunchKernelGGL(sb_gate_up_kernel<false>, g_gu, dim3(256), 0, st, x, W, T, H, E, k, I, I_s, d);
+    hipLaunchKernelGGL(sb_down_kernel<false>, g_dn, dim3(256), 0, st, W, T, H, E, k, I, I_s, d);
+  }
   hipLaunchKernelGGL(sb_combine_kernel, dim3((T * H + 255) / 256), dim3(256), 0, st, T, H, k, I_s, d, y);
   return hipGetLastError();
 }

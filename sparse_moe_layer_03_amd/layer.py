@@ -13,6 +13,7 @@ import numpy as np
 from . import moe
 
 BF16_KEYS = ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down", "w_sg")
+FP8_KEYS = ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
 
 
 def to_device_bf16(a: Optional[np.ndarray], device):
@@ -39,12 +40,25 @@ class Shapes:
 
 
 class DeviceLayer:
-    """The layer's weights on one GPU plus a reusable workspace."""
+    """The layer's weights on one GPU plus a reusable workspace.
 
-    def __init__(self, weights: Dict[str, np.ndarray], k: int, device="cuda:0"):
+    ``fp8``: also upload the FP8 expert weights (``<key>_fp8`` codes and
+    ``<key>_scale`` row scales of ``weights``); ``forward`` then calls
+    ``moe_forward_fp8``.
+    """
+
+    def __init__(self, weights: Dict[str, np.ndarray], k: int, device="cuda:0", fp8: bool = False):
         import torch
         self.device = torch.device(device)
+        self.fp8 = fp8
         self.w = {key: to_device_bf16(weights.get(key), self.device) for key in BF16_KEYS}
+        self.q = {}
+        if fp8:
+            for key in FP8_KEYS:
+                c, sc = weights.get(key + "_fp8"), weights.get(key + "_scale")
+                self.q[key] = None if c is None else torch.from_numpy(np.ascontiguousarray(c, np.uint8)).to(self.device)
+                self.q[key + "_scale"] = (None if sc is None else
+                                          torch.from_numpy(np.ascontiguousarray(sc, np.float32)).to(self.device))
         b = weights.get("bias")
         self.bias = None if b is None else torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(self.device)
         E, I, H = weights["w_gate"].shape
@@ -54,8 +68,8 @@ class DeviceLayer:
         self._ws_bytes = 0
 
     @classmethod
-    def from_inputs(cls, inp, device="cuda:0"):
-        return cls(inp, inp["wl"].k, device)
+    def from_inputs(cls, inp, device="cuda:0", fp8: bool = False):
+        return cls(inp, inp["wl"].k, device, fp8=fp8)
 
     def workspace(self, T: int):
         import torch
@@ -77,6 +91,13 @@ class DeviceLayer:
             y = torch.empty((T, s.H), dtype=torch.bfloat16, device=self.device)
         ws, nbytes = self.workspace(T)
         W = self.w
+        if self.fp8:
+            q = self.q
+            moe.moe_forward_fp8(x, W["w_router"], self.bias, q["w_gate"], q["w_gate_scale"], q["w_up"],
+                                q["w_up_scale"], q["w_down"], q["w_down_scale"], q["ws_gate"], q["ws_gate_scale"],
+                                q["ws_up"], q["ws_up_scale"], q["ws_down"], q["ws_down_scale"], W["w_sg"],
+                                T, s.H, s.E, s.k, s.I, s.I_s, y, ws, nbytes, stream)
+            return y
         moe.moe_forward(x, W["w_router"], self.bias, W["w_gate"], W["w_up"], W["w_down"], W["ws_gate"], W["ws_up"],
                         W["ws_down"], W["w_sg"], T, s.H, s.E, s.k, s.I, s.I_s, y, ws, nbytes, stream)
         return y

@@ -23,11 +23,12 @@ MOE_ERR_WORKSPACE = -4
 MOE_ERR_ARCH = -5
 MOE_ERR_HIP = -6
 SMALL_BATCH_MAX_T = 32  # MOE_SMALL_BATCH_MAX_T: moe_forward's small-batch path covers 2 <= T <= this
+FP8_MAX_T = 32  # MOE_FP8_MAX_T: moe_forward_fp8 covers 1 <= T <= this
 
 EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_align_tile_rows", "moe_align_small_tile_rows", "moe_align_max_rows",
     "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward_ids_offset", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
-    "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine",
+    "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine", "moe_forward_fp8", "moe_e4m3_to_f32",
 )
 
 
@@ -66,6 +67,8 @@ def lib():
             "moe_grouped_gate_up": ([p] * 8 + [i] * 6 + [p, p, p], i),
             "moe_grouped_down": ([p] * 5 + [i] * 5 + [p, p], i),
             "moe_combine": ([p] * 5 + [i] * 4 + [p, p], i),
+            "moe_forward_fp8": ([p] * 16 + [i] * 6 + [p, p, z, p], i),
+            "moe_e4m3_to_f32": ([p, p, i64, p], i),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -143,6 +146,19 @@ def moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, 
     _check(lib().moe_forward(_p(x), _p(w_router), _p(router_bias), _p(w_gate), _p(w_up), _p(w_down),
                              _p(ws_gate), _p(ws_up), _p(ws_down), _p(w_sg), T, H, E, k, I, I_s,
                              _p(y), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_forward_fp8(x, w_router, router_bias, q_gate, sc_gate, q_up, sc_up, q_down, sc_down,
+                    qs_gate, ssc_gate, qs_up, ssc_up, qs_down, ssc_down, w_sg,
+                    T, H, E, k, I, I_s, y, workspace, ws_bytes: int, stream=None):
+    _check(lib().moe_forward_fp8(_p(x), _p(w_router), _p(router_bias), _p(q_gate), _p(sc_gate), _p(q_up),
+                                 _p(sc_up), _p(q_down), _p(sc_down), _p(qs_gate), _p(ssc_gate), _p(qs_up),
+                                 _p(ssc_up), _p(qs_down), _p(ssc_down), _p(w_sg), T, H, E, k, I, I_s,
+                                 _p(y), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_e4m3_to_f32(codes, out, n: int, stream=None):
+    _check(lib().moe_e4m3_to_f32(_p(codes), _p(out), n, _stream(stream)))
 
 
 def moe_route(x, w_router, router_bias, w_sg, T, H, E, k, ids, w, s, logits, stream=None):

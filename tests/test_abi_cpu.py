@@ -144,3 +144,36 @@ def test_stage_argument_errors(L):
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="host without a GPU only")
 def test_valid_call_without_gpu_reports_arch(L):
     assert fwd(L) == moe.MOE_ERR_ARCH
+
+
+def fwd8(L, **kw):
+    """moe_forward_fp8 with fake (never dereferenced) aligned pointers; overrides by name."""
+    p = 1 << 12
+    a = dict(x=p, wr=p, b=None, qg=p, sg=p, qu=p, su=p, qd=p, sd=p, qsg=None, ssg=None, qsu=None, ssu=None,
+             qsd=None, ssd=None, wsg=None, T=4, H=256, E=8, k=2, I=128, I_s=0, y=p, ws=p, nbytes=1 << 30)
+    a.update(kw)
+    return L.moe_forward_fp8(a["x"], a["wr"], a["b"], a["qg"], a["sg"], a["qu"], a["su"], a["qd"], a["sd"],
+                             a["qsg"], a["ssg"], a["qsu"], a["ssu"], a["qsd"], a["ssd"], a["wsg"],
+                             a["T"], a["H"], a["E"], a["k"], a["I"], a["I_s"], a["y"], a["ws"], a["nbytes"], None)
+
+
+def test_forward_fp8_argument_errors(L):
+    p = 1 << 12
+    assert fwd8(L, T=0) == moe.MOE_OK
+    assert fwd8(L, qg=None) == moe.MOE_ERR_NULL
+    assert fwd8(L, sd=None) == moe.MOE_ERR_NULL  # a scale is missing
+    assert fwd8(L, T=moe.FP8_MAX_T + 1) == moe.MOE_ERR_SHAPE
+    assert "FP8" in moe.last_error()
+    assert fwd8(L, qsg=p) == moe.MOE_ERR_SHAPE  # shared tensors with I_s = 0
+    assert fwd8(L, I_s=128, qsg=p, ssg=p, qsu=p, ssu=p, qsd=p, ssd=p) == moe.MOE_ERR_NULL  # w_sg missing
+    assert fwd8(L, sg=p + 4) == moe.MOE_ERR_ALIGN
+    assert fwd8(L, nbytes=100) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_e4m3_to_f32(p, p, -1, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_e4m3_to_f32(None, p, 8, None) == moe.MOE_ERR_NULL
+    assert L.moe_e4m3_to_f32(None, None, 0, None) == moe.MOE_OK
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="host without a GPU only")
+def test_valid_fp8_call_without_gpu_reports_arch(L):
+    assert fwd8(L) == moe.MOE_ERR_ARCH
+    assert fwd8(L, T=1) == moe.MOE_ERR_ARCH

@@ -1,0 +1,175 @@
+"""GPU parity of the FP8-weight path (moe_forward_fp8, moe_e4m3_to_f32) against the oracle.
+
+Expert weights are OCP FP8 E4M3 codes with one fp32 scale per output row
+(kongchang.com "GFX1151 engine", section on the two weight formats).  The
+single-token and small-batch kernels are checked against the oracle's FP8
+layer under the BF16 tolerance, and against the BF16 kernels bitwise where
+the dequantised weights are exact in BF16 and the scales powers of two.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_moe_layer_03_amd import moe, synth
+from sparse_moe_layer_03_amd.layer import DeviceLayer
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return G.torch_cuda()
+
+
+@pytest.fixture(scope="module")
+def fp8_layer(torch):
+    """Full-shape layer (hidden 2048, 256 experts, top-8, FFN 512, shared 512) with FP8 expert weights."""
+    G.say("[setup] quantising the full-shape weights to FP8 and uploading them")
+    return DeviceLayer(G.full_fp8_weights(0), k=8, fp8=True)
+
+
+def _fp8_layer_for(inp, fp8_layer):
+    wl = inp["wl"]
+    if (wl.H, wl.E, wl.I, wl.I_s, wl.k) == (2048, 256, 512, 512, 8):
+        import torch
+        fp8_layer.bias = None if inp["bias"] is None else torch.from_numpy(inp["bias"]).to("cuda:0")
+        return fp8_layer
+    return DeviceLayer.from_inputs(inp, fp8=True)
+
+
+def test_e4m3_conversion_every_code(torch):
+    """The device conversion of every E4M3 code (with a ragged tail) equals the oracle's decoding."""
+    codes = np.concatenate([np.tile(np.arange(256, dtype=np.uint8), 4), np.array([0x7E, 0x01, 0x80, 0xFF, 0x38],
+                                                                                  np.uint8)])
+    n = codes.size
+    G.say(f"[e4m3] n={n}")
+    d_codes = torch.from_numpy(codes).cuda()
+    out = torch.full((n,), 7.0, dtype=torch.float32, device="cuda")
+    moe.moe_e4m3_to_f32(d_codes, out, n)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = oracle.e4m3_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fp8_decode_parity(torch, fp8_layer, seed):
+    """T = 1 with FP8 expert weights vs the oracle's FP8 layer."""
+    G.say(f"[fp8-decode] seed={seed}")
+    inp = G.with_fp8(G.inputs("decode", 1, seed=0))
+    inp["x"] = synth._draw_bf16(200 + seed, "x", (1, 2048), 1.0)
+    lay = _fp8_layer_for(inp, fp8_layer)
+    y = lay.forward(G.to_dev_x(inp))
+    ids = lay.forward_ids(1).cpu().numpy()
+    torch.cuda.synchronize()
+    y_ref, _ = G.reference_y(inp, ids, f"fp8 decode seed {seed}", fp8=True)
+    G.check_y(G.y_to_f64(y), y_ref, f"fp8 decode seed {seed}")
+
+
+FP8_CASES = [
+    ("full-T1-bias", dict(wl="prefill8k", T=1)),
+    ("full-T2", dict(wl="prefill1k", T=2)),
+    ("full-T8", dict(wl="prefill1k", T=8)),
+    ("full-T32-bias", dict(wl="prefill8k", T=32)),
+    ("k16-T1", dict(wl=synth.Workload("f16", T=1, H=512, E=32, k=16, I=256, I_s=128))),
+    ("k16-T20", dict(wl=synth.Workload("f16b", T=20, H=512, E=32, k=16, I=256, I_s=128))),
+    ("noshared-T1", dict(wl=synth.Workload("f9", T=1, H=256, E=12, k=9, I=384, I_s=0))),
+    ("noshared-T7", dict(wl=synth.Workload("f9b", T=7, H=256, E=12, k=9, I=384, I_s=0))),
+    ("wide-T1", dict(wl=synth.Workload("fw", T=1, H=4096, E=64, k=4, I=640, I_s=256, bias="normal"))),
+    ("wide-T10", dict(wl=synth.Workload("fwb", T=10, H=4096, E=64, k=4, I=640, I_s=256, bias="normal"))),
+    ("k1-T5", dict(wl=synth.Workload("f1", T=5, H=256, E=8, k=1, I=128, I_s=128))),
+]
+
+
+def _case_inputs(case, seed=4):
+    wl = case["wl"]
+    if isinstance(wl, str):
+        return G.with_fp8(G.inputs(wl, case.get("T")))
+    return synth.add_fp8_weights(synth.make_inputs(wl, seed=seed))
+
+
+@pytest.mark.parametrize("label,case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fp8_parity(torch, fp8_layer, label, case):
+    """moe_forward_fp8 at 1..32 tokens vs the oracle's FP8 layer; ids exact outside near-ties."""
+    inp = _case_inputs(case)
+    wl = inp["wl"]
+    T = inp["x"].shape[0]
+    G.say(f"[fp8] {label}: T={T} H={wl.H} E={wl.E} k={wl.k} I={wl.I} I_s={wl.I_s}")
+    lay = _fp8_layer_for(inp, fp8_layer)
+    y = lay.forward(G.to_dev_x(inp))
+    ids = lay.forward_ids(T).cpu().numpy()
+    torch.cuda.synchronize()
+    y_ref, _ = G.reference_y(inp, ids, f"fp8 {label}", fp8=True)
+    G.check_y(G.y_to_f64(y), y_ref, f"fp8 {label}")
+
+
+def _exact_fp8(inp, seed):
+    """Random non-NaN codes and power-of-two row scales, and the BF16 matrices they dequantise to (exactly)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    out = dict(inp)
+    for key in synth.FP8_KEYS:
+        if inp.get(key) is None:
+            out[key + "_fp8"] = out[key + "_scale"] = None
+            continue
+        shape = inp[key].shape
+        # magnitudes drawn like quantised N(0,1) rows: codes 0x20..0x5F, random signs
+        codes = (rng.integers(0x20, 0x60, size=shape, dtype=np.uint8) |
+                 (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7)).astype(np.uint8)
+        scale = np.ldexp(1.0, rng.integers(-10, -6, size=shape[:-1])).astype(np.float32)
+        vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy() * scale[..., None]
+        out[key + "_fp8"], out[key + "_scale"] = codes, scale
+        out[key] = synth.f32_to_bf16_bits(vals.astype(np.float32))
+        assert np.array_equal(synth.bf16_bits_to_f32(out[key]), vals)
+    return out
+
+
+@pytest.mark.parametrize("T", [1, 2, 13, 32])
+def test_fp8_equals_bf16_kernels_on_exact_weights(torch, T):
+    """With power-of-two row scales every dequantised weight is exact in BF16 and every scaled sum is
+    exact, so the FP8 kernels give bitwise the BF16 kernels' output on those BF16 weights."""
+    wl = synth.Workload("fx", T=T, H=1024, E=32, k=6, I=384, I_s=256, bias="normal")
+    inp = _exact_fp8(synth.make_inputs(wl, seed=7), seed=T)
+    G.say(f"[fp8-vs-bf16] T={T}")
+    x = G.to_dev_x(inp)
+    y8 = DeviceLayer.from_inputs(inp, fp8=True).forward(x)
+    y16 = DeviceLayer.from_inputs(inp).forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y8.view(torch.int16), y16.view(torch.int16))
+
+
+def test_fp8_graph_replay_and_determinism(torch, fp8_layer):
+    """FP8 decode and small-batch calls: eager repeats and HIP-graph replays are bitwise identical."""
+    for T in (1, 16):
+        inp = G.with_fp8(G.inputs("prefill1k", T))
+        lay = _fp8_layer_for(inp, fp8_layer)
+        x = G.to_dev_x(inp)
+        y1 = lay.forward(x).clone()
+        y2 = lay.forward(x).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+        yg = torch.empty_like(y1)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            lay.forward(x, y=yg)
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            lay.forward(x, y=yg)
+        for i in range(3):
+            yg.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            _ = (x.float() * 2).sum().item()
+            assert torch.equal(yg.view(torch.int16), y1.view(torch.int16)), f"T={T} replay {i}"
+
+
+def test_fp8_rejects_large_T(torch, fp8_layer):
+    inp = G.with_fp8(G.inputs("prefill1k", moe.FP8_MAX_T + 1))
+    with pytest.raises(moe.MoEError):
+        _fp8_layer_for(inp, fp8_layer).forward(G.to_dev_x(inp))
