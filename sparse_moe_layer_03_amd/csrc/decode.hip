@@ -173,11 +173,12 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
     const WE* sg = static_cast<const WE*>(W.s_gate);
     const WE* su = static_cast<const WE*>(W.s_up);
     for (int i = blockIdx.x * 3 + wave - 1; i < I_s; i += 3 * gridDim.x) {
+      const float scg = Q ? W.ssc_gate[i] : 1.0f, scu = Q ? W.ssc_up[i] : 1.0f;  // issued with the row loads
       float g, u;
       row_dots<Q>(nullptr, x, sg + (size_t)i * H, su + (size_t)i * H, H, threadIdx.x & 63, g, u);
       if (Q) {
-        g *= W.ssc_gate[i];
-        u *= W.ssc_up[i];
+        g *= scg;
+        u *= scu;
       }
       if ((threadIdx.x & 63) == 0) d.hs[i] = silu(g) * u;
     }
@@ -196,6 +197,7 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
   const size_t rix = (size_t)sel_e[rr / I] * I + rr % I;  // row of W_gate / W_up
   const WC* gp = reinterpret_cast<const WC*>(static_cast<const WE*>(W.gate) + rix * H);
   const WC* up = reinterpret_cast<const WC*>(static_cast<const WE*>(W.up) + rix * H);
+  const float scg = Q ? W.sc_gate[rix] : 1.0f, scu = Q ? W.sc_up[rix] : 1.0f;  // in flight with the rows
   float g = 0.0f, u = 0.0f;
   for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
     WC a[4], b[4];
@@ -219,8 +221,8 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
   }
   float gs = wave_sum(g), us = wave_sum(u);
   if (Q) {
-    gs *= W.sc_gate[rix];
-    us *= W.sc_up[rix];
+    gs *= scg;
+    us *= scu;
   }
   if (row < k * I && lane == 0) d.h[row] = silu(gs) * us;
 }
@@ -250,6 +252,11 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
   }
 #pragma unroll
   for (int j = 0; j < KT; ++j) ids[j] = j < k ? ids[j] : 0;  // keep unused rows in range
+  // row scales, loaded with the first weight rows rather than after the sums
+  float scd[KT], scs = 1.0f;
+#pragma unroll
+  for (int j = 0; j < KT; ++j) scd[j] = Q ? W.sc_down[(size_t)ids[j] * H + c0] : 1.0f;
+  if (Q && I_s > 0) scs = W.ssc_down[c0];
   float part[KT + 1];
 #pragma unroll
   for (int j = 0; j <= KT; ++j) part[j] = 0.0f;
@@ -303,12 +310,12 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
   for (int j = 0; j < KT; ++j)
     if (j < k) {
       float oj = wave_sum(part[j]);
-      if (Q) oj *= W.sc_down[(size_t)ids[j] * H + c0];
+      if (Q) oj *= scd[j];
       yv += wsel[j] * oj;  // rank order
     }
   if (I_s > 0) {
     float os = wave_sum(part[KT]);
-    if (Q) os *= W.ssc_down[c0];
+    if (Q) os *= scs;
     yv += d.s[0] * os;
   }
   if (lane == 0) y[c0] = f32_to_bf16(yv);
