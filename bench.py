@@ -130,6 +130,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight calls")
+    ap.add_argument("--no-chunks", action="store_true", help="skip the bucketed-prefill runner")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--kernel", choices=["gate_up"], default=None,
@@ -268,6 +269,40 @@ def main():
     }
     del layers, bufs
     torch.cuda.empty_cache()
+
+    # ------------------------------------- prefill through buckets (runner)
+    if not args.no_chunks:
+        from sparse_moe_layer_03_amd.layer import PrefillRunner
+        Tc = 16380  # just under two 8192-token buckets: the last segment is padded
+        xc = to_device_bf16(synth._draw_bf16(3, "x", (Tc, H), 1.0), dev)
+        yc = torch.empty((Tc, H), dtype=torch.bfloat16, device=dev)
+        run = PrefillRunner(base)
+        segs, lens = run.plan(Tc)
+        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+        def timed(fn, reps=10):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ce0.record(stream)
+            for _ in range(reps):
+                fn()
+            ce1.record(stream)
+            torch.cuda.synchronize()
+            return ce0.elapsed_time(ce1) / reps
+
+        run_ms = timed(lambda: run.run(xc, yc))
+        one_ms = timed(lambda: base.forward(xc, yc))  # one moe_forward call over all Tc tokens
+        run.close()
+        out["chunks"] = {"workload": f"T={Tc} tokens (prefill8k layer), buckets {list(run.buckets)}",
+                         "segments": segs, "segment_tokens": lens,
+                         "runner_ms": run_ms, "runner_tokens_per_s": Tc / (run_ms * 1e-3),
+                         "single_call_ms": one_ms, "single_call_tokens_per_s": Tc / (one_ms * 1e-3)}
+        log(f"[bench] T={Tc} through buckets {segs}: {run_ms:.3f} ms ({Tc / run_ms / 1e3:.2f} M tok/s); "
+            f"one moe_forward call {one_ms:.3f} ms")
+        del xc, yc
+        base._ws = None
+        torch.cuda.empty_cache()
 
     if args.calib_copy:
         a = torch.ones(64 << 20, dtype=torch.float32, device=dev)

@@ -23,7 +23,9 @@
  *     back to the host, so a call can be captured in a HIP graph.
  *   - The caller owns every buffer, including `workspace`.  The library never
  *     allocates or frees device memory and keeps no state between calls
- *     except a per-device cached architecture check.
+ *     except a per-device cached architecture check -- apart from the
+ *     prefill runner (moe_prefill_runner_*), which owns its buffers and
+ *     graphs.
  *   - Argument errors are reported before anything is enqueued.  No C++
  *     exception crosses this boundary.  A status other than MOE_OK leaves the
  *     outputs unspecified; moe_last_error() gives a message (thread-local).
@@ -173,6 +175,58 @@ int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* ro
  * aligned; n >= 0 (0: no-op).  For checking the conversion.
  */
 int moe_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream);
+
+/*
+ * Prefill of any length through fixed-size buckets.  guanjiawei.ai "AIMA
+ * AMD395 Qwen3.6-35B-A3B" (data-path section) decomposes any prompt into
+ * optimised 8192- and 1024-token tiles and a tail; its runtime section keeps
+ * 1024/2048/4096/8192-token buckets resident, covers each prompt with the
+ * smallest bucket total and pads only the final segment.
+ *
+ * moe_bucket_plan: the segments covering T tokens with the given bucket sizes
+ *   (host only, no device call).  Rule: the smallest total of bucket sizes
+ *   that is >= T; among covers with that total, the fewest segments; among
+ *   those, the lexicographically largest sequence in descending order.  The
+ *   segments come in that (descending) order; every segment is full except
+ *   the last, which holds T minus the others' tokens (> 0).
+ *   buckets [n_buckets] host ints: 1 <= n_buckets <= 16, distinct, each in
+ *   [1, 65536], largest / gcd(all) <= 1022.  Outputs (host): *n_segs (set
+ *   even when it exceeds max_segs, which is then MOE_ERR_SHAPE),
+ *   seg_bucket[i] = bucket size and seg_len[i] = real tokens of segment i.
+ *   T = 0 gives no segments.
+ */
+int moe_bucket_plan(int T, const int* buckets, int n_buckets, int* seg_bucket, int* seg_len, int max_segs,
+                    int* n_segs);
+
+/*
+ * A prefill runner owns, on the device current at creation: a staging input
+ * and output of the largest bucket's size, one workspace and, per bucket, an
+ * instantiated HIP graph of one moe_forward call over that many tokens (the
+ * weights given here, which must stay valid while the runner lives).
+ *   moe_prefill_runner_create: weights and shapes as moe_forward (BF16);
+ *     buckets as moe_bucket_plan (each bucket must be a valid moe_forward
+ *     size).  Allocates device memory and captures the graphs (the only
+ *     entry points that allocate).  *out = NULL on error.
+ *   moe_prefill_runner_run: y [T,H] = the layer on x [T,H] (device, 16-byte
+ *     aligned), enqueued on `stream`, per segment of moe_bucket_plan(T): a
+ *     full segment runs the bucket's launches on its rows of x and y
+ *     directly; the partial last segment is gathered into the staging input
+ *     (its padding rows repeat the segment's own rows), run by the bucket's
+ *     graph, and its real rows are copied into y.  The result of every token is that of
+ *     moe_forward on the token (tokens do not interact).  Calls on one runner
+ *     share its buffers: keep them on one stream (or ordered).  The current
+ *     device must be the runner's.
+ *   moe_prefill_runner_destroy: frees everything; call it after the last run
+ *     has completed.  NULL is a no-op.
+ */
+typedef struct moe_prefill_runner moe_prefill_runner;
+int moe_prefill_runner_create(const uint16_t* w_router, const float* router_bias,
+                              const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                              const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
+                              const uint16_t* w_sg, int H, int E, int k, int I, int I_s,
+                              const int* buckets, int n_buckets, moe_prefill_runner** out);
+int moe_prefill_runner_run(moe_prefill_runner* runner, const uint16_t* x, int T, uint16_t* y, void* stream);
+int moe_prefill_runner_destroy(moe_prefill_runner* runner);
 
 /*
  * Router stage: logits (fp32 accumulation of bf16 products), optional bias,

@@ -136,6 +136,11 @@ Layout layout(int T, int H, int E, int k, int I, int I_s) {
 
 }  // namespace
 
+int moe::set_error(int code, const char* msg) {
+  if (code == MOE_OK) return ok();
+  return fail(code, "%s", msg);
+}
+
 extern "C" {
 
 const char* moe_status_str(int status) {

@@ -106,6 +106,10 @@ struct ExpertWeights {
   bool fp8;
 };
 
+// Sets the thread's error message returned by moe_last_error() (cleared for
+// MOE_OK) and returns `code`.
+int set_error(int code, const char* msg);
+
 // Host-side launch helpers (defined in the .hip files).
 // Router GEMM over token tiles: fp32 logits (+ bias, -0 -> +0; stored when
 // logits is not NULL), the top-k ids and renormalised weights of every token

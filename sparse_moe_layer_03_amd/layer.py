@@ -187,3 +187,45 @@ class DeviceLayer:
         self.run_down(T, b, stream)
         self.run_combine(T, b, stream)
         return b
+
+
+class PrefillRunner:
+    """Prefill of any length through per-bucket HIP graphs (moe_prefill_runner_*) for a DeviceLayer's
+    BF16 weights.  The layer must outlive the runner."""
+
+    PAGE_BUCKETS = (1024, 2048, 4096, 8192)
+
+    def __init__(self, layer: DeviceLayer, buckets=PAGE_BUCKETS):
+        s = layer.shapes
+        W = layer.w
+        self.layer = layer
+        self.buckets = tuple(buckets)
+        self.handle = moe.moe_prefill_runner_create(W["w_router"], layer.bias, W["w_gate"], W["w_up"], W["w_down"],
+                                                    W["ws_gate"], W["ws_up"], W["ws_down"], W["w_sg"], s.H, s.E,
+                                                    s.k, s.I, s.I_s, list(self.buckets))
+
+    def plan(self, T: int):
+        return moe.moe_bucket_plan(T, list(self.buckets))
+
+    def run(self, x, y=None, stream=None):
+        """y = layer(x) for a [T, H] bfloat16 device tensor, segment by segment."""
+        import torch
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.layer.shapes.H), dtype=torch.bfloat16, device=self.layer.device)
+        moe.moe_prefill_runner_run(self.handle, x, T, y, stream)
+        return y
+
+    def close(self):
+        """Free the runner's buffers and graphs (after its last run has completed)."""
+        if self.handle:
+            import torch
+            torch.cuda.synchronize(self.layer.device)
+            moe.moe_prefill_runner_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -29,6 +29,7 @@ EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_align_tile_rows", "moe_align_small_tile_rows", "moe_align_max_rows",
     "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward_ids_offset", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
     "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine", "moe_forward_fp8", "moe_e4m3_to_f32",
+    "moe_bucket_plan", "moe_prefill_runner_create", "moe_prefill_runner_run", "moe_prefill_runner_destroy",
 )
 
 
@@ -69,6 +70,10 @@ def lib():
             "moe_combine": ([p] * 5 + [i] * 4 + [p, p], i),
             "moe_forward_fp8": ([p] * 16 + [i] * 6 + [p, p, z, p], i),
             "moe_e4m3_to_f32": ([p, p, i64, p], i),
+            "moe_bucket_plan": ([i, p, i, p, p, i, p], i),
+            "moe_prefill_runner_create": ([p] * 9 + [i] * 5 + [p, i, p], i),
+            "moe_prefill_runner_run": ([p, p, i, p, p], i),
+            "moe_prefill_runner_destroy": ([p], i),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -159,6 +164,42 @@ def moe_forward_fp8(x, w_router, router_bias, q_gate, sc_gate, q_up, sc_up, q_do
 
 def moe_e4m3_to_f32(codes, out, n: int, stream=None):
     _check(lib().moe_e4m3_to_f32(_p(codes), _p(out), n, _stream(stream)))
+
+
+def moe_bucket_plan(T: int, buckets):
+    """(segment bucket sizes, real tokens per segment) covering T tokens (host only)."""
+    nb = len(buckets)
+    barr = (C.c_int * max(nb, 1))(*buckets)
+    n = C.c_int(0)
+    cap = 64
+    while True:
+        sb, sl = (C.c_int * cap)(), (C.c_int * cap)()
+        rc = lib().moe_bucket_plan(T, barr, nb, sb, sl, cap, C.byref(n))
+        if rc == MOE_ERR_SHAPE and n.value > cap:
+            cap = n.value
+            continue
+        _check(rc)
+        return list(sb[:n.value]), list(sl[:n.value])
+
+
+def moe_prefill_runner_create(w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg,
+                              H, E, k, I, I_s, buckets) -> int:
+    """Opaque runner handle (an int); free it with moe_prefill_runner_destroy."""
+    nb = len(buckets)
+    barr = (C.c_int * max(nb, 1))(*buckets)
+    out = C.c_void_p()
+    _check(lib().moe_prefill_runner_create(_p(w_router), _p(router_bias), _p(w_gate), _p(w_up), _p(w_down),
+                                           _p(ws_gate), _p(ws_up), _p(ws_down), _p(w_sg), H, E, k, I, I_s,
+                                           barr, nb, C.byref(out)))
+    return out.value
+
+
+def moe_prefill_runner_run(runner: int, x, T: int, y, stream=None):
+    _check(lib().moe_prefill_runner_run(runner, _p(x), T, _p(y), _stream(stream)))
+
+
+def moe_prefill_runner_destroy(runner: Optional[int]):
+    _check(lib().moe_prefill_runner_destroy(runner))
 
 
 def moe_route(x, w_router, router_bias, w_sg, T, H, E, k, ids, w, s, logits, stream=None):

@@ -1,0 +1,92 @@
+"""Bucket composition (host only): the oracle's brute force pinned to the closed form for the
+1024/2048/4096/8192 buckets, and the library's planner checked against the oracle."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle.bucket_plan import bucket_plan as oracle_plan
+from sparse_moe_layer_03_amd import moe
+
+PAGE_BUCKETS = (1024, 2048, 4096, 8192)
+# lengths just off a bucket multiple (the near-bucket prompt lengths of the
+# engine's release notes), plus exact multiples, tiny and mixed lengths
+PAGE_T = [1, 2, 1023, 1024, 1025, 2047, 3072, 5000, 8191, 8192, 8193, 10000, 12345, 15361, 16380, 16384, 20000,
+          32758, 65519]
+
+
+def closed_form(T, unit=1024, top=8):
+    """Buckets unit * 2^j up to unit * top: n = ceil(T / unit) units; as many of the largest as fit, then
+    the binary digits of the remainder, largest first."""
+    n = -(-T // unit)
+    seq = [unit * top] * (n // top)
+    r = n % top
+    for j in range(int(math.log2(top)) - 1, -1, -1):
+        if r >> j & 1:
+            seq.append(unit << j)
+    lens, left = [], T
+    for b in seq:
+        lens.append(min(left, b))
+        left -= lens[-1]
+    return seq, lens
+
+
+@pytest.mark.parametrize("T", PAGE_T)
+def test_oracle_matches_closed_form(T):
+    assert oracle_plan(T, PAGE_BUCKETS) == closed_form(T)
+
+
+def test_oracle_small_cases_by_hand():
+    assert oracle_plan(0, (4, 6)) == ([], [])
+    assert oracle_plan(7, (4, 6)) == ([4, 4], [4, 3])   # total 8 < 6 + 4 = 10
+    assert oracle_plan(10, (4, 6)) == ([6, 4], [6, 4])  # exact; [6, 4] before [4, 4, ...]
+    assert oracle_plan(5, (3, 5)) == ([5], [5])
+    assert oracle_plan(9, (3, 5)) == ([3, 3, 3], [3, 3, 3])  # 9 exact beats 10 = 5 + 5
+    assert oracle_plan(12, (4, 6, 8)) == ([8, 4], [8, 4])    # total 12: [8, 4] beats [6, 6] (largest first)
+
+
+@pytest.mark.parametrize("T", PAGE_T + [131037, 262143, 1 << 20])
+def test_library_page_buckets(T):
+    got = moe.moe_bucket_plan(T, list(PAGE_BUCKETS))
+    assert got == closed_form(T)
+    seq, lens = got
+    assert sum(lens) == T and all(l == b for l, b in zip(lens[:-1], seq[:-1])) and 0 < lens[-1] <= seq[-1]
+
+
+def test_library_matches_oracle_random_sets():
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        nb = int(rng.integers(1, 4))
+        bs = sorted(set(int(v) for v in rng.integers(1, 40, size=nb)), reverse=True)
+        T = int(rng.integers(0, 120))
+        got = moe.moe_bucket_plan(T, bs)
+        assert got == oracle_plan(T, bs), (T, bs, got)
+
+
+def test_library_bucket_order_does_not_matter():
+    assert moe.moe_bucket_plan(10000, [8192, 1024, 4096, 2048]) == moe.moe_bucket_plan(10000, [1024, 2048, 4096, 8192])
+
+
+def test_library_rejects_bad_buckets():
+    for bs in ([], [0, 4], [4, 4], [70000], [1, 2000]):
+        with pytest.raises(moe.MoEError):
+            moe.moe_bucket_plan(10, bs)
+    with pytest.raises(moe.MoEError):
+        moe.moe_bucket_plan(-1, [4])
+
+
+def test_runner_argument_errors():
+    L = moe.lib()
+    import ctypes as C
+    out = C.c_void_p(123)
+    b = (C.c_int * 2)(64, 128)
+    p = 1 << 12
+    assert L.moe_prefill_runner_create(p, None, p, p, p, None, None, None, None, 256, 8, 2, 128, 0, b, 2, None) == \
+        moe.MOE_ERR_NULL
+    assert L.moe_prefill_runner_create(p, None, p, p, p, None, None, None, None, 256, 8, 2, 128, 0, b, 0,
+                                       C.byref(out)) == moe.MOE_ERR_SHAPE
+    assert out.value is None
+    assert L.moe_prefill_runner_create(p, None, p, p, p, p, None, None, None, 256, 8, 2, 128, 0, b, 2,
+                                       C.byref(out)) == moe.MOE_ERR_SHAPE  # shared tensor with I_s = 0
+    assert L.moe_prefill_runner_run(None, p, 10, p, None) == moe.MOE_ERR_NULL
+    assert L.moe_prefill_runner_destroy(None) == moe.MOE_OK
