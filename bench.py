@@ -466,10 +466,32 @@ def main():
                                "touched_experts": float(np.mean(touched)), "bytes_per_call": qb,
                                "GB_per_s": qb / (qus * 1e-6) / 1e9, "hbm_frac": qb / (qus * 1e-6) / 1e9 / PEAK_HBM_GBS}
                 log(f"[bench] FP8 weights T={Tb}: {qus:.1f} us/call, {f8[str(Tb)]['GB_per_s']:.0f} GB/s")
+            # the 8192-token prefill with FP8 expert weights (tiled GEMMs on widened codes)
+            Q0 = qcopies[0]
+            yq = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            pws, pws_bytes = qbase.workspace(T)
+
+            def qprefill():
+                moe.moe_forward_fp8(x, Wr, base.bias, Q0["w_gate"], Q0["w_gate_scale"], Q0["w_up"], Q0["w_up_scale"],
+                                    Q0["w_down"], Q0["w_down_scale"], Q0["ws_gate"], Q0["ws_gate_scale"], Q0["ws_up"],
+                                    Q0["ws_up_scale"], Q0["ws_down"], Q0["ws_down_scale"], Wsg, T, H, E, k, I, I_s,
+                                    yq, pws, pws_bytes)
+            for _ in range(5):
+                qprefill()
+            torch.cuda.synchronize()
+            d0.record()
+            for _ in range(10):
+                qprefill()
+            d1.record()
+            torch.cuda.synchronize()
+            qms = d0.elapsed_time(d1) / 10
+            log(f"[bench] FP8 weights prefill T={T}: {qms:.3f} ms/step ({T / qms / 1e3:.2f} M tok/s)")
             out["fp8"] = {"workload": "1, 2, 8 and 32 tokens per call, decode-config shapes, expert weights as OCP "
-                                      "FP8 E4M3 with one fp32 scale per output row, no router bias",
+                                      "FP8 E4M3 with one fp32 scale per output row, no router bias; and the "
+                                      f"{T}-token prefill workload (router bias) with the same FP8 weights",
                           "timing": f"HIP graph of {nx} (T=1) or 16 calls over {len(qcopies)} weight copies, "
-                                    f"{reps} replays", "per_T": f8}
+                                    f"{reps} replays; prefill: 10 eager steps after 5", "per_T": f8,
+                          "prefill": {"T": T, "ms_per_step": qms, "tokens_per_s": T / (qms * 1e-3)}}
             del qcopies, qbase
             torch.cuda.empty_cache()
 

@@ -155,11 +155,13 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
  *          or all set; everything else as in moe_forward.
  * Workspace: moe_workspace_size(T,H,E,k,I,I_s) bytes, 256-byte aligned;
  *          moe_forward_ids_offset() locates the selected ids as for moe_forward.
- * Sizes: 1 <= T <= MOE_FP8_MAX_T (the single-token and small-batch kernels,
- *          where reading the weights bounds the step); larger T gives
- *          MOE_ERR_SHAPE.  Codes that are NaN give NaN outputs (not checked).
+ * Paths: T == 1 and T <= MOE_SMALL_BATCH_MAX_T run the single-token and
+ *          small-batch kernels on the codes (8 bytes per 8 weights); larger
+ *          T runs the tiled GEMMs with tiles of at most 128 rows, the codes
+ *          widened exactly to bf16 on their way into on-chip memory and the
+ *          row scales applied to the accumulators.  Codes that are NaN give
+ *          NaN outputs (not checked).
  */
-#define MOE_FP8_MAX_T 32
 int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
                     const uint8_t* q_gate, const float* sc_gate, const uint8_t* q_up, const float* sc_up,
                     const uint8_t* q_down, const float* sc_down,

@@ -109,6 +109,13 @@ struct GemmParams {
   float* gate_s;         // ROUTER: s = sigmoid(x . w_sg) [T] (when w_sg is given)
   int32_t* ids;          // ROUTER: top-k experts [T, k]
   float* wts;            // ROUTER: their renormalised weights [T, k]
+  // FP8 weights (kernels instantiated with Q): b0/b1/bs0/bs1 then point at
+  // E4M3 codes (one byte per weight), and each weight row has an fp32 scale:
+  // routed sc0/sc1 [E * N], shared ssc0/ssc1 [N_s]
+  const float* sc0;
+  const float* sc1;
+  const float* ssc0;
+  const float* ssc1;
 };
 
 // 16-byte chunk swizzles of an LDS row of KCH chunks.  Any 16 consecutive rows
@@ -209,21 +216,49 @@ __device__ __forceinline__ const uint16_t* a_row(const GemmParams& p, const Item
 // Weight row of tile B-row j (0..255) and whether it carries data.  For
 // gate/up items rows 0..127 are gate rows and 128..255 the up rows of the
 // same 128 intermediate columns; router rows past E point at row 0.
-template <int MODE>
+// With Q the matrices hold one byte per weight (E4M3 codes); the returned
+// pointer is then a byte address in the same type.
+template <int MODE, bool Q = false>
 __device__ __forceinline__ const uint16_t* b_row(const GemmParams& p, const Item it, int j, bool& ok) {
+  constexpr size_t EB = Q ? 1 : 2;  // bytes per weight
   ok = true;
   if (MODE == ROUTER && it.kind == K_ROUTER) {
     ok = j < p.E;
     return p.br + (size_t)(ok ? j : 0) * p.K;
   }
+  size_t row;  // weight row within the matrix
+  const uint16_t* m;
   if (it.kind == K_GU) {
-    const size_t col = (size_t)it.nb * 128 + (j & 127);
-    const uint16_t* base = (j < 128) ? (it.dense ? p.bs0 : p.b0 + (size_t)it.expert * p.N * p.K)
-                                     : (it.dense ? p.bs1 : p.b1 + (size_t)it.expert * p.N * p.K);
-    return base + col * p.K;
+    m = (j < 128) ? (it.dense ? p.bs0 : p.b0) : (it.dense ? p.bs1 : p.b1);
+    row = (size_t)it.nb * 128 + (j & 127);
+  } else {
+    m = it.dense ? p.bs0 : p.b0;
+    row = (size_t)it.nb * 256 + j;
   }
-  const size_t col = (size_t)it.nb * 256 + j;
-  return (it.dense ? p.bs0 : p.b0 + (size_t)it.expert * p.N * p.K) + col * p.K;
+  if (!it.dense) row += (size_t)it.expert * p.N;
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(m) + row * p.K * EB);
+}
+
+// Scale of weight row j of the item's B tile (FP8 weights), as b_row.
+template <int MODE>
+__device__ __forceinline__ float b_scale(const GemmParams& p, const Item it, int j) {
+  if (it.kind == K_GU) {
+    const float* sc = (j < 128) ? (it.dense ? p.ssc0 : p.sc0) : (it.dense ? p.ssc1 : p.sc1);
+    return sc[(it.dense ? 0 : (size_t)it.expert * p.N) + (size_t)it.nb * 128 + (j & 127)];
+  }
+  return (it.dense ? p.ssc0 : p.sc0)[(it.dense ? 0 : (size_t)it.expert * p.N) + (size_t)it.nb * 256 + j];
+}
+
+// Eight E4M3 codes -> eight bf16 (exact: every E4M3 value is a bf16), by the
+// gfx950 scaled conversion with scale 1.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(const u32x2& c) {
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    r[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q], 1.0f, false));
+    r[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[q], 1.0f, true));
+  }
+  return r;
 }
 
 // Weighted sum of token t's k expert outputs at columns ocol..ocol+7, in
@@ -456,8 +491,13 @@ constexpr size_t lds_bytes() {
 }
 
 // BM x 256 tile, K steps of BK columns, OCC workgroups per CU (register budget).
-template <int BM, int BK, int OCC, int MODE>
+// Q: the B matrices are E4M3 codes with one fp32 scale per weight row; the
+// codes are loaded as 8 bytes per 8 weights, widened to bf16 (exactly) when
+// written to LDS, and the row scales multiply the accumulators in the
+// epilogue.
+template <int BM, int BK, int OCC, int MODE, bool Q = false>
 __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmParams p) {
+  static_assert(!Q || MODE != ROUTER, "the router weights stay bf16");
   using C = Cfg<BM>;
   constexpr int KCH = BK / 8;               // 16-byte chunks per row per K step
   constexpr int RPP = C::NT / KCH;          // rows covered by one pass of the NT threads
@@ -486,22 +526,35 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     bool ok;
-    brow[i] = b_row<MODE>(p, it, trow + RPP * i, ok);
+    brow[i] = b_row<MODE, Q>(p, it, trow + RPP * i, ok);
     bmask |= ok ? (1u << i) : 0u;
   }
 
   u32x4* sA = reinterpret_cast<u32x4*>(smem);  // [2][BM*KCH]
   u32x4* sB = sA + 2 * BM * KCH;               // [2][BNB*KCH]
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 pa0[NA], pb0[NB], pa1[NA], pb1[NB];
-  auto gload = [&](u32x4 (&pa)[NA], u32x4 (&pb)[NB], int kb) {
+  typedef wchunk_t<Q> BC;  // B chunk as loaded: 8 bf16, or 8 E4M3 codes
+  u32x4 pa0[NA], pa1[NA];
+  BC pb0[NB], pb1[NB];
+  auto gload = [&](u32x4 (&pa)[NA], BC (&pb)[NB], int kb) {
     const int koff = kb * BK + chunk * 8;
 #pragma unroll
     for (int i = 0; i < NA; ++i) pa[i] = *reinterpret_cast<const u32x4*>(arow[i] + koff);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) pb[i] = *reinterpret_cast<const u32x4*>(brow[i] + koff);
+    for (int i = 0; i < NB; ++i) {
+      if constexpr (Q)
+        pb[i] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(brow[i]) + koff);
+      else
+        pb[i] = *reinterpret_cast<const u32x4*>(brow[i] + koff);
+    }
   };
-  auto sstore = [&](const u32x4 (&pa)[NA], const u32x4 (&pb)[NB], int st) {
+  auto widen = [&](const BC& c) -> u32x4 {
+    if constexpr (Q)
+      return e4m3x8_to_bf16x8(c);
+    else
+      return c;
+  };
+  auto sstore = [&](const u32x4 (&pa)[NA], const BC (&pb)[NB], int st) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       const int r = trow + RPP * i;
@@ -513,7 +566,7 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
       if constexpr (MODE == ROUTER)
         sB[st * BNB * KCH + r * KCH + swz<KCH>(r, chunk)] = ((bmask >> i) & 1u) ? pb[i] : zero;
       else
-        sB[st * BNB * KCH + r * KCH + swz<KCH>(r, chunk)] = pb[i];
+        sB[st * BNB * KCH + r * KCH + swz<KCH>(r, chunk)] = widen(pb[i]);
     }
   };
   int bb[C::NJ];
@@ -593,7 +646,7 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
   static_assert(MODE != ROUTER || BM * KCH == C::NT, "router gate needs one A chunk per thread");
   auto kloop = [&](auto LIVE) {
     constexpr bool L = decltype(LIVE)::value;
-    auto stage = [&](int st, u32x4 (&pa)[NA], u32x4 (&pb)[NB], int next_kb, int ks) {
+    auto stage = [&](int st, u32x4 (&pa)[NA], BC (&pb)[NB], int next_kb, int ks) {
       u32x4 gv = {0u, 0u, 0u, 0u};
       if constexpr (MODE == ROUTER) {
         if (p.w_sg) gv = *reinterpret_cast<const u32x4*>(p.w_sg + ks * BK + (tid % KCH) * 8);
@@ -645,6 +698,17 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
     if (p.w_sg) router_gate<BM, KCH>(p, it, gacc);
     router_epilogue<BM, C::NT, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
   } else {
+    if constexpr (Q) {
+      // row scales of this lane's B columns (one per column block j)
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) {
+        const float scl = b_scale<MODE>(p, it, bb[j] + (lane & 31));
+#pragma unroll
+        for (int m = 0; m < C::MI; ++m)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[m][j][q] *= scl;
+      }
+    }
     epilogue<BM, C::NT, MODE, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
   }
 }
@@ -961,15 +1025,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   *reinterpret_cast<u32x4*>(y + (size_t)t * H + col) = pk;
 }
 
-template <int BM, int BK, int OCC, int MODE>
+template <int BM, int BK, int OCC, int MODE, bool Q = false>
 hipError_t launch_mode(const GemmParams& p, int64_t max_items, hipStream_t st) {
   const int64_t grid = ((max_items + kNumXcd - 1) / kNumXcd) * kNumXcd;
   if (grid <= 0) return hipSuccess;
   constexpr size_t lds = lds_bytes<BM, BK, MODE>();
-  hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<BM, BK, OCC, MODE>,
+  hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<BM, BK, OCC, MODE, Q>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BK, OCC, MODE>), dim3((unsigned)grid), dim3(Cfg<BM>::NT), lds, st, p);
+  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BK, OCC, MODE, Q>), dim3((unsigned)grid), dim3(Cfg<BM>::NT), lds, st,
+                     p);
   return hipGetLastError();
 }
 
@@ -1012,17 +1077,17 @@ hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st) {
 
 constexpr int router_rows(int bm, int, int) { return bm; }
 
-template <int MODE>
+template <int MODE, bool Q = false>
 hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t st) {
   switch (BM) {
-    case 32: return launch_mode<MOE_GEMM_CFG_32, MODE>(p, max_items, st);
-    case 64: return launch_mode<MOE_GEMM_CFG_64, MODE>(p, max_items, st);
+    case 32: return launch_mode<MOE_GEMM_CFG_32, MODE, Q>(p, max_items, st);
+    case 64: return launch_mode<MOE_GEMM_CFG_64, MODE, Q>(p, max_items, st);
     case 128:
-      if constexpr (MODE == DOWN) return launch_mode<MOE_DOWN_CFG_128, MODE>(p, max_items, st);
-      return launch_mode<MOE_GEMM_CFG_128, MODE>(p, max_items, st);
+      if constexpr (MODE == DOWN) return launch_mode<MOE_DOWN_CFG_128, MODE, Q>(p, max_items, st);
+      return launch_mode<MOE_GEMM_CFG_128, MODE, Q>(p, max_items, st);
     case 256:
-      if constexpr (MODE == GATE_UP || MODE == DOWN) return launch_dma<MODE>(p, max_items, st);
-      return hipErrorInvalidValue;
+      if constexpr ((MODE == GATE_UP || MODE == DOWN) && !Q) return launch_dma<MODE>(p, max_items, st);
+      return hipErrorInvalidValue;  // FP8 weights: tiles of at most 128 rows
     default: return hipErrorInvalidValue;
   }
 }
@@ -1051,16 +1116,16 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const floa
   return launch_mode<MOE_ROUTER_CFG, ROUTER>(p, (int64_t)((T + BM - 1) / BM), st);
 }
 
-hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const int32_t* sorted,
+hipError_t launch_gate_up(const uint16_t* x, const void* w_gate, const void* w_up, const int32_t* sorted,
                           const int32_t* tiles, const int32_t* n_tiles, int T, int H, int k, int I, int BM,
-                          int64_t max_tiles, uint16_t* h, const uint16_t* ws_gate, const uint16_t* ws_up, int I_s,
-                          uint16_t* h_s, hipStream_t st) {
+                          int64_t max_tiles, uint16_t* h, const void* ws_gate, const void* ws_up, int I_s,
+                          uint16_t* h_s, hipStream_t st, const FP8Scales* q) {
   GemmParams p = {};
   p.a = x;
   p.lda = H;
   p.K = H;
-  p.b0 = w_gate;
-  p.b1 = w_up;
+  p.b0 = static_cast<const uint16_t*>(w_gate);
+  p.b1 = static_cast<const uint16_t*>(w_up);
   p.N = I;
   p.sorted = sorted;
   p.tiles = tiles;
@@ -1070,24 +1135,28 @@ hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint1
   p.out = h;
   p.ldo = I;
   if (I_s > 0) {
-    p.bs0 = ws_gate;
-    p.bs1 = ws_up;
+    p.bs0 = static_cast<const uint16_t*>(ws_gate);
+    p.bs1 = static_cast<const uint16_t*>(ws_up);
     p.N_s = I_s;
     p.out_s = h_s;
     p.ldo_s = I_s;
   }
   const int64_t shared_items = I_s > 0 ? (int64_t)((T + BM - 1) / BM) * (I_s / 128) : 0;
+  if (q) {
+    p.sc0 = q->gate, p.sc1 = q->up, p.ssc0 = q->s_gate, p.ssc1 = q->s_up;
+    return launch_bm<GATE_UP, true>(BM, p, max_tiles * (I / 128) + shared_items, st);
+  }
   return launch_bm<GATE_UP>(BM, p, max_tiles * (I / 128) + shared_items, st);
 }
 
-hipError_t launch_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,
+hipError_t launch_down(const uint16_t* h, const void* w_down, const int32_t* sorted, const int32_t* tiles,
                        const int32_t* n_tiles, int T, int H, int k, int I, int BM, int64_t max_tiles, uint16_t* o,
-                       hipStream_t st) {
+                       hipStream_t st, const FP8Scales* q) {
   GemmParams p = {};
   p.a = h;
   p.lda = I;
   p.K = I;
-  p.b0 = w_down;
+  p.b0 = static_cast<const uint16_t*>(w_down);
   p.N = H;
   p.sorted = sorted;
   p.tiles = tiles;
@@ -1096,12 +1165,16 @@ hipError_t launch_down(const uint16_t* h, const uint16_t* w_down, const int32_t*
   p.k = k;
   p.out = o;
   p.ldo = H;
+  if (q) {
+    p.sc0 = q->down;
+    return launch_bm<DOWN, true>(BM, p, max_tiles * (H / 256), st);
+  }
   return launch_bm<DOWN>(BM, p, max_tiles * (H / 256), st);
 }
 
 hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s,
-                          const uint16_t* ws_down, const float* s, int T, int H, int k, int I_s, uint16_t* y,
-                          hipStream_t st) {
+                          const void* ws_down, const float* s, int T, int H, int k, int I_s, uint16_t* y,
+                          hipStream_t st, const FP8Scales* q) {
   if (I_s == 0) {
     int64_t n = (int64_t)T * (H / 8);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, o, w, T, H, k, y);
@@ -1111,7 +1184,7 @@ hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s
   p.a = h_s;
   p.lda = I_s;
   p.K = I_s;
-  p.bs0 = ws_down;
+  p.bs0 = static_cast<const uint16_t*>(ws_down);
   p.N_s = H;
   p.T = T;
   p.k = k;
@@ -1123,6 +1196,10 @@ hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s
   p.s = s;
   constexpr int BM = 128;
   const int64_t max_items = (int64_t)((T + BM - 1) / BM) * (H / 256);
+  if (q) {
+    p.ssc0 = q->s_down;
+    return launch_mode<MOE_GEMM_CFG_128, SHARED_COMBINE, true>(p, max_items, st);
+  }
   return launch_mode<MOE_GEMM_CFG_128, SHARED_COMBINE>(p, max_items, st);
 }
 

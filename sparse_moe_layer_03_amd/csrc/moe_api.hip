@@ -102,13 +102,39 @@ struct Layout {
       off_scratch, off_h, off_hs, off_o, total;
 };
 
-Layout layout(int T, int H, int E, int k, int I, int I_s) {
+// Tile capacities for tile heights (BIG, SMALL), SMALL <= BIG.
+int64_t max_rows_for(int64_t n, int E, int64_t small) {
+  const int64_t used = n < E ? n : E;
+  return n + used * (small - 1);
+}
+int64_t max_big_for(int64_t n, int E, int64_t big, int64_t small) {
+  const int64_t used = n < E ? n : E;
+  if (small == big) return (n + used * (big - 1)) / big;  // sum of ceil(count / BIG)
+  return n / big;
+}
+int64_t max_tiles_for(int64_t n, int E, int64_t big, int64_t small) {
+  const int64_t used = n < E ? n : E;
+  if (small == big) return max_big_for(n, E, big, small);
+  int64_t max_small = used * (big / small);  // at most big/small SMALL tiles per expert
+  const int64_t bound = (n + used * (small - 1)) / small;
+  if (bound < max_small) max_small = bound;
+  return max_big_for(n, E, big, small) + max_small;
+}
+
+// FP8 expert weights run the tiled GEMMs with tiles of at most this many rows.
+constexpr int kFp8MaxTileRows = 128;
+
+// Workspace layout of the tiled path; max_tile caps the tile heights.
+Layout layout(int T, int H, int E, int k, int I, int I_s, int max_tile = 256) {
   Layout L = {};
   L.BIG = moe_align_tile_rows(T, E, k);
   L.SMALL = moe_align_small_tile_rows(T, E, k);
-  L.max_rows = moe_align_max_rows(T, E, k);
-  L.max_big = moe_align_max_big_tiles(T, E, k);
-  L.max_tiles = moe_align_max_tiles(T, E, k);
+  if (L.BIG > max_tile) L.BIG = max_tile;
+  if (L.SMALL > L.BIG) L.SMALL = L.BIG;
+  const int64_t nA = (int64_t)T * k;
+  L.max_rows = max_rows_for(nA, E, L.SMALL);
+  L.max_big = max_big_for(nA, E, L.BIG, L.SMALL);
+  L.max_tiles = max_tiles_for(nA, E, L.BIG, L.SMALL);
   L.max_small = L.max_tiles - L.max_big;
   const size_t n = (size_t)T * k;
   size_t o = 0;
@@ -176,29 +202,15 @@ int moe_align_small_tile_rows(int T, int E, int k) {
 }
 
 int64_t moe_align_max_rows(int T, int E, int k) {
-  const int64_t n = (int64_t)T * k;
-  const int64_t small = moe_align_small_tile_rows(T, E, k);
-  const int64_t used = n < E ? n : E;
-  return n + used * (small - 1);
+  return max_rows_for((int64_t)T * k, E, moe_align_small_tile_rows(T, E, k));
 }
 
 int64_t moe_align_max_big_tiles(int T, int E, int k) {
-  const int64_t n = (int64_t)T * k;
-  const int64_t big = moe_align_tile_rows(T, E, k), small = moe_align_small_tile_rows(T, E, k);
-  const int64_t used = n < E ? n : E;
-  if (small == big) return (n + used * (big - 1)) / big;  // sum of ceil(count / BIG)
-  return n / big;
+  return max_big_for((int64_t)T * k, E, moe_align_tile_rows(T, E, k), moe_align_small_tile_rows(T, E, k));
 }
 
 int64_t moe_align_max_tiles(int T, int E, int k) {
-  const int64_t n = (int64_t)T * k;
-  const int64_t big = moe_align_tile_rows(T, E, k), small = moe_align_small_tile_rows(T, E, k);
-  const int64_t used = n < E ? n : E;
-  if (small == big) return moe_align_max_big_tiles(T, E, k);
-  int64_t max_small = used * (big / small);  // at most big/small SMALL tiles per expert
-  const int64_t bound = (n + used * (small - 1)) / small;
-  if (bound < max_small) max_small = bound;
-  return moe_align_max_big_tiles(T, E, k) + max_small;
+  return max_tiles_for((int64_t)T * k, E, moe_align_tile_rows(T, E, k), moe_align_small_tile_rows(T, E, k));
 }
 
 size_t moe_align_scratch_size(int T, int E, int k) {
@@ -211,7 +223,9 @@ size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s) {
   if (check_common_shapes(T, H, E, k) != MOE_OK || check_ffn_shapes(I, I_s) != MOE_OK) return 0;
   if (T <= 1) return decode_workspace_size(H, E, k, I, I_s);
   if (T <= kSmallMaxT) return small_batch_workspace_size(T, H, E, k, I, I_s);
-  return layout(T, H, E, k, I, I_s).total;
+  // the larger of the BF16 and FP8 (capped tile height) layouts
+  const size_t a = layout(T, H, E, k, I, I_s).total, b = layout(T, H, E, k, I, I_s, kFp8MaxTileRows).total;
+  return a > b ? a : b;
 }
 
 size_t moe_forward_ids_offset(int T, int H, int E, int k, int I, int I_s) {
@@ -268,28 +282,61 @@ int moe_align(const int32_t* ids, int T, int E, int k, int32_t* counts, int32_t*
 }
 
 namespace {
-// The routed GEMMs of both tile classes.
-hipError_t launch_routed_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up,
-                                 const int32_t* sorted, const int32_t* tiles, const int32_t* n_tiles, int T, int H,
-                                 int E, int k, int I, uint16_t* h, const uint16_t* ws_gate, const uint16_t* ws_up,
-                                 int I_s, uint16_t* h_s, hipStream_t st) {
-  const int BIG = moe_align_tile_rows(T, E, k), SMALL = moe_align_small_tile_rows(T, E, k);
-  const int64_t max_big = moe_align_max_big_tiles(T, E, k), max_small = moe_align_max_tiles(T, E, k) - max_big;
-  hipError_t e = launch_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, BIG, max_big, h, ws_gate, ws_up,
-                                I_s, h_s, st);
-  if (e != hipSuccess || SMALL == BIG) return e;
-  return launch_gate_up(x, w_gate, w_up, sorted, tiles + 2 * max_big, n_tiles + 1, T, H, k, I, SMALL, max_small, h,
-                        nullptr, nullptr, 0, nullptr, st);
+// The routed GEMMs of both tile classes (tile heights and capacities of L).
+hipError_t launch_routed_gate_up(const uint16_t* x, const void* w_gate, const void* w_up, const int32_t* sorted,
+                                 const int32_t* tiles, const int32_t* n_tiles, int T, int H, int k, int I,
+                                 uint16_t* h, const void* ws_gate, const void* ws_up, int I_s, uint16_t* h_s,
+                                 const Layout& L, hipStream_t st, const FP8Scales* q = nullptr) {
+  hipError_t e = launch_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, L.BIG, L.max_big, h, ws_gate,
+                                ws_up, I_s, h_s, st, q);
+  if (e != hipSuccess || L.SMALL == L.BIG) return e;
+  return launch_gate_up(x, w_gate, w_up, sorted, tiles + 2 * L.max_big, n_tiles + 1, T, H, k, I, L.SMALL, L.max_small,
+                        h, nullptr, nullptr, 0, nullptr, st, q);
 }
 
-hipError_t launch_routed_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,
-                              const int32_t* n_tiles, int T, int H, int E, int k, int I, uint16_t* o,
-                              hipStream_t st) {
-  const int BIG = moe_align_tile_rows(T, E, k), SMALL = moe_align_small_tile_rows(T, E, k);
-  const int64_t max_big = moe_align_max_big_tiles(T, E, k), max_small = moe_align_max_tiles(T, E, k) - max_big;
-  hipError_t e = launch_down(h, w_down, sorted, tiles, n_tiles, T, H, k, I, BIG, max_big, o, st);
-  if (e != hipSuccess || SMALL == BIG) return e;
-  return launch_down(h, w_down, sorted, tiles + 2 * max_big, n_tiles + 1, T, H, k, I, SMALL, max_small, o, st);
+hipError_t launch_routed_down(const uint16_t* h, const void* w_down, const int32_t* sorted, const int32_t* tiles,
+                              const int32_t* n_tiles, int T, int H, int k, int I, uint16_t* o, const Layout& L,
+                              hipStream_t st, const FP8Scales* q = nullptr) {
+  hipError_t e = launch_down(h, w_down, sorted, tiles, n_tiles, T, H, k, I, L.BIG, L.max_big, o, st, q);
+  if (e != hipSuccess || L.SMALL == L.BIG) return e;
+  return launch_down(h, w_down, sorted, tiles + 2 * L.max_big, n_tiles + 1, T, H, k, I, L.SMALL, L.max_small, o, st,
+                     q);
+}
+
+// The tiled path of moe_forward / moe_forward_fp8 (T > the small-batch limit)
+// on the workspace layout L; q: FP8 row scales (NULL: BF16 weights).
+int forward_tiled(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const void* w_gate,
+                  const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up, const void* ws_down,
+                  const uint16_t* w_sg, int T, int H, int E, int k, int I, int I_s, uint16_t* y, void* workspace,
+                  const Layout& L, const FP8Scales* q, hipStream_t st) {
+  char* base = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(base + L.off_ids);
+  float* w = reinterpret_cast<float*>(base + L.off_w);
+  float* s = reinterpret_cast<float*>(base + L.off_s);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
+  int32_t* pad_off = reinterpret_cast<int32_t*>(base + L.off_padoff);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.off_sorted);
+  int32_t* inv = reinterpret_cast<int32_t*>(base + L.off_inv);
+  int32_t* tiles = reinterpret_cast<int32_t*>(base + L.off_tiles);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(base + L.off_ntiles);
+  int32_t* scratch = reinterpret_cast<int32_t*>(base + L.off_scratch);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + L.off_h);
+  uint16_t* h_s = I_s > 0 ? reinterpret_cast<uint16_t*>(base + L.off_hs) : nullptr;
+  uint16_t* o = reinterpret_cast<uint16_t*>(base + L.off_o);
+
+  // logits stay in LDS: the router launch selects the experts itself
+  hipError_t e = launch_router(x, w_router, router_bias, I_s > 0 ? w_sg : nullptr, T, H, E, k, nullptr,
+                               I_s > 0 ? s : nullptr, ids, w, st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: router with top-k");
+  e = launch_align(ids, T, E, k, L.BIG, L.SMALL, (int)L.max_big, counts, pad_off, sorted, inv, tiles, n_tiles, scratch,
+                   st);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: align");
+  e = launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, h, ws_gate, ws_up, I_s, h_s, L, st, q);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: gate_up (routed + shared)");
+  e = launch_routed_down(h, w_down, sorted, tiles, n_tiles, T, H, k, I, o, L, st, q);
+  if (e != hipSuccess) return hip_status(e, "moe_forward: down");
+  e = launch_combine(o, w, h_s, ws_down, I_s > 0 ? s : nullptr, T, H, k, I_s, y, st, q);
+  return hip_status(e, "moe_forward: combine");
 }
 }  // namespace
 
@@ -306,8 +353,8 @@ int moe_grouped_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_
       (I_s > 0 && (!aligned16(ws_gate) || !aligned16(ws_up) || !aligned16(h_s))))
     return fail(MOE_ERR_ALIGN, "moe_grouped_gate_up: tensors must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
-  return hip_status(launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, E, k, I, h, ws_gate, ws_up,
-                                          I_s, h_s, (hipStream_t)stream),
+  return hip_status(launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, h, ws_gate, ws_up, I_s,
+                                          h_s, layout(T, H, E, k, I, I_s), (hipStream_t)stream),
                     "moe_grouped_gate_up");
 }
 
@@ -320,7 +367,8 @@ int moe_grouped_down(const uint16_t* h, const uint16_t* w_down, const int32_t* s
   if (!aligned16(h) || !aligned16(w_down) || !aligned16(o))
     return fail(MOE_ERR_ALIGN, "moe_grouped_down: tensors must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
-  return hip_status(launch_routed_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, o, (hipStream_t)stream),
+  return hip_status(launch_routed_down(h, w_down, sorted, tiles, n_tiles, T, H, k, I, o, layout(T, H, E, k, I, 0),
+                                       (hipStream_t)stream),
                     "moe_grouped_down");
 }
 
@@ -372,35 +420,8 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
                       "moe_forward (small batch)");
   }
 
-  const Layout L = layout(T, H, E, k, I, I_s);
-  char* base = static_cast<char*>(workspace);
-  int32_t* ids = reinterpret_cast<int32_t*>(base + L.off_ids);
-  float* w = reinterpret_cast<float*>(base + L.off_w);
-  float* s = reinterpret_cast<float*>(base + L.off_s);
-  int32_t* counts = reinterpret_cast<int32_t*>(base + L.off_counts);
-  int32_t* pad_off = reinterpret_cast<int32_t*>(base + L.off_padoff);
-  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.off_sorted);
-  int32_t* inv = reinterpret_cast<int32_t*>(base + L.off_inv);
-  int32_t* tiles = reinterpret_cast<int32_t*>(base + L.off_tiles);
-  int32_t* n_tiles = reinterpret_cast<int32_t*>(base + L.off_ntiles);
-  int32_t* scratch = reinterpret_cast<int32_t*>(base + L.off_scratch);
-  uint16_t* h = reinterpret_cast<uint16_t*>(base + L.off_h);
-  uint16_t* h_s = I_s > 0 ? reinterpret_cast<uint16_t*>(base + L.off_hs) : nullptr;
-  uint16_t* o = reinterpret_cast<uint16_t*>(base + L.off_o);
-
-  // logits stay in LDS: the router launch selects the experts itself
-  hipError_t e = launch_router(x, w_router, router_bias, I_s > 0 ? w_sg : nullptr, T, H, E, k, nullptr,
-                               I_s > 0 ? s : nullptr, ids, w, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: router with top-k");
-  e = launch_align(ids, T, E, k, L.BIG, L.SMALL, (int)L.max_big, counts, pad_off, sorted, inv, tiles, n_tiles, scratch,
-                   st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: align");
-  e = launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, E, k, I, h, ws_gate, ws_up, I_s, h_s, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: gate_up (routed + shared)");
-  e = launch_routed_down(h, w_down, sorted, tiles, n_tiles, T, H, E, k, I, o, st);
-  if (e != hipSuccess) return hip_status(e, "moe_forward: down");
-  e = launch_combine(o, w, h_s, ws_down, I_s > 0 ? s : nullptr, T, H, k, I_s, y, st);
-  return hip_status(e, "moe_forward: combine");
+  return forward_tiled(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg, T, H, E, k, I,
+                       I_s, y, workspace, layout(T, H, E, k, I, I_s), nullptr, st);
 }
 
 int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint8_t* q_gate,
@@ -411,9 +432,6 @@ int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* ro
                     void* stream) {
   int rc = check_common_shapes(T, H, E, k);
   if (rc || (rc = check_ffn_shapes(I, I_s))) return rc;
-  if (T > MOE_FP8_MAX_T)
-    return fail(MOE_ERR_SHAPE, "moe_forward_fp8: T=%d; FP8 expert weights are supported for T <= %d", T,
-                MOE_FP8_MAX_T);
   const int n_shared = (qs_gate != nullptr) + (ssc_gate != nullptr) + (qs_up != nullptr) + (ssc_up != nullptr) +
                        (qs_down != nullptr) + (ssc_down != nullptr) + (w_sg != nullptr);
   if (I_s == 0 && n_shared != 0) return fail(MOE_ERR_SHAPE, "moe_forward_fp8: shared-expert tensors given with I_s = 0");
@@ -437,8 +455,12 @@ int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* ro
   if (T == 1)
     return hip_status(launch_decode(x, w_router, router_bias, w_sg, W, H, E, k, I, I_s, y, workspace, st),
                       "moe_forward_fp8 (decode)");
-  return hip_status(launch_small_batch(x, w_router, router_bias, w_sg, W, T, H, E, k, I, I_s, y, workspace, st),
-                    "moe_forward_fp8 (small batch)");
+  if (T <= kSmallMaxT)
+    return hip_status(launch_small_batch(x, w_router, router_bias, w_sg, W, T, H, E, k, I, I_s, y, workspace, st),
+                      "moe_forward_fp8 (small batch)");
+  const FP8Scales q = {sc_gate, sc_up, sc_down, ssc_gate, ssc_up, ssc_down};
+  return forward_tiled(x, w_router, router_bias, q_gate, q_up, q_down, qs_gate, qs_up, qs_down, w_sg, T, H, E, k, I,
+                       I_s, y, workspace, layout(T, H, E, k, I, I_s, kFp8MaxTileRows), &q, st);
 }
 
 int moe_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream) {

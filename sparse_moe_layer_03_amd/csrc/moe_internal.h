@@ -126,16 +126,22 @@ int align_num_chunks(int T, int k);
 int align_scratch_ints(int T, int E, int k);
 // Routed gate/up tiles of one tile list; with I_s > 0 the shared expert's
 // gate/up over all T tokens (tiles of BM tokens) joins the same launch.
-hipError_t launch_gate_up(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up, const int32_t* sorted,
+// Row scales of FP8 expert weights for the tiled GEMMs (NULL pointer to the
+// struct: BF16 weights).  Routed gate/up [E,I], down [E,H]; shared gate/up
+// [I_s], down [H].  With FP8 weights the tiles hold at most 128 rows.
+struct FP8Scales {
+  const float *gate, *up, *down, *s_gate, *s_up, *s_down;
+};
+hipError_t launch_gate_up(const uint16_t* x, const void* w_gate, const void* w_up, const int32_t* sorted,
                           const int32_t* tiles, const int32_t* n_tiles, int T, int H, int k, int I, int BM,
-                          int64_t max_tiles, uint16_t* h, const uint16_t* ws_gate, const uint16_t* ws_up, int I_s,
-                          uint16_t* h_s, hipStream_t st);
-hipError_t launch_down(const uint16_t* h, const uint16_t* w_down, const int32_t* sorted, const int32_t* tiles,
+                          int64_t max_tiles, uint16_t* h, const void* ws_gate, const void* ws_up, int I_s,
+                          uint16_t* h_s, hipStream_t st, const FP8Scales* q = nullptr);
+hipError_t launch_down(const uint16_t* h, const void* w_down, const int32_t* sorted, const int32_t* tiles,
                        const int32_t* n_tiles, int T, int H, int k, int I, int BM, int64_t max_tiles, uint16_t* o,
-                       hipStream_t st);
+                       hipStream_t st, const FP8Scales* q = nullptr);
 hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s,
-                          const uint16_t* ws_down, const float* s, int T, int H, int k, int I_s, uint16_t* y,
-                          hipStream_t st);
+                          const void* ws_down, const float* s, int T, int H, int k, int I_s, uint16_t* y,
+                          hipStream_t st, const FP8Scales* q = nullptr);
 hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
                          const ExpertWeights& W, int H, int E, int k, int I, int I_s, uint16_t* y, void* ws,
                          hipStream_t st);

@@ -23,7 +23,6 @@ MOE_ERR_WORKSPACE = -4
 MOE_ERR_ARCH = -5
 MOE_ERR_HIP = -6
 SMALL_BATCH_MAX_T = 32  # MOE_SMALL_BATCH_MAX_T: moe_forward's small-batch path covers 2 <= T <= this
-FP8_MAX_T = 32  # MOE_FP8_MAX_T: moe_forward_fp8 covers 1 <= T <= this
 
 EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_align_tile_rows", "moe_align_small_tile_rows", "moe_align_max_rows",

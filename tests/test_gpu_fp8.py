@@ -2,9 +2,10 @@
 
 Expert weights are OCP FP8 E4M3 codes with one fp32 scale per output row
 (kongchang.com "GFX1151 engine", section on the two weight formats).  The
-single-token and small-batch kernels are checked against the oracle's FP8
-layer under the BF16 tolerance, and against the BF16 kernels bitwise where
-the dequantised weights are exact in BF16 and the scales powers of two.
+single-token, small-batch and tiled kernels are checked against the
+oracle's FP8 layer under the BF16 tolerance, and against the BF16 kernels
+bitwise where the dequantised weights are exact in BF16 and the scales
+powers of two (at token counts where both run tiles of the same height).
 """
 import numpy as np
 import pytest
@@ -128,7 +129,7 @@ def _exact_fp8(inp, seed):
     return out
 
 
-@pytest.mark.parametrize("T", [1, 2, 13, 32])
+@pytest.mark.parametrize("T", [1, 2, 13, 32, 33, 200, 700])
 def test_fp8_equals_bf16_kernels_on_exact_weights(torch, T):
     """With power-of-two row scales every dequantised weight is exact in BF16 and every scaled sum is
     exact, so the FP8 kernels give bitwise the BF16 kernels' output on those BF16 weights."""
@@ -169,7 +170,47 @@ def test_fp8_graph_replay_and_determinism(torch, fp8_layer):
             assert torch.equal(yg.view(torch.int16), y1.view(torch.int16)), f"T={T} replay {i}"
 
 
-def test_fp8_rejects_large_T(torch, fp8_layer):
-    inp = G.with_fp8(G.inputs("prefill1k", moe.FP8_MAX_T + 1))
-    with pytest.raises(moe.MoEError):
-        _fp8_layer_for(inp, fp8_layer).forward(G.to_dev_x(inp))
+FP8_TILED_CASES = [
+    ("full-T33", dict(wl="prefill1k", T=33)),
+    ("full-T300-bias", dict(wl="prefill8k", T=300)),
+    ("full-T1024", dict(wl="prefill1k", T=1024)),
+    ("k16-T200", dict(wl=synth.Workload("f16t", T=200, H=512, E=32, k=16, I=256, I_s=128))),
+    ("noshared-T150", dict(wl=synth.Workload("f9t", T=150, H=256, E=12, k=9, I=384, I_s=0))),
+    ("wide-T400", dict(wl=synth.Workload("fwt", T=400, H=4096, E=64, k=4, I=640, I_s=256, bias="normal"))),
+]
+
+
+@pytest.mark.parametrize("label,case", FP8_TILED_CASES, ids=[c[0] for c in FP8_TILED_CASES])
+def test_fp8_tiled_parity(torch, fp8_layer, label, case):
+    """moe_forward_fp8 above the small-batch limit (the tiled GEMMs on widened codes) vs the oracle."""
+    inp = _case_inputs(case)
+    wl = inp["wl"]
+    T = inp["x"].shape[0]
+    G.say(f"[fp8-tiled] {label}: T={T} H={wl.H} E={wl.E} k={wl.k} I={wl.I} I_s={wl.I_s}")
+    lay = _fp8_layer_for(inp, fp8_layer)
+    y = lay.forward(G.to_dev_x(inp))
+    ids = lay.forward_ids(T).cpu().numpy()
+    torch.cuda.synchronize()
+    y_ref, _ = G.reference_y(inp, ids, f"fp8 {label}", fp8=True)
+    G.check_y(G.y_to_f64(y), y_ref, f"fp8 {label}")
+
+
+@pytest.mark.parametrize("name,T", [("prefill8k", 8192), ("skew32k", 32768)])
+def test_fp8_full_size_sampled(torch, fp8_layer, name, T):
+    """Full workloads with FP8 weights: all ids vs the oracle router, sampled y rows vs the FP8 oracle."""
+    G.say(f"[fp8-full] {name} T={T}")
+    inp = G.with_fp8(G.inputs(name, T))
+    wl = inp["wl"]
+    lay = _fp8_layer_for(inp, fp8_layer)
+    y = lay.forward(G.to_dev_x(inp))
+    ids = lay.forward_ids(T).cpu().numpy()
+    torch.cuda.synchronize()
+    r = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["w_sg"], wl.k)
+    ex = G.excluded_tokens(r["logits"], wl.k, inp.get("tie_rows", ()))
+    G.check_ids(ids, r["ids"], ex, f"fp8 full {name}")
+    rng = np.random.default_rng(T + 1)
+    rows = np.unique(np.concatenate([rng.choice(T, 24, replace=False), [0, T - 1]]).astype(np.int64))
+    sub = dict(inp)
+    sub["x"] = inp["x"][rows]
+    ro = oracle.forward(sub, ids_in=ids[rows], fp8=True)
+    G.check_y(G.y_to_f64(y)[rows], ro["y"], f"fp8 full {name} ({len(rows)} sampled rows)")
