@@ -157,10 +157,10 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
  *          moe_forward_ids_offset() locates the selected ids as for moe_forward.
  * Paths: T == 1 and T <= MOE_SMALL_BATCH_MAX_T run the single-token and
  *          small-batch kernels on the codes (8 bytes per 8 weights); larger
- *          T runs the tiled GEMMs with tiles of at most 128 rows, the codes
- *          widened exactly to bf16 on their way into on-chip memory and the
- *          row scales applied to the accumulators.  Codes that are NaN give
- *          NaN outputs (not checked).
+ *          T runs the tiled GEMMs (same tiles as moe_forward) on the codes,
+ *          widened exactly to bf16 inside the kernel, with the row scales
+ *          applied to the accumulators.  Codes that are NaN give NaN outputs
+ *          (not checked).
  */
 int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
                     const uint8_t* q_gate, const float* sc_gate, const uint8_t* q_up, const float* sc_up,

@@ -733,13 +733,25 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
 //   * A row groups of only padding are not loaded: their LDS rows hold
 //     finite values of earlier data and feed only output rows that are not
 //     stored (a row of A reaches only the same row of the product).
+//   * with FP8 weights (Q) the B rows arrive as E4M3 codes (half the bytes
+//     of every B load), are widened exactly to bf16 as fragments are read,
+//     and the item's 256 row scales arrive by one more direct load into a
+//     small LDS area (two items' worth), from which the epilogue scales the
+//     accumulators.
 constexpr int DBM = 256, DNT = 512, DBK = 64, DKCH = DBK / 8;
-constexpr int DRPI = 64 / DKCH;                    // rows filled by one load instruction (64 lanes x 16 B)
-constexpr int DNQ = 32 / DRPI;                     // load instructions per wave per operand per K step
-constexpr int DSTAGE = (DBM + BNB) * DKCH;         // 16-byte chunks per stage (A rows, then B rows)
-constexpr size_t DLDS = 2 * (size_t)DSTAGE * 16;   // 128 KB
+constexpr int DRPI = 64 / DKCH;                    // A rows filled by one load instruction (64 lanes x 16 B)
+constexpr int DNQ = 32 / DRPI;                     // A load instructions per wave per K step
 constexpr int DESB = 72;                           // bf16 row stride of the down epilogue's staging tile
-static_assert((size_t)DBM * DESB * 2 + DBM * 4 <= (size_t)DSTAGE * 16, "down epilogue staging fits in one stage");
+template <bool Q>
+struct DmaGeom {
+  static constexpr int BKCH = Q ? DKCH / 2 : DKCH;         // 16-byte chunks per B row per K step
+  static constexpr int BRPI = 64 / BKCH;                   // B rows filled by one load instruction
+  static constexpr int BNQ = 32 / BRPI;                    // B load instructions per wave per K step
+  static constexpr int STAGE = DBM * DKCH + BNB * BKCH;    // 16-byte chunks per stage (A rows, then B rows)
+  static constexpr size_t SCALES = Q ? 2 * BNB * 4 : 0;    // LDS bytes of two items' B-row scales
+  static constexpr size_t LDS = 2 * (size_t)STAGE * 16 + SCALES;  // 128 KB (bf16), 98 KB (FP8)
+  static_assert((size_t)DBM * DESB * 2 + DBM * 4 <= (size_t)STAGE * 16, "down epilogue staging fits in one stage");
+};
 
 // One direct-to-LDS load: 16 bytes per lane from src into LDS at
 // lds_base + 16 * lane (lds_base wave-uniform, in M0).  Inline assembly, so
@@ -747,7 +759,7 @@ static_assert((size_t)DBM * DESB * 2 + DBM * 4 <= (size_t)DSTAGE * 16, "down epi
 // it; the K loop waits for it explicitly before the barrier that publishes
 // the stage.  (The compiler's own waits for its loads only grow stronger
 // from loads it does not see: vector-memory counts complete in issue order.)
-__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds_base) {
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
                : "memory", "m0");
 }
@@ -759,14 +771,18 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (0x7
 struct DmaItem {
   Item it;
   const uint16_t* asrc[DNQ];  // this lane's A source of load q (K step 0)
-  const uint16_t* bbase;      // this wave's B rows: bbase + the item-independent lane offsets
+  const char* bbase;          // this wave's B rows: bbase + the item-independent lane byte offsets
+  const float* ssrc;          // FP8: this lane's 16 bytes of the item's B-row scales
+  int spar;                   // FP8: which of the two LDS scale areas the item uses
   uint32_t aon;               // bit q: A group q holds a data row
   bool live;                  // this wave's 64 rows hold data
   int orow[2];                // this lane's epilogue rows (m = 0, 1): assignment (down), or >= 0 if stored
 };
 
-template <int MODE>
-__device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, int wave, int wm, int lane) {
+template <int MODE, bool Q>
+__device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, int wave, int wm, int lane,
+                                            int spar) {
+  constexpr size_t EB = Q ? 1 : 2;  // bytes per weight
   DmaItem d;
   d.it = it;
   d.aon = 0;
@@ -783,12 +799,23 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
   }
   // B rows w*32 .. w*32+31: gate/up items take gate rows in waves 0-3 and up
   // rows in waves 4-7 (the same 128 intermediate columns)
+  const size_t erow = it.dense ? 0 : (size_t)it.expert * p.N;  // the expert's first weight row
   if (MODE == GATE_UP) {
-    const uint16_t* g = it.dense ? p.bs0 : p.b0 + (size_t)it.expert * p.N * p.K;
-    const uint16_t* u = it.dense ? p.bs1 : p.b1 + (size_t)it.expert * p.N * p.K;
-    d.bbase = (wave < 4 ? g : u) + (size_t)it.nb * 128 * p.K;
+    const char* m = reinterpret_cast<const char*>(wave < 4 ? (it.dense ? p.bs0 : p.b0) : (it.dense ? p.bs1 : p.b1));
+    d.bbase = m + (erow + (size_t)it.nb * 128) * p.K * EB;
   } else {
-    d.bbase = (it.dense ? p.bs0 : p.b0 + (size_t)it.expert * p.N * p.K) + (size_t)it.nb * 256 * p.K;
+    d.bbase = reinterpret_cast<const char*>(it.dense ? p.bs0 : p.b0) + (erow + (size_t)it.nb * 256) * p.K * EB;
+  }
+  // the scales of B rows 0..255, 16 bytes per lane: gate/up items take the
+  // 128 gate rows' scales in lanes 0-31 and the up rows' in lanes 32-63
+  d.spar = spar;
+  d.ssrc = nullptr;
+  if constexpr (Q) {
+    if (MODE == GATE_UP)
+      d.ssrc = (lane < 32 ? (it.dense ? p.ssc0 : p.sc0) : (it.dense ? p.ssc1 : p.sc1)) + erow + (size_t)it.nb * 128 +
+               (lane & 31) * 4;
+    else
+      d.ssrc = (it.dense ? p.ssc0 : p.sc0) + erow + (size_t)it.nb * 256 + lane * 4;
   }
   const int r = wm * 64;
   const bool lv = it.dense ? (it.row0 + r < p.T) : (p.sorted[it.row0 + r] >= 0);
@@ -803,10 +830,12 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
   return d;
 }
 
-template <int MODE>
+template <int MODE, bool Q = false>
 __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   static_assert(MODE == GATE_UP || MODE == DOWN, "routed GEMMs only");
   using C = Cfg<DBM>;
+  using G = DmaGeom<Q>;
+  constexpr size_t EB = Q ? 1 : 2;  // bytes per weight
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -825,24 +854,32 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
   // A groups that are never loaded must not hold arbitrary bits on the first item
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int i = tid; i < 2 * DSTAGE; i += DNT) sm[i] = zero;
+  for (int i = tid; i < 2 * G::STAGE; i += DNT) sm[i] = zero;
   __syncthreads();
+  const uint32_t lds_scales = lds0 + (uint32_t)(2 * G::STAGE * 16);
+  const float* scales = reinterpret_cast<const float*>(smem + 2 * G::STAGE * 16);  // [2][BNB]
 
-  // element offset of this lane's B source of load q from the wave's bbase
-  uint32_t boff[DNQ];
+  // byte offset of this lane's B source of load q from the wave's bbase:
+  // lane l fills row w*32 + q*BRPI + l/BKCH, LDS slot l%BKCH, which holds
+  // logical chunk swz(row, l%BKCH)
+  uint32_t boff[G::BNQ];
 #pragma unroll
-  for (int q = 0; q < DNQ; ++q) {
-    const int r = wave * 32 + q * DRPI + lane / DKCH;
-    boff[q] = (uint32_t)((MODE == GATE_UP ? (r & 127) : r) * p.K + swz<DKCH>(r, lane % DKCH) * 8);
+  for (int q = 0; q < G::BNQ; ++q) {
+    const int r = wave * 32 + q * G::BRPI + lane / G::BKCH;
+    boff[q] = (uint32_t)(((MODE == GATE_UP ? (r & 127) : r) * p.K) * EB + swz<G::BKCH>(r, lane % G::BKCH) * 16);
   }
   auto issue = [&](const DmaItem& d, int st, int kb) {
-    const uint32_t base = lds0 + (uint32_t)st * DSTAGE * 16;
+    const uint32_t base = lds0 + (uint32_t)st * G::STAGE * 16;
 #pragma unroll
     for (int q = 0; q < DNQ; ++q)
       if ((d.aon >> q) & 1u) dma16(d.asrc[q] + kb * DBK, base + (uint32_t)(wave * 32 + q * DRPI) * DKCH * 16);
 #pragma unroll
-    for (int q = 0; q < DNQ; ++q)
-      dma16(d.bbase + boff[q] + kb * DBK, base + (uint32_t)(DBM + wave * 32 + q * DRPI) * DKCH * 16);
+    for (int q = 0; q < G::BNQ; ++q)
+      dma16(d.bbase + boff[q] + (size_t)kb * DBK * EB,
+            base + (uint32_t)(DBM * DKCH + (wave * 32 + q * G::BRPI) * G::BKCH) * 16);
+    if constexpr (Q) {
+      if (kb == 0 && wave == 0) dma16(d.ssrc, lds_scales + (uint32_t)d.spar * BNB * 4);
+    }
   };
   int bb[C::NJ];
   {
@@ -856,7 +893,7 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     bf16x8 a[C::MI], b[C::NJ];
   };
   auto read_frags = [&](Frag& f, int st, int sub) {
-    const u32x4* cA = sm + st * DSTAGE;
+    const u32x4* cA = sm + st * G::STAGE;
     const u32x4* cB = cA + DBM * DKCH;
     const int c = 2 * sub + (lane >> 5);
 #pragma unroll
@@ -867,7 +904,14 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
 #pragma unroll
     for (int j = 0; j < C::NJ; ++j) {
       const int r = bb[j] + (lane & 31);
-      f.b[j] = __builtin_bit_cast(bf16x8, cB[r * DKCH + swz<DKCH>(r, c)]);
+      if constexpr (Q) {
+        // K values 8c .. 8c+7 of row r: half (c & 1) of logical 16-byte chunk c / 2
+        const u32x2 codes = *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(cB) +
+                                                            (r * G::BKCH + swz<G::BKCH>(r, c >> 1)) * 16 + (c & 1) * 8);
+        f.b[j] = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(codes));
+      } else {
+        f.b[j] = __builtin_bit_cast(bf16x8, cB[r * DKCH + swz<DKCH>(r, c)]);
+      }
     }
   };
   // Gate/up items compute transposed blocks (the weight fragment is the
@@ -887,13 +931,13 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
 
   constexpr int SUB = DBK / 16;
   const int nk = p.K / DBK;  // even: K is a multiple of 128
-  DmaItem cur = dma_item<MODE>(p, routed_item_at<DBM, MODE>(p, ri, first), wave, wm, lane);
+  DmaItem cur = dma_item<MODE, Q>(p, routed_item_at<DBM, MODE>(p, ri, first), wave, wm, lane, 0);
   issue(cur, 0, 0);
   for (int item = first; item < last; item += nslot) {
     const int nxt = item + nslot;
     const bool has_next = nxt < last;
     DmaItem next = cur;
-    if (has_next) next = dma_item<MODE>(p, routed_item_at<DBM, MODE>(p, ri, nxt), wave, wm, lane);
+    if (has_next) next = dma_item<MODE, Q>(p, routed_item_at<DBM, MODE>(p, ri, nxt), wave, wm, lane, cur.spar ^ 1);
 #pragma unroll
     for (int m = 0; m < C::MI; ++m)
 #pragma unroll
@@ -955,8 +999,19 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               float v[4];
+              if constexpr (Q) {
+                // B rows bb[j] + 8 g + 4 lh + i (gate) and the same of the up half
+                const float* S = scales + cur.spar * BNB;
+                const float4 sg = *reinterpret_cast<const float4*>(S + bb[j] + 8 * g + 4 * lh);
+                const float4 su = *reinterpret_cast<const float4*>(S + bb[j + C::NJ / 2] + 8 * g + 4 * lh);
+                const float fg[4] = {sg.x, sg.y, sg.z, sg.w}, fu[4] = {su.x, su.y, su.z, su.w};
 #pragma unroll
-              for (int i = 0; i < 4; ++i) v[i] = silu(acc[m][j][4 * g + i]) * acc[m][j + C::NJ / 2][4 * g + i];
+                for (int i = 0; i < 4; ++i)
+                  v[i] = silu(acc[m][j][4 * g + i] * fg[i]) * (acc[m][j + C::NJ / 2][4 * g + i] * fu[i]);
+              } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = silu(acc[m][j][4 * g + i]) * acc[m][j + C::NJ / 2][4 * g + i];
+              }
               const uint2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
               *reinterpret_cast<uint2*>(orow + bb[j] + 8 * g + 4 * lh) = pk;
             }
@@ -969,7 +1024,7 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       // fragments are read) and stored as 128-byte row segments, 64 output
       // columns a pass.
       __syncthreads();  // every fragment read of that stage has completed
-      uint16_t* es = reinterpret_cast<uint16_t*>(smem) + (size_t)((nk - 1) & 1) * DSTAGE * 8;
+      uint16_t* es = reinterpret_cast<uint16_t*>(smem) + (size_t)((nk - 1) & 1) * G::STAGE * 8;
       const int cr = tid >> 3, cc = (tid & 7) * 8;
       constexpr int RG = DNT / 8, RPT = DBM / RG;
       // the assignment of each copy-out row (-1: padding, not stored), read
@@ -986,10 +1041,11 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
           for (int j = 0; j < C::NJ; ++j) {
             const int col = bb[j] + (lane & 31) - pass * EPW;
             if (col >= 0 && col < EPW) {
+              const float scl = Q ? scales[cur.spar * BNB + bb[j] + (lane & 31)] : 1.0f;  // B row of this column
 #pragma unroll
               for (int q = 0; q < 16; ++q) {
                 const int row = wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                es[row * DESB + col] = f32_to_bf16(acc[m][j][q]);
+                es[row * DESB + col] = f32_to_bf16(Q ? acc[m][j][q] * scl : acc[m][j][q]);
               }
             }
           }
@@ -1039,7 +1095,7 @@ hipError_t launch_mode(const GemmParams& p, int64_t max_items, hipStream_t st) {
 }
 
 // Persistent launch: one workgroup per CU (at most one per item).
-template <int MODE>
+template <int MODE, bool Q = false>
 hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st) {
   if (max_items <= 0) return hipSuccess;
   if (p.K % (2 * DBK) != 0) return hipErrorInvalidValue;
@@ -1049,10 +1105,11 @@ hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st) {
   if (e != hipSuccess) return e;
   int64_t grid = n_cu < max_items ? n_cu : max_items;
   grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  e = hipFuncSetAttribute((const void*)grouped_gemm_dma_kernel<MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)DLDS);
+  constexpr size_t lds = DmaGeom<Q>::LDS;
+  e = hipFuncSetAttribute((const void*)grouped_gemm_dma_kernel<MODE, Q>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE>), dim3((unsigned)grid), dim3(DNT), DLDS, st, p);
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE, Q>), dim3((unsigned)grid), dim3(DNT), lds, st, p);
   return hipGetLastError();
 }
 
@@ -1086,8 +1143,8 @@ hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t
       if constexpr (MODE == DOWN) return launch_mode<MOE_DOWN_CFG_128, MODE, Q>(p, max_items, st);
       return launch_mode<MOE_GEMM_CFG_128, MODE, Q>(p, max_items, st);
     case 256:
-      if constexpr ((MODE == GATE_UP || MODE == DOWN) && !Q) return launch_dma<MODE>(p, max_items, st);
-      return hipErrorInvalidValue;  // FP8 weights: tiles of at most 128 rows
+      if constexpr (MODE == GATE_UP || MODE == DOWN) return launch_dma<MODE, Q>(p, max_items, st);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -121,16 +121,11 @@ int64_t max_tiles_for(int64_t n, int E, int64_t big, int64_t small) {
   return max_big_for(n, E, big, small) + max_small;
 }
 
-// FP8 expert weights run the tiled GEMMs with tiles of at most this many rows.
-constexpr int kFp8MaxTileRows = 128;
-
-// Workspace layout of the tiled path; max_tile caps the tile heights.
-Layout layout(int T, int H, int E, int k, int I, int I_s, int max_tile = 256) {
+// Workspace layout of the tiled path (BF16 and FP8 weights alike).
+Layout layout(int T, int H, int E, int k, int I, int I_s) {
   Layout L = {};
   L.BIG = moe_align_tile_rows(T, E, k);
   L.SMALL = moe_align_small_tile_rows(T, E, k);
-  if (L.BIG > max_tile) L.BIG = max_tile;
-  if (L.SMALL > L.BIG) L.SMALL = L.BIG;
   const int64_t nA = (int64_t)T * k;
   L.max_rows = max_rows_for(nA, E, L.SMALL);
   L.max_big = max_big_for(nA, E, L.BIG, L.SMALL);
@@ -223,9 +218,7 @@ size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s) {
   if (check_common_shapes(T, H, E, k) != MOE_OK || check_ffn_shapes(I, I_s) != MOE_OK) return 0;
   if (T <= 1) return decode_workspace_size(H, E, k, I, I_s);
   if (T <= kSmallMaxT) return small_batch_workspace_size(T, H, E, k, I, I_s);
-  // the larger of the BF16 and FP8 (capped tile height) layouts
-  const size_t a = layout(T, H, E, k, I, I_s).total, b = layout(T, H, E, k, I, I_s, kFp8MaxTileRows).total;
-  return a > b ? a : b;
+  return layout(T, H, E, k, I, I_s).total;
 }
 
 size_t moe_forward_ids_offset(int T, int H, int E, int k, int I, int I_s) {
@@ -460,7 +453,7 @@ int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* ro
                       "moe_forward_fp8 (small batch)");
   const FP8Scales q = {sc_gate, sc_up, sc_down, ssc_gate, ssc_up, ssc_down};
   return forward_tiled(x, w_router, router_bias, q_gate, q_up, q_down, qs_gate, qs_up, qs_down, w_sg, T, H, E, k, I,
-                       I_s, y, workspace, layout(T, H, E, k, I, I_s, kFp8MaxTileRows), &q, st);
+                       I_s, y, workspace, layout(T, H, E, k, I, I_s), &q, st);
 }
 
 int moe_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream) {

@@ -128,7 +128,7 @@ int align_scratch_ints(int T, int E, int k);
 // gate/up over all T tokens (tiles of BM tokens) joins the same launch.
 // Row scales of FP8 expert weights for the tiled GEMMs (NULL pointer to the
 // struct: BF16 weights).  Routed gate/up [E,I], down [E,H]; shared gate/up
-// [I_s], down [H].  With FP8 weights the tiles hold at most 128 rows.
+// [I_s], down [H].
 struct FP8Scales {
   const float *gate, *up, *down, *s_gate, *s_up, *s_down;
 };

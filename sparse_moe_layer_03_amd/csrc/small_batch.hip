@@ -280,7 +280,13 @@ __global__ __launch_bounds__(1024) void sb_select_kernel(int T, int E, int k, Sm
 // wave), every token routed to the expert, GT at a time, with their x rows
 // staged in LDS (2048 columns at a time).  Slot u == n_u is the shared expert
 // over all T tokens when I_s > 0.
-constexpr int GP = 2, GR = 4 * GP, GT = 16;
+// Tokens staged per pass (8: 32 KB of LDS, so several workgroups share a CU
+// and more weight loads are in flight; 16 was 11% slower with FP8 weights at
+// 8 and 32 tokens and the same with BF16).
+#ifndef SB_GATE_UP_TOKENS
+#define SB_GATE_UP_TOKENS 8
+#endif
+constexpr int GP = 2, GR = 4 * GP, GT = SB_GATE_UP_TOKENS;
 template <bool Q>
 __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restrict__ x, ExpertWeights W, int T,
                                                          int H, int E, int k, int I, int I_s, SmallWs d) {
@@ -374,13 +380,18 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
 // +63): a wave per 16 columns.  Lane l takes column c0 + l / 4 and the
 // reduction chunks j * 4 + l % 4 (four adjacent lanes read 64 contiguous
 // bytes of a row); the four partial sums of a column meet in two DPP steps.
-// h rows of the expert's assignments (fp32) are staged in LDS, 16 at a time.
+// h rows of the expert's assignments (fp32) are staged in LDS, DT at a time.
+// h rows staged per pass (8: 16 KB of LDS), as for gate/up.
+#ifndef SB_DOWN_TOKENS
+#define SB_DOWN_TOKENS 8
+#endif
+constexpr int DT = SB_DOWN_TOKENS;  // h rows staged at a time
 template <bool Q>
 __global__ __launch_bounds__(256) void sb_down_kernel(ExpertWeights W, int T, int H, int E, int k, int I, int I_s,
                                                       SmallWs d) {
   typedef wchunk_t<Q> WC;
   typedef welem_t<Q> WE;
-  __shared__ float4 shh[TB * 128];  // 16 rows of up to 512 fp32 reduction values
+  __shared__ float4 shh[DT * 128];  // DT rows of up to 512 fp32 reduction values
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nu = d.plan[0];
   const int u = blockIdx.y;
@@ -400,15 +411,15 @@ __global__ __launch_bounds__(256) void sb_down_kernel(ExpertWeights W, int T, in
     WC wv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) wv[j] = reinterpret_cast<const WC*>(wrow)[kb + min(j * 4 + (lane & 3), nb - 1)];
-    for (int q0 = 0; q0 < cnt; q0 += TB) {
-      const int nt = min(TB, cnt - q0);
+    for (int q0 = 0; q0 < cnt; q0 += DT) {
+      const int nt = min(DT, cnt - q0);
       __syncthreads();
       {
         // one 1 KB load instruction per (assignment, half of the block's 512
         // values); halves past the reduction length are not loaded (those
         // lanes' chunks are skipped below)
         const uint32_t hb = lds_addr(shh);
-        for (int ins = __builtin_amdgcn_readfirstlane(wave); ins < TB * 2; ins += 4) {
+        for (int ins = __builtin_amdgcn_readfirstlane(wave); ins < DT * 2; ins += 4) {
           const int t = ins >> 1, half = ins & 1;
           if (t < nt && half * 64 < nb * 2) {
             const int a = asg_at(q0 + t);

@@ -129,7 +129,7 @@ def _exact_fp8(inp, seed):
     return out
 
 
-@pytest.mark.parametrize("T", [1, 2, 13, 32, 33, 200, 700])
+@pytest.mark.parametrize("T", [1, 2, 13, 32, 33, 200, 700, 1500])
 def test_fp8_equals_bf16_kernels_on_exact_weights(torch, T):
     """With power-of-two row scales every dequantised weight is exact in BF16 and every scaled sum is
     exact, so the FP8 kernels give bitwise the BF16 kernels' output on those BF16 weights."""
