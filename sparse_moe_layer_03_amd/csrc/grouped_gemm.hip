@@ -738,15 +738,25 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
 //     and the item's 256 row scales arrive by one more direct load into a
 //     small LDS area (two items' worth), from which the epilogue scales the
 //     accumulators.
-constexpr int DBM = 256, DNT = 512, DBK = 64, DKCH = DBK / 8;
+#ifndef MOE_DMA_WAVES
+#define MOE_DMA_WAVES 8
+#endif
+// Wave layout of the persistent kernel's 256 x 256 tile: NW wavefronts, two
+// across the columns (128 each), NW / 2 down the rows.
+struct DCfg {
+  static constexpr int NW = MOE_DMA_WAVES, NT = NW * 64, WAVES_N = 2, WAVES_M = NW / 2;
+  static constexpr int WTM = 256 / WAVES_M, MI = WTM / 32, WTN = 128, NJ = 4;
+  static constexpr int RPW = 256 / NW;  // A rows (and B rows) each wave loads
+};
+constexpr int DBM = 256, DNT = DCfg::NT, DBK = 64, DKCH = DBK / 8;
 constexpr int DRPI = 64 / DKCH;                    // A rows filled by one load instruction (64 lanes x 16 B)
-constexpr int DNQ = 32 / DRPI;                     // A load instructions per wave per K step
+constexpr int DNQ = DCfg::RPW / DRPI;              // A load instructions per wave per K step
 constexpr int DESB = 72;                           // bf16 row stride of the down epilogue's staging tile
 template <bool Q>
 struct DmaGeom {
   static constexpr int BKCH = Q ? DKCH / 2 : DKCH;         // 16-byte chunks per B row per K step
   static constexpr int BRPI = 64 / BKCH;                   // B rows filled by one load instruction
-  static constexpr int BNQ = 32 / BRPI;                    // B load instructions per wave per K step
+  static constexpr int BNQ = DCfg::RPW / BRPI;             // B load instructions per wave per K step
   static constexpr int STAGE = DBM * DKCH + BNB * BKCH;    // 16-byte chunks per stage (A rows, then B rows)
   static constexpr size_t SCALES = Q ? 2 * BNB * 4 : 0;    // LDS bytes of two items' B-row scales
   static constexpr size_t LDS = 2 * (size_t)STAGE * 16 + SCALES;  // 128 KB (bf16), 98 KB (FP8)
@@ -776,7 +786,7 @@ struct DmaItem {
   int spar;                   // FP8: which of the two LDS scale areas the item uses
   uint32_t aon;               // bit q: A group q holds a data row
   bool live;                  // this wave's 64 rows hold data
-  int orow[2];                // this lane's epilogue rows (m = 0, 1): assignment (down), or >= 0 if stored
+  int orow[DCfg::MI];         // this lane's epilogue rows (block m): assignment (down), or >= 0 if stored
 };
 
 template <int MODE, bool Q>
@@ -791,7 +801,7 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
   // chunk swz(row, l%8) (the swizzle is its own inverse)
 #pragma unroll
   for (int q = 0; q < DNQ; ++q) {
-    const int r = wave * 32 + q * DRPI + lane / DKCH;
+    const int r = wave * DCfg::RPW + q * DRPI + lane / DKCH;
     const int ch = swz<DKCH>(r, lane % DKCH);
     bool ok;
     d.asrc[q] = a_row<MODE>(p, it, r, ok) + ch * 8;
@@ -801,7 +811,8 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
   // rows in waves 4-7 (the same 128 intermediate columns)
   const size_t erow = it.dense ? 0 : (size_t)it.expert * p.N;  // the expert's first weight row
   if (MODE == GATE_UP) {
-    const char* m = reinterpret_cast<const char*>(wave < 4 ? (it.dense ? p.bs0 : p.b0) : (it.dense ? p.bs1 : p.b1));
+    const char* m =
+        reinterpret_cast<const char*>(wave < DCfg::NW / 2 ? (it.dense ? p.bs0 : p.b0) : (it.dense ? p.bs1 : p.b1));
     d.bbase = m + (erow + (size_t)it.nb * 128) * p.K * EB;
   } else {
     d.bbase = reinterpret_cast<const char*>(it.dense ? p.bs0 : p.b0) + (erow + (size_t)it.nb * 256) * p.K * EB;
@@ -817,13 +828,13 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
     else
       d.ssrc = (it.dense ? p.ssc0 : p.sc0) + erow + (size_t)it.nb * 256 + lane * 4;
   }
-  const int r = wm * 64;
+  const int r = wm * DCfg::WTM;
   const bool lv = it.dense ? (it.row0 + r < p.T) : (p.sorted[it.row0 + r] >= 0);
   d.live = __builtin_amdgcn_readfirstlane((int)lv) != 0;
   // the epilogue's rows, read here so that the epilogue issues no load (a
   // load there would wait behind the next item's loads already in flight)
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < DCfg::MI; ++m) {
     const int rr = r + m * 32 + (lane & 31);
     d.orow[m] = it.dense ? (it.row0 + rr < p.T ? it.row0 + rr : -1) : p.sorted[it.row0 + rr];
   }
@@ -833,7 +844,7 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
 template <int MODE, bool Q = false>
 __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   static_assert(MODE == GATE_UP || MODE == DOWN, "routed GEMMs only");
-  using C = Cfg<DBM>;
+  using C = DCfg;
   using G = DmaGeom<Q>;
   constexpr size_t EB = Q ? 1 : 2;  // bytes per weight
   extern __shared__ __align__(16) unsigned char smem[];
@@ -865,18 +876,19 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   uint32_t boff[G::BNQ];
 #pragma unroll
   for (int q = 0; q < G::BNQ; ++q) {
-    const int r = wave * 32 + q * G::BRPI + lane / G::BKCH;
+    const int r = wave * DCfg::RPW + q * G::BRPI + lane / G::BKCH;
     boff[q] = (uint32_t)(((MODE == GATE_UP ? (r & 127) : r) * p.K) * EB + swz<G::BKCH>(r, lane % G::BKCH) * 16);
   }
   auto issue = [&](const DmaItem& d, int st, int kb) {
     const uint32_t base = lds0 + (uint32_t)st * G::STAGE * 16;
 #pragma unroll
     for (int q = 0; q < DNQ; ++q)
-      if ((d.aon >> q) & 1u) dma16(d.asrc[q] + kb * DBK, base + (uint32_t)(wave * 32 + q * DRPI) * DKCH * 16);
+      if ((d.aon >> q) & 1u)
+        dma16(d.asrc[q] + kb * DBK, base + (uint32_t)(wave * DCfg::RPW + q * DRPI) * DKCH * 16);
 #pragma unroll
     for (int q = 0; q < G::BNQ; ++q)
       dma16(d.bbase + boff[q] + (size_t)kb * DBK * EB,
-            base + (uint32_t)(DBM * DKCH + (wave * 32 + q * G::BRPI) * G::BKCH) * 16);
+            base + (uint32_t)(DBM * DKCH + (wave * DCfg::RPW + q * G::BRPI) * G::BKCH) * 16);
     if constexpr (Q) {
       if (kb == 0 && wave == 0) dma16(d.ssrc, lds_scales + (uint32_t)d.spar * BNB * 4);
     }
@@ -986,7 +998,6 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       // A reaches only the same row of the product, so whatever a padding
       // row of h holds stays in padding rows of o.
       const int lr = lane & 31, lh = lane >> 5;
-      static_assert(C::MI == 2, "two epilogue rows per lane");
 #pragma unroll
       for (int m = 0; m < C::MI; ++m) {
         const int r = wm * C::WTM + m * 32 + lr;  // tile row
