@@ -66,8 +66,12 @@ class Oracle:
         L.oracle_forward.argtypes = [p] * 10 + [i] * 6 + [p] * 10
         L.oracle_forward_fp8.argtypes = [p] * 16 + [i] * 6 + [p] * 10
         L.oracle_e4m3_decode.argtypes = [p, C.c_long, p]
+        L.oracle_forward_q4.argtypes = [p] * 16 + [i] * 6 + [p] * 10
+        L.oracle_f16_decode.argtypes = [p, C.c_long, p]
+        L.oracle_q4_dequant.argtypes = [p, p, C.c_long, i, p]
         for f in (L.oracle_route, L.oracle_route_from_logits, L.oracle_align, L.oracle_forward,
-                  L.oracle_forward_fp8, L.oracle_e4m3_decode):
+                  L.oracle_forward_fp8, L.oracle_e4m3_decode, L.oracle_forward_q4, L.oracle_f16_decode,
+                  L.oracle_q4_dequant):
             f.restype = C.c_int
         self.lib = L
         self.path = lib_path
@@ -115,24 +119,44 @@ class Oracle:
         _check(self.lib.oracle_e4m3_decode(_ptr(codes), codes.size, _ptr(out)), "oracle_e4m3_decode")
         return out
 
+    def f16_decode(self, bits) -> np.ndarray:
+        """Values (float64) of IEEE fp16 bit patterns."""
+        bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(bits.shape, np.float64)
+        _check(self.lib.oracle_f16_decode(_ptr(bits), bits.size, _ptr(out)), "oracle_f16_decode")
+        return out
+
+    def q4_dequant(self, codes, scales) -> np.ndarray:
+        """Dequantised 4-bit matrix: codes [..., n/2] uint8, fp16 scale bits [..., n/32] -> [..., n] float64."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.uint16)
+        n = codes.shape[-1] * 2
+        rows = codes.size * 2 // n
+        out = np.empty(codes.shape[:-1] + (n,), np.float64)
+        _check(self.lib.oracle_q4_dequant(_ptr(codes), _ptr(scales), rows, n, _ptr(out)), "oracle_q4_dequant")
+        return out
+
     def forward(self, inp: Dict[str, np.ndarray], k: Optional[int] = None, ids_in=None,
-                want=(), fp8: bool = False) -> Dict[str, np.ndarray]:
+                want=(), fp8: bool = False, q4: bool = False) -> Dict[str, np.ndarray]:
         """Whole layer on the arrays of ``inp`` (keys as produced by the seeded generator).
 
         ``want`` may name any of "h", "o", "hs", "os" for per-stage outputs.
         ``fp8``: take the expert weights from the ``*_fp8`` codes and
         ``*_scale`` row scales of ``inp`` instead of the BF16 arrays.
+        ``q4``: take them from the ``*_q4`` codes and ``*_q4scale`` fp16
+        group scales.
         """
         x = _c(inp["x"], np.uint16)
         wr = _c(inp["w_router"], np.uint16)
         bias = _c(inp.get("bias"), np.float32)
-        sfx = "_fp8" if fp8 else ""
-        wg = _c(inp["w_gate" + sfx], np.uint8 if fp8 else np.uint16)
-        wu = _c(inp["w_up" + sfx], np.uint8 if fp8 else np.uint16)
-        wd = _c(inp["w_down" + sfx], np.uint8 if fp8 else np.uint16)
-        sg = _c(inp.get("ws_gate" + sfx), np.uint8 if fp8 else np.uint16)
-        su = _c(inp.get("ws_up" + sfx), np.uint8 if fp8 else np.uint16)
-        sd = _c(inp.get("ws_down" + sfx), np.uint8 if fp8 else np.uint16)
+        sfx = "_fp8" if fp8 else ("_q4" if q4 else "")
+        dt = np.uint8 if (fp8 or q4) else np.uint16
+        wg = _c(inp["w_gate" + sfx], dt)
+        wu = _c(inp["w_up" + sfx], dt)
+        wd = _c(inp["w_down" + sfx], dt)
+        sg = _c(inp.get("ws_gate" + sfx), dt)
+        su = _c(inp.get("ws_up" + sfx), dt)
+        sd = _c(inp.get("ws_down" + sfx), dt)
         wsg = _c(inp.get("w_sg"), np.uint16)
         T, H = x.shape
         E, I, _ = wg.shape
@@ -151,7 +175,14 @@ class Oracle:
         os_ = np.empty((T, H), np.float64) if ("os" in want and I_s) else None
         tail = (_ptr(ids_in), _ptr(y), _ptr(ids), _ptr(w), _ptr(s), _ptr(logits),
                 _ptr(h), _ptr(o), _ptr(hs), _ptr(os_))
-        if fp8:
+        if q4:
+            codes = (wg, wu, wd, sg, su, sd)
+            scales = [_c(inp.get(key + "_q4scale"), np.uint16)
+                      for key in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
+            mats = [a for pair in zip(codes, scales) for a in pair]
+            _check(self.lib.oracle_forward_q4(_ptr(x), _ptr(wr), _ptr(bias), *[_ptr(a) for a in mats], _ptr(wsg),
+                                              T, H, E, k, I, I_s, *tail), "oracle_forward_q4")
+        elif fp8:
             codes = (wg, wu, wd, sg, su, sd)
             scales = [_c(inp.get(key + "_scale"), np.float32)
                       for key in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
@@ -202,6 +233,14 @@ def forward(*a, **kw):
 
 def e4m3_decode(*a, **kw):
     return default().e4m3_decode(*a, **kw)
+
+
+def f16_decode(*a, **kw):
+    return default().f16_decode(*a, **kw)
+
+
+def q4_dequant(*a, **kw):
+    return default().q4_dequant(*a, **kw)
 
 
 def topk_margin(logits: np.ndarray, k: int) -> np.ndarray:

@@ -42,6 +42,15 @@
  * BF16.  Dequantised weights are exact in double (4 + 24 significant bits),
  * so the layer's arithmetic is otherwise the BF16 one.
  *
+ * 4-bit expert weights (oracle_forward_q4): kongchang.com "GFX1151 engine"
+ * (section on the two weight formats) names GGUF files with 4-bit integer
+ * (Q4) quantisation but gives no block layout.  Read here as a plain
+ * group-wise format: every output row is cut into groups of 32 consecutive
+ * weights along the reduction index, each group has one IEEE fp16 scale,
+ * each weight is a signed 4-bit integer q in [-8, 7] (two's complement),
+ * two per byte (even index in the low nibble), and w = scale * q.  The
+ * dequantised weights are exact in double.
+ *
  * Parallelism: OpenMP over tokens (routing) and over assignments (FFN).
  * Every output element is computed by exactly one thread with a fixed
  * operation order, so results do not depend on the thread count.
@@ -125,17 +134,69 @@ static int all_finite_e4m3(const uint8_t* p, size_t n) {
     return 1;
 }
 
-/* One expert-weight operand: BF16 bits, or E4M3 codes with a scale per row. */
+/* IEEE binary16: bit 15 sign, bits 14..10 biased exponent (bias 15), bits
+ * 9..0 mantissa; exponent 0 is subnormal (m/1024 * 2^-14); exponent 31 is
+ * infinity (m = 0) or NaN. */
+static double f16_value(uint16_t h) {
+    int sgn = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double mag;
+    if (e == 31) mag = m ? NAN : INFINITY;
+    else if (e == 0) mag = ldexp((double)m / 1024.0, -14);
+    else mag = ldexp(1.0 + (double)m / 1024.0, e - 15);
+    return sgn ? -mag : mag;
+}
+
+/* Decoded values of n fp16 bit patterns. */
+int oracle_f16_decode(const uint16_t* bits, long n, double* out) {
+    if (n < 0) return ORC_ERR_SHAPE;
+    if (n > 0 && (!bits || !out)) return ORC_ERR_NULL;
+    for (long i = 0; i < n; ++i) out[i] = f16_value(bits[i]);
+    return ORC_OK;
+}
+
+#define Q4_GROUP 32
+
+/* Signed 4-bit weight c of a row of packed nibbles (even c: low nibble). */
+static int q4_weight(const uint8_t* row, size_t c) {
+    int nib = (c & 1) ? (row[c / 2] >> 4) : (row[c / 2] & 15);
+    return nib >= 8 ? nib - 16 : nib;
+}
+
+/* Dequantised 4-bit matrix [rows, n] (n a multiple of 32) into out [rows, n]
+ * double: out[r][c] = scale[r][c / 32] * q[r][c]. */
+int oracle_q4_dequant(const uint8_t* codes, const uint16_t* scales, long rows, int n, double* out) {
+    if (rows < 0 || n < Q4_GROUP || n % Q4_GROUP) return ORC_ERR_SHAPE;
+    if (rows > 0 && (!codes || !scales || !out)) return ORC_ERR_NULL;
+    for (long r = 0; r < rows; ++r)
+        for (int c = 0; c < n; ++c)
+            out[(size_t)r * n + c] = f16_value(scales[(size_t)r * (n / Q4_GROUP) + c / Q4_GROUP]) *
+                                     (double)q4_weight(codes + (size_t)r * (n / 2), (size_t)c);
+    return ORC_OK;
+}
+
+static int all_finite_f16(const uint16_t* p, size_t n) {
+    for (size_t i = 0; i < n; ++i)
+        if ((p[i] & 0x7C00u) == 0x7C00u) return 0;
+    return 1;
+}
+
+/* One expert-weight operand: BF16 bits, E4M3 codes with a scale per row, or
+ * 4-bit codes (q4) with an fp16 scale per group of 32. */
 typedef struct {
     const uint16_t* bf;
     const uint8_t* q;
     const float* scale;
+    const uint8_t* q4;
+    const uint16_t* s4;
 } wmat;
 
-static int wmat_set(wmat m) { return m.bf != NULL || (m.q != NULL && m.scale != NULL); }
+static int wmat_set(wmat m) {
+    return m.bf != NULL || (m.q != NULL && m.scale != NULL) || (m.q4 != NULL && m.s4 != NULL);
+}
 
 static int wmat_finite(wmat m, size_t rows, size_t cols) {
     if (m.bf) return all_finite_bf16(m.bf, rows * cols);
+    if (m.q4) return all_finite_f16(m.s4, rows * (cols / Q4_GROUP));
     return all_finite_e4m3(m.q, rows * cols) && all_finite_f32(m.scale, rows);
 }
 
@@ -143,9 +204,16 @@ static int wmat_finite(wmat m, size_t rows, size_t cols) {
  * (length n) of an expert operand. */
 static double dot_row_f64(const uint16_t* x, wmat m, size_t r, int n) {
     if (m.bf) return dot_bf16_f64(x, m.bf + r * (size_t)n, n);
+    double acc = 0.0;
+    if (m.q4) {
+        const uint8_t* q = m.q4 + r * (size_t)(n / 2);
+        const uint16_t* s = m.s4 + r * (size_t)(n / Q4_GROUP);
+        for (int i = 0; i < n; ++i)
+            acc += (double)bf16_to_f32(x[i]) * (f16_value(s[i / Q4_GROUP]) * (double)q4_weight(q, (size_t)i));
+        return acc;
+    }
     const uint8_t* q = m.q + r * (size_t)n;
     const double sc = (double)m.scale[r];
-    double acc = 0.0;
     for (int i = 0; i < n; ++i) acc += (double)bf16_to_f32(x[i]) * (sc * e4m3_value(q[i]));
     return acc;
 }
@@ -153,6 +221,9 @@ static double dot_row_f64(const uint16_t* x, wmat m, size_t r, int n) {
 /* Element (r, c) of an expert operand with rows of length n, as a double. */
 static double wmat_at(wmat m, size_t r, size_t c, int n) {
     if (m.bf) return (double)bf16_to_f32(m.bf[r * (size_t)n + c]);
+    if (m.q4)
+        return f16_value(m.s4[r * (size_t)(n / Q4_GROUP) + c / Q4_GROUP]) *
+               (double)q4_weight(m.q4 + r * (size_t)(n / 2), c);
     return (double)m.scale[r] * e4m3_value(m.q[r * (size_t)n + c]);
 }
 
@@ -455,8 +526,9 @@ int oracle_forward(const uint16_t* x, const uint16_t* w_router, const float* bia
                    const int32_t* ids_in, double* y,
                    int32_t* ids_out, double* w_out, double* s_out, float* logits_out,
                    double* h_out, double* o_out, double* hs_out, double* os_out) {
-    wmat g = {w_gate, NULL, NULL}, u = {w_up, NULL, NULL}, d = {w_down, NULL, NULL};
-    wmat sg = {ws_gate, NULL, NULL}, su = {ws_up, NULL, NULL}, sd = {ws_down, NULL, NULL};
+    wmat g = {w_gate, NULL, NULL, NULL, NULL}, u = {w_up, NULL, NULL, NULL, NULL};
+    wmat d = {w_down, NULL, NULL, NULL, NULL}, sg = {ws_gate, NULL, NULL, NULL, NULL};
+    wmat su = {ws_up, NULL, NULL, NULL, NULL}, sd = {ws_down, NULL, NULL, NULL, NULL};
     return forward_impl(x, w_router, bias, g, u, d, sg, su, sd, w_sg, T, H, E, k, I, I_s, ids_in, y, ids_out, w_out,
                         s_out, logits_out, h_out, o_out, hs_out, os_out);
 }
@@ -477,8 +549,35 @@ int oracle_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float*
                        const int32_t* ids_in, double* y,
                        int32_t* ids_out, double* w_out, double* s_out, float* logits_out,
                        double* h_out, double* o_out, double* hs_out, double* os_out) {
-    wmat g = {NULL, q_gate, sc_gate}, u = {NULL, q_up, sc_up}, d = {NULL, q_down, sc_down};
-    wmat sg = {NULL, qs_gate, ssc_gate}, su = {NULL, qs_up, ssc_up}, sd = {NULL, qs_down, ssc_down};
+    wmat g = {NULL, q_gate, sc_gate, NULL, NULL}, u = {NULL, q_up, sc_up, NULL, NULL};
+    wmat d = {NULL, q_down, sc_down, NULL, NULL}, sg = {NULL, qs_gate, ssc_gate, NULL, NULL};
+    wmat su = {NULL, qs_up, ssc_up, NULL, NULL}, sd = {NULL, qs_down, ssc_down, NULL, NULL};
+    return forward_impl(x, w_router, bias, g, u, d, sg, su, sd, w_sg, T, H, E, k, I, I_s, ids_in, y, ids_out, w_out,
+                        s_out, logits_out, h_out, o_out, hs_out, os_out);
+}
+
+/*
+ * The whole layer with 4-bit expert weights (routed and shared): codes
+ * q_gate/q_up [E, I, H/2], q_down [E, H, I/2], qs_gate/qs_up [I_s, H/2],
+ * qs_down [H, I_s/2] (two weights per byte), and fp16 group scales (bits)
+ * s_gate/s_up [E, I, H/32], s_down [E, H, I/32], ss_gate/ss_up [I_s, H/32],
+ * ss_down [H, I_s/32].  H, I and I_s must be multiples of 32.  Router, bias,
+ * w_sg and every output as in oracle_forward.  A non-finite scale gives
+ * ORC_ERR_NONFINITE.
+ */
+int oracle_forward_q4(const uint16_t* x, const uint16_t* w_router, const float* bias,
+                      const uint8_t* q_gate, const uint16_t* s_gate, const uint8_t* q_up, const uint16_t* s_up,
+                      const uint8_t* q_down, const uint16_t* s_down,
+                      const uint8_t* qs_gate, const uint16_t* ss_gate, const uint8_t* qs_up, const uint16_t* ss_up,
+                      const uint8_t* qs_down, const uint16_t* ss_down, const uint16_t* w_sg,
+                      int T, int H, int E, int k, int I, int I_s,
+                      const int32_t* ids_in, double* y,
+                      int32_t* ids_out, double* w_out, double* s_out, float* logits_out,
+                      double* h_out, double* o_out, double* hs_out, double* os_out) {
+    if (H % Q4_GROUP || I % Q4_GROUP || I_s % Q4_GROUP) return ORC_ERR_SHAPE;
+    wmat g = {NULL, NULL, NULL, q_gate, s_gate}, u = {NULL, NULL, NULL, q_up, s_up};
+    wmat d = {NULL, NULL, NULL, q_down, s_down}, sg = {NULL, NULL, NULL, qs_gate, ss_gate};
+    wmat su = {NULL, NULL, NULL, qs_up, ss_up}, sd = {NULL, NULL, NULL, qs_down, ss_down};
     return forward_impl(x, w_router, bias, g, u, d, sg, su, sd, w_sg, T, H, E, k, I, I_s, ids_in, y, ids_out, w_out,
                         s_out, logits_out, h_out, o_out, hs_out, os_out);
 }

@@ -256,6 +256,41 @@ def add_fp8_weights(inp: Dict[str, object]) -> Dict[str, object]:
     return out
 
 
+Q4_GROUP = 32
+
+
+def add_q4_weights(inp: Dict[str, object]) -> Dict[str, object]:
+    """Add 4-bit copies of the expert weights of ``inp`` (a make_inputs result).
+
+    For every expert matrix key K in FP8_KEYS that is present, adds
+    ``K + "_q4"`` (uint8, last axis halved: two signed 4-bit weights per
+    byte, the even index in the low nibble) and ``K + "_q4scale"`` (uint16
+    fp16 bit patterns, last axis / 32: one scale per group of 32 weights).
+    The scale of a group is its largest magnitude / 7 rounded to fp16 by
+    NumPy (1 for an all-zero group); the weights are the bf16 values divided
+    by the group's scale, rounded to the nearest integer (NumPy's rint) and
+    clamped to [-8, 7].  Returns a new dict; the BF16 arrays stay as they are.
+    """
+    out = dict(inp)
+    for key in FP8_KEYS:
+        w = inp.get(key)
+        if w is None:
+            out[key + "_q4"] = out[key + "_q4scale"] = None
+            continue
+        v = bf16_bits_to_f32(w).astype(np.float32)
+        shape = v.shape
+        g = v.reshape(shape[:-1] + (shape[-1] // Q4_GROUP, Q4_GROUP))
+        amax = np.abs(g).max(axis=-1)
+        scale = np.where(amax > 0, amax / np.float32(7.0), np.float32(1.0)).astype(np.float16)
+        s32 = scale.astype(np.float32)
+        s32 = np.where(s32 > 0, s32, np.float32(1.0))
+        q = np.clip(np.rint(g / s32[..., None]), -8, 7).astype(np.int8).reshape(shape)
+        u = (q.astype(np.int16) & 15).astype(np.uint8)
+        out[key + "_q4"] = (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+        out[key + "_q4scale"] = scale.view(np.uint16).copy()
+    return out
+
+
 def content_hash(inputs: Dict[str, object]) -> str:
     h = hashlib.sha256()
     for key in ("x", "w_router", "bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down", "w_sg"):

@@ -20,7 +20,12 @@ when the oracle disagrees with what the mathematics fixes:
 * FP8 expert weights: the E4M3 decoder against the values the OCP FP8
   definition fixes and against torch's float8_e4m3fn cast for all 256
   codes; the FP8 layer against the BF16 layer on the same (exactly
-  representable) dequantised weights, and against the dense mixture.
+  representable) dequantised weights, and against the dense mixture;
+* 4-bit expert weights: the fp16 decoder against NumPy's float16 for all
+  65,536 patterns; the dequantiser against integer weights packed here
+  (nibble order, sign, group of each scale); the 4-bit layer against the
+  BF16 layer on exactly representable weights and against the dense
+  mixture.
 
 The same functions run against deliberately mutated builds of the oracle
 (tests/test_oracle_mutants.py) to show that each planted mistake trips at
@@ -73,15 +78,25 @@ def _e4m3_torch(codes):
     return t.to(torch.float32).numpy().astype(F64)
 
 
-def _wf(inp, key, fp8):
-    """float64 expert matrix ``key``: bf16 values, or codes * row scale."""
+def _q4_pack(q):
+    """int weights in [-8, 7] [..., n] -> bytes [..., n/2], even index in the low nibble."""
+    u = (np.asarray(q).astype(np.int16) & 15).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _wf(inp, key, fp8, q4=False):
+    """float64 expert matrix ``key``: bf16 values, codes * row scale (FP8), or the 4-bit source
+    integers * group scale (``<key>_q4int`` kept by the pins that pack their own weights)."""
     if fp8:
         return _e4m3_torch(inp[key + "_fp8"]) * inp[key + "_scale"].astype(F64)[..., None]
+    if q4:
+        sc = inp[key + "_q4scale"].view(np.float16).astype(F64)
+        return inp[key + "_q4int"].astype(F64) * np.repeat(sc, 32, axis=-1)
     return _f(inp[key])
 
 
 # ------------------------------------------------------------ dense mixture
-def dense_gated_mixture(inp, k, fp8=False):
+def dense_gated_mixture(inp, k, fp8=False, q4=False):
     """float64 dense evaluation: every expert on every token, then the gate."""
     x = _f(inp["x"])
     wr = _f(inp["w_router"])
@@ -99,15 +114,15 @@ def dense_gated_mixture(inp, k, fp8=False):
     p = p / p.sum(axis=1, keepdims=True)
     G = np.where(sel, p, 0.0)
     G = G / G.sum(axis=1, keepdims=True)
-    wg, wu, wd = _wf(inp, "w_gate", fp8), _wf(inp, "w_up", fp8), _wf(inp, "w_down", fp8)
+    wg, wu, wd = _wf(inp, "w_gate", fp8, q4), _wf(inp, "w_up", fp8, q4), _wf(inp, "w_down", fp8, q4)
     y = np.zeros((T, x.shape[1]), F64)
     for e in range(E):
         he = _silu(x @ wg[e].T) * (x @ wu[e].T)
         y += G[:, e:e + 1] * (he @ wd[e].T)
     if inp.get("ws_gate") is not None:
         s = 1.0 / (1.0 + np.exp(-(x @ _f(inp["w_sg"]))))
-        hs = _silu(x @ _wf(inp, "ws_gate", fp8).T) * (x @ _wf(inp, "ws_up", fp8).T)
-        y += s[:, None] * (hs @ _wf(inp, "ws_down", fp8).T)
+        hs = _silu(x @ _wf(inp, "ws_gate", fp8, q4).T) * (x @ _wf(inp, "ws_up", fp8, q4).T)
+        y += s[:, None] * (hs @ _wf(inp, "ws_down", fp8, q4).T)
     ids = np.argsort(np.where(sel, rank, E + 1), axis=1, kind="stable")[:, :k]
     margin = np.sort(logits, axis=1)[:, ::-1]
     gaps = (margin[:, :min(k + 1, E) - 1] - margin[:, 1:min(k + 1, E)]).min(axis=1) if E > 1 else np.full(T, np.inf)
@@ -442,6 +457,81 @@ def pin_fp8_dense_mixture(orc):
     # the FP8 copy is close to the BF16 layer it was made from (a check of the generator)
     r16 = orc.forward(inp)
     assert _rel_l2(r["y"][clear], r16["y"][clear]) < 0.1
+
+
+# ----------------------------------------------------------- 4-bit weights
+def pin_f16_all_patterns(orc):
+    """fp16 decoder: every one of the 65,536 bit patterns against NumPy's float16."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = orc.f16_decode(bits)
+    ref = bits.view(np.float16).astype(F64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(v), nan)
+    assert np.array_equal(v[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(v[~nan]), np.signbit(ref[~nan]))
+
+
+def _q4_inputs(seed, pow2_scales, **kw):
+    """Tiny layer with 4-bit weights packed here from random integers in [-8, 7]."""
+    inp = _inputs(seed=seed, **kw)
+    rng = np.random.default_rng(seed + 200)
+    for key in synth.FP8_KEYS:
+        if inp.get(key) is None:
+            inp[key + "_q4"] = inp[key + "_q4scale"] = inp[key + "_q4int"] = None
+            continue
+        shape = inp[key].shape
+        q = rng.integers(-8, 8, size=shape)
+        ng = shape[:-1] + (shape[-1] // 32,)
+        if pow2_scales:
+            sc = np.ldexp(1.0, rng.integers(-10, -5, size=ng)).astype(np.float16)
+        else:
+            sc = (rng.uniform(0.5, 2.0, size=ng) * 2.0 ** -7).astype(np.float16)
+        inp[key + "_q4int"] = q
+        inp[key + "_q4"] = _q4_pack(q)
+        inp[key + "_q4scale"] = sc.view(np.uint16)
+    return inp
+
+
+def pin_q4_dequant_roundtrip(orc):
+    """Dequantised 4-bit matrix == the packed integers times their group's fp16 scale."""
+    rng = np.random.default_rng(40)
+    for rows, n in ((3, 32), (5, 96), (2, 256)):
+        q = rng.integers(-8, 8, size=(rows, n))
+        q[0, :16] = np.arange(-8, 8)  # every value, at even and odd positions
+        sc = (rng.uniform(-2.0, 2.0, size=(rows, n // 32))).astype(np.float16)
+        got = orc.q4_dequant(_q4_pack(q), sc.view(np.uint16))
+        assert np.array_equal(got, q.astype(F64) * np.repeat(sc.astype(F64), 32, axis=1))
+
+
+def pin_q4_matches_bf16_on_exact_weights(orc):
+    """Power-of-two group scales make every 4-bit weight exact in bf16: the layers agree bitwise."""
+    for kw in (dict(), dict(I_s=32, E=6, k=3)):
+        inp = _q4_inputs(41, True, **kw)
+        bf = dict(inp)
+        for key in synth.FP8_KEYS:
+            if inp.get(key) is None:
+                continue
+            w = _wf(inp, key, False, True)
+            bits = synth.f32_to_bf16_bits(w.astype(np.float32))
+            assert np.array_equal(synth.bf16_bits_to_f32(bits).astype(F64), w)
+            bf[key] = bits
+        r4 = orc.forward(inp, q4=True, want=("h", "o"))
+        r16 = orc.forward(bf, want=("h", "o"))
+        for name in ("y", "h", "o", "w", "ids"):
+            assert np.array_equal(r4[name], r16[name]), name
+
+
+def pin_q4_dense_mixture(orc):
+    """4-bit layer with arbitrary fp16 group scales == dense gated mixture on the dequantised weights."""
+    inp = _q4_inputs(42, False, I_s=32)
+    inp["bias"] = (np.random.default_rng(43).standard_normal(8) * 0.5).astype(np.float32)
+    y_ref, ids_ref, _, gaps = dense_gated_mixture(inp, inp["wl"].k, q4=True)
+    r = orc.forward(inp, q4=True)
+    clear = gaps > 1e-4
+    assert clear.sum() >= 0.8 * len(clear)
+    assert np.array_equal(r["ids"][clear], ids_ref[clear])
+    assert _rel_l2(r["y"][clear], y_ref[clear]) < 1e-6
+    np.testing.assert_allclose(r["y"][clear], y_ref[clear], rtol=0, atol=1e-7)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -44,6 +44,12 @@ MUTANTS = {
     "fp8_scale_by_column": ("acc += (double)bf16_to_f32(x[i]) * (sc * e4m3_value(q[i]));",
                             "acc += (double)bf16_to_f32(x[i]) * ((double)m.scale[i % 8] * e4m3_value(q[i]));"),
     "fp8_down_scale_by_column": ("return (double)m.scale[r] * e4m3_value", "return (double)m.scale[c] * e4m3_value"),
+    "q4_nibbles_swapped": ("int nib = (c & 1) ? (row[c / 2] >> 4) : (row[c / 2] & 15);",
+                           "int nib = (c & 1) ? (row[c / 2] & 15) : (row[c / 2] >> 4);"),
+    "q4_offset_binary": ("return nib >= 8 ? nib - 16 : nib;", "return nib - 8;"),
+    "q4_group_of_scale": ("(f16_value(s[i / Q4_GROUP]) * (double)q4_weight(q, (size_t)i));",
+                          "(f16_value(s[i % (n / Q4_GROUP)]) * (double)q4_weight(q, (size_t)i));"),
+    "f16_exponent_bias": ("mag = ldexp(1.0 + (double)m / 1024.0, e - 15);", "mag = ldexp(1.0 + (double)m / 1024.0, e - 16);"),
     "align_not_stable": ("for (size_t a = 0; a < n; ++a) {\n        int e = ids[a];",
                          "for (size_t a = n; a-- > 0;) {\n        int e = ids[a];"),
     "logit_dot_stride": ("float v = dot_bf16_f32(xt, w_router + (size_t)e * H, H);",
