@@ -131,6 +131,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight calls")
     ap.add_argument("--no-chunks", action="store_true", help="skip the bucketed-prefill runner")
+    ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit-weight calls")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--kernel", choices=["gate_up"], default=None,
@@ -493,6 +494,52 @@ def main():
                                     f"{reps} replays; prefill: 10 eager steps after 5", "per_T": f8,
                           "prefill": {"T": T, "ms_per_step": qms, "tokens_per_s": T / (qms * 1e-3)}}
             del qcopies, qbase
+            torch.cuda.empty_cache()
+
+        # 4-bit expert weights (signed nibbles, fp16 scale per 32 weights): T = 1, 2, 8, 32.
+        # bytes = router (bf16) + per touched expert 3*H*I/2 code bytes and 3*H*I/32 fp16 scales
+        # + the shared expert likewise + x + y
+        if not args.no_q4:
+            t0 = time.time()
+            q4 = synth.add_q4_weights(dinp)
+            log(f"[bench] 4-bit weights made in {time.time() - t0:.1f}s")
+            q4base = DeviceLayer.from_inputs(q4, dev, q4=True)
+            q4copies = [q4base.q]
+            for _ in range(max(0, args.decode_copies - 1)):
+                q4copies.append({key: (None if v is None else v.clone()) for key, v in q4base.q.items()})
+            Wr4, Wsg4 = q4base.w["w_router"], q4base.w["w_sg"]
+
+            def q4_bytes(n_touched, Tb):
+                per_e = 3 * H * I // 2 + 3 * H * I // 32 * 2
+                shared = 3 * H * I_s // 2 + 3 * H * I_s // 32 * 2
+                return 2 * (E * H + H) + n_touched * per_e + shared + 2 * 2 * Tb * H
+
+            f4 = {}
+            for Tb in (1, 2, 8, 32):
+                nc = nx if Tb == 1 else ncall
+                xb = to_device_bf16(synth._draw_bf16(1 if Tb == 1 else 2, "x", (nc * Tb, H), 1.0), dev)
+                yb = torch.empty((nc * Tb, H), dtype=torch.bfloat16, device=dev)
+                q4ws, q4ws_bytes = q4base.workspace(Tb)
+
+                def q4step(i, Tb=Tb, xb=xb, yb=yb, q4ws=q4ws, q4ws_bytes=q4ws_bytes):
+                    Q = q4copies[i % len(q4copies)]
+                    moe.moe_forward_q4(xb[i * Tb:(i + 1) * Tb], Wr4, None, Q["w_gate_q4"], Q["w_gate_q4scale"],
+                                       Q["w_up_q4"], Q["w_up_q4scale"], Q["w_down_q4"], Q["w_down_q4scale"],
+                                       Q["ws_gate_q4"], Q["ws_gate_q4scale"], Q["ws_up_q4"], Q["ws_up_q4scale"],
+                                       Q["ws_down_q4"], Q["ws_down_q4scale"], Wsg4, Tb, H, E, k, I, I_s,
+                                       yb[i * Tb:(i + 1) * Tb], q4ws, q4ws_bytes)
+                touched = [k] * nc if Tb == 1 else touched_experts(q4step, Tb, q4ws, nc)
+                qb = float(np.mean([q4_bytes(n, Tb) for n in touched]))
+                qus = graph_us(q4step, nc)
+                f4[str(Tb)] = {"us_per_call": qus, "tokens_per_s": Tb / (qus * 1e-6),
+                               "touched_experts": float(np.mean(touched)), "bytes_per_call": qb,
+                               "GB_per_s": qb / (qus * 1e-6) / 1e9, "hbm_frac": qb / (qus * 1e-6) / 1e9 / PEAK_HBM_GBS}
+                log(f"[bench] 4-bit weights T={Tb}: {qus:.1f} us/call, {f4[str(Tb)]['GB_per_s']:.0f} GB/s")
+            out["q4"] = {"workload": "1, 2, 8 and 32 tokens per call, decode-config shapes, expert weights as "
+                                     "signed 4-bit integers with an fp16 scale per 32 weights, no router bias",
+                         "timing": f"HIP graph of {nx} (T=1) or 16 calls over {len(q4copies)} weight copies, "
+                                   f"{reps} replays", "per_T": f4}
+            del q4copies, q4base
             torch.cuda.empty_cache()
 
     # -------------------------------------------------------- cpu baseline

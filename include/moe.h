@@ -171,6 +171,36 @@ int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* ro
                     uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * The whole layer with 4-bit expert weights, for 1 <= T <= MOE_Q4_MAX_T
+ * (single-token and small-batch steps, where reading the weights bounds the
+ * step).  kongchang.com "GFX1151 engine" (section on the two weight formats)
+ * names GGUF files with 4-bit integer (Q4) quantisation; the layout here is a
+ * plain group-wise one of this library's own (not a GGUF block layout):
+ * every output row is cut into groups of 32 consecutive weights along the
+ * reduction index, each group has one IEEE fp16 scale, each weight is a
+ * signed 4-bit integer q in [-8, 7] (two's complement), two per byte with the
+ * even index in the low nibble:  W[r][c] = scale[r][c / 32] * q[r][c].
+ * Same arithmetic and outputs as moe_forward on the dequantised weights.
+ *
+ * Inputs:  q_gate, q_up [E,I,H/2] and q_down [E,H,I/2] uint8 with fp16 scale
+ *          bits s_gate, s_up [E,I,H/32] and s_down [E,H,I/32]; shared expert
+ *          qs_gate, qs_up [I_s,H/2], qs_down [H,I_s/2] with ss_gate, ss_up
+ *          [I_s,H/32], ss_down [H,I_s/32] -- these six and w_sg all NULL with
+ *          I_s = 0, or all set; router, bias, w_sg, y and the workspace
+ *          (moe_workspace_size) as in moe_forward.
+ * T > MOE_Q4_MAX_T gives MOE_ERR_SHAPE.  Non-finite scales give non-finite
+ * outputs (not checked).
+ */
+#define MOE_Q4_MAX_T 32
+int moe_forward_q4(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
+                   const uint8_t* q_gate, const uint16_t* s_gate, const uint8_t* q_up, const uint16_t* s_up,
+                   const uint8_t* q_down, const uint16_t* s_down,
+                   const uint8_t* qs_gate, const uint16_t* ss_gate, const uint8_t* qs_up, const uint16_t* ss_up,
+                   const uint8_t* qs_down, const uint16_t* ss_down, const uint16_t* w_sg,
+                   int T, int H, int E, int k, int I, int I_s,
+                   uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * out[i] = value of the E4M3 code codes[i] (as defined for moe_forward_fp8),
  * computed with the same device conversion the FP8 kernels use; NaN codes
  * give NaN.  codes [n] uint8 and out [n] fp32, device pointers, 16-byte

@@ -21,10 +21,12 @@
 // Wave sums use DPP row shifts and row broadcasts (no LDS round trips).
 //
 // The expert matrices may be FP8 E4M3 codes with one fp32 scale per output
-// row (kongchang.com "GFX1151 engine", section on the two weight formats:
-// FP8-quantised weights for speed and memory): then every weight load moves
-// 8 bytes for the same 8 values, the codes are converted to fp32 in
-// registers, and the row's scale multiplies the row's dot product.
+// row, or 4-bit weights with an fp16 scale per group of 32 (kongchang.com
+// "GFX1151 engine", section on the two weight formats: FP8-quantised and
+// 4-bit GGUF weights): then every weight load moves 8 or 4 bytes for the same
+// 8 values, the codes are converted to fp32 in registers, and the FP8 row's
+// scale multiplies the row's dot product (a 4-bit group's scale multiplies
+// its weights as they are converted).
 #include "moe_internal.h"
 #include "moe_topk.h"
 
@@ -60,7 +62,8 @@ DecodeWs carve(void* base, int H, int E, int k, int I, int I_s) {
   return d;
 }
 
-// Dot product of 8 bf16 x values with 8 weights (bf16 or E4M3 codes).
+// Dot product of 8 bf16 x values with 8 weights (bf16, E4M3 codes, or 4-bit
+// weights times their group scale).
 template <class W>
 __device__ __forceinline__ float dot8(u32x4 a, const W& b) {
   float f[8];
@@ -74,14 +77,14 @@ __device__ __forceinline__ float dot8(u32x4 a, const W& b) {
   return s;
 }
 
-// Dot products of x with one or two weight rows of length H (bf16, or E4M3
-// codes with Q; unscaled).  x comes from LDS (sx) when given, else straight
+// Dot products of x with one or two weight rows of length H (r1 used when
+// two; FP8 rows unscaled).  x comes from LDS (sx) when given, else straight
 // from global memory; every load of a group of 4 chunks per lane (x's
 // included) is issued before the arithmetic.
-template <bool Q>
-__device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* xg, const void* r0, const void* r1, int H,
-                                         int lane, float& d0, float& d1) {
-  typedef wchunk_t<Q> WC;
+template <int F>
+__device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* xg, const WRow<F>& r0, const WRow<F>& r1,
+                                         bool two, int H, int lane, float& d0, float& d1) {
+  typedef wchunk_t<F> WC;
   const int nch = H / 8;
   d0 = 0.0f;
   d1 = 0.0f;
@@ -92,8 +95,8 @@ __device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* xg, co
     for (int q = 0; q < 4; ++q) {
       int c = base + q * 64 + lane;
       if (c < nch) {
-        a[q] = reinterpret_cast<const WC*>(r0)[c];
-        if (r1) b[q] = reinterpret_cast<const WC*>(r1)[c];
+        a[q] = r0[c];
+        if (two) b[q] = r1[c];
         xv[q] = sx ? sx[c] : reinterpret_cast<const u32x4*>(xg)[c];
       }
     }
@@ -102,7 +105,7 @@ __device__ __forceinline__ void row_dots(const u32x4* sx, const uint16_t* xg, co
       int c = base + q * 64 + lane;
       if (c < nch) {
         d0 += dot8(xv[q], a[q]);
-        if (r1) d1 += dot8(xv[q], b[q]);
+        if (two) d1 += dot8(xv[q], b[q]);
       }
     }
   }
@@ -119,14 +122,16 @@ __global__ __launch_bounds__(256) void decode_router_kernel(const uint16_t* __re
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   float d0, d1;
   if (row < E) {
-    row_dots<false>(nullptr, x, wr + (size_t)row * H, nullptr, H, lane, d0, d1);
+    const WRow<W_BF16> r = wrow<W_BF16>(wr, nullptr, (size_t)row, H);
+    row_dots<W_BF16>(nullptr, x, r, r, false, H, lane, d0, d1);
     if (lane == 0) {
       float v = d0 + (bias ? bias[row] : 0.0f);
       if (v == 0.0f) v = 0.0f;
       d.logits[row] = v;
     }
   } else if (row == E && w_sg) {
-    row_dots<false>(nullptr, x, w_sg, nullptr, H, lane, d0, d1);
+    const WRow<W_BF16> r = wrow<W_BF16>(w_sg, nullptr, 0, H);
+    row_dots<W_BF16>(nullptr, x, r, r, false, H, lane, d0, d1);
     if (lane == 0) d.s[0] = 1.0f / (1.0f + expf(-d0));
   }
 }
@@ -157,11 +162,11 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ logits, int
 
 // While wave 0 selects the experts, waves 1..3 compute the shared expert's
 // gate/up rows (they do not depend on the routing): row i = silu(g) * u -> h_s.
-template <bool Q>
+template <int F>
 __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t* __restrict__ x, ExpertWeights W,
                                                                   int H, int E, int k, int I, int I_s, DecodeWs d) {
-  typedef wchunk_t<Q> WC;
-  typedef welem_t<Q> WE;
+  typedef wchunk_t<F> WC;
+  constexpr bool RS = F == W_FP8;  // one scale per row, applied to the row's dot product
   __shared__ u32x4 sx[1024];
   __shared__ int sel_e[kMaxK];
   __shared__ float sel_w[kMaxK];
@@ -170,13 +175,12 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
   if (wave == 0) {
     block_topk(d.logits, E, k, sel_e, sel_w);
   } else {
-    const WE* sg = static_cast<const WE*>(W.s_gate);
-    const WE* su = static_cast<const WE*>(W.s_up);
     for (int i = blockIdx.x * 3 + wave - 1; i < I_s; i += 3 * gridDim.x) {
-      const float scg = Q ? W.ssc_gate[i] : 1.0f, scu = Q ? W.ssc_up[i] : 1.0f;  // issued with the row loads
+      const float scg = RS ? W.ssc_gate[i] : 1.0f, scu = RS ? W.ssc_up[i] : 1.0f;  // issued with the row loads
       float g, u;
-      row_dots<Q>(nullptr, x, sg + (size_t)i * H, su + (size_t)i * H, H, threadIdx.x & 63, g, u);
-      if (Q) {
+      row_dots<F>(nullptr, x, wrow<F>(W.s_gate, W.gss_gate, (size_t)i, H), wrow<F>(W.s_up, W.gss_up, (size_t)i, H),
+                  true, H, threadIdx.x & 63, g, u);
+      if (RS) {
         g *= scg;
         u *= scu;
       }
@@ -195,9 +199,9 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
   const int nch = H / 8;  // chunks per weight row; lane handles chunks lane + 64 c
   const int rr = row < k * I ? row : 0;
   const size_t rix = (size_t)sel_e[rr / I] * I + rr % I;  // row of W_gate / W_up
-  const WC* gp = reinterpret_cast<const WC*>(static_cast<const WE*>(W.gate) + rix * H);
-  const WC* up = reinterpret_cast<const WC*>(static_cast<const WE*>(W.up) + rix * H);
-  const float scg = Q ? W.sc_gate[rix] : 1.0f, scu = Q ? W.sc_up[rix] : 1.0f;  // in flight with the rows
+  const WRow<F> gp = wrow<F>(W.gate, W.gs_gate, rix, H);
+  const WRow<F> up = wrow<F>(W.up, W.gs_up, rix, H);
+  const float scg = RS ? W.sc_gate[rix] : 1.0f, scu = RS ? W.sc_up[rix] : 1.0f;  // in flight with the rows
   float g = 0.0f, u = 0.0f;
   for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
     WC a[4], b[4];
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
     }
   }
   float gs = wave_sum(g), us = wave_sum(u);
-  if (Q) {
+  if (RS) {
     gs *= scg;
     us *= scu;
   }
@@ -229,16 +233,14 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
 
 // Wave per output column: the k + 1 weight rows of the column are loaded
 // together (I / 8 chunks each), and each h value read serves them all.
-template <int KT, bool Q>  // k <= KT
+template <int KT, int F>  // k <= KT
 __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H, int k, int I, int I_s, DecodeWs d,
                                                           uint16_t* __restrict__ y) {
-  typedef wchunk_t<Q> WC;
-  typedef welem_t<Q> WE;
+  typedef wchunk_t<F> WC;
+  constexpr bool RS = F == W_FP8;
   const int lane = threadIdx.x & 63;
   const int c0 = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (c0 >= H) return;
-  const WE* wd = static_cast<const WE*>(W.down);
-  const WE* wsd = static_cast<const WE*>(W.s_down);
   // ids and weights: KT entries read with 16-byte loads (their workspace
   // slots hold 64 entries), entries past k unused
   int ids[KT];
@@ -255,8 +257,12 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
   // row scales, loaded with the first weight rows rather than after the sums
   float scd[KT], scs = 1.0f;
 #pragma unroll
-  for (int j = 0; j < KT; ++j) scd[j] = Q ? W.sc_down[(size_t)ids[j] * H + c0] : 1.0f;
-  if (Q && I_s > 0) scs = W.ssc_down[c0];
+  for (int j = 0; j < KT; ++j) scd[j] = RS ? W.sc_down[(size_t)ids[j] * H + c0] : 1.0f;
+  if (RS && I_s > 0) scs = W.ssc_down[c0];
+  WRow<F> rows[KT];
+#pragma unroll
+  for (int j = 0; j < KT; ++j) rows[j] = wrow<F>(W.down, W.gs_down, (size_t)ids[j] * H + c0, I);
+  const WRow<F> srow = wrow<F>(W.s_down, W.gss_down, (size_t)c0, I_s);
   float part[KT + 1];
 #pragma unroll
   for (int j = 0; j <= KT; ++j) part[j] = 0.0f;
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
     WC wsv;
     float4 hs0 = {}, hs1 = {};
     if (okS) {
-      wsv = reinterpret_cast<const WC*>(wsd + (size_t)c0 * I_s)[ch];
+      wsv = srow[ch];
       const float4* hp = reinterpret_cast<const float4*>(d.hs + ch * 8);
       hs0 = hp[0];
       hs1 = hp[1];
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
     WC wv[KT];
 #pragma unroll
     for (int j = 0; j < KT; ++j)
-      if (j < k && okI) wv[j] = reinterpret_cast<const WC*>(wd + ((size_t)ids[j] * H + c0) * I)[ch];
+      if (j < k && okI) wv[j] = rows[j][ch];
     if (okS) {
       const float hv[8] = {hs0.x, hs0.y, hs0.z, hs0.w, hs1.x, hs1.y, hs1.z, hs1.w};
       accum(part[KT], wsv, hv);
@@ -310,12 +316,12 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
   for (int j = 0; j < KT; ++j)
     if (j < k) {
       float oj = wave_sum(part[j]);
-      if (Q) oj *= scd[j];
+      if (RS) oj *= scd[j];
       yv += wsel[j] * oj;  // rank order
     }
   if (I_s > 0) {
     float os = wave_sum(part[KT]);
-    if (Q) os *= scs;
+    if (RS) os *= scs;
     yv += d.s[0] * os;
   }
   if (lane == 0) y[c0] = f32_to_bf16(yv);
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(256) void e4m3_to_f32_kernel(const uint8_t* __restr
   }
 }
 
-template <bool Q>
+template <int F>
 void launch_decode_t(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
                      const ExpertWeights& W, int H, int E, int k, int I, int I_s, uint16_t* y, DecodeWs d,
                      hipStream_t st) {
@@ -347,13 +353,13 @@ void launch_decode_t(const uint16_t* x, const uint16_t* w_router, const float* b
   hipLaunchKernelGGL(decode_router_kernel, dim3((rows1 + 3) / 4), dim3(256), 0, st, x, w_router, bias,
                      I_s > 0 ? w_sg : nullptr, H, E, d);
   // 4 waves per workgroup, one routed row pair per wave; waves 1..3 also take the shared rows
-  hipLaunchKernelGGL(decode_topk_gate_up_kernel<Q>, dim3((k * I + 3) / 4), dim3(256), 0, st, x, W, H, E, k, I, I_s,
+  hipLaunchKernelGGL(decode_topk_gate_up_kernel<F>, dim3((k * I + 3) / 4), dim3(256), 0, st, x, W, H, E, k, I, I_s,
                      d);
   // 4 waves per workgroup, one output column per wave (H is a multiple of 256)
   if (k <= 8)
-    hipLaunchKernelGGL((decode_down_kernel<8, Q>), dim3((H + 3) / 4), dim3(256), 0, st, W, H, k, I, I_s, d, y);
+    hipLaunchKernelGGL((decode_down_kernel<8, F>), dim3((H + 3) / 4), dim3(256), 0, st, W, H, k, I, I_s, d, y);
   else
-    hipLaunchKernelGGL((decode_down_kernel<kMaxK, Q>), dim3((H + 3) / 4), dim3(256), 0, st, W, H, k, I, I_s, d, y);
+    hipLaunchKernelGGL((decode_down_kernel<kMaxK, F>), dim3((H + 3) / 4), dim3(256), 0, st, W, H, k, I, I_s, d, y);
 }
 
 }  // namespace
@@ -370,10 +376,12 @@ hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const floa
                          const ExpertWeights& W, int H, int E, int k, int I, int I_s, uint16_t* y, void* ws,
                          hipStream_t st) {
   DecodeWs d = carve(ws, H, E, k, I, I_s);
-  if (W.fp8)
-    launch_decode_t<true>(x, w_router, bias, w_sg, W, H, E, k, I, I_s, y, d, st);
+  if (W.fmt == W_FP8)
+    launch_decode_t<W_FP8>(x, w_router, bias, w_sg, W, H, E, k, I, I_s, y, d, st);
+  else if (W.fmt == W_Q4)
+    launch_decode_t<W_Q4>(x, w_router, bias, w_sg, W, H, E, k, I, I_s, y, d, st);
   else
-    launch_decode_t<false>(x, w_router, bias, w_sg, W, H, E, k, I, I_s, y, d, st);
+    launch_decode_t<W_BF16>(x, w_router, bias, w_sg, W, H, E, k, I, I_s, y, d, st);
   return hipGetLastError();
 }
 

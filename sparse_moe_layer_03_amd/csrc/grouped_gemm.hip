@@ -533,7 +533,7 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
   u32x4* sA = reinterpret_cast<u32x4*>(smem);  // [2][BM*KCH]
   u32x4* sB = sA + 2 * BM * KCH;               // [2][BNB*KCH]
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  typedef wchunk_t<Q> BC;  // B chunk as loaded: 8 bf16, or 8 E4M3 codes
+  typedef wchunk_t<Q ? W_FP8 : W_BF16> BC;  // B chunk as loaded: 8 bf16, or 8 E4M3 codes
   u32x4 pa0[NA], pa1[NA];
   BC pb0[NB], pb1[NB];
   auto gload = [&](u32x4 (&pa)[NA], BC (&pb)[NB], int kb) {

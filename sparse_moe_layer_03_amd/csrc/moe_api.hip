@@ -404,8 +404,9 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
   hipStream_t st = (hipStream_t)stream;
 
   if (T <= kSmallMaxT) {
-    const ExpertWeights W = {w_gate,  w_up,    w_down,  ws_gate, ws_up,   ws_down, nullptr,
-                             nullptr, nullptr, nullptr, nullptr, nullptr, false};
+    ExpertWeights W = {};
+    W.gate = w_gate, W.up = w_up, W.down = w_down, W.s_gate = ws_gate, W.s_up = ws_up, W.s_down = ws_down;
+    W.fmt = W_BF16;
     if (T == 1)
       return hip_status(launch_decode(x, w_router, router_bias, w_sg, W, H, E, k, I, I_s, y, workspace, st),
                         "moe_forward (decode)");
@@ -443,8 +444,11 @@ int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* ro
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
   if ((rc = check_arch())) return rc;
   hipStream_t st = (hipStream_t)stream;
-  const ExpertWeights W = {q_gate,  q_up,   q_down,  qs_gate,  qs_up,  qs_down, sc_gate,
-                           sc_up,   sc_down, ssc_gate, ssc_up, ssc_down, true};
+  ExpertWeights W = {};
+  W.gate = q_gate, W.up = q_up, W.down = q_down, W.s_gate = qs_gate, W.s_up = qs_up, W.s_down = qs_down;
+  W.sc_gate = sc_gate, W.sc_up = sc_up, W.sc_down = sc_down;
+  W.ssc_gate = ssc_gate, W.ssc_up = ssc_up, W.ssc_down = ssc_down;
+  W.fmt = W_FP8;
   if (T == 1)
     return hip_status(launch_decode(x, w_router, router_bias, w_sg, W, H, E, k, I, I_s, y, workspace, st),
                       "moe_forward_fp8 (decode)");
@@ -454,6 +458,46 @@ int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* ro
   const FP8Scales q = {sc_gate, sc_up, sc_down, ssc_gate, ssc_up, ssc_down};
   return forward_tiled(x, w_router, router_bias, q_gate, q_up, q_down, qs_gate, qs_up, qs_down, w_sg, T, H, E, k, I,
                        I_s, y, workspace, layout(T, H, E, k, I, I_s), &q, st);
+}
+
+int moe_forward_q4(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint8_t* q_gate,
+                   const uint16_t* s_gate, const uint8_t* q_up, const uint16_t* s_up, const uint8_t* q_down,
+                   const uint16_t* s_down, const uint8_t* qs_gate, const uint16_t* ss_gate, const uint8_t* qs_up,
+                   const uint16_t* ss_up, const uint8_t* qs_down, const uint16_t* ss_down, const uint16_t* w_sg, int T,
+                   int H, int E, int k, int I, int I_s, uint16_t* y, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  int rc = check_common_shapes(T, H, E, k);
+  if (rc || (rc = check_ffn_shapes(I, I_s))) return rc;
+  if (T > MOE_Q4_MAX_T)
+    return fail(MOE_ERR_SHAPE, "moe_forward_q4: T=%d; 4-bit expert weights are supported for T <= %d", T, MOE_Q4_MAX_T);
+  const int n_shared = (qs_gate != nullptr) + (ss_gate != nullptr) + (qs_up != nullptr) + (ss_up != nullptr) +
+                       (qs_down != nullptr) + (ss_down != nullptr) + (w_sg != nullptr);
+  if (I_s == 0 && n_shared != 0) return fail(MOE_ERR_SHAPE, "moe_forward_q4: shared-expert tensors given with I_s = 0");
+  if (I_s > 0 && n_shared != 7)
+    return fail(MOE_ERR_NULL, "moe_forward_q4: I_s > 0 needs qs_*, ss_* (gate, up, down) and w_sg");
+  if (T == 0) return ok();
+  if (!x || !w_router || !q_gate || !s_gate || !q_up || !s_up || !q_down || !s_down || !y || !workspace)
+    return fail(MOE_ERR_NULL, "moe_forward_q4: x, w_router, q_*/s_* (gate, up, down), y and workspace are required");
+  const void* ptrs[] = {x,       w_router, q_gate, s_gate, q_up,    s_up,    q_down, s_down, y,
+                        qs_gate, ss_gate,  qs_up,  ss_up,  qs_down, ss_down, w_sg};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MOE_ERR_ALIGN, "moe_forward_q4: tensor pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MOE_ERR_ALIGN, "moe_forward_q4: workspace must be 256-byte aligned");
+  const size_t need = moe_workspace_size(T, H, E, k, I, I_s);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  if ((rc = check_arch())) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  ExpertWeights W = {};
+  W.gate = q_gate, W.up = q_up, W.down = q_down, W.s_gate = qs_gate, W.s_up = qs_up, W.s_down = qs_down;
+  W.gs_gate = s_gate, W.gs_up = s_up, W.gs_down = s_down;
+  W.gss_gate = ss_gate, W.gss_up = ss_up, W.gss_down = ss_down;
+  W.fmt = W_Q4;
+  if (T == 1)
+    return hip_status(launch_decode(x, w_router, router_bias, w_sg, W, H, E, k, I, I_s, y, workspace, st),
+                      "moe_forward_q4 (decode)");
+  return hip_status(launch_small_batch(x, w_router, router_bias, w_sg, W, T, H, E, k, I, I_s, y, workspace, st),
+                    "moe_forward_q4 (small batch)");
 }
 
 int moe_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n, void* stream) {

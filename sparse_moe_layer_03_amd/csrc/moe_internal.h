@@ -36,12 +36,45 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// Eight consecutive weights of one row as one load: 16 bytes of BF16, or 8
-// bytes of FP8 E4M3 codes (Q).
-template <bool Q> struct WChunk { typedef u32x4 type; };
-template <> struct WChunk<true> { typedef u32x2 type; };
-template <bool Q> using wchunk_t = typename WChunk<Q>::type;
-template <bool Q> using welem_t = typename std::conditional<Q, uint8_t, uint16_t>::type;
+// Formats of the expert weight matrices.
+enum { W_BF16 = 0, W_FP8 = 1, W_Q4 = 2 };
+
+// 8 signed 4-bit weights (weight i in bits 4i..4i+3) and the fp16 bits of
+// their group's scale.
+struct q4chunk {
+  uint32_t w, s;
+};
+
+// Eight consecutive weights of one row as one load: 16 bytes of BF16, 8 bytes
+// of FP8 E4M3 codes, or 4 bytes of 4-bit weights with their group scale.
+template <int F> struct WChunk { typedef u32x4 type; };
+template <> struct WChunk<W_FP8> { typedef u32x2 type; };
+template <> struct WChunk<W_Q4> { typedef q4chunk type; };
+template <int F> using wchunk_t = typename WChunk<F>::type;
+
+// One weight row as the single-token and small-batch kernels read it: chunk
+// ch holds weights 8ch .. 8ch+7.
+template <int F>
+struct WRow {
+  const char* p;      // row start
+  const uint16_t* s;  // W_Q4: the row's fp16 group scales (one per 32 weights)
+  __device__ __forceinline__ wchunk_t<F> operator[](int ch) const {
+    if constexpr (F == W_Q4)
+      return q4chunk{reinterpret_cast<const uint32_t*>(p)[ch], (uint32_t)s[ch >> 2]};
+    else
+      return reinterpret_cast<const wchunk_t<F>*>(p)[ch];
+  }
+};
+
+// Row r (K weights long) of the matrix at m (gs: its group scales for W_Q4).
+template <int F>
+__device__ __forceinline__ WRow<F> wrow(const void* m, const uint16_t* gs, size_t r, int K) {
+  WRow<F> w;
+  const size_t bytes = F == W_BF16 ? (size_t)K * 2 : F == W_FP8 ? (size_t)K : (size_t)K / 2;
+  w.p = static_cast<const char*>(m) + r * bytes;
+  w.s = F == W_Q4 ? gs + r * (size_t)(K / 32) : nullptr;
+  return w;
+}
 
 __device__ __forceinline__ void chunk_to_f32(const u32x4& w, float* f) {
 #pragma unroll
@@ -63,6 +96,14 @@ __device__ __forceinline__ void chunk_to_f32(const u32x2& w, float* f) {
     f[4 * q + 2] = hi[0];
     f[4 * q + 3] = hi[1];
   }
+}
+
+// 4-bit weights times their group scale (exact in fp32: an 11-bit fp16
+// significand times an integer of at most 4 bits).
+__device__ __forceinline__ void chunk_to_f32(const q4chunk& c, float* f) {
+  const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)c.s);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = sc * (float)((int32_t)(c.w << (28 - 4 * i)) >> 28);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
@@ -95,15 +136,16 @@ __device__ __forceinline__ int xcd_item(int bid, int n_items) {
   return item < n_items ? item : -1;
 }
 
-// Expert weights as the single-token and small-batch kernels take them: BF16
-// matrices (fp8 false; scale pointers unused), or OCP FP8 E4M3 codes with one
-// fp32 scale per output row (fp8 true).  Routed gate/up [E,I,H] with scales
-// [E,I], down [E,H,I] with scales [E,H]; shared gate/up [I_s,H] with scales
-// [I_s], down [H,I_s] with scales [H].
+// Expert weights as the single-token and small-batch kernels take them (fmt):
+// BF16 matrices; OCP FP8 E4M3 codes with one fp32 scale per output row (sc_*,
+// ssc_*); or 4-bit weights, two per byte, with an fp16 scale per group of 32
+// weights of a row (gs_*, gss_*).  Routed gate/up [E,I,H], down [E,H,I];
+// shared gate/up [I_s,H], down [H,I_s].
 struct ExpertWeights {
   const void *gate, *up, *down, *s_gate, *s_up, *s_down;
   const float *sc_gate, *sc_up, *sc_down, *ssc_gate, *ssc_up, *ssc_down;
-  bool fp8;
+  const uint16_t *gs_gate, *gs_up, *gs_down, *gss_gate, *gss_up, *gss_down;
+  int fmt;
 };
 
 // Sets the thread's error message returned by moe_last_error() (cleared for

@@ -18,9 +18,10 @@
 //   S4 down: (touched expert, block of 64 output columns) per workgroup:
 //      o[a][c] = h[a] . W_down[e][c] in fp32 (shared: o_s[t][c])
 //   S5 combine: y[t][c] = sum_j w[t][j] o[t*k+j][c] (j ascending) + s[t] o_s[t][c]
-// With FP8 E4M3 expert weights (one fp32 scale per output row) the weight
-// loads move 8 bytes per 8 values, the codes are converted in registers and
-// the row's scale multiplies each dot product.
+// With FP8 E4M3 expert weights (one fp32 scale per output row) or 4-bit
+// weights (an fp16 scale per group of 32) the weight loads move 8 or 4 bytes
+// per 8 values and the codes are converted in registers; the FP8 row's scale
+// multiplies each dot product, a 4-bit group's scale its converted weights.
 #include "moe_internal.h"
 #include "moe_topk.h"
 
@@ -287,11 +288,11 @@ __global__ __launch_bounds__(1024) void sb_select_kernel(int T, int E, int k, Sm
 #define SB_GATE_UP_TOKENS 8
 #endif
 constexpr int GP = 2, GR = 4 * GP, GT = SB_GATE_UP_TOKENS;
-template <bool Q>
+template <int F>
 __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restrict__ x, ExpertWeights W, int T,
                                                          int H, int E, int k, int I, int I_s, SmallWs d) {
-  typedef wchunk_t<Q> WC;
-  typedef welem_t<Q> WE;
+  typedef wchunk_t<F> WC;
+  constexpr bool Q = F == W_FP8;  // one scale per row, applied to the row's dot products
   __shared__ u32x4 sx[GT * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nu = d.plan[0];
@@ -306,8 +307,12 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
   // assignment q of the expert (shared expert: token q)
   auto asg_at = [&](int q) { return shared ? q : (q < TBR ? rec[4 + q] : d.asg[off + q]); };
   const size_t r0 = shared ? (size_t)i0 : (size_t)e * I + i0;  // first of the wave's GP rows
-  const WE* g0 = static_cast<const WE*>(shared ? W.s_gate : W.gate) + r0 * H;
-  const WE* u0 = static_cast<const WE*>(shared ? W.s_up : W.up) + r0 * H;
+  WRow<F> gr[GP], ur[GP];
+#pragma unroll
+  for (int p = 0; p < GP; ++p) {
+    gr[p] = wrow<F>(shared ? W.s_gate : W.gate, shared ? W.gss_gate : W.gs_gate, r0 + p, H);
+    ur[p] = wrow<F>(shared ? W.s_up : W.up, shared ? W.gss_up : W.gs_up, r0 + p, H);
+  }
   float scg[GP], scu[GP];
 #pragma unroll
   for (int p = 0; p < GP; ++p) {
@@ -329,8 +334,8 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const int c = min(base + c4 * 64 + lane, nch - 1);
-          gv[p][c4] = reinterpret_cast<const WC*>(g0 + (size_t)p * H)[c];
-          uv[p][c4] = reinterpret_cast<const WC*>(u0 + (size_t)p * H)[c];
+          gv[p][c4] = gr[p][c];
+          uv[p][c4] = ur[p][c];
         }
       __syncthreads();
       stage_x<GT>(sx, x, H, base, nt, [&](int t) { return shared ? q0 + t : asg_at(q0 + t) / k; });
@@ -386,11 +391,11 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
 #define SB_DOWN_TOKENS 8
 #endif
 constexpr int DT = SB_DOWN_TOKENS;  // h rows staged at a time
-template <bool Q>
+template <int F>
 __global__ __launch_bounds__(256) void sb_down_kernel(ExpertWeights W, int T, int H, int E, int k, int I, int I_s,
                                                       SmallWs d) {
-  typedef wchunk_t<Q> WC;
-  typedef welem_t<Q> WE;
+  typedef wchunk_t<F> WC;
+  constexpr bool Q = F == W_FP8;
   __shared__ float4 shh[DT * 128];  // DT rows of up to 512 fp32 reduction values
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nu = d.plan[0];
@@ -403,14 +408,14 @@ __global__ __launch_bounds__(256) void sb_down_kernel(ExpertWeights W, int T, in
   const int e = shared ? 0 : rec[0], off = shared ? 0 : rec[1], cnt = shared ? T : rec[2];
   auto asg_at = [&](int q) { return shared ? q : (q < TBR ? rec[4 + q] : d.asg[off + q]); };
   const size_t wr = shared ? (size_t)col : (size_t)e * H + col;  // row of W_down / Ws_down
-  const WE* wrow = static_cast<const WE*>(shared ? W.s_down : W.down) + wr * K;
+  const WRow<F> wrw = wrow<F>(shared ? W.s_down : W.down, shared ? W.gss_down : W.gs_down, wr, K);
   const float sc = Q ? (shared ? W.ssc_down : W.sc_down)[wr] : 1.0f;
   const int nch = K / 8;
   for (int kb = 0; kb < nch; kb += 64) {  // reduction blocks of 512 values
     const int nb = min(64, nch - kb);        // chunks in this block (a multiple of 16)
     WC wv[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) wv[j] = reinterpret_cast<const WC*>(wrow)[kb + min(j * 4 + (lane & 3), nb - 1)];
+    for (int j = 0; j < 16; ++j) wv[j] = wrw[kb + min(j * 4 + (lane & 3), nb - 1)];
     for (int q0 = 0; q0 < cnt; q0 += DT) {
       const int nt = min(DT, cnt - q0);
       __syncthreads();
@@ -490,12 +495,15 @@ hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const
   const int max_u = (T * k < E ? T * k : E) + (I_s > 0 ? 1 : 0);
   const int nrow = I > I_s ? I : I_s;
   const dim3 g_gu((nrow + GR - 1) / GR, max_u), g_dn(H / 64, max_u);
-  if (W.fp8) {
-    hipLaunchKernelGGL(sb_gate_up_kernel<true>, g_gu, dim3(256), 0, st, x, W, T, H, E, k, I, I_s, d);
-    hipLaunchKernelGGL(sb_down_kernel<true>, g_dn, dim3(256), 0, st, W, T, H, E, k, I, I_s, d);
+  if (W.fmt == W_FP8) {
+    hipLaunchKernelGGL(sb_gate_up_kernel<W_FP8>, g_gu, dim3(256), 0, st, x, W, T, H, E, k, I, I_s, d);
+    hipLaunchKernelGGL(sb_down_kernel<W_FP8>, g_dn, dim3(256), 0, st, W, T, H, E, k, I, I_s, d);
+  } else if (W.fmt == W_Q4) {
+    hipLaunchKernelGGL(sb_gate_up_kernel<W_Q4>, g_gu, dim3(256), 0, st, x, W, T, H, E, k, I, I_s, d);
+    hipLaunchKernelGGL(sb_down_kernel<W_Q4>, g_dn, dim3(256), 0, st, W, T, H, E, k, I, I_s, d);
   } else {
-    hipLaunchKernelGGL(sb_gate_up_kernel<false>, g_gu, dim3(256), 0, st, x, W, T, H, E, k, I, I_s, d);
-    hipLaunchKernelGGL(sb_down_kernel<false>, g_dn, dim3(256), 0, st, W, T, H, E, k, I, I_s, d);
+    hipLaunchKernelGGL(sb_gate_up_kernel<W_BF16>, g_gu, dim3(256), 0, st, x, W, T, H, E, k, I, I_s, d);
+    hipLaunchKernelGGL(sb_down_kernel<W_BF16>, g_dn, dim3(256), 0, st, W, T, H, E, k, I, I_s, d);
   }
   hipLaunchKernelGGL(sb_combine_kernel, dim3((T * H + 255) / 256), dim3(256), 0, st, T, H, k, I_s, d, y);
   return hipGetLastError();

@@ -44,13 +44,16 @@ class DeviceLayer:
 
     ``fp8``: also upload the FP8 expert weights (``<key>_fp8`` codes and
     ``<key>_scale`` row scales of ``weights``); ``forward`` then calls
-    ``moe_forward_fp8``.
+    ``moe_forward_fp8``.  ``q4``: likewise the 4-bit weights (``<key>_q4``
+    codes and ``<key>_q4scale`` fp16 group scales) and ``moe_forward_q4``.
     """
 
-    def __init__(self, weights: Dict[str, np.ndarray], k: int, device="cuda:0", fp8: bool = False):
+    def __init__(self, weights: Dict[str, np.ndarray], k: int, device="cuda:0", fp8: bool = False,
+                 q4: bool = False):
         import torch
         self.device = torch.device(device)
         self.fp8 = fp8
+        self.q4 = q4
         self.w = {key: to_device_bf16(weights.get(key), self.device) for key in BF16_KEYS}
         self.q = {}
         if fp8:
@@ -59,6 +62,13 @@ class DeviceLayer:
                 self.q[key] = None if c is None else torch.from_numpy(np.ascontiguousarray(c, np.uint8)).to(self.device)
                 self.q[key + "_scale"] = (None if sc is None else
                                           torch.from_numpy(np.ascontiguousarray(sc, np.float32)).to(self.device))
+        if q4:
+            for key in FP8_KEYS:
+                c, sc = weights.get(key + "_q4"), weights.get(key + "_q4scale")
+                self.q[key + "_q4"] = (None if c is None else
+                                       torch.from_numpy(np.ascontiguousarray(c, np.uint8)).to(self.device))
+                self.q[key + "_q4scale"] = (None if sc is None else torch.from_numpy(
+                    np.ascontiguousarray(sc, np.uint16).view(np.int16)).to(self.device))
         b = weights.get("bias")
         self.bias = None if b is None else torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(self.device)
         E, I, H = weights["w_gate"].shape
@@ -68,8 +78,8 @@ class DeviceLayer:
         self._ws_bytes = 0
 
     @classmethod
-    def from_inputs(cls, inp, device="cuda:0", fp8: bool = False):
-        return cls(inp, inp["wl"].k, device, fp8=fp8)
+    def from_inputs(cls, inp, device="cuda:0", fp8: bool = False, q4: bool = False):
+        return cls(inp, inp["wl"].k, device, fp8=fp8, q4=q4)
 
     def workspace(self, T: int):
         import torch
@@ -91,6 +101,13 @@ class DeviceLayer:
             y = torch.empty((T, s.H), dtype=torch.bfloat16, device=self.device)
         ws, nbytes = self.workspace(T)
         W = self.w
+        if self.q4:
+            q = self.q
+            moe.moe_forward_q4(x, W["w_router"], self.bias, q["w_gate_q4"], q["w_gate_q4scale"], q["w_up_q4"],
+                               q["w_up_q4scale"], q["w_down_q4"], q["w_down_q4scale"], q["ws_gate_q4"],
+                               q["ws_gate_q4scale"], q["ws_up_q4"], q["ws_up_q4scale"], q["ws_down_q4"],
+                               q["ws_down_q4scale"], W["w_sg"], T, s.H, s.E, s.k, s.I, s.I_s, y, ws, nbytes, stream)
+            return y
         if self.fp8:
             q = self.q
             moe.moe_forward_fp8(x, W["w_router"], self.bias, q["w_gate"], q["w_gate_scale"], q["w_up"],

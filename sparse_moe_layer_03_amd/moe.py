@@ -23,11 +23,12 @@ MOE_ERR_WORKSPACE = -4
 MOE_ERR_ARCH = -5
 MOE_ERR_HIP = -6
 SMALL_BATCH_MAX_T = 32  # MOE_SMALL_BATCH_MAX_T: moe_forward's small-batch path covers 2 <= T <= this
+Q4_MAX_T = 32  # MOE_Q4_MAX_T: moe_forward_q4 covers 1 <= T <= this
 
 EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_align_tile_rows", "moe_align_small_tile_rows", "moe_align_max_rows",
     "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward_ids_offset", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
-    "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine", "moe_forward_fp8", "moe_e4m3_to_f32",
+    "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine", "moe_forward_fp8", "moe_e4m3_to_f32", "moe_forward_q4",
     "moe_bucket_plan", "moe_prefill_runner_create", "moe_prefill_runner_run", "moe_prefill_runner_destroy",
 )
 
@@ -69,6 +70,7 @@ def lib():
             "moe_combine": ([p] * 5 + [i] * 4 + [p, p], i),
             "moe_forward_fp8": ([p] * 16 + [i] * 6 + [p, p, z, p], i),
             "moe_e4m3_to_f32": ([p, p, i64, p], i),
+            "moe_forward_q4": ([p] * 16 + [i] * 6 + [p, p, z, p], i),
             "moe_bucket_plan": ([i, p, i, p, p, i, p], i),
             "moe_prefill_runner_create": ([p] * 9 + [i] * 5 + [p, i, p], i),
             "moe_prefill_runner_run": ([p, p, i, p, p], i),
@@ -159,6 +161,15 @@ def moe_forward_fp8(x, w_router, router_bias, q_gate, sc_gate, q_up, sc_up, q_do
                                  _p(sc_up), _p(q_down), _p(sc_down), _p(qs_gate), _p(ssc_gate), _p(qs_up),
                                  _p(ssc_up), _p(qs_down), _p(ssc_down), _p(w_sg), T, H, E, k, I, I_s,
                                  _p(y), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_forward_q4(x, w_router, router_bias, q_gate, s_gate, q_up, s_up, q_down, s_down,
+                   qs_gate, ss_gate, qs_up, ss_up, qs_down, ss_down, w_sg,
+                   T, H, E, k, I, I_s, y, workspace, ws_bytes: int, stream=None):
+    _check(lib().moe_forward_q4(_p(x), _p(w_router), _p(router_bias), _p(q_gate), _p(s_gate), _p(q_up),
+                                _p(s_up), _p(q_down), _p(s_down), _p(qs_gate), _p(ss_gate), _p(qs_up),
+                                _p(ss_up), _p(qs_down), _p(ss_down), _p(w_sg), T, H, E, k, I, I_s,
+                                _p(y), _p(workspace), ws_bytes, _stream(stream)))
 
 
 def moe_e4m3_to_f32(codes, out, n: int, stream=None):

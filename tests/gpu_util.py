@@ -64,6 +64,24 @@ def with_fp8(inp, seed: int = 0):
     return synth.add_fp8_weights(inp)
 
 
+@functools.lru_cache(maxsize=None)
+def full_q4_weights(seed: int = 0):
+    """4-bit (fp16 group scale) copies of the full-shape expert weights, made once."""
+    return synth.add_q4_weights(full_weights(seed))
+
+
+def with_q4(inp, seed: int = 0):
+    """``inp`` plus 4-bit expert weights (the cached full-shape ones when the shapes match)."""
+    wl = inp["wl"]
+    if (wl.H, wl.E, wl.I, wl.I_s) == (2048, 256, 512, 512):
+        out = dict(inp)
+        src = full_q4_weights(seed)
+        for key in synth.FP8_KEYS:
+            out[key + "_q4"], out[key + "_q4scale"] = src[key + "_q4"], src[key + "_q4scale"]
+        return out
+    return synth.add_q4_weights(inp)
+
+
 def inputs(name: str, T=None, seed: int = 0, **over):
     wl = synth.workload(name, **({"T": T} if T is not None else {}), **over)
     if (wl.H, wl.E, wl.I, wl.I_s) == (2048, 256, 512, 512):
@@ -105,26 +123,26 @@ def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, label: str):
     return max_abs, rel
 
 
-def oracle_y_with_gpu_ids(inp, rows, gpu_ids, ref, fp8=False):
+def oracle_y_with_gpu_ids(inp, rows, gpu_ids, ref, fp8=False, q4=False):
     """Oracle y for ``rows`` of ``inp`` evaluated under ``gpu_ids`` (near-tie tokens)."""
     sub = dict(inp)
     sub["x"] = inp["x"][rows]
-    r = oracle.forward(sub, ids_in=gpu_ids, fp8=fp8)
+    r = oracle.forward(sub, ids_in=gpu_ids, fp8=fp8, q4=q4)
     return r["y"]
 
 
-def reference_y(inp, gpu_ids: np.ndarray, label: str, fp8: bool = False):
+def reference_y(inp, gpu_ids: np.ndarray, label: str, fp8: bool = False, q4: bool = False):
     """Oracle y for every token, with near-tie tokens re-evaluated on the GPU's selection.
 
-    ``fp8``: the oracle takes the FP8 expert weights of ``inp``."""
-    r = oracle.forward(inp, fp8=fp8)
+    ``fp8`` / ``q4``: the oracle takes the FP8 / 4-bit expert weights of ``inp``."""
+    r = oracle.forward(inp, fp8=fp8, q4=q4)
     wl = inp["wl"]
     ex = excluded_tokens(r["logits"], wl.k, inp.get("tie_rows", ()))
     check_ids(gpu_ids, r["ids"], ex, label)
     y = r["y"].copy()
     diff = np.nonzero(np.any(gpu_ids != r["ids"], axis=1))[0]
     if len(diff):
-        y[diff] = oracle_y_with_gpu_ids(inp, diff, gpu_ids[diff], r, fp8=fp8)
+        y[diff] = oracle_y_with_gpu_ids(inp, diff, gpu_ids[diff], r, fp8=fp8, q4=q4)
     return y, r
 
 

@@ -177,3 +177,26 @@ def test_valid_fp8_call_without_gpu_reports_arch(L):
     assert fwd8(L) == moe.MOE_ERR_ARCH
     assert fwd8(L, T=1) == moe.MOE_ERR_ARCH
     assert fwd8(L, T=100) == moe.MOE_ERR_ARCH
+
+
+def test_forward_q4_argument_errors(L):
+    p = 1 << 12
+    a = dict(x=p, wr=p, b=None, qg=p, sg=p, qu=p, su=p, qd=p, sd=p, qsg=None, ssg=None, qsu=None, ssu=None,
+             qsd=None, ssd=None, wsg=None, T=4, H=256, E=8, k=2, I=128, I_s=0, y=p, ws=p, nbytes=1 << 30)
+
+    def q4(**kw):
+        b = dict(a)
+        b.update(kw)
+        return L.moe_forward_q4(b["x"], b["wr"], b["b"], b["qg"], b["sg"], b["qu"], b["su"], b["qd"], b["sd"],
+                                b["qsg"], b["ssg"], b["qsu"], b["ssu"], b["qsd"], b["ssd"], b["wsg"],
+                                b["T"], b["H"], b["E"], b["k"], b["I"], b["I_s"], b["y"], b["ws"], b["nbytes"], None)
+    assert q4(T=0) == moe.MOE_OK
+    assert q4(qd=None) == moe.MOE_ERR_NULL
+    assert q4(T=moe.Q4_MAX_T + 1) == moe.MOE_ERR_SHAPE
+    assert "4-bit" in moe.last_error()
+    assert q4(qsg=p) == moe.MOE_ERR_SHAPE
+    assert q4(I_s=128, qsg=p, ssg=p, qsu=p, ssu=p, qsd=p, ssd=p) == moe.MOE_ERR_NULL
+    assert q4(su=p + 2) == moe.MOE_ERR_ALIGN
+    assert q4(nbytes=100) == moe.MOE_ERR_WORKSPACE
+    if not os.path.exists("/dev/kfd"):
+        assert q4() == moe.MOE_ERR_ARCH
