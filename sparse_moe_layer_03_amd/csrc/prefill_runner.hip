@@ -212,15 +212,15 @@ int moe_prefill_runner_create(const uint16_t* w_router, const float* router_bias
   hipStream_t cap = nullptr;
   hipGraph_t graph = nullptr;
   auto bail = [&](int code, const char* what, hipError_t e) {
+    char msg[512];
+    if (e != hipSuccess)
+      snprintf(msg, sizeof msg, "%s: %s", what, hipGetErrorString(e));
+    else
+      snprintf(msg, sizeof msg, "moe_prefill_runner_create: %s", moe_last_error());  // set by the failing call
     if (graph) (void)hipGraphDestroy(graph);
     if (cap) (void)hipStreamDestroy(cap);
-    moe_prefill_runner_destroy(r);
-    if (e != hipSuccess) {
-      char msg[256];
-      snprintf(msg, sizeof msg, "%s: %s", what, hipGetErrorString(e));
-      return plan_error(code, msg);
-    }
-    return code;  // message already set
+    moe_prefill_runner_destroy(r);  // clears the message
+    return plan_error(code, msg);
   };
   hipError_t e;
   if ((e = hipMalloc(&r->x_stage, io_bytes)) != hipSuccess || (e = hipMalloc(&r->y_stage, io_bytes)) != hipSuccess ||

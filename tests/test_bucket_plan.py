@@ -90,3 +90,15 @@ def test_runner_argument_errors():
                                        C.byref(out)) == moe.MOE_ERR_SHAPE  # shared tensor with I_s = 0
     assert L.moe_prefill_runner_run(None, p, 10, p, None) == moe.MOE_ERR_NULL
     assert L.moe_prefill_runner_destroy(None) == moe.MOE_OK
+
+
+@pytest.mark.skipif(__import__("os").path.exists("/dev/kfd"), reason="host without a GPU only")
+def test_runner_without_gpu_reports_arch():
+    import ctypes as C
+    L = moe.lib()
+    out = C.c_void_p(123)
+    b = (C.c_int * 2)(64, 128)
+    p = 1 << 12
+    rc = L.moe_prefill_runner_create(p, None, p, p, p, None, None, None, None, 256, 8, 2, 128, 0, b, 2, C.byref(out))
+    assert rc == moe.MOE_ERR_ARCH and out.value is None
+    assert moe.last_error()
