@@ -200,3 +200,13 @@ def test_forward_q4_argument_errors(L):
     assert q4(nbytes=100) == moe.MOE_ERR_WORKSPACE
     if not os.path.exists("/dev/kfd"):
         assert q4() == moe.MOE_ERR_ARCH
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library every call raises."""
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "libmoe355.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(ImportError):
+        moe.lib()
+    with pytest.raises(ImportError):
+        moe.moe_workspace_size(16, 256, 8, 2, 128, 0)
