@@ -1,0 +1,44 @@
+"""GPU parity at the edges of the supported shapes, for every weight format.
+
+Largest hidden size (8192) with the widest top-k (16 of 256 experts), a
+single expert (E = k = 1), the smallest FFN (128) without a shared expert,
+and token counts on each path: 1 (single-token kernels), a few (small-batch
+kernels) and above 32 (tiled GEMMs; 4-bit weights stop at 32).
+"""
+import pytest
+
+from sparse_moe_layer_03_amd import synth
+from sparse_moe_layer_03_amd.layer import DeviceLayer
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+EDGE_SHAPES = {
+    "H8192-k16": dict(H=8192, E=256, k=16, I=128, I_s=128, bias="normal"),
+    "E1-k1": dict(H=256, E=1, k=1, I=128, I_s=128),
+    "I128-noshared": dict(H=512, E=8, k=2, I=128, I_s=0),
+}
+CASES = [(name, T, fmt) for name in EDGE_SHAPES for T in (1, 5, 40) for fmt in ("bf16", "fp8", "q4")
+         if not (fmt == "q4" and T > 32)]
+
+
+@pytest.fixture(scope="module")
+def torch():
+    return G.torch_cuda()
+
+
+@pytest.mark.parametrize("name,T,fmt", CASES, ids=[f"{n}-T{t}-{f}" for n, t, f in CASES])
+def test_edge_shapes(torch, name, T, fmt):
+    wl = synth.Workload("edge-" + name, T=T, **EDGE_SHAPES[name])
+    inp = synth.make_inputs(wl, seed=9)
+    if fmt == "fp8":
+        inp = synth.add_fp8_weights(inp)
+    elif fmt == "q4":
+        inp = synth.add_q4_weights(inp)
+    G.say(f"[edge] {name} T={T} {fmt}")
+    lay = DeviceLayer.from_inputs(inp, fp8=fmt == "fp8", q4=fmt == "q4")
+    y = lay.forward(G.to_dev_x(inp))
+    ids = lay.forward_ids(T).cpu().numpy()
+    torch.cuda.synchronize()
+    y_ref, _ = G.reference_y(inp, ids, f"edge {name} T={T} {fmt}", fp8=fmt == "fp8", q4=fmt == "q4")
+    G.check_y(G.y_to_f64(y), y_ref, f"edge {name} T={T} {fmt}")
