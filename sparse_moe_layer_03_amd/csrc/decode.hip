@@ -231,15 +231,19 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
   if (row < k * I && lane == 0) d.h[row] = silu(gs) * us;
 }
 
-// Wave per output column: the k + 1 weight rows of the column are loaded
-// together (I / 8 chunks each), and each h value read serves them all.
+// Wave per CPW output columns: the k + 1 weight rows of each column are
+// loaded together (I / 8 chunks each), and each h value read serves them all.
+#ifndef MOE_DECODE_DOWN_COLS
+#define MOE_DECODE_DOWN_COLS 1
+#endif
+constexpr int CPW = MOE_DECODE_DOWN_COLS;
 template <int KT, int F>  // k <= KT
 __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H, int k, int I, int I_s, DecodeWs d,
                                                           uint16_t* __restrict__ y) {
   typedef wchunk_t<F> WC;
   constexpr bool RS = F == W_FP8;
   const int lane = threadIdx.x & 63;
-  const int c0 = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * CPW;
   if (c0 >= H) return;
   // ids and weights: KT entries read with 16-byte loads (their workspace
   // slots hold 64 entries), entries past k unused
@@ -255,17 +259,25 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
 #pragma unroll
   for (int j = 0; j < KT; ++j) ids[j] = j < k ? ids[j] : 0;  // keep unused rows in range
   // row scales, loaded with the first weight rows rather than after the sums
-  float scd[KT], scs = 1.0f;
+  float scd[CPW][KT], scs[CPW];
 #pragma unroll
-  for (int j = 0; j < KT; ++j) scd[j] = RS ? W.sc_down[(size_t)ids[j] * H + c0] : 1.0f;
-  if (RS && I_s > 0) scs = W.ssc_down[c0];
-  WRow<F> rows[KT];
+  for (int c = 0; c < CPW; ++c) {
 #pragma unroll
-  for (int j = 0; j < KT; ++j) rows[j] = wrow<F>(W.down, W.gs_down, (size_t)ids[j] * H + c0, I);
-  const WRow<F> srow = wrow<F>(W.s_down, W.gss_down, (size_t)c0, I_s);
-  float part[KT + 1];
+    for (int j = 0; j < KT; ++j) scd[c][j] = RS ? W.sc_down[(size_t)ids[j] * H + c0 + c] : 1.0f;
+    scs[c] = (RS && I_s > 0) ? W.ssc_down[c0 + c] : 1.0f;
+  }
+  WRow<F> rows[CPW][KT], srow[CPW];
 #pragma unroll
-  for (int j = 0; j <= KT; ++j) part[j] = 0.0f;
+  for (int c = 0; c < CPW; ++c) {
+#pragma unroll
+    for (int j = 0; j < KT; ++j) rows[c][j] = wrow<F>(W.down, W.gs_down, (size_t)ids[j] * H + c0 + c, I);
+    srow[c] = wrow<F>(W.s_down, W.gss_down, (size_t)(c0 + c), I_s);
+  }
+  float part[CPW][KT + 1];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int j = 0; j <= KT; ++j) part[c][j] = 0.0f;
   auto accum = [&](float& acc, const WC& wv, const float* hv) {
     float f[8];
     chunk_to_f32(wv, f);
@@ -273,16 +285,17 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
     for (int q = 0; q < 8; ++q) acc += hv[q] * f[q];
   };
   // Per step of 64 chunks: the loads that do not depend on the routing (the
-  // shared row, h_s and every h_j) are issued first, then the k routed rows.
+  // shared rows, h_s and every h_j) are issued first, then the routed rows.
   const int nI = I / 8, nS = I_s > 0 ? I_s / 8 : 0;
   const int nmax = nI > nS ? nI : nS;
   for (int base = 0; base < nmax; base += 64) {
     const int ch = base + lane;
     const bool okS = ch < nS, okI = ch < nI;
-    WC wsv;
+    WC wsv[CPW];
     float4 hs0 = {}, hs1 = {};
     if (okS) {
-      wsv = srow[ch];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) wsv[c] = srow[c][ch];
       const float4* hp = reinterpret_cast<const float4*>(d.hs + ch * 8);
       hs0 = hp[0];
       hs1 = hp[1];
@@ -295,36 +308,43 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
         h0[j] = hp[0];
         h1[j] = hp[1];
       }
-    WC wv[KT];
+    WC wv[KT][CPW];
 #pragma unroll
     for (int j = 0; j < KT; ++j)
-      if (j < k && okI) wv[j] = rows[j][ch];
+      if (j < k && okI)
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) wv[j][c] = rows[c][j][ch];
     if (okS) {
       const float hv[8] = {hs0.x, hs0.y, hs0.z, hs0.w, hs1.x, hs1.y, hs1.z, hs1.w};
-      accum(part[KT], wsv, hv);
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) accum(part[c][KT], wsv[c], hv);
     }
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
       if (j < k && okI) {
         const float hv[8] = {h0[j].x, h0[j].y, h0[j].z, h0[j].w, h1[j].x, h1[j].y, h1[j].z, h1[j].w};
-        accum(part[j], wv[j], hv);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) accum(part[c][j], wv[j][c], hv);
       }
     }
   }
-  float yv = 0.0f;
 #pragma unroll
-  for (int j = 0; j < KT; ++j)
-    if (j < k) {
-      float oj = wave_sum(part[j]);
-      if (RS) oj *= scd[j];
-      yv += wsel[j] * oj;  // rank order
+  for (int c = 0; c < CPW; ++c) {
+    float yv = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KT; ++j)
+      if (j < k) {
+        float oj = wave_sum(part[c][j]);
+        if (RS) oj *= scd[c][j];
+        yv += wsel[j] * oj;  // rank order
+      }
+    if (I_s > 0) {
+      float os = wave_sum(part[c][KT]);
+      if (RS) os *= scs[c];
+      yv += d.s[0] * os;
     }
-  if (I_s > 0) {
-    float os = wave_sum(part[KT]);
-    if (RS) os *= scs;
-    yv += d.s[0] * os;
+    if (lane == 0) y[c0 + c] = f32_to_bf16(yv);
   }
-  if (lane == 0) y[c0] = f32_to_bf16(yv);
 }
 
 __global__ __launch_bounds__(256) void e4m3_to_f32_kernel(const uint8_t* __restrict__ codes, float* __restrict__ out,
@@ -355,11 +375,12 @@ void launch_decode_t(const uint16_t* x, const uint16_t* w_router, const float* b
   // 4 waves per workgroup, one routed row pair per wave; waves 1..3 also take the shared rows
   hipLaunchKernelGGL(decode_topk_gate_up_kernel<F>, dim3((k * I + 3) / 4), dim3(256), 0, st, x, W, H, E, k, I, I_s,
                      d);
-  // 4 waves per workgroup, one output column per wave (H is a multiple of 256)
+  // 4 waves per workgroup, CPW output columns per wave (H is a multiple of 256)
+  const dim3 g_dn((H / CPW + 3) / 4);
   if (k <= 8)
-    hipLaunchKernelGGL((decode_down_kernel<8, F>), dim3((H + 3) / 4), dim3(256), 0, st, W, H, k, I, I_s, d, y);
+    hipLaunchKernelGGL((decode_down_kernel<8, F>), g_dn, dim3(256), 0, st, W, H, k, I, I_s, d, y);
   else
-    hipLaunchKernelGGL((decode_down_kernel<kMaxK, F>), dim3((H + 3) / 4), dim3(256), 0, st, W, H, k, I, I_s, d, y);
+    hipLaunchKernelGGL((decode_down_kernel<kMaxK, F>), g_dn, dim3(256), 0, st, W, H, k, I, I_s, d, y);
 }
 
 }  // namespace
