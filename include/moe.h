@@ -20,7 +20,12 @@
  *     Ws_gate/Ws_up [I_s,H], Ws_down [H,I_s], w_sg [H].
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work and return; nothing is synchronised and no value is read
- *     back to the host, so a call can be captured in a HIP graph.
+ *     back to the host, so a call can be captured in a HIP graph (the prefill
+ *     runner's creation and destruction excepted: they allocate, capture and
+ *     synchronise).
+ *   - Expert weights are BF16 (moe_forward and the stage entry points), OCP
+ *     FP8 E4M3 with a row scale (moe_forward_fp8) or signed 4-bit with a
+ *     group scale (moe_forward_q4); the router weights are always BF16.
  *   - The caller owns every buffer, including `workspace`.  The library never
  *     allocates or frees device memory and keeps no state between calls
  *     except a per-device cached architecture check -- apart from the
