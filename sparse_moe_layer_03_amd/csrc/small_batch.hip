@@ -381,16 +381,23 @@ __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restr
   }
 }
 
-// S4: workgroup (expert slot u = blockIdx.y, output columns 64 blockIdx.x ..
-// +63): a wave per 16 columns.  Lane l takes column c0 + l / 4 and the
-// reduction chunks j * 4 + l % 4 (four adjacent lanes read 64 contiguous
-// bytes of a row); the four partial sums of a column meet in two DPP steps.
+// S4: workgroup (expert slot u = blockIdx.y, output columns 4*DCW blockIdx.x ..
+// +4*DCW-1): a wave per DCW columns.  Lane l takes column c0 + l / LPC and
+// the reduction chunks j * LPC + l % LPC (adjacent lanes read contiguous
+// bytes of a row); the LPC partial sums of a column meet in DPP steps.
 // h rows of the expert's assignments (fp32) are staged in LDS, DT at a time.
 // h rows staged per pass (8: 16 KB of LDS), as for gate/up.
 #ifndef SB_DOWN_TOKENS
 #define SB_DOWN_TOKENS 8
 #endif
 constexpr int DT = SB_DOWN_TOKENS;  // h rows staged at a time
+// Lanes per output column (4, 8 or 16): a wave takes 64 / LPC columns, a lane
+// 64 / LPC of the 64 chunks of a 512-value reduction block.
+#ifndef SB_DOWN_LANES_PER_COL
+#define SB_DOWN_LANES_PER_COL 8
+#endif
+constexpr int LPC = SB_DOWN_LANES_PER_COL, DCW = 64 / LPC, DNCH = 64 / LPC;
+static_assert(LPC == 4 || LPC == 8 || LPC == 16, "lanes per column");
 template <int F>
 __global__ __launch_bounds__(256) void sb_down_kernel(ExpertWeights W, int T, int H, int E, int k, int I, int I_s,
                                                       SmallWs d) {
@@ -403,7 +410,7 @@ __global__ __launch_bounds__(256) void sb_down_kernel(ExpertWeights W, int T, in
   const bool shared = (u == nu);
   if (u > nu || (shared && I_s == 0)) return;  // uniform over the workgroup
   const int K = shared ? I_s : I;
-  const int col = blockIdx.x * 64 + wave * 16 + (lane >> 2);
+  const int col = blockIdx.x * (4 * DCW) + wave * DCW + lane / LPC;
   const int32_t* rec = d.plan + kRec0 + (shared ? 0 : u) * kRecInts;
   const int e = shared ? 0 : rec[0], off = shared ? 0 : rec[1], cnt = shared ? T : rec[2];
   auto asg_at = [&](int q) { return shared ? q : (q < TBR ? rec[4 + q] : d.asg[off + q]); };
@@ -413,9 +420,9 @@ __global__ __launch_bounds__(256) void sb_down_kernel(ExpertWeights W, int T, in
   const int nch = K / 8;
   for (int kb = 0; kb < nch; kb += 64) {  // reduction blocks of 512 values
     const int nb = min(64, nch - kb);        // chunks in this block (a multiple of 16)
-    WC wv[16];
+    WC wv[DNCH];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) wv[j] = wrw[kb + min(j * 4 + (lane & 3), nb - 1)];
+    for (int j = 0; j < DNCH; ++j) wv[j] = wrw[kb + min(j * LPC + lane % LPC, nb - 1)];
     for (int q0 = 0; q0 < cnt; q0 += DT) {
       const int nt = min(DT, cnt - q0);
       __syncthreads();
@@ -439,16 +446,18 @@ __global__ __launch_bounds__(256) void sb_down_kernel(ExpertWeights W, int T, in
       for (int t = 0; t < nt; ++t) {
         float part = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int ch = j * 4 + (lane & 3);
+        for (int j = 0; j < DNCH; ++j) {
+          const int ch = j * LPC + lane % LPC;
           if (ch < nb) part += dot8_f32w(shh[t * 128 + 2 * ch], shh[t * 128 + 2 * ch + 1], wv[j]);
         }
-        // sum of the four lanes of this column (lanes 4c .. 4c+3): DPP quad
-        // permutes, so every lane of the quad holds the total
+        // sum of the LPC lanes of this column: DPP quad permutes (every lane
+        // of a quad holds the quad's total), then the two quads of 8 lanes
         part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0xB1, 0xf, 0xf, false));  // [1,0,3,2]
         part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x4E, 0xf, 0xf, false));  // [2,3,0,1]
+        if (LPC >= 8) part += __shfl_xor(part, 4);
+        if (LPC >= 16) part += __shfl_xor(part, 8);
         if (Q) part *= sc;
-        if ((lane & 3) == 0) {
+        if (lane % LPC == 0) {
           const int a = asg_at(q0 + t);
           float* out = (shared ? d.os : d.o) + (size_t)a * H + col;
           if (kb == 0)
@@ -494,7 +503,7 @@ hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const
   // expert slots: at most min(E, T*k) touched experts, plus the shared expert
   const int max_u = (T * k < E ? T * k : E) + (I_s > 0 ? 1 : 0);
   const int nrow = I > I_s ? I : I_s;
-  const dim3 g_gu((nrow + GR - 1) / GR, max_u), g_dn(H / 64, max_u);
+  const dim3 g_gu((nrow + GR - 1) / GR, max_u), g_dn(H / (4 * DCW), max_u);
   if (W.fmt == W_FP8) {
     hipLaunchKernelGGL(sb_gate_up_kernel<W_FP8>, g_gu, dim3(256), 0, st, x, W, T, H, E, k, I, I_s, d);
     hipLaunchKernelGGL(sb_down_kernel<W_FP8>, g_dn, dim3(256), 0, st, W, T, H, E, k, I, I_s, d);
