@@ -287,7 +287,12 @@ __global__ __launch_bounds__(1024) void sb_select_kernel(int T, int E, int k, Sm
 #ifndef SB_GATE_UP_TOKENS
 #define SB_GATE_UP_TOKENS 8
 #endif
-constexpr int GP = 2, GR = 4 * GP, GT = SB_GATE_UP_TOKENS;
+// Gate/up row pairs per wave (1: 4 pairs, 32 KB of weights, per workgroup;
+// 2 pairs per wave were 8% slower at 8..32 tokens: fewer, larger workgroups).
+#ifndef SB_GATE_UP_ROW_PAIRS
+#define SB_GATE_UP_ROW_PAIRS 1
+#endif
+constexpr int GP = SB_GATE_UP_ROW_PAIRS, GR = 4 * GP, GT = SB_GATE_UP_TOKENS;
 template <int F>
 __global__ __launch_bounds__(256) void sb_gate_up_kernel(const uint16_t* __restrict__ x, ExpertWeights W, int T,
                                                          int H, int E, int k, int I, int I_s, SmallWs d) {
