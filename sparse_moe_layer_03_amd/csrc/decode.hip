@@ -162,20 +162,25 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ logits, int
 
 // While wave 0 selects the experts, waves 1..3 compute the shared expert's
 // gate/up rows (they do not depend on the routing): row i = silu(g) * u -> h_s.
+#ifndef MOE_DECODE_GU_WAVES
+#define MOE_DECODE_GU_WAVES 4
+#endif
+constexpr int DGW = MOE_DECODE_GU_WAVES;  // waves per workgroup of the gate/up launch
 template <int F>
-__global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t* __restrict__ x, ExpertWeights W,
-                                                                  int H, int E, int k, int I, int I_s, DecodeWs d) {
+__global__ __launch_bounds__(64 * DGW) void decode_topk_gate_up_kernel(const uint16_t* __restrict__ x,
+                                                                       ExpertWeights W, int H, int E, int k, int I,
+                                                                       int I_s, DecodeWs d) {
   typedef wchunk_t<F> WC;
   constexpr bool RS = F == W_FP8;  // one scale per row, applied to the row's dot product
   __shared__ u32x4 sx[1024];
   __shared__ int sel_e[kMaxK];
   __shared__ float sel_w[kMaxK];
-  for (int c = threadIdx.x; c < H / 8; c += 256) sx[c] = reinterpret_cast<const u32x4*>(x)[c];
+  for (int c = threadIdx.x; c < H / 8; c += 64 * DGW) sx[c] = reinterpret_cast<const u32x4*>(x)[c];
   const int wave = threadIdx.x >> 6;
   if (wave == 0) {
     block_topk(d.logits, E, k, sel_e, sel_w);
   } else {
-    for (int i = blockIdx.x * 3 + wave - 1; i < I_s; i += 3 * gridDim.x) {
+    for (int i = blockIdx.x * (DGW - 1) + wave - 1; i < I_s; i += (DGW - 1) * gridDim.x) {
       const float scg = RS ? W.ssc_gate[i] : 1.0f, scu = RS ? W.ssc_up[i] : 1.0f;  // issued with the row loads
       float g, u;
       row_dots<F>(nullptr, x, wrow<F>(W.s_gate, W.gss_gate, (size_t)i, H), wrow<F>(W.s_up, W.gss_up, (size_t)i, H),
@@ -192,10 +197,10 @@ __global__ __launch_bounds__(256) void decode_topk_gate_up_kernel(const uint16_t
     d.ids[threadIdx.x] = sel_e[threadIdx.x];
     d.w[threadIdx.x] = sel_w[threadIdx.x];
   }
-  // wave w of workgroup b takes row pair b*4 + w; its loads are all issued
+  // wave w of workgroup b takes row pair b*DGW + w; its loads are all issued
   // before any reduction
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * DGW + (threadIdx.x >> 6);
   const int nch = H / 8;  // chunks per weight row; lane handles chunks lane + 64 c
   const int rr = row < k * I ? row : 0;
   const size_t rix = (size_t)sel_e[rr / I] * I + rr % I;  // row of W_gate / W_up
@@ -372,9 +377,9 @@ void launch_decode_t(const uint16_t* x, const uint16_t* w_router, const float* b
   const int rows1 = E + (I_s > 0 ? 1 : 0);
   hipLaunchKernelGGL(decode_router_kernel, dim3((rows1 + 3) / 4), dim3(256), 0, st, x, w_router, bias,
                      I_s > 0 ? w_sg : nullptr, H, E, d);
-  // 4 waves per workgroup, one routed row pair per wave; waves 1..3 also take the shared rows
-  hipLaunchKernelGGL(decode_topk_gate_up_kernel<F>, dim3((k * I + 3) / 4), dim3(256), 0, st, x, W, H, E, k, I, I_s,
-                     d);
+  // DGW waves per workgroup, one routed row pair per wave; waves 1.. also take the shared rows
+  hipLaunchKernelGGL(decode_topk_gate_up_kernel<F>, dim3((k * I + DGW - 1) / DGW), dim3(64 * DGW), 0, st, x, W, H, E,
+                     k, I, I_s, d);
   // 4 waves per workgroup, CPW output columns per wave (H is a multiple of 256)
   const dim3 g_dn((H / CPW + 3) / 4);
   if (k <= 8)
