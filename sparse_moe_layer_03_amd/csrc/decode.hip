@@ -352,6 +352,86 @@ __global__ __launch_bounds__(256) void decode_down_kernel(ExpertWeights W, int H
   }
 }
 
+// The same with one column per wave, I and I_s at most 512 (one chunk per
+// lane) and k * I at most kDownStage floats: the k hidden rows are staged in
+// LDS once per workgroup (after the wave's weight loads are issued) instead of
+// being read from L2 by every wave.
+constexpr int kDownStage = 4096;
+template <int KT, int F>  // k <= KT
+__global__ __launch_bounds__(256) void decode_down_staged_kernel(ExpertWeights W, int H, int k, int I, int I_s,
+                                                                 DecodeWs d, uint16_t* __restrict__ y) {
+  typedef wchunk_t<F> WC;
+  constexpr bool RS = F == W_FP8;
+  __shared__ float4 shh[kDownStage / 4];
+  const int lane = threadIdx.x & 63;
+  const int c0 = blockIdx.x * 4 + (threadIdx.x >> 6);  // < H: the grid covers H exactly
+  int ids[KT];
+  float wsel[KT];
+#pragma unroll
+  for (int q = 0; q < KT / 4; ++q) {
+    const int4 iv = reinterpret_cast<const int4*>(d.ids)[q];
+    const float4 wv = reinterpret_cast<const float4*>(d.w)[q];
+    ids[4 * q] = iv.x, ids[4 * q + 1] = iv.y, ids[4 * q + 2] = iv.z, ids[4 * q + 3] = iv.w;
+    wsel[4 * q] = wv.x, wsel[4 * q + 1] = wv.y, wsel[4 * q + 2] = wv.z, wsel[4 * q + 3] = wv.w;
+  }
+#pragma unroll
+  for (int j = 0; j < KT; ++j) ids[j] = j < k ? ids[j] : 0;  // keep unused rows in range
+  float scd[KT], scs = 1.0f;
+#pragma unroll
+  for (int j = 0; j < KT; ++j) scd[j] = RS ? W.sc_down[(size_t)ids[j] * H + c0] : 1.0f;
+  if (RS && I_s > 0) scs = W.ssc_down[c0];
+  const int ch = lane;  // the lane's chunk of 8 reduction values
+  const bool okS = ch < I_s / 8, okI = ch < I / 8;
+  WC wsv, wv[KT];
+  float4 hs0 = {}, hs1 = {};
+  if (okS) {
+    wsv = wrow<F>(W.s_down, W.gss_down, (size_t)c0, I_s)[ch];
+    const float4* hp = reinterpret_cast<const float4*>(d.hs + ch * 8);
+    hs0 = hp[0];
+    hs1 = hp[1];
+  }
+#pragma unroll
+  for (int j = 0; j < KT; ++j)
+    if (j < k && okI) wv[j] = wrow<F>(W.down, W.gs_down, (size_t)ids[j] * H + c0, I)[ch];
+  for (int i = threadIdx.x; i < k * I / 4; i += 256) shh[i] = reinterpret_cast<const float4*>(d.h)[i];
+  __syncthreads();
+  auto accum = [&](float& acc, const WC& w, const float* hv) {
+    float f[8];
+    chunk_to_f32(w, f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc += hv[q] * f[q];
+  };
+  float part[KT + 1];
+#pragma unroll
+  for (int j = 0; j <= KT; ++j) part[j] = 0.0f;
+  if (okS) {
+    const float hv[8] = {hs0.x, hs0.y, hs0.z, hs0.w, hs1.x, hs1.y, hs1.z, hs1.w};
+    accum(part[KT], wsv, hv);
+  }
+#pragma unroll
+  for (int j = 0; j < KT; ++j) {
+    if (j < k && okI) {
+      const float4 h0 = shh[(j * I + ch * 8) / 4], h1 = shh[(j * I + ch * 8) / 4 + 1];
+      const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      accum(part[j], wv[j], hv);
+    }
+  }
+  float yv = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KT; ++j)
+    if (j < k) {
+      float oj = wave_sum(part[j]);
+      if (RS) oj *= scd[j];
+      yv += wsel[j] * oj;  // rank order
+    }
+  if (I_s > 0) {
+    float os = wave_sum(part[KT]);
+    if (RS) os *= scs;
+    yv += d.s[0] * os;
+  }
+  if (lane == 0) y[c0] = f32_to_bf16(yv);
+}
+
 __global__ __launch_bounds__(256) void e4m3_to_f32_kernel(const uint8_t* __restrict__ codes, float* __restrict__ out,
                                                           int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
@@ -382,6 +462,16 @@ void launch_decode_t(const uint16_t* x, const uint16_t* w_router, const float* b
                      k, I, I_s, d);
   // 4 waves per workgroup, CPW output columns per wave (H is a multiple of 256)
   const dim3 g_dn((H / CPW + 3) / 4);
+#ifndef MOE_DECODE_DOWN_STAGE_H
+#define MOE_DECODE_DOWN_STAGE_H 1
+#endif
+  if (MOE_DECODE_DOWN_STAGE_H && CPW == 1 && I <= 512 && I_s <= 512 && k * I <= kDownStage) {
+    if (k <= 8)
+      hipLaunchKernelGGL((decode_down_staged_kernel<8, F>), g_dn, dim3(256), 0, st, W, H, k, I, I_s, d, y);
+    else
+      hipLaunchKernelGGL((decode_down_staged_kernel<kMaxK, F>), g_dn, dim3(256), 0, st, W, H, k, I, I_s, d, y);
+    return;
+  }
   if (k <= 8)
     hipLaunchKernelGGL((decode_down_kernel<8, F>), g_dn, dim3(256), 0, st, W, H, k, I, I_s, d, y);
   else
