@@ -465,7 +465,8 @@ void launch_decode_t(const uint16_t* x, const uint16_t* w_router, const float* b
 #ifndef MOE_DECODE_DOWN_STAGE_H
 #define MOE_DECODE_DOWN_STAGE_H 1
 #endif
-  if (MOE_DECODE_DOWN_STAGE_H && CPW == 1 && I <= 512 && I_s <= 512 && k * I <= kDownStage) {
+  // (not for 4-bit weights: staged, their decode took 19.5 us against 17.4 us)
+  if (MOE_DECODE_DOWN_STAGE_H && F != W_Q4 && CPW == 1 && I <= 512 && I_s <= 512 && k * I <= kDownStage) {
     if (k <= 8)
       hipLaunchKernelGGL((decode_down_staged_kernel<8, F>), g_dn, dim3(256), 0, st, W, H, k, I, I_s, d, y);
     else
