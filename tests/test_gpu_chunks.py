@@ -93,3 +93,24 @@ def test_runner_page_buckets_full_shape(torch, T):
     G.check_y(G.y_to_f64(y)[rows], y_ref, f"runner full T={T} (sampled)")
     G.check_y(G.y_to_f64(y), G.y_to_f64(y_full), f"runner vs moe_forward T={T}")
     run.close()
+
+
+@pytest.mark.parametrize("T", [1, 7, 8, 9, 31, 57])
+def test_runner_small_batch_buckets(torch, T):
+    """Buckets of 8, 16 and 32 tokens: the captured graphs run the small-batch kernels."""
+    wl = synth.Workload("chunks-sb", T=64, H=512, E=16, k=4, I=256, I_s=128, bias="normal")
+    inp = synth.make_inputs(wl, seed=6)
+    lay = DeviceLayer.from_inputs(inp)
+    run = PrefillRunner(lay, (8, 16, 32))
+    segs, lens = run.plan(T)
+    G.say(f"[chunks-sb] T={T} segments={segs} lens={lens}")
+    x = G.to_dev_x(inp)[:T].contiguous()
+    y = run.run(x)
+    torch.cuda.synchronize()
+    sub = dict(inp)
+    sub["x"] = inp["x"][:T]
+    r = oracle.forward(sub)
+    ex = G.excluded_tokens(r["logits"], wl.k)
+    keep = ~ex
+    G.check_y(G.y_to_f64(y)[keep], r["y"][keep], f"runner small buckets T={T}")
+    run.close()
