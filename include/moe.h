@@ -244,6 +244,9 @@ int moe_bucket_plan(int T, const int* buckets, int n_buckets, int* seg_bucket, i
  *     buckets as moe_bucket_plan (each bucket must be a valid moe_forward
  *     size).  Allocates device memory and captures the graphs (the only
  *     entry points that allocate).  *out = NULL on error.
+ *   moe_prefill_runner_create_fp8: the same with the expert weights of
+ *     moe_forward_fp8 (E4M3 codes and fp32 row scales; the graphs hold
+ *     moe_forward_fp8 calls).
  *   moe_prefill_runner_run: y [T,H] = the layer on x [T,H] (device, 16-byte
  *     aligned), enqueued on `stream`, per segment of moe_bucket_plan(T): a
  *     full segment runs the bucket's launches on its rows of x and y
@@ -262,6 +265,13 @@ int moe_prefill_runner_create(const uint16_t* w_router, const float* router_bias
                               const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
                               const uint16_t* w_sg, int H, int E, int k, int I, int I_s,
                               const int* buckets, int n_buckets, moe_prefill_runner** out);
+int moe_prefill_runner_create_fp8(const uint16_t* w_router, const float* router_bias,
+                                  const uint8_t* q_gate, const float* sc_gate, const uint8_t* q_up,
+                                  const float* sc_up, const uint8_t* q_down, const float* sc_down,
+                                  const uint8_t* qs_gate, const float* ssc_gate, const uint8_t* qs_up,
+                                  const float* ssc_up, const uint8_t* qs_down, const float* ssc_down,
+                                  const uint16_t* w_sg, int H, int E, int k, int I, int I_s,
+                                  const int* buckets, int n_buckets, moe_prefill_runner** out);
 int moe_prefill_runner_run(moe_prefill_runner* runner, const uint16_t* x, int T, uint16_t* y, void* stream);
 int moe_prefill_runner_destroy(moe_prefill_runner* runner);
 

@@ -18,6 +18,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <memory>
 #include <new>
 #include <vector>
 
@@ -130,9 +131,14 @@ int plan(int T, const std::vector<int>& b_desc, int g, std::vector<int>& seg_buc
 struct moe_prefill_runner {
   int device = -1;
   int H = 0, E = 0, k = 0, I = 0, I_s = 0;
-  const uint16_t *w_router = nullptr, *w_gate = nullptr, *w_up = nullptr, *w_down = nullptr;
-  const uint16_t *ws_gate = nullptr, *ws_up = nullptr, *ws_down = nullptr, *w_sg = nullptr;
+  const uint16_t *w_router = nullptr, *w_sg = nullptr;
   const float* bias = nullptr;
+  // BF16 expert weights, or (fp8) E4M3 codes with their row scales
+  bool fp8 = false;
+  const void *w_gate = nullptr, *w_up = nullptr, *w_down = nullptr;
+  const void *ws_gate = nullptr, *ws_up = nullptr, *ws_down = nullptr;
+  const float *sc_gate = nullptr, *sc_up = nullptr, *sc_down = nullptr;
+  const float *ssc_gate = nullptr, *ssc_up = nullptr, *ssc_down = nullptr;
   std::vector<int> buckets;  // descending
   int g = 1;
   uint16_t* x_stage = nullptr;
@@ -140,6 +146,20 @@ struct moe_prefill_runner {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   std::vector<hipGraphExec_t> exec;  // per bucket, same order
+
+  // one layer call over T rows of x / y with the runner's workspace
+  int forward(const uint16_t* x, int T, uint16_t* y, hipStream_t st) const {
+    if (fp8)
+      return moe_forward_fp8(x, w_router, bias, static_cast<const uint8_t*>(w_gate), sc_gate,
+                             static_cast<const uint8_t*>(w_up), sc_up, static_cast<const uint8_t*>(w_down), sc_down,
+                             static_cast<const uint8_t*>(ws_gate), ssc_gate, static_cast<const uint8_t*>(ws_up),
+                             ssc_up, static_cast<const uint8_t*>(ws_down), ssc_down, w_sg, T, H, E, k, I, I_s, y, ws,
+                             ws_bytes, st);
+    return moe_forward(x, w_router, bias, static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+                       static_cast<const uint16_t*>(w_down), static_cast<const uint16_t*>(ws_gate),
+                       static_cast<const uint16_t*>(ws_up), static_cast<const uint16_t*>(ws_down), w_sg, T, H, E, k,
+                       I, I_s, y, ws, ws_bytes, st);
+  }
 };
 
 extern "C" {
@@ -179,31 +199,29 @@ int moe_prefill_runner_destroy(moe_prefill_runner* r) {
   return set_error(MOE_OK, "");
 }
 
-int moe_prefill_runner_create(const uint16_t* w_router, const float* router_bias, const uint16_t* w_gate,
-                              const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate,
-                              const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int H, int E,
-                              int k, int I, int I_s, const int* buckets, int n_buckets, moe_prefill_runner** out) {
+}  // extern "C"
+
+namespace {
+// Buffers, eager calls and graph capture for a runner whose weights and
+// shapes are set in *proto (consumed).
+int runner_create(moe_prefill_runner* proto, const int* buckets, int n_buckets, moe_prefill_runner** out) {
+  std::unique_ptr<moe_prefill_runner> owned(proto);
   if (!out) return plan_error(MOE_ERR_NULL, "out is required");
   *out = nullptr;
   std::vector<int> b;
   int g = 1;
   int rc = check_buckets(buckets, n_buckets, b, g);
   if (rc) return rc;
+  const int H = proto->H, E = proto->E, k = proto->k, I = proto->I, I_s = proto->I_s;
   for (int bt : b)
     if (moe_workspace_size(bt, H, E, k, I, I_s) == 0) return plan_error(MOE_ERR_SHAPE, "unsupported layer shapes");
-  const int n_shared = (ws_gate != nullptr) + (ws_up != nullptr) + (ws_down != nullptr) + (w_sg != nullptr);
-  if ((I_s == 0 && n_shared) || (I_s > 0 && n_shared != 4))
-    return plan_error(I_s == 0 ? MOE_ERR_SHAPE : MOE_ERR_NULL, "shared-expert tensors: all four with I_s > 0, none else");
-  if (!w_router || !w_gate || !w_up || !w_down) return plan_error(MOE_ERR_NULL, "weights are required");
-  moe_prefill_runner* r = new (std::nothrow) moe_prefill_runner();
-  if (!r) return plan_error(MOE_ERR_HIP, "out of host memory");
+  if (!proto->w_router || !proto->w_gate || !proto->w_up || !proto->w_down)
+    return plan_error(MOE_ERR_NULL, "weights are required");
+  moe_prefill_runner* r = owned.release();
   if (hipGetDevice(&r->device) != hipSuccess) {
     delete r;
     return plan_error(MOE_ERR_ARCH, "no HIP device");
   }
-  r->H = H, r->E = E, r->k = k, r->I = I, r->I_s = I_s;
-  r->w_router = w_router, r->bias = router_bias, r->w_gate = w_gate, r->w_up = w_up, r->w_down = w_down;
-  r->ws_gate = ws_gate, r->ws_up = ws_up, r->ws_down = ws_down, r->w_sg = w_sg;
   r->buckets = b;
   r->g = g;
   size_t ws_bytes = 0;
@@ -233,17 +251,13 @@ int moe_prefill_runner_create(const uint16_t* w_router, const float* router_bias
   // outside capture (the staging input is zeroed, so the call is well defined)
   if ((e = hipMemsetAsync(r->x_stage, 0, io_bytes, cap)) != hipSuccess)
     return bail(MOE_ERR_HIP, "moe_prefill_runner_create: clear", e);
-  for (int bt : b) {
-    rc = moe_forward(r->x_stage, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg, bt, H, E,
-                     k, I, I_s, r->y_stage, r->ws, r->ws_bytes, cap);
-    if (rc) return bail(rc, "", hipSuccess);
-  }
+  for (int bt : b)
+    if ((rc = r->forward(r->x_stage, bt, r->y_stage, cap))) return bail(rc, "", hipSuccess);
   if ((e = hipStreamSynchronize(cap)) != hipSuccess) return bail(MOE_ERR_HIP, "moe_prefill_runner_create: sync", e);
   for (int bt : b) {
     if ((e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal)) != hipSuccess)
       return bail(MOE_ERR_HIP, "moe_prefill_runner_create: begin capture", e);
-    rc = moe_forward(r->x_stage, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg, bt, H, E,
-                     k, I, I_s, r->y_stage, r->ws, r->ws_bytes, cap);
+    rc = r->forward(r->x_stage, bt, r->y_stage, cap);
     e = hipStreamEndCapture(cap, &graph);
     if (rc) return bail(rc, "", hipSuccess);
     if (e != hipSuccess) return bail(MOE_ERR_HIP, "moe_prefill_runner_create: end capture", e);
@@ -257,6 +271,48 @@ int moe_prefill_runner_create(const uint16_t* w_router, const float* router_bias
   (void)hipStreamDestroy(cap);
   *out = r;
   return set_error(MOE_OK, "");
+}
+}  // namespace
+
+extern "C" {
+
+int moe_prefill_runner_create(const uint16_t* w_router, const float* router_bias, const uint16_t* w_gate,
+                              const uint16_t* w_up, const uint16_t* w_down, const uint16_t* ws_gate,
+                              const uint16_t* ws_up, const uint16_t* ws_down, const uint16_t* w_sg, int H, int E,
+                              int k, int I, int I_s, const int* buckets, int n_buckets, moe_prefill_runner** out) {
+  if (out) *out = nullptr;
+  const int n_shared = (ws_gate != nullptr) + (ws_up != nullptr) + (ws_down != nullptr) + (w_sg != nullptr);
+  if ((I_s == 0 && n_shared) || (I_s > 0 && n_shared != 4))
+    return plan_error(I_s == 0 ? MOE_ERR_SHAPE : MOE_ERR_NULL, "shared-expert tensors: all four with I_s > 0, none else");
+  moe_prefill_runner* r = new (std::nothrow) moe_prefill_runner();
+  if (!r) return plan_error(MOE_ERR_HIP, "out of host memory");
+  r->H = H, r->E = E, r->k = k, r->I = I, r->I_s = I_s;
+  r->w_router = w_router, r->bias = router_bias, r->w_sg = w_sg;
+  r->w_gate = w_gate, r->w_up = w_up, r->w_down = w_down, r->ws_gate = ws_gate, r->ws_up = ws_up, r->ws_down = ws_down;
+  return runner_create(r, buckets, n_buckets, out);
+}
+
+int moe_prefill_runner_create_fp8(const uint16_t* w_router, const float* router_bias, const uint8_t* q_gate,
+                                  const float* sc_gate, const uint8_t* q_up, const float* sc_up, const uint8_t* q_down,
+                                  const float* sc_down, const uint8_t* qs_gate, const float* ssc_gate,
+                                  const uint8_t* qs_up, const float* ssc_up, const uint8_t* qs_down,
+                                  const float* ssc_down, const uint16_t* w_sg, int H, int E, int k, int I, int I_s,
+                                  const int* buckets, int n_buckets, moe_prefill_runner** out) {
+  if (out) *out = nullptr;
+  const int n_shared = (qs_gate != nullptr) + (ssc_gate != nullptr) + (qs_up != nullptr) + (ssc_up != nullptr) +
+                       (qs_down != nullptr) + (ssc_down != nullptr) + (w_sg != nullptr);
+  if ((I_s == 0 && n_shared) || (I_s > 0 && n_shared != 7))
+    return plan_error(I_s == 0 ? MOE_ERR_SHAPE : MOE_ERR_NULL, "shared-expert tensors: all seven with I_s > 0, none else");
+  if (!sc_gate || !sc_up || !sc_down) return plan_error(MOE_ERR_NULL, "row scales are required");
+  moe_prefill_runner* r = new (std::nothrow) moe_prefill_runner();
+  if (!r) return plan_error(MOE_ERR_HIP, "out of host memory");
+  r->H = H, r->E = E, r->k = k, r->I = I, r->I_s = I_s;
+  r->w_router = w_router, r->bias = router_bias, r->w_sg = w_sg;
+  r->fp8 = true;
+  r->w_gate = q_gate, r->w_up = q_up, r->w_down = q_down, r->ws_gate = qs_gate, r->ws_up = qs_up, r->ws_down = qs_down;
+  r->sc_gate = sc_gate, r->sc_up = sc_up, r->sc_down = sc_down;
+  r->ssc_gate = ssc_gate, r->ssc_up = ssc_up, r->ssc_down = ssc_down;
+  return runner_create(r, buckets, n_buckets, out);
 }
 
 int moe_prefill_runner_run(moe_prefill_runner* r, const uint16_t* x, int T, uint16_t* y, void* stream) {
@@ -280,9 +336,7 @@ int moe_prefill_runner_run(moe_prefill_runner* r, const uint16_t* x, int T, uint
     if (len == bt) {
       // a full segment: the same launches as the bucket's graph, straight on
       // the caller's rows (no staging copies)
-      rc = moe_forward(x + start * r->H, r->w_router, r->bias, r->w_gate, r->w_up, r->w_down, r->ws_gate, r->ws_up,
-                       r->ws_down, r->w_sg, bt, r->H, r->E, r->k, r->I, r->I_s, y + start * r->H, r->ws, r->ws_bytes,
-                       st);
+      rc = r->forward(x + start * r->H, bt, y + start * r->H, st);
       if (rc) return rc;
     } else {
       // the padded last segment: staged rows, the bucket's graph, real rows out

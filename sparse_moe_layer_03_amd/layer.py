@@ -208,7 +208,8 @@ class DeviceLayer:
 
 class PrefillRunner:
     """Prefill of any length through per-bucket HIP graphs (moe_prefill_runner_*) for a DeviceLayer's
-    BF16 weights.  The layer must outlive the runner."""
+    weights: its FP8 codes when the layer was built with ``fp8``, else its BF16 weights.  The layer
+    must outlive the runner."""
 
     PAGE_BUCKETS = (1024, 2048, 4096, 8192)
 
@@ -217,9 +218,20 @@ class PrefillRunner:
         W = layer.w
         self.layer = layer
         self.buckets = tuple(buckets)
-        self.handle = moe.moe_prefill_runner_create(W["w_router"], layer.bias, W["w_gate"], W["w_up"], W["w_down"],
-                                                    W["ws_gate"], W["ws_up"], W["ws_down"], W["w_sg"], s.H, s.E,
-                                                    s.k, s.I, s.I_s, list(self.buckets))
+        self.handle = None
+        if layer.q4:
+            raise ValueError("the prefill runner takes BF16 or FP8 weights (4-bit weights serve T <= %d)"
+                             % moe.Q4_MAX_T)
+        if layer.fp8:
+            q = layer.q
+            self.handle = moe.moe_prefill_runner_create_fp8(
+                W["w_router"], layer.bias, q["w_gate"], q["w_gate_scale"], q["w_up"], q["w_up_scale"], q["w_down"],
+                q["w_down_scale"], q["ws_gate"], q["ws_gate_scale"], q["ws_up"], q["ws_up_scale"], q["ws_down"],
+                q["ws_down_scale"], W["w_sg"], s.H, s.E, s.k, s.I, s.I_s, list(self.buckets))
+        else:
+            self.handle = moe.moe_prefill_runner_create(W["w_router"], layer.bias, W["w_gate"], W["w_up"],
+                                                        W["w_down"], W["ws_gate"], W["ws_up"], W["ws_down"],
+                                                        W["w_sg"], s.H, s.E, s.k, s.I, s.I_s, list(self.buckets))
 
     def plan(self, T: int):
         return moe.moe_bucket_plan(T, list(self.buckets))

@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_align_tile_rows", "moe_align_small_tile_rows", "moe_align_max_rows",
     "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward_ids_offset", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
     "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine", "moe_forward_fp8", "moe_e4m3_to_f32", "moe_forward_q4",
-    "moe_bucket_plan", "moe_prefill_runner_create", "moe_prefill_runner_run", "moe_prefill_runner_destroy",
+    "moe_bucket_plan", "moe_prefill_runner_create", "moe_prefill_runner_create_fp8", "moe_prefill_runner_run", "moe_prefill_runner_destroy",
 )
 
 
@@ -73,6 +73,7 @@ def lib():
             "moe_forward_q4": ([p] * 16 + [i] * 6 + [p, p, z, p], i),
             "moe_bucket_plan": ([i, p, i, p, p, i, p], i),
             "moe_prefill_runner_create": ([p] * 9 + [i] * 5 + [p, i, p], i),
+            "moe_prefill_runner_create_fp8": ([p] * 15 + [i] * 5 + [p, i, p], i),
             "moe_prefill_runner_run": ([p, p, i, p, p], i),
             "moe_prefill_runner_destroy": ([p], i),
         }
@@ -201,6 +202,20 @@ def moe_prefill_runner_create(w_router, router_bias, w_gate, w_up, w_down, ws_ga
     _check(lib().moe_prefill_runner_create(_p(w_router), _p(router_bias), _p(w_gate), _p(w_up), _p(w_down),
                                            _p(ws_gate), _p(ws_up), _p(ws_down), _p(w_sg), H, E, k, I, I_s,
                                            barr, nb, C.byref(out)))
+    return out.value
+
+
+def moe_prefill_runner_create_fp8(w_router, router_bias, q_gate, sc_gate, q_up, sc_up, q_down, sc_down,
+                                  qs_gate, ssc_gate, qs_up, ssc_up, qs_down, ssc_down, w_sg,
+                                  H, E, k, I, I_s, buckets) -> int:
+    """Runner over FP8 expert weights (codes and row scales as moe_forward_fp8)."""
+    nb = len(buckets)
+    barr = (C.c_int * max(nb, 1))(*buckets)
+    out = C.c_void_p()
+    _check(lib().moe_prefill_runner_create_fp8(_p(w_router), _p(router_bias), _p(q_gate), _p(sc_gate), _p(q_up),
+                                               _p(sc_up), _p(q_down), _p(sc_down), _p(qs_gate), _p(ssc_gate),
+                                               _p(qs_up), _p(ssc_up), _p(qs_down), _p(ssc_down), _p(w_sg),
+                                               H, E, k, I, I_s, barr, nb, C.byref(out)))
     return out.value
 
 

@@ -88,6 +88,14 @@ def test_runner_argument_errors():
     assert out.value is None
     assert L.moe_prefill_runner_create(p, None, p, p, p, p, None, None, None, 256, 8, 2, 128, 0, b, 2,
                                        C.byref(out)) == moe.MOE_ERR_SHAPE  # shared tensor with I_s = 0
+    # FP8 runner: 15 pointers (router, bias, 3 code/scale pairs, 3 shared pairs, w_sg)
+    args = [p, None, p, p, p, p, p, p] + [None] * 7
+    assert L.moe_prefill_runner_create_fp8(*args, 256, 8, 2, 128, 0, b, 2, None) == moe.MOE_ERR_NULL
+    assert L.moe_prefill_runner_create_fp8(*args, 256, 8, 2, 128, 0, b, 0, C.byref(out)) == moe.MOE_ERR_SHAPE
+    assert L.moe_prefill_runner_create_fp8(*args, 256, 8, 2, 128, 64, b, 2, C.byref(out)) == moe.MOE_ERR_NULL
+    no_scale = [p, None, p, None, p, p, p, p] + [None] * 7
+    assert L.moe_prefill_runner_create_fp8(*no_scale, 256, 8, 2, 128, 0, b, 2, C.byref(out)) == moe.MOE_ERR_NULL
+    assert out.value is None
     assert L.moe_prefill_runner_run(None, p, 10, p, None) == moe.MOE_ERR_NULL
     assert L.moe_prefill_runner_destroy(None) == moe.MOE_OK
 

@@ -114,3 +114,48 @@ def test_runner_small_batch_buckets(torch, T):
     keep = ~ex
     G.check_y(G.y_to_f64(y)[keep], r["y"][keep], f"runner small buckets T={T}")
     run.close()
+
+
+@pytest.mark.parametrize("T", [1, 39, 41, 129, 300])
+def test_runner_fp8_small_buckets(torch, T):
+    """A runner over FP8 expert weights (graphs of moe_forward_fp8) against the oracle on the same codes."""
+    inp = G.with_fp8(synth.make_inputs(SMALL_WL, seed=7, T=300))
+    lay = DeviceLayer.from_inputs(inp, fp8=True)
+    run = PrefillRunner(lay, SMALL_BUCKETS)
+    segs, lens = run.plan(T)
+    G.say(f"[chunks-fp8] T={T} segments={segs} lens={lens}")
+    x = G.to_dev_x(inp)[:T].contiguous()
+    y = run.run(x)
+    y_full = lay.forward(x)
+    ids = lay.forward_ids(T).cpu().numpy()
+    torch.cuda.synchronize()
+    sub = dict(inp)
+    sub["x"] = inp["x"][:T]
+    y_ref, _ = G.reference_y(sub, ids, f"chunks fp8 T={T}", fp8=True)
+    G.check_y(G.y_to_f64(y), y_ref, f"fp8 runner T={T}")
+    G.check_y(G.y_to_f64(y_full), y_ref, f"moe_forward_fp8 T={T}")
+    run.close()
+
+
+def test_runner_fp8_page_buckets_full_shape(torch):
+    """FP8 weights at full shape, 10000 tokens (8192 + a padded 2048): sampled tokens against the oracle,
+    the whole output against one moe_forward_fp8 call."""
+    T = 10000
+    inp = G.with_fp8(G.inputs("prefill8k", T))
+    lay = DeviceLayer.from_inputs(inp, fp8=True)
+    run = PrefillRunner(lay)
+    segs, lens = run.plan(T)
+    G.say(f"[chunks-fp8-full] T={T} segments={segs} lens={lens}")
+    x = G.to_dev_x(inp)
+    y = run.run(x)
+    y_full = lay.forward(x)
+    ids = lay.forward_ids(T).cpu().numpy()
+    torch.cuda.synchronize()
+    starts = np.cumsum([0] + lens[:-1])
+    rows = sorted(set(int(v) for s0, l in zip(starts, lens) for v in (s0, s0 + l // 2, s0 + l - 1)))
+    sub = dict(inp)
+    sub["x"] = inp["x"][rows]
+    y_ref, _ = G.reference_y(sub, ids[rows], f"chunks fp8 full T={T}", fp8=True)
+    G.check_y(G.y_to_f64(y)[rows], y_ref, f"fp8 runner full T={T} (sampled)")
+    G.check_y(G.y_to_f64(y), G.y_to_f64(y_full), f"fp8 runner vs moe_forward_fp8 T={T}")
+    run.close()
