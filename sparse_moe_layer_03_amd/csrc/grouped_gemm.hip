@@ -722,12 +722,13 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
 //   * two 64 KB stages: the loads of step k + 1 are in flight while step k
 //     is computed, and the last step of an item overlaps the first loads of
 //     the next item, which also run under the epilogue;
-//   * gate/up MFMAs produce transposed output blocks, so every lane holds
-//     runs of 4 consecutive output columns of one row and the epilogue
+//   * the MFMAs produce transposed output blocks, so every lane holds runs
+//     of 4 consecutive output columns of one row: the gate/up epilogue
 //     stores them as 8-byte writes straight from the accumulators (no LDS
-//     staging, no barrier); down items (rows of o are 4 KB apart) stage
-//     bf16 results in the stage that the last K step used and store 128-byte
-//     row segments; either way the next item's first loads are in flight;
+//     staging, no barrier); down items (rows of o are 4 KB apart) write them
+//     as 8-byte bf16 runs into the stage that the last K step used and store
+//     128-byte row segments; either way the next item's first loads are in
+//     flight;
 //   * the rows the epilogue stores to are read at item setup, so the
 //     epilogue issues no load that would wait behind those loads;
 //   * A row groups of only padding are not loaded: their LDS rows hold
@@ -926,19 +927,21 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       }
     }
   };
-  // Gate/up items compute transposed blocks (the weight fragment is the
-  // MFMA's first operand): lane l then holds output row (l & 31) and, for
+  // Items compute transposed blocks (TR: the weight fragment is the MFMA's
+  // first operand): lane l then holds output row (l & 31) and, for
   // q = 4 g + i, output column 8 g + 4 (l >> 5) + i -- four consecutive
-  // columns of one row per group g.  Down items keep the plain layout (lane l
-  // holds column l & 31 of rows 8 (q >> 2) + 4 (l >> 5) + (q & 3)).
+  // columns of one row per group g, stored as one 8-byte write.  Down items
+  // with FP8 weights keep the plain layout (lane l holds column l & 31 of
+  // rows 8 (q >> 2) + 4 (l >> 5) + (q & 3)), which measured faster there.
+  constexpr bool TR = MODE == GATE_UP || !Q;
   f32x16 acc[C::MI][C::NJ];
   auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int m = 0; m < C::MI; ++m)
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j)
-        acc[m][j] = (MODE == GATE_UP) ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0)
-                                      : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
+        acc[m][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0)
+                       : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
   };
 
   constexpr int SUB = DBK / 16;
@@ -1050,13 +1053,31 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
         for (int m = 0; m < C::MI; ++m) {
 #pragma unroll
           for (int j = 0; j < C::NJ; ++j) {
-            const int col = bb[j] + (lane & 31) - pass * EPW;
-            if (col >= 0 && col < EPW) {
-              const float scl = Q ? scales[cur.spar * BNB + bb[j] + (lane & 31)] : 1.0f;  // B row of this column
+            const int c0 = bb[j] - pass * EPW;  // the block's first column in this pass (wave-uniform)
+            if constexpr (!TR) {
+              const int col = c0 + (lane & 31);
+              if (c0 >= 0 && c0 < EPW) {
+                const float scl = Q ? scales[cur.spar * BNB + bb[j] + (lane & 31)] : 1.0f;  // B row of this column
 #pragma unroll
-              for (int q = 0; q < 16; ++q) {
-                const int row = wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                es[row * DESB + col] = f32_to_bf16(Q ? acc[m][j][q] * scl : acc[m][j][q]);
+                for (int q = 0; q < 16; ++q) {
+                  const int row = wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                  es[row * DESB + col] = f32_to_bf16(Q ? acc[m][j][q] * scl : acc[m][j][q]);
+                }
+              }
+            } else if (c0 >= 0 && c0 < EPW) {
+              const int row = wm * C::WTM + m * 32 + (lane & 31);
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int bc = bb[j] + 8 * g + 4 * (lane >> 5);  // B row of the first of the four columns
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = acc[m][j][4 * g + i];
+                if constexpr (Q) {
+                  const float4 sc = *reinterpret_cast<const float4*>(scales + cur.spar * BNB + bc);
+                  v[0] *= sc.x, v[1] *= sc.y, v[2] *= sc.z, v[3] *= sc.w;
+                }
+                const uint2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                *reinterpret_cast<uint2*>(es + row * DESB + c0 + 8 * g + 4 * (lane >> 5)) = pk;
               }
             }
           }
