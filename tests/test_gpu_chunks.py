@@ -159,3 +159,31 @@ def test_runner_fp8_page_buckets_full_shape(torch):
     G.check_y(G.y_to_f64(y)[rows], y_ref, f"fp8 runner full T={T} (sampled)")
     G.check_y(G.y_to_f64(y), G.y_to_f64(y_full), f"fp8 runner vs moe_forward_fp8 T={T}")
     run.close()
+
+
+@pytest.mark.parametrize("T", [7, 57])
+def test_runner_fp8_small_batch_buckets(torch, T):
+    """FP8 weights with 8/16/32-token buckets: the graphs run the FP8 small-batch kernels."""
+    wl = synth.Workload("chunks-sb", T=64, H=512, E=16, k=4, I=256, I_s=128, bias="normal")
+    inp = G.with_fp8(synth.make_inputs(wl, seed=8))
+    lay = DeviceLayer.from_inputs(inp, fp8=True)
+    run = PrefillRunner(lay, (8, 16, 32))
+    segs, lens = run.plan(T)
+    G.say(f"[chunks-sb-fp8] T={T} segments={segs} lens={lens}")
+    x = G.to_dev_x(inp)[:T].contiguous()
+    y = run.run(x)
+    torch.cuda.synchronize()
+    sub = dict(inp)
+    sub["x"] = inp["x"][:T]
+    r = oracle.forward(sub, fp8=True)
+    keep = ~G.excluded_tokens(r["logits"], wl.k)
+    G.check_y(G.y_to_f64(y)[keep], r["y"][keep], f"fp8 runner small buckets T={T}")
+    run.close()
+
+
+def test_runner_rejects_4bit_layer(torch):
+    """4-bit weights serve T <= 32 only: the runner refuses such a layer instead of using other weights."""
+    inp = synth.add_q4_weights(synth.make_inputs(SMALL_WL, seed=9, T=8))
+    lay = DeviceLayer.from_inputs(inp, q4=True)
+    with pytest.raises(ValueError):
+        PrefillRunner(lay, SMALL_BUCKETS)
