@@ -731,6 +731,8 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
 //     flight;
 //   * the rows the epilogue stores to are read at item setup, so the
 //     epilogue issues no load that would wait behind those loads;
+//   * a wave issues no MFMA for a 32-row block of only padding rows (the
+//     rows of a tile are sorted with padding last);
 //   * A row groups of only padding are not loaded: their LDS rows hold
 //     finite values of earlier data and feed only output rows that are not
 //     stored (a row of A reaches only the same row of the product).
@@ -741,6 +743,9 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
 //     accumulators.
 #ifndef MOE_DMA_WAVES
 #define MOE_DMA_WAVES 8
+#endif
+#ifndef MOE_DMA_SKIP_PAD_BLOCKS
+#define MOE_DMA_SKIP_PAD_BLOCKS 1
 #endif
 // Wave layout of the persistent kernel's 256 x 256 tile: NW wavefronts, two
 // across the columns (128 each), NW / 2 down the rows.
@@ -787,6 +792,7 @@ struct DmaItem {
   int spar;                   // FP8: which of the two LDS scale areas the item uses
   uint32_t aon;               // bit q: A group q holds a data row
   bool live;                  // this wave's 64 rows hold data
+  int nm;                     // 32-row blocks of this wave that hold data (padding rows are last)
   int orow[DCfg::MI];         // this lane's epilogue rows (block m): assignment (down), or >= 0 if stored
 };
 
@@ -830,8 +836,14 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
       d.ssrc = (it.dense ? p.ssc0 : p.sc0) + erow + (size_t)it.nb * 256 + lane * 4;
   }
   const int r = wm * DCfg::WTM;
-  const bool lv = it.dense ? (it.row0 + r < p.T) : (p.sorted[it.row0 + r] >= 0);
-  d.live = __builtin_amdgcn_readfirstlane((int)lv) != 0;
+  d.nm = 0;
+#pragma unroll
+  for (int m = 0; m < DCfg::MI; ++m) {
+    const int rm = it.row0 + r + m * 32;
+    const bool lv = it.dense ? (rm < p.T) : (p.sorted[rm] >= 0);
+    d.nm += __builtin_amdgcn_readfirstlane((int)lv);
+  }
+  d.live = d.nm > 0;
   // the epilogue's rows, read here so that the epilogue issues no load (a
   // load there would wait behind the next item's loads already in flight)
 #pragma unroll
@@ -935,13 +947,16 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   // rows 8 (q >> 2) + 4 (l >> 5) + (q & 3)), which measured faster there.
   constexpr bool TR = MODE == GATE_UP || !Q;
   f32x16 acc[C::MI][C::NJ];
+  int live_blocks = C::MI;  // the item's 32-row blocks of this wave that hold data
   auto mma = [&](const Frag& f) {
+    // 32-row blocks of only padding rows are skipped (a scalar branch)
 #pragma unroll
     for (int m = 0; m < C::MI; ++m)
+      if (!MOE_DMA_SKIP_PAD_BLOCKS || m == 0 || m < live_blocks)
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j)
-        acc[m][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0)
-                       : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
+        for (int j = 0; j < C::NJ; ++j)
+          acc[m][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
   };
 
   constexpr int SUB = DBK / 16;
@@ -959,6 +974,7 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[m][j][q] = 0.0f;
+    live_blocks = cur.nm;
     // K loop: wait for this wave's loads of step kb, barrier (everyone's have
     // landed and everyone has finished reading the other stage), then load
     // step kb + 1 (or the next item's step 0) into the other stage and
