@@ -139,7 +139,7 @@ def main():
                          "--steps times, then a 256 MiB device copy: the run that hardware counters are taken on")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
 
