@@ -416,8 +416,11 @@ static int forward_impl(const uint16_t* x, const uint16_t* w_router, const float
     err = oracle_route(x, w_router, bias, w_sg, T, H, E, k, lg, ids, w, s);
     if (err) goto done;
     if (ids_in) {
+        /* a selection is k distinct experts of [0, E) */
         for (size_t a = 0; a < nA; ++a) {
             if (ids_in[a] < 0 || ids_in[a] >= E) { err = ORC_ERR_SHAPE; goto done; }
+            for (size_t b = a - a % (size_t)k; b < a; ++b)
+                if (ids_in[b] == ids_in[a]) { err = ORC_ERR_SHAPE; goto done; }
         }
         for (int t = 0; t < T; ++t) {
             const float* l = lg + (size_t)t * E;
@@ -514,6 +517,9 @@ done:
  *   ids_in [T,k] (nullable): when given, routing selection is replaced by
  *   these ids and the weights are the renormalised softmax probabilities of
  *   these ids (used to evaluate a token under another side's selection).
+ *   Each row must hold k distinct experts in [0, E) (else ORC_ERR_SHAPE);
+ *   the order of a row is kept (w[t,j] belongs to ids_in[t,j] and the
+ *   combine sums in that order).
  *   y [T,H] double (out).
  *   Optional outputs (nullable): ids_out [T,k], w_out [T,k] double,
  *   s_out [T] double, logits_out [T,E] fp32, h_out [T*k, I] double (hidden

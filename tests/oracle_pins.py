@@ -371,6 +371,66 @@ def pin_ids_in_reevaluation(orc):
     assert np.array_equal(r3["ids"], alt)
 
 
+def dense_mixture_given(inp, ids):
+    """float64 dense evaluation under a given selection ``ids`` [T, k] (distinct experts per row):
+    G[t, e] = softmax(logits[t])[e] / sum over the row's experts, zero off the selection; every expert
+    runs on every token and y = sum_e G[t, e] FFN_e(x_t) + s_t FFN_s(x_t).  Returns y and the gate of
+    each position, w[t, j] = G[t, ids[t, j]]."""
+    x = _f(inp["x"])
+    wr = _f(inp["w_router"])
+    T, E = x.shape[0], wr.shape[0]
+    logits = x @ wr.T
+    if inp.get("bias") is not None:
+        logits = logits + inp["bias"].astype(F64)[None, :]
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    sel = np.zeros((T, E), bool)
+    sel[np.arange(T)[:, None], ids] = True
+    G = np.where(sel, p, 0.0)
+    G = G / G.sum(axis=1, keepdims=True)
+    wg, wu, wd = _f(inp["w_gate"]), _f(inp["w_up"]), _f(inp["w_down"])
+    y = np.zeros((T, x.shape[1]), F64)
+    for e in range(E):
+        y += G[:, e:e + 1] * ((_silu(x @ wg[e].T) * (x @ wu[e].T)) @ wd[e].T)
+    if inp.get("ws_gate") is not None:
+        s = 1.0 / (1.0 + np.exp(-(x @ _f(inp["w_sg"]))))
+        y += s[:, None] * ((_silu(x @ _f(inp["ws_gate"]).T) * (x @ _f(inp["ws_up"]).T)) @ _f(inp["ws_down"]).T)
+    return y, np.take_along_axis(G, ids, axis=1)
+
+
+def pin_ids_in_foreign_selection(orc):
+    """ids_in under a selection that is not the top-k (random distinct experts in random order) equals the
+    float64 dense mixture gated by that selection, per position in w and in y; a reordered own selection
+    permutes w with it and leaves y unchanged; a row that repeats an expert is refused."""
+    inp = _inputs(seed=22, I_s=8, E=8, k=3)
+    E, k = 8, 3
+    T = inp["x"].shape[0]
+    inp["bias"] = (np.random.default_rng(23).standard_normal(E) * 0.5).astype(np.float32)
+    rng = np.random.default_rng(24)
+    foreign = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    r = orc.forward(inp)
+    assert np.any(np.sort(foreign, 1) != np.sort(r["ids"], 1))  # not the top-k for some tokens
+    y_ref, w_ref = dense_mixture_given(inp, foreign)
+    rf = orc.forward(inp, ids_in=foreign)
+    assert np.array_equal(rf["ids"], foreign)
+    np.testing.assert_allclose(rf["w"], w_ref, rtol=0, atol=1e-7)
+    assert _rel_l2(rf["y"], y_ref) < 1e-6
+    np.testing.assert_allclose(rf["y"], y_ref, rtol=0, atol=1e-7)
+    # the oracle's own selection in another order: w follows the positions, y is the same sum
+    perm = np.stack([rng.permutation(k) for _ in range(T)])
+    own = np.take_along_axis(r["ids"], perm, axis=1)
+    ro = orc.forward(inp, ids_in=own)
+    np.testing.assert_allclose(ro["w"], np.take_along_axis(r["w"], perm, axis=1), rtol=1e-14, atol=0)
+    assert _rel_l2(ro["y"], r["y"]) < 1e-14
+    bad = foreign.copy()
+    bad[5, 2] = bad[5, 0]
+    try:
+        orc.forward(inp, ids_in=bad)
+    except Exception:
+        return
+    raise AssertionError("a selection that repeats an expert was accepted")
+
+
 def pin_stage_outputs(orc):
     """h and o of an assignment are the expert's SwiGLU hidden and output."""
     inp = _inputs(seed=21, I_s=8)

@@ -52,6 +52,12 @@ MUTANTS = {
     "f16_exponent_bias": ("mag = ldexp(1.0 + (double)m / 1024.0, e - 15);", "mag = ldexp(1.0 + (double)m / 1024.0, e - 16);"),
     "align_not_stable": ("for (size_t a = 0; a < n; ++a) {\n        int e = ids[a];",
                          "for (size_t a = n; a-- > 0;) {\n        int e = ids[a];"),
+    "ids_in_duplicates_accepted": ("if (ids_in[b] == ids_in[a]) { err = ORC_ERR_SHAPE; goto done; }",
+                                   "if (ids_in[b] == ids_in[a] && 0) { err = ORC_ERR_SHAPE; goto done; }"),
+    "ids_in_weights_from_own_selection": (
+        "ids[(size_t)t * k + j] = e;\n                w[(size_t)t * k + j] = exp((double)l[e] - m) / z;",
+        "w[(size_t)t * k + j] = exp((double)l[ids[(size_t)t * k + j]] - m) / z;\n"
+        "                ids[(size_t)t * k + j] = e;"),
     "logit_dot_stride": ("float v = dot_bf16_f32(xt, w_router + (size_t)e * H, H);",
                          "float v = dot_bf16_f32(xt, w_router + (size_t)e, H - e);"),
 }
