@@ -181,13 +181,16 @@ static int all_finite_f16(const uint16_t* p, size_t n) {
 }
 
 /* One expert-weight operand: BF16 bits, E4M3 codes with a scale per row, or
- * 4-bit codes (q4) with an fp16 scale per group of 32. */
+ * 4-bit codes (q4) with an fp16 scale per group of 32.  q_val holds the value
+ * of every E4M3 code (e4m3_value of the code, filled once per call), so that
+ * the inner loops do not re-derive it per element. */
 typedef struct {
     const uint16_t* bf;
     const uint8_t* q;
     const float* scale;
     const uint8_t* q4;
     const uint16_t* s4;
+    const double* q_val;
 } wmat;
 
 static int wmat_set(wmat m) {
@@ -214,7 +217,7 @@ static double dot_row_f64(const uint16_t* x, wmat m, size_t r, int n) {
     }
     const uint8_t* q = m.q + r * (size_t)n;
     const double sc = (double)m.scale[r];
-    for (int i = 0; i < n; ++i) acc += (double)bf16_to_f32(x[i]) * (sc * e4m3_value(q[i]));
+    for (int i = 0; i < n; ++i) acc += (double)bf16_to_f32(x[i]) * (sc * m.q_val[q[i]]);
     return acc;
 }
 
@@ -224,7 +227,7 @@ static double wmat_at(wmat m, size_t r, size_t c, int n) {
     if (m.q4)
         return f16_value(m.s4[r * (size_t)(n / Q4_GROUP) + c / Q4_GROUP]) *
                (double)q4_weight(m.q4 + r * (size_t)(n / 2), c);
-    return (double)m.scale[r] * e4m3_value(m.q[r * (size_t)n + c]);
+    return (double)m.scale[r] * m.q_val[m.q[r * (size_t)n + c]];
 }
 
 /* Steps 2-3 for one token: select k experts by (logit desc, index asc) and
@@ -532,9 +535,9 @@ int oracle_forward(const uint16_t* x, const uint16_t* w_router, const float* bia
                    const int32_t* ids_in, double* y,
                    int32_t* ids_out, double* w_out, double* s_out, float* logits_out,
                    double* h_out, double* o_out, double* hs_out, double* os_out) {
-    wmat g = {w_gate, NULL, NULL, NULL, NULL}, u = {w_up, NULL, NULL, NULL, NULL};
-    wmat d = {w_down, NULL, NULL, NULL, NULL}, sg = {ws_gate, NULL, NULL, NULL, NULL};
-    wmat su = {ws_up, NULL, NULL, NULL, NULL}, sd = {ws_down, NULL, NULL, NULL, NULL};
+    wmat g = {w_gate, NULL, NULL, NULL, NULL, NULL}, u = {w_up, NULL, NULL, NULL, NULL, NULL};
+    wmat d = {w_down, NULL, NULL, NULL, NULL, NULL}, sg = {ws_gate, NULL, NULL, NULL, NULL, NULL};
+    wmat su = {ws_up, NULL, NULL, NULL, NULL, NULL}, sd = {ws_down, NULL, NULL, NULL, NULL, NULL};
     return forward_impl(x, w_router, bias, g, u, d, sg, su, sd, w_sg, T, H, E, k, I, I_s, ids_in, y, ids_out, w_out,
                         s_out, logits_out, h_out, o_out, hs_out, os_out);
 }
@@ -555,9 +558,11 @@ int oracle_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float*
                        const int32_t* ids_in, double* y,
                        int32_t* ids_out, double* w_out, double* s_out, float* logits_out,
                        double* h_out, double* o_out, double* hs_out, double* os_out) {
-    wmat g = {NULL, q_gate, sc_gate, NULL, NULL}, u = {NULL, q_up, sc_up, NULL, NULL};
-    wmat d = {NULL, q_down, sc_down, NULL, NULL}, sg = {NULL, qs_gate, ssc_gate, NULL, NULL};
-    wmat su = {NULL, qs_up, ssc_up, NULL, NULL}, sd = {NULL, qs_down, ssc_down, NULL, NULL};
+    double val[256];
+    for (int c = 0; c < 256; ++c) val[c] = e4m3_value((uint8_t)c);
+    wmat g = {NULL, q_gate, sc_gate, NULL, NULL, val}, u = {NULL, q_up, sc_up, NULL, NULL, val};
+    wmat d = {NULL, q_down, sc_down, NULL, NULL, val}, sg = {NULL, qs_gate, ssc_gate, NULL, NULL, val};
+    wmat su = {NULL, qs_up, ssc_up, NULL, NULL, val}, sd = {NULL, qs_down, ssc_down, NULL, NULL, val};
     return forward_impl(x, w_router, bias, g, u, d, sg, su, sd, w_sg, T, H, E, k, I, I_s, ids_in, y, ids_out, w_out,
                         s_out, logits_out, h_out, o_out, hs_out, os_out);
 }
@@ -581,9 +586,9 @@ int oracle_forward_q4(const uint16_t* x, const uint16_t* w_router, const float* 
                       int32_t* ids_out, double* w_out, double* s_out, float* logits_out,
                       double* h_out, double* o_out, double* hs_out, double* os_out) {
     if (H % Q4_GROUP || I % Q4_GROUP || I_s % Q4_GROUP) return ORC_ERR_SHAPE;
-    wmat g = {NULL, NULL, NULL, q_gate, s_gate}, u = {NULL, NULL, NULL, q_up, s_up};
-    wmat d = {NULL, NULL, NULL, q_down, s_down}, sg = {NULL, NULL, NULL, qs_gate, ss_gate};
-    wmat su = {NULL, NULL, NULL, qs_up, ss_up}, sd = {NULL, NULL, NULL, qs_down, ss_down};
+    wmat g = {NULL, NULL, NULL, q_gate, s_gate, NULL}, u = {NULL, NULL, NULL, q_up, s_up, NULL};
+    wmat d = {NULL, NULL, NULL, q_down, s_down, NULL}, sg = {NULL, NULL, NULL, qs_gate, ss_gate, NULL};
+    wmat su = {NULL, NULL, NULL, qs_up, ss_up, NULL}, sd = {NULL, NULL, NULL, qs_down, ss_down, NULL};
     return forward_impl(x, w_router, bias, g, u, d, sg, su, sd, w_sg, T, H, E, k, I, I_s, ids_in, y, ids_out, w_out,
                         s_out, logits_out, h_out, o_out, hs_out, os_out);
 }

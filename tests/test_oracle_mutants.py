@@ -41,9 +41,9 @@ MUTANTS = {
     "e4m3_exponent_bias": ("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
     "e4m3_subnormal_as_normal": ("ldexp((double)m / 8.0, 1 - 7)", "ldexp(1.0 + (double)m / 8.0, 0 - 7)"),
     "e4m3_sign_dropped": ("return sgn ? -mag : mag;", "return mag;"),
-    "fp8_scale_by_column": ("acc += (double)bf16_to_f32(x[i]) * (sc * e4m3_value(q[i]));",
-                            "acc += (double)bf16_to_f32(x[i]) * ((double)m.scale[i % 8] * e4m3_value(q[i]));"),
-    "fp8_down_scale_by_column": ("return (double)m.scale[r] * e4m3_value", "return (double)m.scale[c] * e4m3_value"),
+    "fp8_scale_by_column": ("acc += (double)bf16_to_f32(x[i]) * (sc * m.q_val[q[i]]);",
+                            "acc += (double)bf16_to_f32(x[i]) * ((double)m.scale[i % 8] * m.q_val[q[i]]);"),
+    "fp8_down_scale_by_column": ("return (double)m.scale[r] * m.q_val", "return (double)m.scale[c] * m.q_val"),
     "q4_nibbles_swapped": ("int nib = (c & 1) ? (row[c / 2] >> 4) : (row[c / 2] & 15);",
                            "int nib = (c & 1) ? (row[c / 2] & 15) : (row[c / 2] >> 4);"),
     "q4_offset_binary": ("return nib >= 8 ? nib - 16 : nib;", "return nib - 8;"),
