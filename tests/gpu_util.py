@@ -7,9 +7,14 @@ Comparison rules
     is below 1e-4, unless it is an engineered exact-tie token (x_t = 0,
     whose logits are the bias on both sides); exclusions are counted.  Ids
     fed from the oracle's own logits are compared for every token.
+  * an excluded token's GPU selection must still be admissible: k distinct
+    experts in [0, E) that are a top-k, in rank order, of some logits within
+    the fp32 summation bound of the oracle's (check_admissible).
   * outputs y: max |dy| <= 2e-2 and ||dy||_2 / ||y_ref||_2 <= 1e-2 over all
     tokens; a token whose GPU selection differs (a near-tie) is compared
     with the oracle re-evaluated on the GPU's selection.
+  * stage outputs (h, o): every element, |d| <= 2^-8 |ref| + 2^-8 rms(ref)
+    and rel-L2 <= 1e-2 (check_stage).
 """
 from __future__ import annotations
 
@@ -107,11 +112,62 @@ def excluded_tokens(logits: np.ndarray, k: int, tie_rows=()) -> np.ndarray:
     return ex
 
 
-def check_ids(gpu_ids: np.ndarray, orc_ids: np.ndarray, excluded: np.ndarray, label: str):
+def logit_error_bound(inp, rows) -> np.ndarray:
+    """Bound on |l_gpu - l_oracle| for the tokens ``rows`` and every expert [len(rows), E].
+
+    Both sides sum the same H exact products of bf16 values in fp32 (a bf16 x bf16 product is exact
+    in fp32), in different orders.  A recursive fp32 sum of n terms is within gamma_n * sum|x w| of
+    the exact sum (gamma_n = n u / (1 - n u), u = 2^-24), so the two sides differ by at most twice
+    that.  The bias is then added with one rounding on each side (inside the 1e-6 floor)."""
+    rows = np.asarray(rows, np.int64)
+    xa = np.abs(synth.bf16_bits_to_f32(inp["x"][rows]).astype(np.float64))
+    wa = np.abs(synth.bf16_bits_to_f32(inp["w_router"]).astype(np.float64))
+    H = xa.shape[1]
+    u = 2.0 ** -24
+    gamma = H * u / (1.0 - H * u)
+    return 2.0 * gamma * (xa @ wa.T) + 1e-6
+
+
+def check_admissible(gpu_ids: np.ndarray, inp, logits: np.ndarray, rows, label: str):
+    """The GPU's selection for each token of ``rows`` is a legitimate top-k of the oracle's fp32 logits.
+
+    Its k ids are distinct experts in [0, E), and there are logits within ``logit_error_bound`` of the
+    oracle's of which they are the top k in rank order: every selected logit plus its bound is at
+    least every unselected logit minus its bound, and consecutive ranks satisfy the same."""
+    rows = np.asarray(rows, np.int64)
+    if rows.size == 0:
+        return
+    g = np.asarray(gpu_ids)[rows]
+    n, k = g.shape
+    E = logits.shape[1]
+    assert np.all((g >= 0) & (g < E)), f"{label}: ids outside [0, {E})"
+    assert all(len(set(r)) == k for r in g.tolist()), f"{label}: a selection repeats an expert"
+    lo = np.asarray(logits, np.float64)[rows]
+    b = logit_error_bound(inp, rows)
+    up, down = lo + b, lo - b
+    sel = np.zeros((n, E), bool)
+    sel[np.arange(n)[:, None], g] = True
+    up_sel = np.take_along_axis(up, g, axis=1)
+    down_sel = np.take_along_axis(down, g, axis=1)
+    if k < E:
+        best_unsel = np.where(sel, -np.inf, down).max(axis=1)
+        bad = np.nonzero(up_sel.min(axis=1) < best_unsel)[0]
+        assert len(bad) == 0, f"{label}: tokens {rows[bad][:10]} select an expert below an unselected one"
+    bad = np.nonzero(np.any(up_sel[:, :-1] < down_sel[:, 1:], axis=1))[0]
+    assert len(bad) == 0, f"{label}: tokens {rows[bad][:10]} list their experts out of rank order"
+
+
+def check_ids(gpu_ids: np.ndarray, orc_ids: np.ndarray, excluded: np.ndarray, label: str, inp=None, logits=None):
+    """Exact ids outside the near-ties; with ``inp`` and the oracle's ``logits``, the near-tie tokens'
+    selections must be admissible (check_admissible)."""
     keep = ~excluded
     bad = np.nonzero(np.any(gpu_ids[keep] != orc_ids[keep], axis=1))[0]
-    say(f"[{label}] ids: {keep.sum()} compared, {excluded.sum()} near-tie tokens excluded, {len(bad)} mismatches")
+    ndiff = int(np.any(gpu_ids[excluded] != orc_ids[excluded], axis=1).sum()) if excluded.any() else 0
+    say(f"[{label}] ids: {keep.sum()} compared, {excluded.sum()} near-tie tokens excluded "
+        f"({ndiff} of them select differently), {len(bad)} mismatches")
     assert len(bad) == 0, f"{label}: ids differ on tokens {np.nonzero(keep)[0][bad][:10]}"
+    if inp is not None and logits is not None:
+        check_admissible(gpu_ids, inp, logits, np.nonzero(excluded)[0], label)
 
 
 def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, label: str):
@@ -131,19 +187,86 @@ def oracle_y_with_gpu_ids(inp, rows, gpu_ids, ref, fp8=False, q4=False):
     return r["y"]
 
 
-def reference_y(inp, gpu_ids: np.ndarray, label: str, fp8: bool = False, q4: bool = False):
-    """Oracle y for every token, with near-tie tokens re-evaluated on the GPU's selection.
+def reference_y(inp, gpu_ids: np.ndarray, label: str, fp8: bool = False, q4: bool = False, want=()):
+    """Oracle y for every token, with near-tie tokens re-evaluated on the GPU's selection (after the
+    selection is checked admissible).
 
-    ``fp8`` / ``q4``: the oracle takes the FP8 / 4-bit expert weights of ``inp``."""
-    r = oracle.forward(inp, fp8=fp8, q4=q4)
+    ``fp8`` / ``q4``: the oracle takes the FP8 / 4-bit expert weights of ``inp``; ``want``: stage
+    outputs the oracle also returns (as ``oracle.forward``)."""
+    r = oracle.forward(inp, fp8=fp8, q4=q4, want=want)
     wl = inp["wl"]
     ex = excluded_tokens(r["logits"], wl.k, inp.get("tie_rows", ()))
-    check_ids(gpu_ids, r["ids"], ex, label)
+    check_ids(gpu_ids, r["ids"], ex, label, inp=inp, logits=r["logits"])
     y = r["y"].copy()
     diff = np.nonzero(np.any(gpu_ids != r["ids"], axis=1))[0]
     if len(diff):
         y[diff] = oracle_y_with_gpu_ids(inp, diff, gpu_ids[diff], r, fp8=fp8, q4=q4)
     return y, r
+
+
+def check_stage(got: np.ndarray, ref: np.ndarray, label: str, extra=None):
+    """Every element of a stage output (h or o, bf16 on the GPU) against the oracle's float64 value.
+
+    The GPU rounds the stage to bf16 to nearest (relative error <= 2^-8, the bf16 unit roundoff) after
+    fp32 sums whose rounding error is far below that.  Bound: |d| <= 2^-7 |ref| + 2^-8 rms(ref) +
+    extra, i.e. twice the rounding, a floor for elements near zero, and ``extra`` for error carried in
+    from an earlier bf16 stage (down_rounding_bound).  A wrong row, column or term gives errors of
+    the order of the values themselves, far above it."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    lim = 2.0 ** -7 * np.abs(ref) + 2.0 ** -8 * rms
+    if extra is not None:
+        lim += extra
+    over = d > lim
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)) if ref.size else 0.0
+    say(f"[{label}] {ref.size} elements: max|d| {float(d.max()) if d.size else 0.0:.3e}, "
+        f"max |d| / bound {float((d / lim).max()) if d.size else 0.0:.3f}, rel-L2 {rel:.3e}")
+    assert not over.any(), f"{label}: {int(over.sum())} elements outside the bound, first at {np.argwhere(over)[:5]}"
+    assert rel <= 1e-2, label
+
+
+def down_rounding_bound(h_ref: np.ndarray, ids: np.ndarray, w_down_bits: np.ndarray) -> np.ndarray:
+    """Bound on what the bf16 rounding of h carries into o = W_down[e] h: the GPU multiplies the rounded
+    h~ (|h~_i - h_i| <= 2^-8 |h_i|), so |sum_i (h~_i - h_i) W[c,i]| <= 2^-8 sum_i |h_i| |W[c,i]|.
+    h_ref [T*k, I] in assignment order, ids [T, k]; returns [T*k, H] (with 10% slack for the float32
+    evaluation of the sums)."""
+    e_of = np.asarray(ids).reshape(-1)
+    habs = np.abs(np.asarray(h_ref, np.float32))
+    E, H, _ = w_down_bits.shape
+    out = np.empty((e_of.size, H), np.float64)
+    for e in np.unique(e_of):
+        rows = np.nonzero(e_of == e)[0]
+        wa = np.abs(synth.bf16_bits_to_f32(w_down_bits[e]))
+        out[rows] = habs[rows] @ wa.T
+    return 1.1 * 2.0 ** -8 * out
+
+
+def runner_reference(lay, run, x, inp, T: int, label: str, fp8: bool = False):
+    """Every token of a prefill-runner call over x[:T] checked through the runner's own selections.
+
+    The runner evaluates each segment as one moe_forward call over the bucket's tokens (the partial
+    last one padded by repeating its own rows), so the same call made here gives, bit for bit, the
+    runner's output and selection of each segment; that output is compared with the oracle under
+    the selection (near-ties admissible and re-evaluated).  Returns the runner-equivalent y [T, H]."""
+    import torch
+    segs, lens = run.plan(T)
+    y_cat = []
+    start = 0
+    for b, n in zip(segs, lens):
+        rows = start + (np.arange(b) % n)
+        xs = x[torch.from_numpy(rows).to(x.device)].contiguous()
+        ys = lay.forward(xs)
+        ids = lay.forward_ids(b).cpu().numpy()
+        torch.cuda.synchronize()
+        sub = dict(inp)
+        sub["x"] = inp["x"][start:start + n]
+        y_ref, _ = reference_y(sub, ids[:n], f"{label} segment at {start}", fp8=fp8)
+        check_y(y_to_f64(ys[:n]), y_ref, f"{label} segment at {start} ({n} of {b} rows)")
+        y_cat.append(ys[:n])
+        start += n
+    return torch.cat(y_cat) if y_cat else None
 
 
 def gpu_env_note():

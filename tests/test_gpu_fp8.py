@@ -193,24 +193,3 @@ def test_fp8_tiled_parity(torch, fp8_layer, label, case):
     torch.cuda.synchronize()
     y_ref, _ = G.reference_y(inp, ids, f"fp8 {label}", fp8=True)
     G.check_y(G.y_to_f64(y), y_ref, f"fp8 {label}")
-
-
-@pytest.mark.parametrize("name,T", [("prefill8k", 8192), ("skew32k", 32768)])
-def test_fp8_full_size_sampled(torch, fp8_layer, name, T):
-    """Full workloads with FP8 weights: all ids vs the oracle router, sampled y rows vs the FP8 oracle."""
-    G.say(f"[fp8-full] {name} T={T}")
-    inp = G.with_fp8(G.inputs(name, T))
-    wl = inp["wl"]
-    lay = _fp8_layer_for(inp, fp8_layer)
-    y = lay.forward(G.to_dev_x(inp))
-    ids = lay.forward_ids(T).cpu().numpy()
-    torch.cuda.synchronize()
-    r = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["w_sg"], wl.k)
-    ex = G.excluded_tokens(r["logits"], wl.k, inp.get("tie_rows", ()))
-    G.check_ids(ids, r["ids"], ex, f"fp8 full {name}")
-    rng = np.random.default_rng(T + 1)
-    rows = np.unique(np.concatenate([rng.choice(T, 24, replace=False), [0, T - 1]]).astype(np.int64))
-    sub = dict(inp)
-    sub["x"] = inp["x"][rows]
-    ro = oracle.forward(sub, ids_in=ids[rows], fp8=True)
-    G.check_y(G.y_to_f64(y)[rows], ro["y"], f"fp8 full {name} ({len(rows)} sampled rows)")

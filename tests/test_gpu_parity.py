@@ -78,7 +78,7 @@ def test_route_generated(torch, full_layer, name, T):
     assert np.all(np.abs(lg.astype(np.float64) - r["logits"]) <= bound)
     ex = G.excluded_tokens(r["logits"], wl.k, inp.get("tie_rows", ()))
     ids = b["ids"].cpu().numpy()
-    G.check_ids(ids, r["ids"], ex, f"route {name}")
+    G.check_ids(ids, r["ids"], ex, f"route {name}", inp=inp, logits=r["logits"])
     same = np.all(ids == r["ids"], axis=1)
     # w_j = exp(l_j - l_0) / sum: a logit error d moves w_j by at most about 2 w_j max|d|
     dl = np.abs(lg.astype(np.float64) - r["logits"]).max(axis=1, keepdims=True)
@@ -244,12 +244,11 @@ def test_decode_parity(torch, full_layer, seed):
     lay = _layer_for(inp, full_layer)
     x = G.to_dev_x(inp)
     y = lay.forward(x)
+    ids = lay.forward_ids(1).cpu().numpy()
     torch.cuda.synchronize()
-    r = oracle.forward(inp)
-    ex = G.excluded_tokens(r["logits"], 8)
-    if ex[0]:
-        pytest.skip("near-tie token")
-    G.check_y(G.y_to_f64(y), r["y"], f"decode seed {seed}")
+    # a near-tie token is compared under the GPU's (admissible) selection
+    y_ref, _ = G.reference_y(inp, ids, f"decode seed {seed}")
+    G.check_y(G.y_to_f64(y), y_ref, f"decode seed {seed}")
 
 
 DECODE_SHAPES = [
@@ -295,22 +294,18 @@ def test_decode_repeated_calls(torch, full_layer):
     lay = _layer_for(inp, full_layer)
     n = 24
     xs = synth._draw_bf16(300, "x", (n, 2048), 1.0)
-    ys = []
+    ys, ids = [], []
     for i in range(n):
         sub = dict(inp)
         sub["x"] = xs[i:i + 1]
         ys.append(lay.forward(G.to_dev_x(sub)))
+        ids.append(lay.forward_ids(1).clone())  # stream-ordered: this call's selection
     torch.cuda.synchronize()
-    checked = 0
-    for i in range(0, n, 3):
+    for i in range(n):
         sub = dict(inp)
         sub["x"] = xs[i:i + 1]
-        r = oracle.forward(sub)
-        if G.excluded_tokens(r["logits"], 8)[0]:
-            continue
-        G.check_y(G.y_to_f64(ys[i]), r["y"], f"decode call {i}")
-        checked += 1
-    assert checked >= 4
+        y_ref, _ = G.reference_y(sub, ids[i].cpu().numpy(), f"decode call {i}")
+        G.check_y(G.y_to_f64(ys[i]), y_ref, f"decode call {i}")
 
 
 def test_decode_graph_replay(torch, full_layer):
@@ -396,32 +391,3 @@ def test_zero_tokens_is_noop(torch):
     y = lay.forward(x)
     torch.cuda.synchronize()
     assert y.shape == (0, 256)
-
-
-# ------------------------------------------------ full sizes, sampled outputs
-@pytest.mark.parametrize("name,T", [("prefill1k", 1024), ("prefill8k", 8192), ("skew32k", 32768)])
-def test_full_size_sampled(torch, full_layer, name, T):
-    """Full workloads as the benchmark launches them: all ids vs the oracle router, sampled y rows."""
-    G.say(f"[full] {name} T={T}")
-    inp = G.inputs(name, T)
-    wl = inp["wl"]
-    lay = _layer_for(inp, full_layer)
-    x = G.to_dev_x(inp)
-    y = lay.forward(x)
-    b = lay.alloc_stage_buffers(T)
-    lay.run_route(x, b)
-    torch.cuda.synchronize()
-    ids = b["ids"].cpu().numpy()
-    r = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["w_sg"], wl.k)
-    ex = G.excluded_tokens(r["logits"], wl.k, inp.get("tie_rows", ()))
-    G.check_ids(ids, r["ids"], ex, f"full {name}")
-    rng = np.random.default_rng(T)
-    rows = np.unique(np.concatenate([rng.choice(T, 40, replace=False), [0, T - 1],
-                                     np.asarray(inp.get("tie_rows", []))[:4]]).astype(np.int64))
-    sub = dict(inp)
-    sub["x"] = inp["x"][rows]
-    ro = oracle.forward(sub, ids_in=ids[rows])
-    yg = G.y_to_f64(y)
-    G.check_y(yg[rows], ro["y"], f"full {name} ({len(rows)} sampled rows)")
-    if len(inp.get("tie_rows", ())):
-        assert np.all(yg[inp["tie_rows"]] == 0.0)
