@@ -142,6 +142,27 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
                 uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * moe_forward without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * arithmetic and outputs as moe_forward; the workspace is one array of MOE_NOALLOC_WS_BYTES bytes in
+ * each GPU's memory, allocated with the library's code and held until the process ends.  The call
+ * allocates and frees nothing.
+ *   - Sizes whose moe_workspace_size exceeds MOE_NOALLOC_WS_BYTES give MOE_ERR_WORKSPACE before
+ *     anything is enqueued (at hidden 2048, 256 experts, top-8, FFN 512, shared 512: up to 1,398
+ *     tokens per call).
+ *   - Every call on a GPU uses that GPU's one array and leaves its contents there (no part of it has
+ *     to start at zero).  Calls that overlap on one GPU (other streams, other host threads) race:
+ *     order them.
+ *   - The first call on a device looks up the array's device address (hipGetSymbolAddress).
+ */
+#define MOE_NOALLOC_WS_BYTES (64u << 20)
+int moe_forward_noalloc(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
+                        const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                        const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
+                        const uint16_t* w_sg, int T, int H, int E, int k, int I, int I_s, uint16_t* y,
+                        void* stream);
+
+/*
  * The whole layer with FP8 expert weights.  kongchang.com "GFX1151 engine"
  * (section on the two weight formats) describes a HuggingFace-native format
  * whose weights are FP8-quantised, for speed and a smaller memory footprint.

@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "moe_internal.h"
 
@@ -416,6 +418,55 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
 
   return forward_tiled(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg, T, H, E, k, I,
                        I_s, y, workspace, layout(T, H, E, k, I, I_s), nullptr, st);
+}
+
+// Workspace of moe_forward_noalloc: one array in every GPU's memory, held until the process ends.
+// Host code reaches it only through the per-device address hipGetSymbolAddress returns (the array's
+// name is a host-side stand-in there).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_WS_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch` per device index, set at the first call there
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_ARCH, "no HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_ARCH, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "moe_forward_noalloc: hipGetSymbolAddress of the workspace array: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_forward_noalloc(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
+                        const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                        const uint16_t* ws_gate, const uint16_t* ws_up, const uint16_t* ws_down,
+                        const uint16_t* w_sg, int T, int H, int E, int k, int I, int I_s, uint16_t* y,
+                        void* stream) {
+  int rc = check_common_shapes(T, H, E, k);
+  if (rc || (rc = check_ffn_shapes(I, I_s))) return rc;
+  if (T == 0) return ok();
+  const size_t need = moe_workspace_size(T, H, E, k, I, I_s);
+  if (need > (size_t)MOE_NOALLOC_WS_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: these sizes need %zu bytes of workspace, more than its fixed %zu "
+                "(use moe_forward with a caller workspace)",
+                need, (size_t)MOE_NOALLOC_WS_BYTES);
+  if ((rc = check_arch())) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg, T, H, E, k, I,
+                     I_s, y, ws, (size_t)MOE_NOALLOC_WS_BYTES, stream);
 }
 
 int moe_forward_fp8(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint8_t* q_gate,

@@ -30,7 +30,9 @@ EXPORTS = (
     "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward_ids_offset", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
     "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine", "moe_forward_fp8", "moe_e4m3_to_f32", "moe_forward_q4",
     "moe_bucket_plan", "moe_prefill_runner_create", "moe_prefill_runner_create_fp8", "moe_prefill_runner_run", "moe_prefill_runner_destroy",
+    "moe_forward_noalloc",
 )
+NOALLOC_WS_BYTES = 64 << 20  # MOE_NOALLOC_WS_BYTES: the fixed workspace of moe_forward_noalloc
 
 
 class MoEError(RuntimeError):
@@ -61,6 +63,7 @@ def lib():
             "moe_workspace_size": ([i, i, i, i, i, i], z),
             "moe_forward_ids_offset": ([i, i, i, i, i, i], z),
             "moe_forward": ([p] * 10 + [i] * 6 + [p, p, z, p], i),
+            "moe_forward_noalloc": ([p] * 10 + [i] * 6 + [p, p], i),
             "moe_route": ([p, p, p, p, i, i, i, i, p, p, p, p, p], i),
             "moe_route_from_logits": ([p, i, i, i, p, p, p], i),
             "moe_align_scratch_size": ([i, i, i], z),
@@ -153,6 +156,13 @@ def moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, 
     _check(lib().moe_forward(_p(x), _p(w_router), _p(router_bias), _p(w_gate), _p(w_up), _p(w_down),
                              _p(ws_gate), _p(ws_up), _p(ws_down), _p(w_sg), T, H, E, k, I, I_s,
                              _p(y), _p(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_forward_noalloc(x, w_router, router_bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, w_sg,
+                        T, H, E, k, I, I_s, y, stream=None):
+    _check(lib().moe_forward_noalloc(_p(x), _p(w_router), _p(router_bias), _p(w_gate), _p(w_up), _p(w_down),
+                                     _p(ws_gate), _p(ws_up), _p(ws_down), _p(w_sg), T, H, E, k, I, I_s,
+                                     _p(y), _stream(stream)))
 
 
 def moe_forward_fp8(x, w_router, router_bias, q_gate, sc_gate, q_up, sc_up, q_down, sc_down,
