@@ -21,11 +21,15 @@
 //               SMALL tiles likewise from entry small_base on
 //   n_tiles     {number of BIG tiles, number of SMALL tiles}
 //
-// Three kernels: per-chunk histograms (LDS integer counters: the counts do
-// not depend on the order of the increments), one workgroup that scans the
-// chunk histograms and the expert totals, and a scatter in which every chunk
-// ranks its assignments in order with wave ballots (no ordering atomics) and
-// writes the tile entries and padding rows of a share of the experts.
+// Two kernels: per-chunk histograms (LDS integer counters: the counts do not
+// depend on the order of the increments), then one workgroup per chunk that
+// reads every chunk's histogram (a few tens of KB from L2), derives the expert
+// totals, the padded offsets (block scans over the experts) and its own
+// chunk's starting row per expert, ranks its assignments in order with wave
+// ballots (no ordering atomics), and writes the tile entries and padding rows
+// of a share of the experts.  Every workgroup computes the same totals and
+// offsets, so no workgroup waits for another (a single scanning workgroup
+// between the two launches cost ~7 us of latency at 65,536 assignments).
 #include "moe_internal.h"
 
 namespace moe {
@@ -66,34 +70,43 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sbuf, int& total
   return wave_off + incl - v;
 }
 
-__global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restrict__ chunk_hist,
-                                                         int32_t* __restrict__ chunk_off, int n_chunks, int E,
-                                                         int BIG, int SMALL, int32_t* __restrict__ counts, int32_t* __restrict__ pad_off,
-                                                         int32_t* __restrict__ tile_off, int32_t* __restrict__ n_tiles) {
+// One workgroup per chunk c.  Every workgroup derives the totals and padded
+// offsets from the chunk histograms (the same integer sums everywhere);
+// workgroup 0 stores counts, pad_off and n_tiles.  Then the chunk's
+// assignments are ranked in order and scattered, and the tile-table entries
+// and padding rows of the experts e = c, c + gridDim.x, ... are written.
+__global__ __launch_bounds__(256) void align_scan_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                                 int nc, int BIG, int SMALL, int small_base,
+                                                                 const int32_t* __restrict__ chunk_hist,
+                                                                 int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ pad_off,
+                                                                 int32_t* __restrict__ n_tiles,
+                                                                 int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
+                                                                 int32_t* __restrict__ tiles) {
+  __shared__ int32_t base[kMaxE];
+  __shared__ int32_t wcnt[4][kMaxE];
+  __shared__ int32_t s_run[kMaxE], s_poff[kMaxE], s_boff[kMaxE], s_soff[kMaxE];
   __shared__ int sbuf[4];
-  const int e = threadIdx.x;
-  int run = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x;
+  // expert e = tid: its total over all chunks and its share in the chunks before c (the chunk
+  // counts of one expert are contiguous, nc a multiple of 4, read 64 at a time with 16-byte loads)
+  const int e = tid;
+  int run = 0, pre = 0;
   if (e < E) {
-    // exclusive offset of every chunk within expert e; the expert's counts are
-    // contiguous (nc is a multiple of 4), read 64 at a time with 16-byte loads
-    const int4* src = reinterpret_cast<const int4*>(chunk_hist + (size_t)e * n_chunks);
-    int4* dst = reinterpret_cast<int4*>(chunk_off + (size_t)e * n_chunks);
-    for (int c0 = 0; c0 < n_chunks / 4; c0 += 16) {
+    const int4* src = reinterpret_cast<const int4*>(chunk_hist + (size_t)e * nc);
+    for (int q0 = 0; q0 < nc / 4; q0 += 16) {
       int4 hv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) hv[i] = (c0 + i < n_chunks / 4) ? src[c0 + i] : make_int4(0, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) hv[i] = (q0 + i < nc / 4) ? src[q0 + i] : make_int4(0, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        int4 o;
-        o.x = run;
-        o.y = o.x + hv[i].x;
-        o.z = o.y + hv[i].y;
-        o.w = o.z + hv[i].z;
-        run = o.w + hv[i].w;
-        if (c0 + i < n_chunks / 4) dst[c0 + i] = o;
+        const int c0 = 4 * (q0 + i);
+        run += hv[i].x + hv[i].y + hv[i].z + hv[i].w;
+        pre += (c0 < c ? hv[i].x : 0) + (c0 + 1 < c ? hv[i].y : 0) + (c0 + 2 < c ? hv[i].z : 0) +
+               (c0 + 3 < c ? hv[i].w : 0);
       }
     }
-    counts[e] = run;
   }
   const bool one = SMALL == BIG;
   const int nbig = (e < E) ? (one ? (run + BIG - 1) / BIG : run / BIG) : 0;
@@ -105,55 +118,46 @@ __global__ __launch_bounds__(256) void align_scan_kernel(const int32_t* __restri
   const int big_off = block_exclusive_scan(nbig, sbuf, total_big);
   const int small_off = block_exclusive_scan(nsmall, sbuf, total_small);
   if (e < E) {
-    pad_off[e] = rows_off;
-    tile_off[e] = big_off;  // first BIG-list entry of expert e
-    tile_off[kMaxE + e] = small_off;
+    base[e] = rows_off + pre;
+    s_run[e] = run;
+    s_poff[e] = rows_off;
+    s_boff[e] = big_off;
+    s_soff[e] = small_off;
+    if (c == 0) {
+      counts[e] = run;
+      pad_off[e] = rows_off;
+    }
   }
-  if (e == 0) {
+  if (c == 0 && e == 0) {
     pad_off[E] = total_rows;
     n_tiles[0] = total_big;
     n_tiles[1] = total_small;
   }
-}
+  __syncthreads();
 
-// Also writes, for the experts e = blockIdx.x, blockIdx.x + gridDim.x, ...,
-// their tile-table entries and the -1 of their padding rows (all threads of
-// the workgroup share each expert's writes).
-__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int n, int E, int nc,
-                                                            int BIG, int SMALL, int small_base,
-                                                            const int32_t* __restrict__ chunk_off,
-                                                            const int32_t* __restrict__ pad_off,
-                                                            const int32_t* __restrict__ counts,
-                                                            const int32_t* __restrict__ tile_off,
-                                                            int32_t* __restrict__ sorted, int32_t* __restrict__ inv,
-                                                            int32_t* __restrict__ tiles) {
-  __shared__ int32_t base[kMaxE];
-  __shared__ int32_t wcnt[4][kMaxE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int a0 = blockIdx.x * CH;
+  const int a0 = c * CH;
   const int a1 = min(a0 + CH, n);
-  for (int e = tid; e < E; e += 256) base[e] = pad_off[e] + chunk_off[(size_t)e * nc + blockIdx.x];
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int s0 = a0; s0 < a1; s0 += 256) {
     for (int i = tid; i < 4 * kMaxE; i += 256) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     const int a = s0 + tid;
     const bool valid = a < a1;
-    const int e = valid ? ids[a] : 0;
+    const int ea = valid ? ids[a] : 0;
     uint64_t peers = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const bool bit = (e >> b) & 1;
+      const bool bit = (ea >> b) & 1;
       const uint64_t m = __ballot(bit);
       peers &= bit ? m : ~m;
     }
     if (!valid) peers = 0;
     const int rank = __popcll(peers & lt_mask);
-    if (valid && rank == 0) wcnt[wave][e] = __popcll(peers);  // lowest peer reports the group size
+    if (valid && rank == 0) wcnt[wave][ea] = __popcll(peers);  // lowest peer reports the group size
     __syncthreads();
     if (valid) {
-      int pos = base[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+      int pos = base[ea] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][ea];
       sorted[pos] = a;
       inv[a] = pos;
     }
@@ -161,22 +165,21 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
     for (int ee = tid; ee < E; ee += 256) base[ee] += wcnt[0][ee] + wcnt[1][ee] + wcnt[2][ee] + wcnt[3][ee];
     __syncthreads();
   }
-  const bool one = SMALL == BIG;
-  for (int e = blockIdx.x; e < E; e += gridDim.x) {
-    const int run = counts[e];
-    const int nbig = one ? (run + BIG - 1) / BIG : run / BIG;
-    const int nsmall = one ? 0 : (run - nbig * BIG + SMALL - 1) / SMALL;
-    const int padded = nbig * BIG + nsmall * SMALL;
-    const int p0 = pad_off[e], b0 = tile_off[e], s0 = small_base + tile_off[kMaxE + e];
-    for (int i = tid; i < nbig; i += 256) {
-      tiles[2 * (b0 + i)] = e;
+  for (int e2 = c; e2 < E; e2 += gridDim.x) {
+    const int r2 = s_run[e2];
+    const int nb2 = one ? (r2 + BIG - 1) / BIG : r2 / BIG;
+    const int ns2 = one ? 0 : (r2 - nb2 * BIG + SMALL - 1) / SMALL;
+    const int pd2 = nb2 * BIG + ns2 * SMALL;
+    const int p0 = s_poff[e2], b0 = s_boff[e2], t0 = small_base + s_soff[e2];
+    for (int i = tid; i < nb2; i += 256) {
+      tiles[2 * (b0 + i)] = e2;
       tiles[2 * (b0 + i) + 1] = p0 + i * BIG;
     }
-    for (int i = tid; i < nsmall; i += 256) {
-      tiles[2 * (s0 + i)] = e;
-      tiles[2 * (s0 + i) + 1] = p0 + nbig * BIG + i * SMALL;
+    for (int i = tid; i < ns2; i += 256) {
+      tiles[2 * (t0 + i)] = e2;
+      tiles[2 * (t0 + i) + 1] = p0 + nb2 * BIG + i * SMALL;
     }
-    for (int r = run + tid; r < padded; r += 256) sorted[p0 + r] = -1;
+    for (int r = r2 + tid; r < pd2; r += 256) sorted[p0 + r] = -1;
   }
 }
 
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __res
 
 // Chunks of CH assignments, rounded up to a multiple of 4 (the scan reads 4
 // chunk counts per 16-byte load; chunks past the end are empty).
-int align_scratch_ints(int T, int E, int k) { return 2 * align_num_chunks(T, k) * E + 2 * kMaxE; }
+int align_scratch_ints(int T, int E, int k) { return align_num_chunks(T, k) * E + 64; }
 
 int align_num_chunks(int T, int k) { return (int)((((int64_t)T * k + CH - 1) / CH + 3) / 4 * 4); }
 
@@ -194,13 +197,9 @@ hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SM
   const int n = T * k;
   const int nc = align_num_chunks(T, k);
   int32_t* chunk_hist = scratch;
-  int32_t* chunk_off = scratch + (size_t)nc * E;
-  int32_t* tile_off = chunk_off + (size_t)nc * E;  // [2][kMaxE]
   hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, chunk_hist);
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(256), 0, st, chunk_hist, chunk_off, nc, E, BIG, SMALL, counts,
-                     pad_off, tile_off, n_tiles);
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, BIG, SMALL, small_base, chunk_off,
-                     pad_off, counts, tile_off, sorted, inv, tiles);
+  hipLaunchKernelGGL(align_scan_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, BIG, SMALL, small_base,
+                     chunk_hist, counts, pad_off, n_tiles, sorted, inv, tiles);
   return hipGetLastError();
 }
 
