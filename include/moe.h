@@ -107,6 +107,17 @@ size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s);
 size_t moe_forward_ids_offset(int T, int H, int E, int k, int I, int I_s);
 
 /*
+ * Sections of the workspace moe_forward carves for these sizes (the path T
+ * selects: single-token, small-batch or tiled), for checking: offsets[i] and
+ * bytes[i] (host arrays of `max` entries, either may be NULL) receive the
+ * byte offset and the size of section i.  Sections start 256-byte aligned
+ * and each is followed by at least 256 bytes that no kernel writes.  Returns
+ * the number of sections (entries past `max` are not written), 0 for
+ * unsupported sizes.  Host only.
+ */
+int moe_workspace_sections(int T, int H, int E, int k, int I, int I_s, size_t* offsets, size_t* bytes, int max);
+
+/*
  * The whole layer:  y = sum_{j<k} w[t,j] * FFN_{ids[t,j]}(x_t) + s_t * FFN_s(x_t)
  *
  *   logits[t,e] = sum_h x[t,h] W_router[e,h] (+ router_bias[e]), fp32 accumulation
@@ -148,7 +159,7 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
  * each GPU's memory, allocated with the library's code and held until the process ends.  The call
  * allocates and frees nothing.
  *   - Sizes whose moe_workspace_size exceeds MOE_NOALLOC_WS_BYTES give MOE_ERR_WORKSPACE before
- *     anything is enqueued (at hidden 2048, 256 experts, top-8, FFN 512, shared 512: up to 1,398
+ *     anything is enqueued (at hidden 2048, 256 experts, top-8, FFN 512, shared 512: up to 1,399
  *     tokens per call).
  *   - Every call on a GPU uses that GPU's one array and leaves its contents there (no part of it has
  *     to start at zero).  Calls that overlap on one GPU (other streams, other host threads) race:
@@ -297,10 +308,15 @@ int moe_prefill_runner_run(moe_prefill_runner* runner, const uint16_t* x, int T,
 int moe_prefill_runner_destroy(moe_prefill_runner* runner);
 
 /*
- * Router stage: logits (fp32 accumulation of bf16 products), optional bias,
- * top-k by (logit desc, index asc), renormalised softmax weights, and the
- * shared-expert gate s = sigmoid(x . w_sg), in one launch (the selection
- * reads the logits from on-chip memory).
+ * Router stage.  kongchang.com "GFX1151 engine" (section on the MoE kernel:
+ * of many expert sub-networks only a few are activated for each token) and
+ * guanjiawei.ai "AIMA AMD395 Qwen3.6-35B-A3B" (section on the data path: the
+ * block runs as a selected-expert MoE) define the selection; the arithmetic
+ * is the plain reading of a Qwen3-class router: logits (fp32 accumulation of
+ * bf16 products), optional bias, top-k by (logit desc, index asc),
+ * renormalised softmax weights, and the shared-expert gate
+ * s = sigmoid(x . w_sg), in one launch (the selection reads the logits from
+ * on-chip memory).
  *   Outputs: ids [T,k] int32, w [T,k] fp32; logits [T,E] fp32 (includes the
  *   bias; NULL: not stored); s [T] fp32 (required iff w_sg is given, else
  *   ignored).
@@ -310,14 +326,24 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_b
               int32_t* ids, float* w, float* s, float* logits, void* stream);
 
 /*
- * Top-k and weights on caller-supplied fp32 logits [T,E] (same selection
- * rule and weights as moe_route; -0 and +0 compare equal).
+ * Top-k and weights on caller-supplied fp32 logits [T,E]: the selection of
+ * moe_route alone (the same pages and passages: only a few experts per
+ * token, chosen by the router).  Same rule and weights as moe_route; -0 and
+ * +0 compare equal.  logits [T,E] fp32, ids [T,k] int32, w [T,k] fp32,
+ * device pointers; the logits must be finite (NaN is out of contract).
  */
 int moe_route_from_logits(const float* logits, int T, int E, int k,
                           int32_t* ids, float* w, void* stream);
 
 /*
  * Expert histogram, prefix scan and stable permutation into padded tiles.
+ * kongchang.com "GFX1151 engine" (section on the MoE kernel: sparse routing
+ * makes the compute and memory-access pattern unlike a dense layer's) and
+ * guanjiawei.ai "AIMA AMD395 Qwen3.6-35B-A3B" (section on the data path: only
+ * the selected experts are evaluated): grouping every expert's assignments
+ * into contiguous, tile-padded rows turns the selected-expert evaluation into
+ * one dense GEMM tile sequence per expert.  Integer work, bit-exact and
+ * independent of scheduling (no ordering atomics).
  *   ids [T,k] int32 (values in [0,E)).  BIG, SMALL as moe_align_tile_rows /
  *   moe_align_small_tile_rows.
  *   counts [E]      number of assignments routed to each expert

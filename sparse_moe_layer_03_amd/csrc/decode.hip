@@ -45,20 +45,15 @@ struct DecodeWs {
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 DecodeWs carve(void* base, int H, int E, int k, int I, int I_s) {
-  (void)H;
+  const WsSections w = decode_sections(H, E, k, I, I_s);
   char* p = static_cast<char*>(base);
   DecodeWs d;
-  d.logits = reinterpret_cast<float*>(p);
-  p += align256((size_t)E * 4);
-  d.ids = reinterpret_cast<int32_t*>(p);  // 256-byte slot: 64 entries, read 16 at a time
-  p += 256;
-  d.w = reinterpret_cast<float*>(p);
-  p += 256;
-  d.s = reinterpret_cast<float*>(p);
-  p += 256;
-  d.hs = reinterpret_cast<float*>(p);
-  p += align256((size_t)(I_s > 0 ? I_s : 1) * 4);
-  d.h = reinterpret_cast<float*>(p);
+  d.logits = reinterpret_cast<float*>(p + w.off[0]);
+  d.ids = reinterpret_cast<int32_t*>(p + w.off[1]);  // 256-byte slot: 64 entries, read 16 at a time
+  d.w = reinterpret_cast<float*>(p + w.off[2]);
+  d.s = reinterpret_cast<float*>(p + w.off[3]);
+  d.hs = reinterpret_cast<float*>(p + w.off[4]);
+  d.h = reinterpret_cast<float*>(p + w.off[5]);
   return d;
 }
 
@@ -481,13 +476,23 @@ void launch_decode_t(const uint16_t* x, const uint16_t* w_router, const float* b
 
 }  // namespace
 
-size_t decode_ids_offset(int E) { return align256((size_t)E * 4); }  // after the logits, as carve() lays them out
-
-size_t decode_workspace_size(int H, int E, int k, int I, int I_s) {
+// logits [E], ids and w (256-byte slots: the down launch reads 16 entries at a time), s, h_s [I_s],
+// h [k, I] (fp32)
+WsSections decode_sections(int H, int E, int k, int I, int I_s) {
   (void)H;
-  return align256((size_t)E * 4) + 2 * 256 + 256 + align256((size_t)(I_s > 0 ? I_s : 1) * 4) +
-         align256((size_t)k * I * 4);
+  WsSections w;
+  w.take((size_t)E * 4);
+  w.take(256);
+  w.take(256);
+  w.take(4);
+  w.take((size_t)(I_s > 0 ? I_s : 1) * 4);
+  w.take((size_t)k * I * 4);
+  return w;
 }
+
+size_t decode_ids_offset(int H, int E, int k, int I, int I_s) { return decode_sections(H, E, k, I, I_s).off[1]; }
+
+size_t decode_workspace_size(int H, int E, int k, int I, int I_s) { return decode_sections(H, E, k, I, I_s).total; }
 
 hipError_t launch_decode(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
                          const ExpertWeights& W, int H, int E, int k, int I, int I_s, uint16_t* y, void* ws,

@@ -102,6 +102,7 @@ struct Layout {
   int64_t max_rows, max_big, max_small, max_tiles;
   size_t off_ids, off_w, off_s, off_counts, off_padoff, off_sorted, off_inv, off_tiles, off_ntiles,
       off_scratch, off_h, off_hs, off_o, total;
+  WsSections sec;
 };
 
 // Tile capacities for tile heights (BIG, SMALL), SMALL <= BIG.
@@ -134,12 +135,7 @@ Layout layout(int T, int H, int E, int k, int I, int I_s) {
   L.max_tiles = max_tiles_for(nA, E, L.BIG, L.SMALL);
   L.max_small = L.max_tiles - L.max_big;
   const size_t n = (size_t)T * k;
-  size_t o = 0;
-  auto take = [&](size_t bytes) {
-    size_t at = o;
-    o += align256(bytes ? bytes : 1);
-    return at;
-  };
+  auto take = [&](size_t bytes) { return L.sec.take(bytes); };
   L.off_ids = take(n * 4);
   L.off_w = take(n * 4);
   L.off_s = take((size_t)T * 4);
@@ -153,7 +149,7 @@ Layout layout(int T, int H, int E, int k, int I, int I_s) {
   L.off_h = take((size_t)L.max_rows * I * 2);
   L.off_hs = take((size_t)T * (I_s > 0 ? I_s : 0) * 2);
   L.off_o = take(n * H * 2);
-  L.total = o;
+  L.total = L.sec.total;
   return L;
 }
 
@@ -225,9 +221,21 @@ size_t moe_workspace_size(int T, int H, int E, int k, int I, int I_s) {
 
 size_t moe_forward_ids_offset(int T, int H, int E, int k, int I, int I_s) {
   if (moe_workspace_size(T, H, E, k, I, I_s) == 0) return 0;
-  if (T <= 1) return decode_ids_offset(E);
-  if (T <= kSmallMaxT) return small_batch_ids_offset(T, E);
+  if (T <= 1) return decode_ids_offset(H, E, k, I, I_s);
+  if (T <= kSmallMaxT) return small_batch_ids_offset(T, H, E, k, I, I_s);
   return layout(T, H, E, k, I, I_s).off_ids;
+}
+
+int moe_workspace_sections(int T, int H, int E, int k, int I, int I_s, size_t* offsets, size_t* bytes, int max) {
+  if (moe_workspace_size(T, H, E, k, I, I_s) == 0) return 0;
+  const WsSections w = T <= 1 ? decode_sections(H, E, k, I, I_s)
+                       : T <= kSmallMaxT ? small_batch_sections(T, H, E, k, I, I_s)
+                                         : layout(T, H, E, k, I, I_s).sec;
+  for (int i = 0; i < w.n && i < max; ++i) {
+    if (offsets) offsets[i] = w.off[i];
+    if (bytes) bytes[i] = w.bytes[i];
+  }
+  return w.n;
 }
 
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint16_t* w_sg, int T,

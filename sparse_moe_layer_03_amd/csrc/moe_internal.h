@@ -150,6 +150,31 @@ struct ExpertWeights {
   int fmt;
 };
 
+// Sections of a workspace: each starts 256-byte aligned and is followed by a
+// gap of at least kWsGuard bytes that no kernel touches (moe_workspace_sections
+// reports the sections, and a test checks that the gaps keep a fill pattern).
+constexpr size_t kWsGuard = 256;
+constexpr int kMaxWsSections = 16;
+struct WsSections {
+  int n = 0;
+  size_t off[kMaxWsSections] = {};
+  size_t bytes[kMaxWsSections] = {};
+  size_t total = 0;
+  // appends a section of `b` bytes and returns its offset
+  size_t take(size_t b) {
+    const size_t at = total;
+    if (n < kMaxWsSections) {
+      off[n] = at;
+      bytes[n] = b;
+      ++n;
+    }
+    total += ((b + 255) & ~(size_t)255) + kWsGuard;
+    return at;
+  }
+};
+WsSections decode_sections(int H, int E, int k, int I, int I_s);
+WsSections small_batch_sections(int T, int H, int E, int k, int I, int I_s);
+
 // Sets the thread's error message returned by moe_last_error() (cleared for
 // MOE_OK) and returns `code`.
 int set_error(int code, const char* msg);
@@ -198,7 +223,7 @@ hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const
 // E4M3 codes to fp32 with the conversion the FP8 kernels use.
 hipError_t launch_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n, hipStream_t st);
 size_t small_batch_workspace_size(int T, int H, int E, int k, int I, int I_s);
-size_t small_batch_ids_offset(int T, int E);
-size_t decode_ids_offset(int E);
+size_t small_batch_ids_offset(int T, int H, int E, int k, int I, int I_s);
+size_t decode_ids_offset(int H, int E, int k, int I, int I_s);
 
 }  // namespace moe

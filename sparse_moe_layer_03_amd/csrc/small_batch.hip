@@ -50,34 +50,20 @@ struct SmallWs {
 };
 
 SmallWs carve_small(void* base, int T, int H, int E, int k, int I, int I_s) {
+  const WsSections w = small_batch_sections(T, H, E, k, I, I_s);
   char* p = static_cast<char*>(base);
   SmallWs d;
-  auto take = [&](size_t bytes) {
-    char* at = p;
-    p += align256(bytes ? bytes : 1);
-    return at;
-  };
-  d.logits = reinterpret_cast<float*>(take((size_t)T * E * 4));
-  d.s = reinterpret_cast<float*>(take((size_t)T * 4));
-  d.ids = reinterpret_cast<int32_t*>(take((size_t)T * k * 4));
-  d.w = reinterpret_cast<float*>(take((size_t)T * k * 4));
-  d.plan = reinterpret_cast<int32_t*>(take((size_t)(kRec0 + kRecInts * E) * 4));
-  d.asg = reinterpret_cast<int32_t*>(take((size_t)T * k * 4));
-  d.h = reinterpret_cast<float*>(take((size_t)T * k * I * 4));
-  d.hs = reinterpret_cast<float*>(take((size_t)T * (I_s > 0 ? I_s : 0) * 4));
-  d.o = reinterpret_cast<float*>(take((size_t)T * k * H * 4));
-  d.os = reinterpret_cast<float*>(take((size_t)T * H * 4));
+  d.logits = reinterpret_cast<float*>(p + w.off[0]);
+  d.s = reinterpret_cast<float*>(p + w.off[1]);
+  d.ids = reinterpret_cast<int32_t*>(p + w.off[2]);
+  d.w = reinterpret_cast<float*>(p + w.off[3]);
+  d.plan = reinterpret_cast<int32_t*>(p + w.off[4]);
+  d.asg = reinterpret_cast<int32_t*>(p + w.off[5]);
+  d.h = reinterpret_cast<float*>(p + w.off[6]);
+  d.hs = reinterpret_cast<float*>(p + w.off[7]);
+  d.o = reinterpret_cast<float*>(p + w.off[8]);
+  d.os = reinterpret_cast<float*>(p + w.off[9]);
   return d;
-}
-
-size_t small_ws_bytes(int T, int H, int E, int k, int I, int I_s) {
-  const size_t sizes[] = {(size_t)T * E * 4,          (size_t)T * 4,     (size_t)T * k * 4,
-                          (size_t)T * k * 4,          (size_t)(kRec0 + kRecInts * E) * 4, (size_t)T * k * 4,
-                          (size_t)T * k * I * 4,      (size_t)T * (I_s > 0 ? I_s : 0) * 4,
-                          (size_t)T * k * H * 4,      (size_t)T * H * 4};
-  size_t total = 0;
-  for (size_t b : sizes) total += align256(b ? b : 1);
-  return total;
 }
 
 // 8 bf16 x values . 8 weights (bf16, or E4M3 codes), ascending.
@@ -488,12 +474,29 @@ __global__ __launch_bounds__(256) void sb_combine_kernel(int T, int H, int k, in
 
 }  // namespace
 
-size_t small_batch_ids_offset(int T, int E) {  // logits, s, then ids, as carve_small() lays them out
-  return align256((size_t)T * E * 4) + align256((size_t)T * 4);
+// logits [T, E], s [T], ids [T, k], w [T, k], the plan, the assignments grouped by expert, h [T*k, I],
+// h_s [T, I_s], o [T*k, H], o_s [T, H] (fp32)
+WsSections small_batch_sections(int T, int H, int E, int k, int I, int I_s) {
+  WsSections w;
+  w.take((size_t)T * E * 4);
+  w.take((size_t)T * 4);
+  w.take((size_t)T * k * 4);
+  w.take((size_t)T * k * 4);
+  w.take((size_t)(kRec0 + kRecInts * E) * 4);
+  w.take((size_t)T * k * 4);
+  w.take((size_t)T * k * I * 4);
+  w.take((size_t)T * (I_s > 0 ? I_s : 0) * 4);
+  w.take((size_t)T * k * H * 4);
+  w.take((size_t)T * H * 4);
+  return w;
+}
+
+size_t small_batch_ids_offset(int T, int H, int E, int k, int I, int I_s) {
+  return small_batch_sections(T, H, E, k, I, I_s).off[2];
 }
 
 size_t small_batch_workspace_size(int T, int H, int E, int k, int I, int I_s) {
-  return small_ws_bytes(T, H, E, k, I, I_s);
+  return small_batch_sections(T, H, E, k, I, I_s).total;
 }
 
 hipError_t launch_small_batch(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,

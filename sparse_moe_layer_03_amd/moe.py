@@ -30,7 +30,7 @@ EXPORTS = (
     "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward_ids_offset", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
     "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine", "moe_forward_fp8", "moe_e4m3_to_f32", "moe_forward_q4",
     "moe_bucket_plan", "moe_prefill_runner_create", "moe_prefill_runner_create_fp8", "moe_prefill_runner_run", "moe_prefill_runner_destroy",
-    "moe_forward_noalloc",
+    "moe_forward_noalloc", "moe_workspace_sections",
 )
 NOALLOC_WS_BYTES = 64 << 20  # MOE_NOALLOC_WS_BYTES: the fixed workspace of moe_forward_noalloc
 
@@ -62,6 +62,7 @@ def lib():
             "moe_align_max_tiles": ([i, i, i], i64),
             "moe_workspace_size": ([i, i, i, i, i, i], z),
             "moe_forward_ids_offset": ([i, i, i, i, i, i], z),
+            "moe_workspace_sections": ([i, i, i, i, i, i, p, p, i], i),
             "moe_forward": ([p] * 10 + [i] * 6 + [p, p, z, p], i),
             "moe_forward_noalloc": ([p] * 10 + [i] * 6 + [p, p], i),
             "moe_route": ([p, p, p, p, i, i, i, i, p, p, p, p, p], i),
@@ -144,6 +145,18 @@ def moe_workspace_size(T: int, H: int, E: int, k: int, I: int, I_s: int) -> int:
 
 def moe_forward_ids_offset(T: int, H: int, E: int, k: int, I: int, I_s: int) -> int:
     return lib().moe_forward_ids_offset(T, H, E, k, I, I_s)
+
+
+def moe_workspace_sections(T: int, H: int, E: int, k: int, I: int, I_s: int):
+    """[(offset, bytes)] of the workspace sections moe_forward carves for these sizes (host only)."""
+    L = lib()
+    n = L.moe_workspace_sections(T, H, E, k, I, I_s, None, None, 0)
+    if n <= 0:
+        return []
+    off = (C.c_size_t * n)()
+    nb = (C.c_size_t * n)()
+    L.moe_workspace_sections(T, H, E, k, I, I_s, off, nb, n)
+    return [(int(off[i]), int(nb[i])) for i in range(n)]
 
 
 def moe_align_scratch_size(T: int, E: int, k: int) -> int:
