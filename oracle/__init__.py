@@ -25,13 +25,17 @@ GCC_CMD = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast
            "-fPIC", "-shared", "-Wall", "-Wextra", _SRC, "-o", LIB_PATH, "-lm"]
 
 
-def build() -> str:
-    """Compile the oracle library (gcc); returns its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = GCC_CMD[:-3] + ["-o", tmp, "-lm"]
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def build(out: str = LIB_PATH, sanitize: bool = False) -> str:
+    """Compile the oracle library (gcc) at ``out`` (``sanitize``: with ASan and UBSan; a process loading
+    it must preload gcc's libasan); returns its path."""
+    tmp = out + ".tmp"
+    cmd = GCC_CMD[:-3] + (SANITIZE_FLAGS if sanitize else []) + ["-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 class OracleError(RuntimeError):

@@ -37,24 +37,40 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source to an object (in parallel) and link the shared library."""
+# Host code instrumented with AddressSanitizer and UndefinedBehaviorSanitizer (device code is not):
+# the build the CPU tests of the argument checks and the bucket planner run under.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime a process must preload to load the sanitized build."""
+    cands = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not cands:
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return cands[-1]
+
+
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    """Compile every HIP source to an object (in parallel) and link the shared library at ``out``
+    (``sanitize``: host code with ASan and UBSan, see SANITIZE_FLAGS)."""
     cc = hipcc()
+    extra = SANITIZE_FLAGS if sanitize else []
     with tempfile.TemporaryDirectory(prefix="moe355_build_") as tmp:
         procs = []
         objs = []
         for src in sources():
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
-            cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+            cmd = [cc, *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
             objs.append(obj)
         failed = []
         for src, p in procs:
-            out, _ = p.communicate()
-            if out and (verbose or p.returncode):
-                lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+            msg, _ = p.communicate()
+            if msg and (verbose or p.returncode):
+                lines = [ln for ln in msg.splitlines() if "packed-fp32-ops" not in ln]
                 if lines:
                     print("\n".join(lines), file=sys.stderr)
             if p.returncode:
@@ -64,9 +80,9 @@ def build(verbose: bool = False) -> str:
         tmp_lib = os.path.join(tmp, "libmoe355.so")
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         subprocess.run(cmd, check=True)
-        shutil.copyfile(tmp_lib, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
-    return LIB
+        shutil.copyfile(tmp_lib, out + ".tmp")
+        os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -13,7 +13,8 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe355.so")
+# MOE355_LIB names another build of this library to load (the sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("MOE355_LIB") or os.path.join(_PKG, "libmoe355.so")
 
 MOE_OK = 0
 MOE_ERR_NULL = -1
