@@ -73,6 +73,12 @@ def algorithmic(T, H, E, k, I, I_s):
     return routed + shared + router, gate_up
 
 
+def prefill_bytes(T, H, E, k, I, I_s, n_touched):
+    """Bytes a prefill call must move at least: the touched experts' weights, the router, the shared
+    gate and the shared expert, x in and y out."""
+    return 2 * (n_touched * 3 * H * I + E * H + H + 3 * H * I_s + 2 * T * H)
+
+
 def decode_bytes(H, E, k, I, I_s):
     """Bytes one T=1 call must move: router, shared gate, k experts, shared expert, x, y."""
     return 2 * (E * H + H + k * 3 * H * I + 3 * H * I_s + H + H)
@@ -117,6 +123,93 @@ def kernel_only(args):
     return 0
 
 
+def cpu_model():
+    """The host CPU's model name (lscpu's "Model name", read from /proc/cpuinfo)."""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, T, sample=0):
+    """The CPU oracle on the first tokens of the workload: median of 3 timed runs with every host thread
+    (OMP_NUM_THREADS, else all), and median of 3 with one thread; each sample sized to ~3-5 s of work."""
+    import statistics
+    import subprocess
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    code = ("import sys, time, numpy as np; sys.path.insert(0, %r); import oracle; "
+            "from sparse_moe_layer_03_amd import synth; "
+            "inp = synth.make_inputs(synth.workload('prefill8k'), seed=0); n = int(sys.argv[1]); "
+            "sub = dict(inp); sub['x'] = inp['x'][:n]; oracle.forward(synth.make_inputs(synth.workload('tiny'), seed=0)); "
+            "r = []\nfor _ in range(3):\n    t = time.perf_counter(); oracle.forward(sub); r.append(time.perf_counter() - t)\n"
+            "print('SECS', *r)") % ROOT
+
+    def run(n, nthreads):
+        env = dict(os.environ, OMP_NUM_THREADS=str(nthreads))
+        p = subprocess.run([sys.executable, "-c", code, str(n)], env=env, capture_output=True, text=True, timeout=600)
+        line = [ln for ln in p.stdout.splitlines() if ln.startswith("SECS")]
+        if p.returncode or not line:
+            raise RuntimeError(f"oracle run failed: {p.stderr[-2000:]}")
+        return [float(v) for v in line[0].split()[1:]]
+
+    res = {}
+    for label, nth, n0 in (("all_threads", threads, sample or max(64, 40 * threads)), ("one_thread", 1, 48)):
+        secs = run(n0, nth)
+        n = n0
+        med = statistics.median(secs)
+        if med < 2.0:  # size the sample to ~3-5 s per run
+            n = int(min(T, max(n0, n0 * 4.0 / max(med, 1e-3))))
+            secs = run(n, nth)
+            med = statistics.median(secs)
+        res[label] = {"tokens": n, "secs": secs, "tokens_per_s": n / med, "threads": nth}
+        log(f"[bench] cpu oracle, {nth} thread(s): {n / med:.1f} tokens/s (median of {[round(v, 2) for v in secs]} s "
+            f"on {n} tokens)")
+    a = res["all_threads"]
+    return {"value": a["tokens_per_s"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {a['tokens']} of the {T} tokens of the same workload, whole layer (route, align, "
+                      f"expert FFNs, shared expert, combine); median of 3 runs of {[round(v, 2) for v in a['secs']]} s",
+            "one_thread": res["one_thread"], "cpu_model": cpu_model(), "runs": 3}
+
+
+def decode_only(args):
+    """Single-token and 8-token calls alone (for rocprofv3 --pmc passes): --steps calls of each, rotating
+    16 weight copies (no copy's weights stay in the 256 MB Infinity Cache between its calls), then a
+    256 MiB device copy that calibrates the byte counters."""
+    import torch
+    from sparse_moe_layer_03_amd import moe, synth
+    from sparse_moe_layer_03_amd.layer import DeviceLayer, to_device_bf16
+    dev = torch.device("cuda:0")
+    dwl = synth.workload("decode")
+    H, E, k, I, I_s = dwl.H, dwl.E, dwl.k, dwl.I, dwl.I_s
+    dinp = synth.make_inputs(dwl, seed=0)
+    dbase = DeviceLayer.from_inputs(dinp, dev)
+    copies = [dbase.w] + [{key: (None if v is None else v.clone()) for key, v in dbase.w.items()} for _ in range(15)]
+    for Tb in (1, 8):
+        xs = to_device_bf16(synth._draw_bf16(1 if Tb == 1 else 2, "x", (args.steps * Tb, H), 1.0), dev)
+        ys = torch.empty((args.steps * Tb, H), dtype=torch.bfloat16, device=dev)
+        ws, nb = dbase.workspace(Tb)
+        for i in range(args.steps):
+            W = copies[i % len(copies)]
+            moe.moe_forward(xs[i * Tb:(i + 1) * Tb], W["w_router"], None, W["w_gate"], W["w_up"], W["w_down"],
+                            W["ws_gate"], W["ws_up"], W["ws_down"], W["w_sg"], Tb, H, E, k, I, I_s,
+                            ys[i * Tb:(i + 1) * Tb], ws, nb)
+        torch.cuda.synchronize()
+        if Tb == 8:
+            off = moe.moe_forward_ids_offset(Tb, H, E, k, I, I_s)
+            touched = len(np.unique(ws[off:off + Tb * k * 4].view(torch.int32).cpu().numpy()))
+            print(json.dumps({"T": Tb, "touched_experts_last_call": touched}), flush=True)
+    a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    c = torch.empty_like(a)
+    c.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel": "decode and 8-token calls", "calls": args.steps, "copy_bytes": a.numel() * 4}),
+          flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,11 +225,13 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weight calls")
     ap.add_argument("--no-chunks", action="store_true", help="skip the bucketed-prefill runner")
     ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit-weight calls")
+    ap.add_argument("--no-reports", action="store_true", help="skip the 1024- and 32768-token report lines")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--kernel", choices=["gate_up"], default=None,
-                    help="run only the dominant kernel (routed gate/up GEMM of the 8192-token workload) "
-                         "--steps times, then a 256 MiB device copy: the run that hardware counters are taken on")
+    ap.add_argument("--kernel", choices=["gate_up", "decode"], default=None,
+                    help="gate_up: only the dominant kernel (routed gate/up GEMM of the 8192-token workload) "
+                         "--steps times; decode: only single-token and 8-token calls, --steps of each; then a "
+                         "256 MiB device copy: the runs that hardware counters are taken on")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
@@ -149,6 +244,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
+    if args.kernel == "decode":
+        return decode_only(args)
     if args.kernel:
         return kernel_only(args)
     dev = torch.device("cuda:0")
@@ -268,6 +365,61 @@ def main():
         "device": {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
+    # ------------------------ the other prefill workloads (report lines, their own rooflines)
+    if not args.no_reports:
+        reports = {}
+        for name, bound in (("prefill1k", "hbm"), ("skew32k", "mfma")):
+            rwl = synth.workload(name)
+            Tr = rwl.T
+            rinp = synth.make_inputs(rwl, seed=0, reuse=inp)
+            rlay = DeviceLayer.__new__(DeviceLayer)  # the same weights in HBM, this workload's router bias
+            rlay.__dict__.update(base.__dict__)
+            rlay.bias = None if rinp["bias"] is None else torch.from_numpy(rinp["bias"]).to(dev)
+            rlay._ws, rlay._ws_bytes = None, 0
+            xr = to_device_bf16(rinp["x"], dev)
+            yr = torch.empty((Tr, H), dtype=torch.bfloat16, device=dev)
+            rcop = [rlay]
+            for lay_c in layers[1:]:
+                c = DeviceLayer.__new__(DeviceLayer)
+                c.__dict__.update(rlay.__dict__)
+                c.w = lay_c.w
+                rcop.append(c)
+            ws_r, wsb_r = rlay.workspace(Tr)
+            for c in rcop:
+                c._ws, c._ws_bytes = ws_r, wsb_r
+            nrep = max(5, min(args.steps, int(40e-3 / max(Tr / 8192 * 0.8e-3, 1e-5))))
+            for i in range(5):
+                rcop[i % len(rcop)].forward(xr, yr)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for i in range(nrep):
+                rcop[i % len(rcop)].forward(xr, yr)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            rms = ev0.elapsed_time(ev1) / nrep
+            ids_r = rlay.forward_ids(Tr).cpu().numpy()
+            touched = int(len(np.unique(ids_r)))
+            rflops, _ = algorithmic(Tr, H, E, k, I, I_s)
+            rbytes = prefill_bytes(Tr, H, E, k, I, I_s, touched)
+            ent = {"workload": f"T={Tr} tokens, same layer; " + ("no router bias (near-uniform load)" if name ==
+                   "prefill1k" else "Zipf(1.1) router bias, 1% exact-tie tokens"),
+                   "ms_per_step": rms, "tokens_per_s": Tr / (rms * 1e-3), "steps": nrep,
+                   "touched_experts": touched, "tflops": rflops / (rms * 1e-3) / 1e12,
+                   "GB_per_s": rbytes / (rms * 1e-3) / 1e9, "algorithmic_bytes": rbytes, "flops": rflops}
+            if bound == "hbm":
+                ent["roofline"] = {"bound": "hbm", "achieved": ent["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": ent["GB_per_s"] / PEAK_HBM_GBS}
+            else:
+                ent["roofline"] = {"bound": "mfma", "achieved": ent["tflops"], "peak": PEAK_BF16_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": ent["tflops"] / PEAK_BF16_TFLOPS}
+            reports[str(Tr)] = ent
+            log(f"[bench] T={Tr}: {rms:.3f} ms/step ({Tr / rms / 1e3:.2f} M tok/s), {ent['tflops']:.0f} TF/s, "
+                f"{ent['GB_per_s']:.0f} GB/s ({touched} experts touched); {bound} frac "
+                f"{ent['roofline']['frac']:.3f}")
+            del rcop, rlay, xr, yr, ws_r
+            torch.cuda.empty_cache()
+        out["reports"] = reports
+
     del layers, bufs
     torch.cuda.empty_cache()
 
@@ -567,30 +719,7 @@ def main():
 
     # -------------------------------------------------------- cpu baseline
     if not args.no_cpu_baseline:
-        import oracle
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        def run_oracle(n):
-            sub = dict(inp)
-            sub["x"] = inp["x"][:n]
-            t1 = time.time()
-            oracle.forward(sub)
-            return time.time() - t1
-
-        sample = args.cpu_sample
-        if sample > 0:
-            secs = run_oracle(sample)
-        else:
-            # grow the sample until it takes about 15 s (every thread busy from the first probe)
-            sample, secs = min(T, 8 * threads), 0.0
-            while True:
-                secs = run_oracle(sample)
-                if secs >= 8.0 or sample >= T:
-                    break
-                sample = int(min(T, max(2 * sample, sample * 15.0 / max(secs, 1e-3))))
-        out["cpu_baseline"] = {"value": sample / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                               "sample": f"first {sample} of the {T} tokens of the same workload, whole layer "
-                                         f"(route, align, expert FFNs, shared expert, combine), {secs:.1f} s"}
-        log(f"[bench] cpu oracle: {sample / secs:.1f} tokens/s on {threads} threads ({sample} tokens, {secs:.1f}s)")
+        out["cpu_baseline"] = cpu_baseline(inp, T, args.cpu_sample)
 
     print(json.dumps(out), flush=True)
 
