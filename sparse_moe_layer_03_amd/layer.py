@@ -76,6 +76,7 @@ class DeviceLayer:
         self.shapes = Shapes(H=H, E=E, k=k, I=I, I_s=I_s)
         self._ws = None
         self._ws_bytes = 0
+        self._ws_streams = []  # streams the current workspace has been used on since it was allocated
 
     @classmethod
     def from_inputs(cls, inp, device="cuda:0", fp8: bool = False, q4: bool = False):
@@ -88,9 +89,27 @@ class DeviceLayer:
         if need == 0 and T > 0:
             raise moe.MoEError(moe.MOE_ERR_SHAPE, "unsupported shapes")
         if self._ws is None or self._ws_bytes < need:
+            if self._ws is not None:
+                # the caching allocator tracks only the allocating stream: keep the old buffer from being
+                # handed out again before work already enqueued on the other streams that used it is done
+                for st in self._ws_streams:
+                    self._ws.record_stream(st)
             self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
             self._ws_bytes = max(need, 256)
+            self._ws_streams = []
         return self._ws, self._ws_bytes
+
+    def _note_stream(self, stream):
+        """Remember a stream (None, a torch stream or a raw handle) the workspace is used on."""
+        import torch
+        if stream is None:
+            st = torch.cuda.current_stream(self.device)
+        elif isinstance(stream, int):
+            st = torch.cuda.ExternalStream(stream, device=self.device)
+        else:
+            st = stream
+        if all(st != u for u in self._ws_streams):
+            self._ws_streams.append(st)
 
     def forward(self, x, y=None, stream=None):
         """y = layer(x); x is a [T, H] bfloat16 device tensor."""
@@ -100,6 +119,7 @@ class DeviceLayer:
         if y is None:
             y = torch.empty((T, s.H), dtype=torch.bfloat16, device=self.device)
         ws, nbytes = self.workspace(T)
+        self._note_stream(stream)
         W = self.w
         if self.q4:
             q = self.q
