@@ -128,10 +128,12 @@ __device__ __forceinline__ int swz<4>(int row, int chunk) { return chunk ^ (((ro
 template <>
 __device__ __forceinline__ int swz<8>(int row, int chunk) { return chunk ^ (((row >> 1) ^ ((row & 1) << 2)) & 7); }
 
-// One work item: a BM-row tile times one block of output columns.
+// One work item: a BM-row tile times one block of output columns.  Flags are
+// ints: with bool members the persistent kernel kept its per-item copies in a
+// private stack object (scratch memory), which cost 2-4% of the GEMM time.
 struct Item {
-  int kind;    // K_GU, K_ROUTER, K_DOWN, K_COMBINE
-  bool dense;  // rows are tokens row0.. (else padded rows of one expert)
+  int kind;   // K_GU, K_ROUTER, K_DOWN, K_COMBINE
+  int dense;  // rows are tokens row0.. (else padded rows of one expert)
   int expert;
   int row0;  // first padded row or first token; -1: no item
   int nb;    // column block
@@ -791,7 +793,7 @@ struct DmaItem {
   const float* ssrc;          // FP8: this lane's 16 bytes of the item's B-row scales
   int spar;                   // FP8: which of the two LDS scale areas the item uses
   uint32_t aon;               // bit q: A group q holds a data row
-  bool live;                  // this wave's 64 rows hold data
+  int live;                   // this wave's 64 rows hold data
   int nm;                     // 32-row blocks of this wave that hold data (padding rows are last)
   int orow[DCfg::MI];         // this lane's epilogue rows (block m): assignment (down), or >= 0 if stored
 };
@@ -1048,11 +1050,52 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
           }
         }
       }
+    } else if constexpr (TR) {
+      // Down, BF16 (transposed blocks): rows of o are 4 KB apart, so each wave
+      // stages its own 64 x 128 block in its own 8 KB of the stage the last K
+      // step used and stores 128-byte row segments, 64 columns a pass.  Only
+      // the first barrier (every wave's fragment reads of that stage are done)
+      // involves the workgroup; a wave's LDS operations complete in order, so
+      // the rest needs none.  16-byte slots are XOR-swizzled by the row.
+      __syncthreads();
+      char* ew = reinterpret_cast<char*>(smem) + (size_t)((nk - 1) & 1) * G::STAGE * 16 + (size_t)wave * 8192;
+      // the assignment of this lane's copy-out rows lane / 8 + 8 i (block m = i / 4)
+      int arow[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) arow[i] = __shfl(cur.orow[i / 4], (lane / 8 + 8 * i) & 31);
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int m = 0; m < C::MI; ++m) {
+          const int row = m * 32 + (lane & 31);  // within the wave's 64 rows
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * pass + jj;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const uint2 pk = {pack_bf16x2(acc[m][j][4 * g], acc[m][j][4 * g + 1]),
+                                pack_bf16x2(acc[m][j][4 * g + 2], acc[m][j][4 * g + 3])};
+              const int slot = (jj * 4 + g) ^ (row & 7);
+              *reinterpret_cast<uint2*>(ew + row * 128 + slot * 16 + (lane >> 5) * 8) = pk;
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = lane / 8 + 8 * i, c = lane & 7;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(ew + r * 128 + (c ^ (r & 7)) * 16);
+          if (arow[i] >= 0)
+            *reinterpret_cast<u32x4*>(p.out + (size_t)arow[i] * p.ldo + it.nb * 256 + wn * 128 + pass * 64 + c * 8) =
+                v;
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
     } else {
-      // Down: rows of o are 4 KB apart, so the results are staged in LDS
-      // (bf16 [256][DESB], the stage the last K step used, free once its
-      // fragments are read) and stored as 128-byte row segments, 64 output
-      // columns a pass.
+      // Down, FP8 weights (plain blocks: lane l holds column l & 31): the
+      // workgroup stages bf16 [256][DESB] in the stage the last K step used
+      // (free once its fragments are read) and stores 128-byte row segments,
+      // 64 output columns a pass.
       __syncthreads();  // every fragment read of that stage has completed
       uint16_t* es = reinterpret_cast<uint16_t*>(smem) + (size_t)((nk - 1) & 1) * G::STAGE * 8;
       const int cr = tid >> 3, cc = (tid & 7) * 8;
@@ -1070,30 +1113,13 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
 #pragma unroll
           for (int j = 0; j < C::NJ; ++j) {
             const int c0 = bb[j] - pass * EPW;  // the block's first column in this pass (wave-uniform)
-            if constexpr (!TR) {
-              const int col = c0 + (lane & 31);
-              if (c0 >= 0 && c0 < EPW) {
-                const float scl = Q ? scales[cur.spar * BNB + bb[j] + (lane & 31)] : 1.0f;  // B row of this column
+            const int col = c0 + (lane & 31);
+            if (c0 >= 0 && c0 < EPW) {
+              const float scl = Q ? scales[cur.spar * BNB + bb[j] + (lane & 31)] : 1.0f;  // B row of this column
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                  const int row = wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                  es[row * DESB + col] = f32_to_bf16(Q ? acc[m][j][q] * scl : acc[m][j][q]);
-                }
-              }
-            } else if (c0 >= 0 && c0 < EPW) {
-              const int row = wm * C::WTM + m * 32 + (lane & 31);
-#pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const int bc = bb[j] + 8 * g + 4 * (lane >> 5);  // B row of the first of the four columns
-                float v[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = acc[m][j][4 * g + i];
-                if constexpr (Q) {
-                  const float4 sc = *reinterpret_cast<const float4*>(scales + cur.spar * BNB + bc);
-                  v[0] *= sc.x, v[1] *= sc.y, v[2] *= sc.z, v[3] *= sc.w;
-                }
-                const uint2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                *reinterpret_cast<uint2*>(es + row * DESB + c0 + 8 * g + 4 * (lane >> 5)) = pk;
+              for (int q = 0; q < 16; ++q) {
+                const int row = wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                es[row * DESB + col] = f32_to_bf16(Q ? acc[m][j][q] * scl : acc[m][j][q]);
               }
             }
           }
