@@ -315,15 +315,23 @@ int moe_prefill_runner_destroy(moe_prefill_runner* runner);
  * is the plain reading of a Qwen3-class router: logits (fp32 accumulation of
  * bf16 products), optional bias, top-k by (logit desc, index asc),
  * renormalised softmax weights, and the shared-expert gate
- * s = sigmoid(x . w_sg), in one launch (the selection reads the logits from
- * on-chip memory).
+ * s = sigmoid(x . w_sg).
  *   Outputs: ids [T,k] int32, w [T,k] fp32; logits [T,E] fp32 (includes the
  *   bias; NULL: not stored); s [T] fp32 (required iff w_sg is given, else
  *   ignored).
+ *   scratch NULL: one launch, the selection reading the logits from on-chip
+ *   memory.  scratch given (scratch_bytes >= moe_route_scratch_size(T,H,E),
+ *   16-byte aligned, else MOE_ERR_WORKSPACE / MOE_ERR_ALIGN): the form
+ *   moe_forward uses for T > 32 -- the GEMM split over slices of H, the fp32
+ *   partial logits left in scratch, then one launch that adds the slices in
+ *   slice order, adds the bias and selects.  Same rule and weights; the two
+ *   forms' logits differ only by fp32 summation order.
  */
+size_t moe_route_scratch_size(int T, int H, int E);
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias,
               const uint16_t* w_sg, int T, int H, int E, int k,
-              int32_t* ids, float* w, float* s, float* logits, void* stream);
+              int32_t* ids, float* w, float* s, float* logits,
+              void* scratch, size_t scratch_bytes, void* stream);
 
 /*
  * Top-k and weights on caller-supplied fp32 logits [T,E]: the selection of

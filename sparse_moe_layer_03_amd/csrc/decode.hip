@@ -115,12 +115,14 @@ __global__ __launch_bounds__(256) void decode_router_kernel(const uint16_t* __re
                                                             DecodeWs d) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the bias is loaded before the dot product, so its latency hides under it
+  const float bv = (bias && row < E) ? bias[row] : 0.0f;
   float d0, d1;
   if (row < E) {
     const WRow<W_BF16> r = wrow<W_BF16>(wr, nullptr, (size_t)row, H);
     row_dots<W_BF16>(nullptr, x, r, r, false, H, lane, d0, d1);
     if (lane == 0) {
-      float v = d0 + (bias ? bias[row] : 0.0f);
+      float v = d0 + bv;
       if (v == 0.0f) v = 0.0f;
       d.logits[row] = v;
     }

@@ -102,6 +102,92 @@ __device__ __forceinline__ void wave_topk_weights_n(const float (&v)[NT][4], con
   for (int t = 0; t < NT; ++t) w[t] = (lane < k) ? expf(sel_v[t] - m[t]) / sum[t] : 0.0f;
 }
 
+// ---- Sixteen lanes per token ----
+// The same selection for 4 tokens per wave, one per 16-lane DPP row: sub-lane
+// s = lane % 16 of row i holds experts 16 s .. 16 s + 15 of token i.  Each
+// candidate becomes a unique 64-bit key, (order key of the logit) << 8 |
+// (255 - expert): a larger key is a larger logit, or the same logit at a
+// lower index, so the selection order is the key order with no ties to
+// break; absent experts have key 0, below every finite logit.  A lane sorts
+// its 16 keys once (Batcher's odd-even merge network); then each round takes
+// the row maximum of the lanes' heads (a 4-step DPP butterfly, the result in
+// every lane of the row) and the lane whose head it is drops it.  All rows
+// run the same instructions, so the 4 tokens cost what one does.
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the 16 lanes of a DPP row, in every lane of the row: lane
+// exchanges xor 1 and xor 2 (quad permutations), then the half-row and the
+// row mirrors.
+__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
+  uint64_t o = dpp_u64<0xB1>(v);  // quad_perm [1,0,3,2]
+  v = v > o ? v : o;
+  o = dpp_u64<0x4E>(v);  // quad_perm [2,3,0,1]
+  v = v > o ? v : o;
+  o = dpp_u64<0x141>(v);  // row_half_mirror
+  v = v > o ? v : o;
+  o = dpp_u64<0x140>(v);  // row_mirror
+  return v > o ? v : o;
+}
+
+// Sorts N (a power of two) keys into descending order: Batcher's odd-even
+// merge sort; every index is a compile-time constant after unrolling.
+template <int N>
+__device__ __forceinline__ void sort_desc_u64(uint64_t (&a)[N]) {
+#pragma unroll
+  for (int p = 1; p < N; p <<= 1)
+#pragma unroll
+    for (int k = p; k >= 1; k >>= 1)
+#pragma unroll
+      for (int j = k % p; j + k < N; j += 2 * k)
+#pragma unroll
+        for (int i = 0; i < k; ++i)
+          if (i + j + k < N && (i + j) / (2 * p) == (i + j + k) / (2 * p)) {
+            const uint64_t x = a[i + j], y = a[i + j + k];
+            a[i + j] = x > y ? x : y;
+            a[i + j + k] = x > y ? y : x;
+          }
+}
+
+// The 64-bit key of expert e's logit v (valid: e exists).
+__device__ __forceinline__ uint64_t topk_key64(float v, int e, bool valid) {
+  if (v == 0.0f) v = 0.0f;  // -0 -> +0
+  return valid ? ((uint64_t)float_order_key(v) << 8) | (uint64_t)(255 - e) : 0ull;
+}
+
+// Selection and weights for the token of this lane's row from its 16 keys
+// (topk_key64, any order; k <= 16 <= number of valid experts is not needed:
+// k <= the valid experts of the token).  Sub-lane r < k ends with rank r's
+// expert in sel_e and logit in sel_v, and returns rank r's weight (0 in the
+// other sub-lanes); the weights are those of wave_topk_weights_n:
+//   w_r = exp(l_r - l_0) / sum_{r' < k} exp(l_r' - l_0), the sum in rank order.
+__device__ __forceinline__ float row16_topk_weights(uint64_t (&key)[16], int k, int sub, int& sel_e, float& sel_v) {
+  sort_desc_u64<16>(key);
+  sel_e = -1;
+  sel_v = 0.0f;
+  float m = 0.0f, sum = 0.0f;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t M = row16_max_u64(key[0]);
+    const bool win = key[0] == M;  // keys are unique: one lane of the row
+#pragma unroll
+    for (int i = 0; i < 15; ++i) key[i] = win ? key[i + 1] : key[i];
+    key[15] = win ? 0ull : key[15];
+    const float val = float_from_order_key((uint32_t)(M >> 8));
+    if (sub == r) {
+      sel_e = 255 - (int)(M & 255u);
+      sel_v = val;
+    }
+    if (r == 0) m = val;
+    sum += expf(val - m);  // rank order
+  }
+  return sub < k ? expf(sel_v - m) / sum : 0.0f;
+}
+
 // One token.
 __device__ __forceinline__ void wave_topk_weights(const float (&v)[4], const bool (&valid)[4], int k, int lane,
                                                   int& sel_e, float& sel_v, float& w) {

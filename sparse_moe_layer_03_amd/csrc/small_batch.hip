@@ -139,6 +139,8 @@ __global__ __launch_bounds__(256) void sb_router_kernel(const uint16_t* __restri
   const bool gate = (r == E);
   const bool live = r < E || (gate && w_sg);
   const uint16_t* row = gate ? w_sg : wr + (size_t)min(r, E - 1) * H;
+  // the bias is loaded before the dot products, so its latency hides under them
+  const float bv = (bias && r < E) ? bias[r] : 0.0f;
   const int nch = H / 8;
   const int t0 = blockIdx.y * TB;
   const int nt = min(TB, T - t0);
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256) void sb_router_kernel(const uint16_t* __restri
           if (gate) {
             d.s[t0 + t] = 1.0f / (1.0f + expf(-v));
           } else {
-            float lv = v + (bias ? bias[r] : 0.0f);
+            float lv = v + bv;
             if (lv == 0.0f) lv = 0.0f;
             d.logits[(size_t)(t0 + t) * E + r] = lv;
           }

@@ -167,17 +167,19 @@ class DeviceLayer:
             "tiles": torch.empty(2 * max_tiles, **i32),
             "n_tiles": torch.empty(2, **i32),
             "scratch": torch.empty(moe.moe_align_scratch_size(T, s.E, s.k), dtype=torch.uint8, device=dev),
+            "route_scratch": torch.empty(moe.moe_route_scratch_size(T, s.H, s.E), dtype=torch.uint8, device=dev),
             "h": torch.empty((max_rows, s.I), dtype=torch.bfloat16, device=dev),
             "h_s": torch.empty((T, s.I_s), dtype=torch.bfloat16, device=dev) if s.I_s else None,
             "o": torch.empty((T * s.k, s.H), dtype=torch.bfloat16, device=dev),
             "y": torch.empty((T, s.H), dtype=torch.bfloat16, device=dev),
         }
 
-    def run_route(self, x, b, stream=None):
+    def run_route(self, x, b, stream=None, split=True):
+        """split: the form moe_forward runs (K slices, then sum and top-k); else the one-launch router."""
         s = self.shapes
         T = x.shape[0]
         moe.moe_route(x, self.w["w_router"], self.bias, self.w["w_sg"], T, s.H, s.E, s.k, b["ids"], b["w"],
-                      b["s"] if s.I_s else None, b["logits"], stream)
+                      b["s"] if s.I_s else None, b["logits"], stream, scratch=b["route_scratch"] if split else None)
 
     def run_align(self, T, b, stream=None):
         s = self.shapes

@@ -28,7 +28,7 @@ Q4_MAX_T = 32  # MOE_Q4_MAX_T: moe_forward_q4 covers 1 <= T <= this
 
 EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_align_tile_rows", "moe_align_small_tile_rows", "moe_align_max_rows",
-    "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward_ids_offset", "moe_forward", "moe_route", "moe_route_from_logits", "moe_align_scratch_size",
+    "moe_align_max_big_tiles", "moe_align_max_tiles", "moe_workspace_size", "moe_forward_ids_offset", "moe_forward", "moe_route", "moe_route_scratch_size", "moe_route_from_logits", "moe_align_scratch_size",
     "moe_align", "moe_grouped_gate_up", "moe_grouped_down", "moe_combine", "moe_forward_fp8", "moe_e4m3_to_f32", "moe_forward_q4",
     "moe_bucket_plan", "moe_prefill_runner_create", "moe_prefill_runner_create_fp8", "moe_prefill_runner_run", "moe_prefill_runner_destroy",
     "moe_forward_noalloc", "moe_workspace_sections",
@@ -66,7 +66,8 @@ def lib():
             "moe_workspace_sections": ([i, i, i, i, i, i, p, p, i], i),
             "moe_forward": ([p] * 10 + [i] * 6 + [p, p, z, p], i),
             "moe_forward_noalloc": ([p] * 10 + [i] * 6 + [p, p], i),
-            "moe_route": ([p, p, p, p, i, i, i, i, p, p, p, p, p], i),
+            "moe_route": ([p, p, p, p, i, i, i, i, p, p, p, p, p, z, p], i),
+            "moe_route_scratch_size": ([i, i, i], z),
             "moe_route_from_logits": ([p, i, i, i, p, p, p], i),
             "moe_align_scratch_size": ([i, i, i], z),
             "moe_align": ([p, i, i, i, p, p, p, p, p, p, p, z, p], i),
@@ -251,9 +252,15 @@ def moe_prefill_runner_destroy(runner: Optional[int]):
     _check(lib().moe_prefill_runner_destroy(runner))
 
 
-def moe_route(x, w_router, router_bias, w_sg, T, H, E, k, ids, w, s, logits, stream=None):
+def moe_route_scratch_size(T, H, E):
+    return lib().moe_route_scratch_size(T, H, E)
+
+
+def moe_route(x, w_router, router_bias, w_sg, T, H, E, k, ids, w, s, logits, stream=None, scratch=None):
+    """scratch (a device tensor of moe_route_scratch_size bytes or more) selects the split form."""
+    nbytes = scratch.numel() * scratch.element_size() if scratch is not None else 0
     _check(lib().moe_route(_p(x), _p(w_router), _p(router_bias), _p(w_sg), T, H, E, k,
-                           _p(ids), _p(w), _p(s), _p(logits), _stream(stream)))
+                           _p(ids), _p(w), _p(s), _p(logits), _p(scratch), nbytes, _stream(stream)))
 
 
 def moe_route_from_logits(logits, T, E, k, ids, w, stream=None):

@@ -123,10 +123,17 @@ def test_forward_argument_errors(L):
 
 def test_stage_argument_errors(L):
     p = 1 << 12
-    assert L.moe_route(None, p, None, None, 16, 256, 8, 2, p, p, None, p, None) == moe.MOE_ERR_NULL
-    assert L.moe_route(p, p, None, None, 16, 256, 8, 2, None, p, None, p, None) == moe.MOE_ERR_NULL  # ids
-    assert L.moe_route(p, p, None, p, 16, 256, 8, 2, p, p, None, p, None) == moe.MOE_ERR_NULL  # s missing
-    assert L.moe_route(p, p, None, None, 16, 256, 8, 20, p, p, None, p, None) == moe.MOE_ERR_SHAPE
+    assert L.moe_route(None, p, None, None, 16, 256, 8, 2, p, p, None, p, None, 0, None) == moe.MOE_ERR_NULL
+    assert L.moe_route(p, p, None, None, 16, 256, 8, 2, None, p, None, p, None, 0, None) == moe.MOE_ERR_NULL  # ids
+    assert L.moe_route(p, p, None, p, 16, 256, 8, 2, p, p, None, p, None, 0, None) == moe.MOE_ERR_NULL  # s missing
+    assert L.moe_route(p, p, None, None, 16, 256, 8, 20, p, p, None, p, None, 0, None) == moe.MOE_ERR_SHAPE
+    # split form: scratch too small, then misaligned
+    need = L.moe_route_scratch_size(16, 256, 8)
+    assert need >= 16 * 8 * 4
+    assert L.moe_route(p, p, None, None, 16, 256, 8, 2, p, p, None, p, p, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert "scratch" in moe.last_error()
+    assert L.moe_route(p, p, None, None, 16, 256, 8, 2, p, p, None, p, p + 4, need, None) == moe.MOE_ERR_ALIGN
+    assert L.moe_route_scratch_size(16, 100, 8) == 0
     assert L.moe_route_from_logits(p, 16, 300, 2, p, p, None) == moe.MOE_ERR_SHAPE
     assert L.moe_route_from_logits(None, 16, 8, 2, p, p, None) == moe.MOE_ERR_NULL
     assert L.moe_align(p, 16, 8, 2, p, p, p, p, p, p, p, 1, None) == moe.MOE_ERR_WORKSPACE
@@ -136,7 +143,7 @@ def test_stage_argument_errors(L):
     assert L.moe_grouped_down(p, p, p, p, p, 16, 256, 8, 2, 100, p, None) == moe.MOE_ERR_SHAPE
     assert L.moe_combine(p, p, p, None, None, 16, 256, 2, 0, p, None) == moe.MOE_ERR_SHAPE
     assert L.moe_combine(p, p, None, None, None, 16, 256, 2, 0, None, None) == moe.MOE_ERR_NULL
-    for f, args in ((L.moe_route, (p, p, None, None, 0, 256, 8, 2, None, None, None, None, None)),
+    for f, args in ((L.moe_route, (p, p, None, None, 0, 256, 8, 2, None, None, None, None, None, 0, None)),
                     (L.moe_align, (None, 0, 8, 2, None, None, None, None, None, None, None, 0, None))):
         assert f(*args) == moe.MOE_OK  # T = 0 is a no-op
 

@@ -57,16 +57,18 @@ def test_route_from_logits_bit_exact(torch, T, E, k):
 ROUTE_CASES = [("tiny", None), ("prefill1k", 300), ("prefill8k", 1000), ("skew32k", 2048)]
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "fused"])
 @pytest.mark.parametrize("name,T", ROUTE_CASES)
-def test_route_generated(torch, full_layer, name, T):
-    """Router GEMM + top-k on generated inputs: ids exact outside near-ties; logits, w, s close."""
-    G.say(f"[route] {name} T={T}")
+def test_route_generated(torch, full_layer, name, T, split):
+    """Router GEMM + top-k on generated inputs, both forms (K slices + sum + top-k, as moe_forward
+    runs it; one launch): ids exact outside near-ties; logits, w, s close."""
+    G.say(f"[route] {name} T={T} split={split}")
     inp = G.inputs(name, T)
     lay = _layer_for(inp, full_layer)
     x = G.to_dev_x(inp)
     Tn = x.shape[0]
     b = lay.alloc_stage_buffers(Tn)
-    lay.run_route(x, b)
+    lay.run_route(x, b, split=split)
     torch.cuda.synchronize()
     wl = inp["wl"]
     r = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["w_sg"], wl.k)
