@@ -89,6 +89,18 @@ __global__ __launch_bounds__(256) void align_scan_scatter_kernel(const int32_t* 
   __shared__ int sbuf[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x;
+  // the chunk's expert ids, loaded before the histograms so that the ranking
+  // below waits for no load (clamped, not skipped: a load under a per-lane
+  // condition is waited for on its own)
+  const int a0 = c * CH;
+  const int a1 = min(a0 + CH, n);
+  int ea_pre[CH / 256];
+#pragma unroll
+  for (int it = 0; it < CH / 256; ++it) {
+    const int a = a0 + it * 256 + tid;
+    const int v = ids[min(a, n - 1)];
+    ea_pre[it] = a < a1 ? v : 0;
+  }
   // expert e = tid: its total over all chunks and its share in the chunks before c (the chunk
   // counts of one expert are contiguous, nc a multiple of 4, read 64 at a time with 16-byte loads)
   const int e = tid;
@@ -135,15 +147,16 @@ __global__ __launch_bounds__(256) void align_scan_scatter_kernel(const int32_t* 
   }
   __syncthreads();
 
-  const int a0 = c * CH;
-  const int a1 = min(a0 + CH, n);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int s0 = a0; s0 < a1; s0 += 256) {
+#pragma unroll
+  for (int it = 0; it < CH / 256; ++it) {
+    const int s0 = a0 + it * 256;
+    if (s0 >= a1) break;  // uniform
     for (int i = tid; i < 4 * kMaxE; i += 256) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     const int a = s0 + tid;
     const bool valid = a < a1;
-    const int ea = valid ? ids[a] : 0;
+    const int ea = ea_pre[it];
     uint64_t peers = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
