@@ -64,7 +64,32 @@ def test_route_generated(torch, full_layer, name, T, split):
     runs it; one launch): ids exact outside near-ties; logits, w, s close."""
     G.say(f"[route] {name} T={T} split={split}")
     inp = G.inputs(name, T)
-    lay = _layer_for(inp, full_layer)
+    _check_route(torch, inp, _layer_for(inp, full_layer), split, name)
+
+
+ROUTE_SHAPES = [
+    # (label, workload): slice counts 2 to 8, expert counts that leave padding in the
+    # 4-float partial rows, k = 1 and k = E, no bias, no shared gate, ragged token counts
+    ("E3-H256-T33", synth.Workload("r3", T=33, H=256, E=3, k=2, I=128, I_s=128, bias="normal")),
+    ("E5-kE-noshared", synth.Workload("r5", T=100, H=512, E=5, k=5, I=128, I_s=0)),
+    ("E13-k1-T257", synth.Workload("r13", T=257, H=1024, E=13, k=1, I=128, I_s=128, bias="normal")),
+    ("E64-k16-H4096", synth.Workload("r64", T=70, H=4096, E=64, k=16, I=256, I_s=256)),
+    ("E200-H768-T1500", synth.Workload("r200", T=1500, H=768, E=200, k=6, I=128, I_s=0, bias="normal")),
+    ("E256-T33", synth.Workload("r256", T=33, H=2048, E=256, k=8, I=512, I_s=512, bias="normal")),
+]
+
+
+@pytest.mark.parametrize("split", [True, False], ids=["split", "fused"])
+@pytest.mark.parametrize("name,wl", ROUTE_SHAPES)
+def test_route_shapes(torch, name, wl, split):
+    """Both router forms at shapes that exercise the slice count, the partial-row padding and
+    the selection's edge cases, against the oracle."""
+    G.say(f"[route-shape] {name} split={split}")
+    inp = synth.make_inputs(wl, seed=5)
+    _check_route(torch, inp, DeviceLayer.from_inputs(inp), split, name)
+
+
+def _check_route(torch, inp, lay, split, name):
     x = G.to_dev_x(inp)
     Tn = x.shape[0]
     b = lay.alloc_stage_buffers(Tn)
