@@ -774,10 +774,11 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
 //   * the MFMAs produce transposed output blocks, so every lane holds runs
 //     of 4 consecutive output columns of one row: the gate/up epilogue
 //     stores them as 8-byte writes straight from the accumulators (no LDS
-//     staging, no barrier); down items (rows of o are 4 KB apart) write them
-//     as 8-byte bf16 runs into the stage that the last K step used and store
-//     128-byte row segments; either way the next item's first loads are in
-//     flight;
+//     staging, no barrier); in down items (rows of o are 4 KB apart) each
+//     wave writes its block as 8-byte bf16 runs into its own part of the
+//     stage that the last K step used and stores 128-byte (BF16) or 64-byte
+//     (FP8: smaller stages) row segments; either way the next item's first
+//     loads are in flight;
 //   * the rows the epilogue stores to are read at item setup, so the
 //     epilogue issues no load that would wait behind those loads;
 //   * a wave issues no MFMA for a 32-row block of only padding rows (the
@@ -806,7 +807,6 @@ struct DCfg {
 constexpr int DBM = 256, DNT = DCfg::NT, DBK = 64, DKCH = DBK / 8;
 constexpr int DRPI = 64 / DKCH;                    // A rows filled by one load instruction (64 lanes x 16 B)
 constexpr int DNQ = DCfg::RPW / DRPI;              // A load instructions per wave per K step
-constexpr int DESB = 72;                           // bf16 row stride of the down epilogue's staging tile
 template <bool Q>
 struct DmaGeom {
   static constexpr int BKCH = Q ? DKCH / 2 : DKCH;         // 16-byte chunks per B row per K step
@@ -815,7 +815,7 @@ struct DmaGeom {
   static constexpr int STAGE = DBM * DKCH + BNB * BKCH;    // 16-byte chunks per stage (A rows, then B rows)
   static constexpr size_t SCALES = Q ? 2 * BNB * 4 : 0;    // LDS bytes of two items' B-row scales
   static constexpr size_t LDS = 2 * (size_t)STAGE * 16 + SCALES;  // 128 KB (bf16), 98 KB (FP8)
-  static_assert((size_t)DBM * DESB * 2 + DBM * 4 <= (size_t)STAGE * 16, "down epilogue staging fits in one stage");
+  static_assert((size_t)DNT / 64 * (Q ? 4096 : 8192) <= (size_t)STAGE * 16, "down epilogue staging fits in one stage");
 };
 
 // One direct-to-LDS load: 16 bytes per lane from src into LDS at
@@ -988,13 +988,10 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       }
     }
   };
-  // Items compute transposed blocks (TR: the weight fragment is the MFMA's
-  // first operand): lane l then holds output row (l & 31) and, for
-  // q = 4 g + i, output column 8 g + 4 (l >> 5) + i -- four consecutive
-  // columns of one row per group g, stored as one 8-byte write.  Down items
-  // with FP8 weights keep the plain layout (lane l holds column l & 31 of
-  // rows 8 (q >> 2) + 4 (l >> 5) + (q & 3)), which measured faster there.
-  constexpr bool TR = MODE == GATE_UP || !Q;
+  // Items compute transposed blocks (the weight fragment is the MFMA's first
+  // operand): lane l then holds output row (l & 31) and, for q = 4 g + i,
+  // output column 8 g + 4 (l >> 5) + i -- four consecutive columns of one row
+  // per group g, stored as one 8-byte write (or staged as one 8-byte run).
   f32x16 acc[C::MI][C::NJ];
   int live_blocks = C::MI;  // the item's 32-row blocks of this wave that hold data
   auto mma = [&](const Frag& f) {
@@ -1004,8 +1001,7 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       if (!MOE_DMA_SKIP_PAD_BLOCKS || m == 0 || m < live_blocks)
 #pragma unroll
         for (int j = 0; j < C::NJ; ++j)
-          acc[m][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0)
-                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[m], f.b[j], acc[m][j], 0, 0, 0);
+          acc[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[m], acc[m][j], 0, 0, 0);
   };
 
   constexpr int SUB = DBK / 16;
@@ -1097,8 +1093,43 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
           }
         }
       }
-    } else if constexpr (TR) {
-      // Down, BF16 (transposed blocks): rows of o are 4 KB apart, so each wave
+    } else if constexpr (Q) {
+      // Down, FP8: as the BF16 epilogue below, in 4 KB per
+      // wave (an FP8 stage holds 48 KB), 32 columns a pass and 64-byte row
+      // segments; each lane scales its 4 consecutive columns by their weight
+      // rows' scales (in LDS since the item's first K step)
+      __syncthreads();
+      char* ew = reinterpret_cast<char*>(smem) + (size_t)((nk - 1) & 1) * G::STAGE * 16 + (size_t)wave * 4096;
+      const float* S = scales + cur.spar * BNB;
+      int arow[4];  // the assignment of this lane's copy-out rows lane / 4 + 16 i (block m = i / 2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) arow[i] = __shfl(cur.orow[i / 2], (lane / 4 + 16 * i) & 31);
+#pragma unroll
+      for (int pass = 0; pass < C::NJ; ++pass) {
+#pragma unroll
+        for (int m = 0; m < C::MI; ++m) {
+          const int row = m * 32 + (lane & 31);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 sc = *reinterpret_cast<const float4*>(S + bb[pass] + 8 * g + 4 * (lane >> 5));
+            const uint2 pk = {pack_bf16x2(acc[m][pass][4 * g] * sc.x, acc[m][pass][4 * g + 1] * sc.y),
+                              pack_bf16x2(acc[m][pass][4 * g + 2] * sc.z, acc[m][pass][4 * g + 3] * sc.w)};
+            *reinterpret_cast<uint2*>(ew + row * 64 + (g ^ (row & 3)) * 16 + (lane >> 5) * 8) = pk;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = lane / 4 + 16 * i, c = lane & 3;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(ew + r * 64 + (c ^ (r & 3)) * 16);
+          if (arow[i] >= 0)
+            *reinterpret_cast<u32x4*>(p.out + (size_t)arow[i] * p.ldo + it.nb * 256 + wn * 128 + pass * 32 + c * 8) =
+                v;
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    } else {
+      // Down, BF16: rows of o are 4 KB apart, so each wave
       // stages its own 64 x 128 block in its own 8 KB of the stage the last K
       // step used and stores 128-byte row segments, 64 columns a pass.  Only
       // the first barrier (every wave's fragment reads of that stage are done)
@@ -1137,50 +1168,6 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
                 v;
         }
         __builtin_amdgcn_wave_barrier();
-      }
-    } else {
-      // Down, FP8 weights (plain blocks: lane l holds column l & 31): the
-      // workgroup stages bf16 [256][DESB] in the stage the last K step used
-      // (free once its fragments are read) and stores 128-byte row segments,
-      // 64 output columns a pass.
-      __syncthreads();  // every fragment read of that stage has completed
-      uint16_t* es = reinterpret_cast<uint16_t*>(smem) + (size_t)((nk - 1) & 1) * G::STAGE * 8;
-      const int cr = tid >> 3, cc = (tid & 7) * 8;
-      constexpr int RG = DNT / 8, RPT = DBM / RG;
-      // the assignment of each copy-out row (-1: padding, not stored), read
-      // from the item's prefetched rows through LDS
-      int* srow = reinterpret_cast<int*>(es + DBM * DESB);
-      if (lane < 32)
-#pragma unroll
-        for (int m = 0; m < C::MI; ++m)
-          if (wn == 0) srow[wm * C::WTM + m * 32 + lane] = cur.orow[m];
-      for (int pass = 0; pass < 256 / EPW; ++pass) {
-#pragma unroll
-        for (int m = 0; m < C::MI; ++m) {
-#pragma unroll
-          for (int j = 0; j < C::NJ; ++j) {
-            const int c0 = bb[j] - pass * EPW;  // the block's first column in this pass (wave-uniform)
-            const int col = c0 + (lane & 31);
-            if (c0 >= 0 && c0 < EPW) {
-              const float scl = Q ? scales[cur.spar * BNB + bb[j] + (lane & 31)] : 1.0f;  // B row of this column
-#pragma unroll
-              for (int q = 0; q < 16; ++q) {
-                const int row = wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-                es[row * DESB + col] = f32_to_bf16(Q ? acc[m][j][q] * scl : acc[m][j][q]);
-              }
-            }
-          }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-          const int r = cr + RG * i;
-          const int a = srow[r];
-          if (a >= 0)
-            *reinterpret_cast<u32x4*>(p.out + (size_t)a * p.ldo + it.nb * 256 + pass * EPW + cc) =
-                *reinterpret_cast<const u32x4*>(es + r * DESB + cc);
-        }
-        __syncthreads();
       }
     }
     cur = next;
