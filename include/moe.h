@@ -319,13 +319,16 @@ int moe_prefill_runner_destroy(moe_prefill_runner* runner);
  *   Outputs: ids [T,k] int32, w [T,k] fp32; logits [T,E] fp32 (includes the
  *   bias; NULL: not stored); s [T] fp32 (required iff w_sg is given, else
  *   ignored).
- *   scratch NULL: one launch, the selection reading the logits from on-chip
- *   memory.  scratch given (scratch_bytes >= moe_route_scratch_size(T,H,E),
- *   16-byte aligned, else MOE_ERR_WORKSPACE / MOE_ERR_ALIGN): the form
- *   moe_forward uses for T > 32 -- the GEMM split over slices of H, the fp32
- *   partial logits left in scratch, then one launch that adds the slices in
- *   slice order, adds the bias and selects.  Same rule and weights; the two
- *   forms' logits differ only by fp32 summation order.
+ *   scratch NULL: one launch, W_router staged through on-chip memory with
+ *   the x tiles, the selection reading the logits from on-chip memory.
+ *   scratch given (scratch_bytes >= moe_route_scratch_size(T,H,E), which
+ *   depends on H and E only; 16-byte aligned, else MOE_ERR_WORKSPACE /
+ *   MOE_ERR_ALIGN): the form moe_forward uses for T > 32 -- a first launch
+ *   copies W_router into scratch in the order of the matrix-core operands,
+ *   then one launch per 32-token tile keeps the tile's x rows on chip,
+ *   streams the weights into registers, and selects and computes s in its
+ *   epilogue.  Same rule and weights; the two forms' logits differ only by
+ *   fp32 summation order.
  */
 size_t moe_route_scratch_size(int T, int H, int E);
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias,

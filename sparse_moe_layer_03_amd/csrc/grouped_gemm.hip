@@ -29,13 +29,6 @@
 //   SHARED_COMBINE  token tiles.  A = h_s rows, B = 256 rows of Ws_down;
 //                   epilogue is the deterministic combine
 //                   y = sum_j w_j o[t*k + j] + s * acc
-//   ROUTER_PART     (token tile, K slice) items: the router GEMM over one
-//                   slice of the hidden dimension; epilogue stores the fp32
-//                   partial logits of the slice (and the slice's partial
-//                   x . w_sg); a second launch sums the slices in order and
-//                   selects (route.hip).  A workgroup's K loop is a fraction
-//                   of H long, so the launch is not paced by one long chain
-//                   of dependent K steps per token tile.
 //
 // Data movement of the BM <= 128 kernel (256 threads, 4 wavefronts, BM x 256
 // tile; the 256-row kernel is described where it is defined):
@@ -62,7 +55,7 @@ namespace {
 
 constexpr int BNB = 256;  // B rows per tile
 
-enum { GATE_UP = 0, DOWN = 1, ROUTER = 2, SHARED_COMBINE = 3, ROUTER_PART = 4 };
+enum { GATE_UP = 0, DOWN = 1, ROUTER = 2, SHARED_COMBINE = 3 };
 
 // Kind of one work item.
 enum { K_GU = 0, K_ROUTER = 1, K_DOWN = 2, K_COMBINE = 3 };
@@ -116,9 +109,6 @@ struct GemmParams {
   float* gate_s;         // ROUTER: s = sigmoid(x . w_sg) [T] (when w_sg is given)
   int32_t* ids;          // ROUTER: top-k experts [T, k]
   float* wts;            // ROUTER: their renormalised weights [T, k]
-  int kslice;            // ROUTER_PART: K columns per slice (K = kslice * slices)
-  float* part;           // ROUTER_PART: partial logits [slices, T, EP], EP = E rounded up to 4
-  float* gpart;          // ROUTER_PART: partial x . w_sg [slices, T] (when w_sg is given)
   // FP8 weights (kernels instantiated with Q): b0/b1/bs0/bs1 then point at
   // E4M3 codes (one byte per weight), and each weight row has an fp32 scale:
   // routed sc0/sc1 [E * N], shared ssc0/ssc1 [N_s]
@@ -188,21 +178,11 @@ template <int BM, int MODE>
 __device__ __forceinline__ Item decode_item(const GemmParams& p) {
   Item it;
   it.kind = (MODE == DOWN) ? K_DOWN : (MODE == SHARED_COMBINE) ? K_COMBINE : K_GU;
-  it.dense = (MODE == ROUTER || MODE == SHARED_COMBINE || MODE == ROUTER_PART);
+  it.dense = (MODE == ROUTER || MODE == SHARED_COMBINE);
   it.expert = 0;
   it.row0 = -1;
   it.nb = 0;
   const int n_tok_tiles = (p.T + BM - 1) / BM;
-  if (MODE == ROUTER_PART) {
-    // slice major: the workgroups of one XCD share a slice of W_router in L2
-    const int slices = p.K / p.kslice;
-    const int item = xcd_item(blockIdx.x, n_tok_tiles * slices);
-    if (item < 0) return it;
-    it.kind = K_ROUTER;
-    it.row0 = (item % n_tok_tiles) * BM;
-    it.nb = item / n_tok_tiles;  // K slice
-    return it;
-  }
   if (MODE == GATE_UP || MODE == DOWN) {
     const RoutedItems r = routed_items<BM, MODE>(p);
     const int item = xcd_item(blockIdx.x, r.total);
@@ -244,7 +224,7 @@ template <int MODE, bool Q = false>
 __device__ __forceinline__ const uint16_t* b_row(const GemmParams& p, const Item it, int j, bool& ok) {
   constexpr size_t EB = Q ? 1 : 2;  // bytes per weight
   ok = true;
-  if ((MODE == ROUTER || MODE == ROUTER_PART) && it.kind == K_ROUTER) {
+  if (MODE == ROUTER && it.kind == K_ROUTER) {
     ok = j < p.E;
     return p.br + (size_t)(ok ? j : 0) * p.K;
   }
@@ -497,7 +477,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const Item it, f32
 template <int BM, int BK, int MODE>
 constexpr size_t lds_bytes() {
   size_t stages = 2 * (size_t)(BM + BNB) * (BK / 8) * 16;
-  size_t epi = MODE == ROUTER_PART ? 0 : (size_t)BM * (MODE == ROUTER ? RLD : ESLD) * 4;
+  size_t epi = (size_t)BM * (MODE == ROUTER ? RLD : ESLD) * 4;
   return stages > epi ? stages : epi;
 }
 
@@ -508,8 +488,8 @@ constexpr size_t lds_bytes() {
 // epilogue.
 template <int BM, int BK, int OCC, int MODE, bool Q = false>
 __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmParams p) {
-  static_assert(!Q || (MODE != ROUTER && MODE != ROUTER_PART), "the router weights stay bf16");
-  constexpr bool RT = MODE == ROUTER || MODE == ROUTER_PART;
+  static_assert(!Q || MODE != ROUTER, "the router weights stay bf16");
+  constexpr bool RT = MODE == ROUTER;
   using C = Cfg<BM>;
   constexpr int KCH = BK / 8;               // 16-byte chunks per row per K step
   constexpr int RPP = C::NT / KCH;          // rows covered by one pass of the NT threads
@@ -548,10 +528,8 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
   typedef wchunk_t<Q ? W_FP8 : W_BF16> BC;  // B chunk as loaded: 8 bf16, or 8 E4M3 codes
   u32x4 pa0[NA], pa1[NA];
   BC pb0[NB], pb1[NB];
-  // first K column of the item (ROUTER_PART: its slice)
-  const int kbase = (MODE == ROUTER_PART) ? it.nb * p.kslice : 0;
   auto gload = [&](u32x4 (&pa)[NA], BC (&pb)[NB], int kb) {
-    const int koff = kbase + kb * BK + chunk * 8;
+    const int koff = kb * BK + chunk * 8;
 #pragma unroll
     for (int i = 0; i < NA; ++i) pa[i] = *reinterpret_cast<const u32x4*>(arow[i] + koff);
 #pragma unroll
@@ -646,7 +624,7 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
     }
     live = __builtin_amdgcn_readfirstlane((int)live) != 0;
   }
-  const int nk = (MODE == ROUTER_PART ? p.kslice : p.K) / BK;
+  const int nk = p.K / BK;
   gload(pa0, pb0, 0);
   gload(pa1, pb1, 1);
   sstore(pa0, pb0, 0);
@@ -668,7 +646,7 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
     auto stage = [&](int st, u32x4 (&pa)[NA], BC (&pb)[NB], int next_kb, int ks) {
       u32x4 gv = {0u, 0u, 0u, 0u};
       if constexpr (RT) {
-        if (p.w_sg) gv = *reinterpret_cast<const u32x4*>(p.w_sg + kbase + ks * BK + (tid % KCH) * 8);
+        if (p.w_sg) gv = *reinterpret_cast<const u32x4*>(p.w_sg + ks * BK + (tid % KCH) * 8);
       }
       if constexpr (L) read_frags(f0, st, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -719,33 +697,6 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
   if constexpr (MODE == ROUTER) {
     if (p.w_sg) router_gate<BM, KCH>(p, it, gacc[0]);
     router_epilogue<BM, C::NT, C::MI, C::NJ, C::WTM>(p, it, acc, wm, bb, smem);
-  } else if constexpr (MODE == ROUTER_PART) {
-    // partial x . w_sg: sum over the KCH lanes of a row, stored by its first
-    if (p.w_sg) {
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        float v = gacc[g];
-#pragma unroll
-        for (int off = 1; off < KCH; off <<= 1) v += __shfl_xor(v, off);
-        const int t = it.row0 + tid / KCH + g * (C::NT / KCH);
-        if (tid % KCH == 0 && t < p.T) p.gpart[(size_t)it.nb * p.T + t] = v;
-      }
-    }
-    // partial logits straight from the accumulators: one store instruction
-    // writes two rows of 32 consecutive experts (128 bytes each)
-    const int EP = (p.E + 3) & ~3;
-    float* out = p.part + (size_t)it.nb * p.T * EP;
-#pragma unroll
-    for (int m = 0; m < C::MI; ++m)
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-        const int col = bb[j] + (lane & 31);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int t = it.row0 + wm * C::WTM + m * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-          if (col < p.E && t < p.T) out[(size_t)t * EP + col] = acc[m][j][q];
-        }
-      }
   } else {
     if constexpr (Q) {
       // row scales of this lane's B columns (one per column block j)
@@ -1280,53 +1231,6 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const floa
   // the launch's whole parallelism.
   constexpr int BM = router_rows(MOE_ROUTER_CFG);
   return launch_mode<MOE_ROUTER_CFG, ROUTER>(p, (int64_t)((T + BM - 1) / BM), st);
-}
-
-// Split router: (token tile, K slice) items, then the in-order sum and the
-// selection per token.  Slices: doubled (up to 8, each a whole number of
-// pairs of K steps) while the launch has fewer than MOE_ROUTER_SPLIT_ITEMS
-// items.
-#ifndef MOE_ROUTER_SPLIT_CFG
-#define MOE_ROUTER_SPLIT_CFG 64, 64, 2
-#endif
-#ifndef MOE_ROUTER_SPLIT_ITEMS
-#define MOE_ROUTER_SPLIT_ITEMS 256
-#endif
-int router_slices(int T, int H) {
-  constexpr int BM = router_rows(MOE_ROUTER_SPLIT_CFG), BK = router_bk(MOE_ROUTER_SPLIT_CFG);
-  const int64_t tiles = (T + BM - 1) / BM;
-  int S = 1;
-  while (S < 8 && tiles * S < MOE_ROUTER_SPLIT_ITEMS && (H / (2 * S)) % (2 * BK) == 0) S *= 2;
-  return S;
-}
-
-size_t router_split_bytes(int T, int H, int E) {
-  const size_t S = (size_t)router_slices(T, H), EP = (size_t)((E + 3) & ~3);
-  return S * T * EP * 4 + 256 + S * T * 4;
-}
-
-hipError_t launch_router_split(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
-                               int T, int H, int E, int k, void* part_buf, float* s, int32_t* ids, float* w,
-                               float* logits, hipStream_t st) {
-  if (T <= 0) return hipSuccess;
-  const int S = router_slices(T, H);
-  GemmParams p = {};
-  p.a = x;
-  p.lda = H;
-  p.K = H;
-  p.kslice = H / S;
-  p.br = w_router;
-  p.E = E;
-  p.T = T;
-  p.k = k;
-  p.w_sg = w_sg;
-  p.part = static_cast<float*>(part_buf);
-  const size_t EP = (size_t)((E + 3) & ~3);
-  p.gpart = reinterpret_cast<float*>(static_cast<char*>(part_buf) + (((size_t)S * T * EP * 4 + 255) & ~(size_t)255));
-  constexpr int BM = router_rows(MOE_ROUTER_SPLIT_CFG);
-  hipError_t e = launch_mode<MOE_ROUTER_SPLIT_CFG, ROUTER_PART>(p, (int64_t)((T + BM - 1) / BM) * S, st);
-  if (e != hipSuccess) return e;
-  return launch_router_reduce_topk(p.part, w_sg ? p.gpart : nullptr, S, T, E, k, bias, ids, w, s, logits, st);
 }
 
 hipError_t launch_gate_up(const uint16_t* x, const void* w_gate, const void* w_up, const int32_t* sorted,

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "moe.h"
@@ -148,10 +149,10 @@ Layout layout(int T, int H, int E, int k, int I, int I_s) {
   L.off_scratch = take(moe_align_scratch_size(T, E, k));
   L.off_h = take((size_t)L.max_rows * I * 2);
   L.off_hs = take((size_t)T * (I_s > 0 ? I_s : 0) * 2);
-  // o; before the down GEMM writes it, the same bytes hold the split
-  // router's partial logits
-  const size_t part = router_split_bytes(T, H, E);
-  L.off_o = take(n * H * 2 > part ? n * H * 2 : part);
+  // o; before the down GEMM writes it, the same bytes hold the router's
+  // fragment-order copy of W_router
+  const size_t pack = router_pack_bytes(H, E);
+  L.off_o = take(n * H * 2 > pack ? n * H * 2 : pack);
   L.total = L.sec.total;
   return L;
 }
@@ -243,7 +244,7 @@ int moe_workspace_sections(int T, int H, int E, int k, int I, int I_s, size_t* o
 
 size_t moe_route_scratch_size(int T, int H, int E) {
   if (check_common_shapes(T, H, E, 1) != MOE_OK) return 0;
-  return T > 0 ? router_split_bytes(T, H, E) : 256;
+  return router_pack_bytes(H, E);
 }
 
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_bias, const uint16_t* w_sg, int T,
@@ -257,7 +258,7 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_b
   if (!aligned16(x) || !aligned16(w_router) || (w_sg && !aligned16(w_sg)))
     return fail(MOE_ERR_ALIGN, "moe_route: bf16 tensors must be 16-byte aligned");
   if (scratch) {
-    const size_t need = router_split_bytes(T, H, E);
+    const size_t need = router_pack_bytes(H, E);
     if (scratch_bytes < need)
       return fail(MOE_ERR_WORKSPACE, "moe_route: scratch holds %zu bytes, %zu needed", scratch_bytes, need);
     if (!aligned16(scratch)) return fail(MOE_ERR_ALIGN, "moe_route: scratch must be 16-byte aligned");
@@ -265,8 +266,8 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_b
   if ((rc = check_arch())) return rc;
   const hipStream_t st = (hipStream_t)stream;
   if (scratch)
-    return hip_status(launch_router_split(x, w_router, router_bias, w_sg, T, H, E, k, scratch, s, ids, w, logits, st),
-                      "moe_route: split router GEMM, then sum and top-k");
+    return hip_status(launch_router_stream(x, w_router, router_bias, w_sg, T, H, E, k, scratch, logits, s, ids, w, st),
+                      "moe_route: streamed router with top-k");
   return hip_status(launch_router(x, w_router, router_bias, w_sg, T, H, E, k, logits, s, ids, w, st),
                     "moe_route: router GEMM with top-k");
 }
@@ -347,8 +348,8 @@ int forward_tiled(const uint16_t* x, const uint16_t* w_router, const float* rout
 
   // router over K slices; the partial logits live in o's bytes until the
   // selection has read them
-  hipError_t e = launch_router_split(x, w_router, router_bias, I_s > 0 ? w_sg : nullptr, T, H, E, k, o,
-                                     I_s > 0 ? s : nullptr, ids, w, nullptr, st);
+  hipError_t e = launch_router_stream(x, w_router, router_bias, I_s > 0 ? w_sg : nullptr, T, H, E, k, o, nullptr,
+                                      I_s > 0 ? s : nullptr, ids, w, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: router with top-k");
   e = launch_align(ids, T, E, k, L.BIG, L.SMALL, (int)L.max_big, counts, pad_off, sorted, inv, tiles, n_tiles, scratch,
                    st);

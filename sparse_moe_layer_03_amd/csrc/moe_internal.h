@@ -186,20 +186,15 @@ int set_error(int code, const char* msg);
 // the same x tiles.
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg, int T,
                          int H, int E, int k, float* logits, float* s, int32_t* ids, float* w, hipStream_t st);
-// Split router for the tiled forward: the router GEMM over (token tile, K
-// slice) items writes fp32 partial logits (and partial x . w_sg) to part_buf
-// (router_split_bytes(T, H, E) bytes, 256-byte aligned), then one launch sums
-// the slices in order, adds the bias and selects; s and logits (NULL: not
-// stored) as launch_router.
-int router_slices(int T, int H);
-size_t router_split_bytes(int T, int H, int E);
-hipError_t launch_router_split(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
-                               int T, int H, int E, int k, void* part_buf, float* s, int32_t* ids, float* w,
-                               float* logits, hipStream_t st);
-// Its second launch: part [S, T, EP] (EP = E rounded up to 4), gpart [S, T] or NULL.
-hipError_t launch_router_reduce_topk(const float* part, const float* gpart, int S, int T, int E, int k,
-                                     const float* bias, int32_t* ids, float* w, float* s, float* logits,
-                                     hipStream_t st);
+// Router for the tiled forward: 32-token tiles, the tile's x rows resident in
+// LDS and W_router streamed into registers from a copy in fragment order
+// (written to wpack, router_pack_bytes(H, E) bytes, 16-byte aligned, by a
+// first launch), the selection and the shared gate in the same launch; the
+// other arguments as launch_router.
+size_t router_pack_bytes(int H, int E);
+hipError_t launch_router_stream(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
+                                int T, int H, int E, int k, void* wpack, float* logits, float* s, int32_t* ids,
+                                float* w, hipStream_t st);
 // Top-k ids and renormalised weights from fp32 logits [T, E].
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,

@@ -174,12 +174,13 @@ class DeviceLayer:
             "y": torch.empty((T, s.H), dtype=torch.bfloat16, device=dev),
         }
 
-    def run_route(self, x, b, stream=None, split=True):
-        """split: the form moe_forward runs (K slices, then sum and top-k); else the one-launch router."""
+    def run_route(self, x, b, stream=None, streamed=True):
+        """streamed: the form moe_forward runs (W_router copied in operand order into scratch, then
+        the streamed router); else the one-launch router with W_router staged through LDS."""
         s = self.shapes
         T = x.shape[0]
         moe.moe_route(x, self.w["w_router"], self.bias, self.w["w_sg"], T, s.H, s.E, s.k, b["ids"], b["w"],
-                      b["s"] if s.I_s else None, b["logits"], stream, scratch=b["route_scratch"] if split else None)
+                      b["s"] if s.I_s else None, b["logits"], stream, scratch=b["route_scratch"] if streamed else None)
 
     def run_align(self, T, b, stream=None):
         s = self.shapes

@@ -257,7 +257,7 @@ def moe_route_scratch_size(T, H, E):
 
 
 def moe_route(x, w_router, router_bias, w_sg, T, H, E, k, ids, w, s, logits, stream=None, scratch=None):
-    """scratch (a device tensor of moe_route_scratch_size bytes or more) selects the split form."""
+    """scratch (a device tensor of moe_route_scratch_size bytes or more) selects the streamed form."""
     nbytes = scratch.numel() * scratch.element_size() if scratch is not None else 0
     _check(lib().moe_route(_p(x), _p(w_router), _p(router_bias), _p(w_sg), T, H, E, k,
                            _p(ids), _p(w), _p(s), _p(logits), _p(scratch), nbytes, _stream(stream)))

@@ -127,9 +127,10 @@ def test_stage_argument_errors(L):
     assert L.moe_route(p, p, None, None, 16, 256, 8, 2, None, p, None, p, None, 0, None) == moe.MOE_ERR_NULL  # ids
     assert L.moe_route(p, p, None, p, 16, 256, 8, 2, p, p, None, p, None, 0, None) == moe.MOE_ERR_NULL  # s missing
     assert L.moe_route(p, p, None, None, 16, 256, 8, 20, p, p, None, p, None, 0, None) == moe.MOE_ERR_SHAPE
-    # split form: scratch too small, then misaligned
+    # streamed form: scratch (W_router in operand order: 32-expert groups x H x 64 bytes) too
+    # small, then misaligned
     need = L.moe_route_scratch_size(16, 256, 8)
-    assert need >= 16 * 8 * 4
+    assert need == 1 * 256 * 64 and L.moe_route_scratch_size(1, 2048, 256) == 8 * 2048 * 64
     assert L.moe_route(p, p, None, None, 16, 256, 8, 2, p, p, None, p, p, need - 1, None) == moe.MOE_ERR_WORKSPACE
     assert "scratch" in moe.last_error()
     assert L.moe_route(p, p, None, None, 16, 256, 8, 2, p, p, None, p, p + 4, need, None) == moe.MOE_ERR_ALIGN

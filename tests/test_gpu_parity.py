@@ -57,43 +57,48 @@ def test_route_from_logits_bit_exact(torch, T, E, k):
 ROUTE_CASES = [("tiny", None), ("prefill1k", 300), ("prefill8k", 1000), ("skew32k", 2048)]
 
 
-@pytest.mark.parametrize("split", [True, False], ids=["split", "fused"])
+@pytest.mark.parametrize("streamed", [True, False], ids=["streamed", "staged"])
 @pytest.mark.parametrize("name,T", ROUTE_CASES)
-def test_route_generated(torch, full_layer, name, T, split):
-    """Router GEMM + top-k on generated inputs, both forms (K slices + sum + top-k, as moe_forward
-    runs it; one launch): ids exact outside near-ties; logits, w, s close."""
-    G.say(f"[route] {name} T={T} split={split}")
+def test_route_generated(torch, full_layer, name, T, streamed):
+    """Router GEMM + top-k on generated inputs, both forms (W_router copied in operand order and
+    streamed into registers, as moe_forward runs it; W_router staged through LDS): ids exact outside
+    near-ties; logits, w, s close."""
+    G.say(f"[route] {name} T={T} streamed={streamed}")
     inp = G.inputs(name, T)
-    _check_route(torch, inp, _layer_for(inp, full_layer), split, name)
+    _check_route(torch, inp, _layer_for(inp, full_layer), streamed, name)
 
 
 ROUTE_SHAPES = [
-    # (label, workload): slice counts 2 to 8, expert counts that leave padding in the
-    # 4-float partial rows, k = 1 and k = E, no bias, no shared gate, ragged token counts
+    # (label, workload): streamed form with 1 to 8 groups of 32 experts (a group's K split over
+    # 4, 2 or 1 waves, idle waves when E <= 224), 4 to 32 sub-steps per block, H in segments
+    # of 2048 (x tile streamed in the first), expert counts that leave columns past E in a
+    # group, k = 1 and k = E, no bias, no shared gate, ragged token counts
     ("E3-H256-T33", synth.Workload("r3", T=33, H=256, E=3, k=2, I=128, I_s=128, bias="normal")),
     ("E5-kE-noshared", synth.Workload("r5", T=100, H=512, E=5, k=5, I=128, I_s=0)),
     ("E13-k1-T257", synth.Workload("r13", T=257, H=1024, E=13, k=1, I=128, I_s=128, bias="normal")),
     ("E64-k16-H4096", synth.Workload("r64", T=70, H=4096, E=64, k=16, I=256, I_s=256)),
     ("E200-H768-T1500", synth.Workload("r200", T=1500, H=768, E=200, k=6, I=128, I_s=0, bias="normal")),
     ("E256-T33", synth.Workload("r256", T=33, H=2048, E=256, k=8, I=512, I_s=512, bias="normal")),
+    ("E100-H1536-T65", synth.Workload("r100", T=65, H=1536, E=100, k=4, I=128, I_s=128, bias="normal")),
+    ("E256-H2560-T40", synth.Workload("r256w", T=40, H=2560, E=256, k=8, I=128, I_s=128, bias="normal")),
 ]
 
 
-@pytest.mark.parametrize("split", [True, False], ids=["split", "fused"])
+@pytest.mark.parametrize("streamed", [True, False], ids=["streamed", "staged"])
 @pytest.mark.parametrize("name,wl", ROUTE_SHAPES)
-def test_route_shapes(torch, name, wl, split):
-    """Both router forms at shapes that exercise the slice count, the partial-row padding and
-    the selection's edge cases, against the oracle."""
-    G.say(f"[route-shape] {name} split={split}")
+def test_route_shapes(torch, name, wl, streamed):
+    """Both router forms at shapes that exercise the streamed router's wave layouts, block depths
+    and K segments, and the selection's edge cases, against the oracle."""
+    G.say(f"[route-shape] {name} streamed={streamed}")
     inp = synth.make_inputs(wl, seed=5)
-    _check_route(torch, inp, DeviceLayer.from_inputs(inp), split, name)
+    _check_route(torch, inp, DeviceLayer.from_inputs(inp), streamed, name)
 
 
-def _check_route(torch, inp, lay, split, name):
+def _check_route(torch, inp, lay, streamed, name):
     x = G.to_dev_x(inp)
     Tn = x.shape[0]
     b = lay.alloc_stage_buffers(Tn)
-    lay.run_route(x, b, split=split)
+    lay.run_route(x, b, streamed=streamed)
     torch.cuda.synchronize()
     wl = inp["wl"]
     r = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["w_sg"], wl.k)
