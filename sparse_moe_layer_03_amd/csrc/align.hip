@@ -216,4 +216,14 @@ hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SM
   return hipGetLastError();
 }
 
+hipError_t launch_align_scan(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
+                             int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
+                             int32_t* n_tiles, int32_t* scratch, hipStream_t st) {
+  const int n = T * k;
+  const int nc = align_num_chunks(T, k);
+  hipLaunchKernelGGL(align_scan_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, BIG, SMALL, small_base,
+                     scratch, counts, pad_off, n_tiles, sorted, inv, tiles);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -1173,6 +1173,9 @@ hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st) {
 }
 
 // Tile configuration per tile height: (rows, K step, workgroups per CU).
+#ifndef MOE_COMBINE_CFG
+#define MOE_COMBINE_CFG 128, 32, 2
+#endif
 #ifndef MOE_GEMM_CFG_128
 #define MOE_GEMM_CFG_128 128, 32, 2
 #endif
@@ -1311,13 +1314,13 @@ hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s
   p.o = o;
   p.w = w;
   p.s = s;
-  constexpr int BM = 128;
+  constexpr int BM = router_rows(MOE_COMBINE_CFG);
   const int64_t max_items = (int64_t)((T + BM - 1) / BM) * (H / 256);
   if (q) {
     p.ssc0 = q->s_down;
-    return launch_mode<MOE_GEMM_CFG_128, SHARED_COMBINE, true>(p, max_items, st);
+    return launch_mode<MOE_COMBINE_CFG, SHARED_COMBINE, true>(p, max_items, st);
   }
-  return launch_mode<MOE_GEMM_CFG_128, SHARED_COMBINE>(p, max_items, st);
+  return launch_mode<MOE_COMBINE_CFG, SHARED_COMBINE>(p, max_items, st);
 }
 
 }  // namespace moe

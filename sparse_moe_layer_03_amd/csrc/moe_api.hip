@@ -266,7 +266,8 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* router_b
   if ((rc = check_arch())) return rc;
   const hipStream_t st = (hipStream_t)stream;
   if (scratch)
-    return hip_status(launch_router_stream(x, w_router, router_bias, w_sg, T, H, E, k, scratch, logits, s, ids, w, st),
+    return hip_status(launch_router_stream(x, w_router, router_bias, w_sg, T, H, E, k, scratch, logits, s, ids, w,
+                                           nullptr, 0, st),
                       "moe_route: streamed router with top-k");
   return hip_status(launch_router(x, w_router, router_bias, w_sg, T, H, E, k, logits, s, ids, w, st),
                     "moe_route: router GEMM with top-k");
@@ -348,11 +349,12 @@ int forward_tiled(const uint16_t* x, const uint16_t* w_router, const float* rout
 
   // router over K slices; the partial logits live in o's bytes until the
   // selection has read them
+  // the router also counts align's chunk histograms into the align scratch
   hipError_t e = launch_router_stream(x, w_router, router_bias, I_s > 0 ? w_sg : nullptr, T, H, E, k, o, nullptr,
-                                      I_s > 0 ? s : nullptr, ids, w, st);
+                                      I_s > 0 ? s : nullptr, ids, w, scratch, align_num_chunks(T, k), st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: router with top-k");
-  e = launch_align(ids, T, E, k, L.BIG, L.SMALL, (int)L.max_big, counts, pad_off, sorted, inv, tiles, n_tiles, scratch,
-                   st);
+  e = launch_align_scan(ids, T, E, k, L.BIG, L.SMALL, (int)L.max_big, counts, pad_off, sorted, inv, tiles, n_tiles,
+                        scratch, st);
   if (e != hipSuccess) return hip_status(e, "moe_forward: align");
   e = launch_routed_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, h, ws_gate, ws_up, I_s, h_s, L, st, q);
   if (e != hipSuccess) return hip_status(e, "moe_forward: gate_up (routed + shared)");

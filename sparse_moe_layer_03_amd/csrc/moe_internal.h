@@ -190,17 +190,24 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const floa
 // LDS and W_router streamed into registers from a copy in fragment order
 // (written to wpack, router_pack_bytes(H, E) bytes, 16-byte aligned, by a
 // first launch), the selection and the shared gate in the same launch; the
-// other arguments as launch_router.
+// other arguments as launch_router.  chunk_hist (NULL: not counted): align's
+// per-chunk expert counts [E][nc] (nc = align_num_chunks(T, k)), zeroed by the
+// first launch and counted by the router, for launch_align_scan.
 size_t router_pack_bytes(int H, int E);
 hipError_t launch_router_stream(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
                                 int T, int H, int E, int k, void* wpack, float* logits, float* s, int32_t* ids,
-                                float* w, hipStream_t st);
+                                float* w, int32_t* chunk_hist, int nc, hipStream_t st);
 // Top-k ids and renormalised weights from fp32 logits [T, E].
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t st);
 hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
                         int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
                         int32_t* n_tiles, int32_t* scratch, hipStream_t st);
 int align_num_chunks(int T, int k);
+// The second launch of launch_align alone, on chunk histograms already in
+// scratch (counted by launch_router_stream).
+hipError_t launch_align_scan(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
+                             int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
+                             int32_t* n_tiles, int32_t* scratch, hipStream_t st);
 int align_scratch_ints(int T, int E, int k);
 // Routed gate/up tiles of one tile list; with I_s > 0 the shared expert's
 // gate/up over all T tokens (tiles of BM tokens) joins the same launch.

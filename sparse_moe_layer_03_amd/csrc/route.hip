@@ -52,6 +52,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // units sit in rows of 128 bytes per 64 columns (chunk), swizzled by the row,
 // so 16 consecutive rows read at one unit hit 16 distinct bank groups.
 constexpr int RS_BM = 32, RS_NT = 512, RS_KSEG = 2048;
+constexpr int RS_CH = 1024;  // align's assignments per chunk
 constexpr int RS_LD = 256 + 8;  // fp32 row stride of the logits tile
 
 struct RouterStreamArgs {
@@ -64,6 +65,8 @@ struct RouterStreamArgs {
   float* s;
   int32_t* ids;
   float* w;
+  int32_t* chunk_hist;  // align's per-chunk expert counts [E][nc] (NULL: not counted), zeroed by the copy launch
+  int nc;
 };
 
 __device__ __forceinline__ int rs_swz(int row, int u) { return u ^ (((row >> 1) ^ ((row & 1) << 2)) & 7); }
@@ -83,11 +86,15 @@ __device__ __forceinline__ void rs_wait_vm() {
 
 // W_router [E, H] -> fragment order [NG][H / 16][64 lanes] of 16 bytes: lane l
 // of group g and sub-step n holds row min(32 g + (l & 31), E - 1), columns
-// 16 n + 8 (l >> 5) .. + 7 -- its operand of v_mfma_f32_32x32x16_bf16.
+// 16 n + 8 (l >> 5) .. + 7 -- its operand of v_mfma_f32_32x32x16_bf16.  The
+// same launch zeroes the nzero ints of zero (align's chunk histograms, which
+// the router adds its counts to).
 __global__ __launch_bounds__(256) void router_pack_kernel(const uint16_t* __restrict__ w, int H, int E, int NG,
-                                                          uint16_t* __restrict__ wp) {
+                                                          uint16_t* __restrict__ wp, int32_t* __restrict__ zero,
+                                                          int64_t nzero) {
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int NS = H / 16;
+  if (u < nzero) zero[u] = 0;
   if (u >= (int64_t)NG * NS * 64) return;
   const int l = (int)(u & 63), n = (int)((u >> 6) % NS), g = (int)((u >> 6) / NS);
   const int e = min(32 * g + (l & 31), E - 1);
@@ -257,6 +264,11 @@ __global__ __launch_bounds__(RS_NT, 1) void router_stream_kernel(RouterStreamArg
   }
   // column 0 of each wave's gate block: lanes 0 and 32
   float* gsum = part + (KS - 1) * NG * 1024;  // [8 waves][32 tokens]
+  // the tile's assignments fall in at most two of align's chunks (32 k <= 512
+  // < RS_CH): their expert counts
+  int* thist = reinterpret_cast<int*>(gsum + 8 * RS_BM);  // [2][E]
+  if (a.chunk_hist)
+    for (int i = tid; i < 2 * a.E; i += RS_NT) thist[i] = 0;
   if (a.w_sg && (lane & 31) == 0)
 #pragma unroll
     for (int q = 0; q < 16; ++q) gsum[wave * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)] = gacc[q];
@@ -292,6 +304,19 @@ __global__ __launch_bounds__(RS_NT, 1) void router_stream_kernel(RouterStreamArg
     a.ids[(size_t)(row0 + tr) * a.k + sub] = sel_e;
     a.w[(size_t)(row0 + tr) * a.k + sub] = wt;
   }
+  if (a.chunk_hist) {
+    // integer counts: the same whatever the order of the additions
+    const int c0 = (int)((int64_t)row0 * a.k / RS_CH);
+    if (tr < nrow && sub < a.k) {
+      const int c = (int)(((int64_t)(row0 + tr) * a.k + sub) / RS_CH);
+      atomicAdd(&thist[(c - c0) * a.E + sel_e], 1);
+    }
+    __syncthreads();
+    for (int i = tid; i < 2 * a.E; i += RS_NT) {
+      const int v = thist[i];
+      if (v) atomicAdd(&a.chunk_hist[(size_t)(i % a.E) * a.nc + c0 + i / a.E], v);
+    }
+  }
 }
 
 }  // namespace
@@ -300,17 +325,20 @@ size_t router_pack_bytes(int H, int E) { return (size_t)((E + 31) / 32) * H * 64
 
 hipError_t launch_router_stream(const uint16_t* x, const uint16_t* w_router, const float* bias, const uint16_t* w_sg,
                                 int T, int H, int E, int k, void* wpack, float* logits, float* s, int32_t* ids,
-                                float* w, hipStream_t st) {
+                                float* w, int32_t* chunk_hist, int nc, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  RouterStreamArgs a = {x, static_cast<const uint16_t*>(wpack), bias, w_sg, T, H, E, k, 0, 0, logits, s, ids, w};
+  RouterStreamArgs a = {x, static_cast<const uint16_t*>(wpack), bias, w_sg, T, H, E, k, 0, 0, logits, s, ids, w,
+                        chunk_hist, nc};
   a.NG = (E + 31) / 32;
   a.KS = a.NG >= 5 ? 1 : a.NG >= 3 ? 2 : 4;
   const int64_t units = (int64_t)a.NG * (H / 16) * 64;
-  hipLaunchKernelGGL(router_pack_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, w_router, H, E,
-                     a.NG, static_cast<uint16_t*>(wpack));
+  const int64_t nzero = chunk_hist ? (int64_t)nc * E : 0;
+  const int64_t nthr = units > nzero ? units : nzero;
+  hipLaunchKernelGGL(router_pack_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st, w_router, H, E,
+                     a.NG, static_cast<uint16_t*>(wpack), chunk_hist, nzero);
   const size_t kseg = (size_t)(H < RS_KSEG ? H : RS_KSEG);
   const size_t tile = (size_t)RS_BM * RS_KSEG * 2 + (w_sg ? (kseg * 2 + 1023) / 1024 * 1024 : 0);
-  const size_t epi = (size_t)RS_BM * RS_LD * 4 + (size_t)(a.KS - 1) * a.NG * 4096 + 8 * RS_BM * 4;
+  const size_t epi = (size_t)RS_BM * RS_LD * 4 + (size_t)(a.KS - 1) * a.NG * 4096 + 8 * RS_BM * 4 + 2 * E * 4;
   const size_t lds = tile > epi ? tile : epi;
   // sub-steps per block: the largest of 32, 16, 8, 4 that divides the
   // sub-step count of every segment (full segments of RS_KSEG columns, then
