@@ -35,18 +35,18 @@
 namespace moe {
 namespace {
 
-constexpr int CH = 1024;  // assignments per chunk
+constexpr int CHMAX = 1024;  // most assignments per chunk (align_chunk)
 
 // chunk_hist[e * nc + c]: assignments of chunk c routed to expert e (expert-major,
 // so the scan reads one expert's chunk counts contiguously)
 __global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int n, int E, int nc,
-                                                         int32_t* __restrict__ chunk_hist) {
+                                                         int ch, int32_t* __restrict__ chunk_hist) {
   __shared__ int32_t hist[kMaxE];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) hist[e] = 0;
   __syncthreads();
-  const int a0 = blockIdx.x * CH;
-  const int a1 = min(a0 + CH, n);
+  const int a0 = blockIdx.x * ch;
+  const int a1 = min(a0 + ch, n);
   for (int a = a0 + tid; a < a1; a += 256) atomicAdd(&hist[ids[a]], 1);
   __syncthreads();
   for (int e = tid; e < E; e += 256) chunk_hist[(size_t)e * nc + blockIdx.x] = hist[e];
@@ -76,7 +76,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sbuf, int& total
 // assignments are ranked in order and scattered, and the tile-table entries
 // and padding rows of the experts e = c, c + gridDim.x, ... are written.
 __global__ __launch_bounds__(256) void align_scan_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
-                                                                 int nc, int BIG, int SMALL, int small_base,
+                                                                 int nc, int ch, int BIG, int SMALL, int small_base,
                                                                  const int32_t* __restrict__ chunk_hist,
                                                                  int32_t* __restrict__ counts,
                                                                  int32_t* __restrict__ pad_off,
@@ -92,11 +92,11 @@ __global__ __launch_bounds__(256) void align_scan_scatter_kernel(const int32_t* 
   // the chunk's expert ids, loaded before the histograms so that the ranking
   // below waits for no load (clamped, not skipped: a load under a per-lane
   // condition is waited for on its own)
-  const int a0 = c * CH;
-  const int a1 = min(a0 + CH, n);
-  int ea_pre[CH / 256];
+  const int a0 = c * ch;
+  const int a1 = min(a0 + ch, n);
+  int ea_pre[CHMAX / 256];
 #pragma unroll
-  for (int it = 0; it < CH / 256; ++it) {
+  for (int it = 0; it < CHMAX / 256; ++it) {
     const int a = a0 + it * 256 + tid;
     const int v = ids[min(a, n - 1)];
     ea_pre[it] = a < a1 ? v : 0;
@@ -149,9 +149,9 @@ __global__ __launch_bounds__(256) void align_scan_scatter_kernel(const int32_t* 
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-  for (int it = 0; it < CH / 256; ++it) {
+  for (int it = 0; it < CHMAX / 256; ++it) {
     const int s0 = a0 + it * 256;
-    if (s0 >= a1) break;  // uniform
+    if (s0 >= a1) break;  // uniform (also past a chunk of fewer than CHMAX)
     for (int i = tid; i < 4 * kMaxE; i += 256) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     const int a = s0 + tid;
@@ -198,21 +198,29 @@ __global__ __launch_bounds__(256) void align_scan_scatter_kernel(const int32_t* 
 
 }  // namespace
 
-// Chunks of CH assignments, rounded up to a multiple of 4 (the scan reads 4
-// chunk counts per 16-byte load; chunks past the end are empty).
+// Chunks of align_chunk assignments, rounded up to a multiple of 4 (the scan
+// reads 4 chunk counts per 16-byte load; chunks past the end are empty).
 int align_scratch_ints(int T, int E, int k) { return align_num_chunks(T, k) * E + 64; }
 
-int align_num_chunks(int T, int k) { return (int)((((int64_t)T * k + CH - 1) / CH + 3) / 4 * 4); }
+int align_chunk(int T, int k) {
+  const int64_t n = (int64_t)T * k;
+  return n >= 65536 ? 1024 : n >= 16384 ? 512 : 256;
+}
+
+int align_num_chunks(int T, int k) {
+  const int64_t ch = align_chunk(T, k);
+  return (int)((((int64_t)T * k + ch - 1) / ch + 3) / 4 * 4);
+}
 
 hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
                         int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
                         int32_t* n_tiles, int32_t* scratch, hipStream_t st) {
   const int n = T * k;
-  const int nc = align_num_chunks(T, k);
+  const int nc = align_num_chunks(T, k), ch = align_chunk(T, k);
   int32_t* chunk_hist = scratch;
-  hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, chunk_hist);
-  hipLaunchKernelGGL(align_scan_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, BIG, SMALL, small_base,
-                     chunk_hist, counts, pad_off, n_tiles, sorted, inv, tiles);
+  hipLaunchKernelGGL(align_hist_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, ch, chunk_hist);
+  hipLaunchKernelGGL(align_scan_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, ch, BIG, SMALL,
+                     small_base, chunk_hist, counts, pad_off, n_tiles, sorted, inv, tiles);
   return hipGetLastError();
 }
 
@@ -220,9 +228,9 @@ hipError_t launch_align_scan(const int32_t* ids, int T, int E, int k, int BIG, i
                              int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
                              int32_t* n_tiles, int32_t* scratch, hipStream_t st) {
   const int n = T * k;
-  const int nc = align_num_chunks(T, k);
-  hipLaunchKernelGGL(align_scan_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, BIG, SMALL, small_base,
-                     scratch, counts, pad_off, n_tiles, sorted, inv, tiles);
+  const int nc = align_num_chunks(T, k), ch = align_chunk(T, k);
+  hipLaunchKernelGGL(align_scan_scatter_kernel, dim3(nc), dim3(256), 0, st, ids, n, E, nc, ch, BIG, SMALL,
+                     small_base, scratch, counts, pad_off, n_tiles, sorted, inv, tiles);
   return hipGetLastError();
 }
 

@@ -202,6 +202,10 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 hipError_t launch_align(const int32_t* ids, int T, int E, int k, int BIG, int SMALL, int small_base,
                         int32_t* counts, int32_t* pad_off, int32_t* sorted, int32_t* inv, int32_t* tiles,
                         int32_t* n_tiles, int32_t* scratch, hipStream_t st);
+// Assignments per align chunk (256, 512 or 1024: more and smaller chunks at
+// fewer assignments, so that align runs on more workgroups): the histogram and
+// scatter unit of align, and of the router's counts.
+int align_chunk(int T, int k);
 int align_num_chunks(int T, int k);
 // The second launch of launch_align alone, on chunk histograms already in
 // scratch (counted by launch_router_stream).

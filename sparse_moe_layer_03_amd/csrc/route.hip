@@ -52,7 +52,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 // units sit in rows of 128 bytes per 64 columns (chunk), swizzled by the row,
 // so 16 consecutive rows read at one unit hit 16 distinct bank groups.
 constexpr int RS_BM = 32, RS_NT = 512, RS_KSEG = 2048;
-constexpr int RS_CH = 1024;  // align's assignments per chunk
 constexpr int RS_LD = 256 + 8;  // fp32 row stride of the logits tile
 
 struct RouterStreamArgs {
@@ -66,7 +65,7 @@ struct RouterStreamArgs {
   int32_t* ids;
   float* w;
   int32_t* chunk_hist;  // align's per-chunk expert counts [E][nc] (NULL: not counted), zeroed by the copy launch
-  int nc;
+  int nc, ch;           // align's chunk count and assignments per chunk (>= 256)
 };
 
 __device__ __forceinline__ int rs_swz(int row, int u) { return u ^ (((row >> 1) ^ ((row & 1) << 2)) & 7); }
@@ -264,11 +263,11 @@ __global__ __launch_bounds__(RS_NT, 1) void router_stream_kernel(RouterStreamArg
   }
   // column 0 of each wave's gate block: lanes 0 and 32
   float* gsum = part + (KS - 1) * NG * 1024;  // [8 waves][32 tokens]
-  // the tile's assignments fall in at most two of align's chunks (32 k <= 512
-  // < RS_CH): their expert counts
-  int* thist = reinterpret_cast<int*>(gsum + 8 * RS_BM);  // [2][E]
+  // the tile's assignments (32 k <= 512) fall in at most three of align's
+  // chunks (>= 256 assignments each): their expert counts
+  int* thist = reinterpret_cast<int*>(gsum + 8 * RS_BM);  // [3][E]
   if (a.chunk_hist)
-    for (int i = tid; i < 2 * a.E; i += RS_NT) thist[i] = 0;
+    for (int i = tid; i < 3 * a.E; i += RS_NT) thist[i] = 0;
   if (a.w_sg && (lane & 31) == 0)
 #pragma unroll
     for (int q = 0; q < 16; ++q) gsum[wave * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)] = gacc[q];
@@ -306,13 +305,13 @@ __global__ __launch_bounds__(RS_NT, 1) void router_stream_kernel(RouterStreamArg
   }
   if (a.chunk_hist) {
     // integer counts: the same whatever the order of the additions
-    const int c0 = (int)((int64_t)row0 * a.k / RS_CH);
+    const int c0 = (int)((int64_t)row0 * a.k / a.ch);
     if (tr < nrow && sub < a.k) {
-      const int c = (int)(((int64_t)(row0 + tr) * a.k + sub) / RS_CH);
+      const int c = (int)(((int64_t)(row0 + tr) * a.k + sub) / a.ch);
       atomicAdd(&thist[(c - c0) * a.E + sel_e], 1);
     }
     __syncthreads();
-    for (int i = tid; i < 2 * a.E; i += RS_NT) {
+    for (int i = tid; i < 3 * a.E; i += RS_NT) {
       const int v = thist[i];
       if (v) atomicAdd(&a.chunk_hist[(size_t)(i % a.E) * a.nc + c0 + i / a.E], v);
     }
@@ -328,7 +327,7 @@ hipError_t launch_router_stream(const uint16_t* x, const uint16_t* w_router, con
                                 float* w, int32_t* chunk_hist, int nc, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   RouterStreamArgs a = {x, static_cast<const uint16_t*>(wpack), bias, w_sg, T, H, E, k, 0, 0, logits, s, ids, w,
-                        chunk_hist, nc};
+                        chunk_hist, nc, align_chunk(T, k)};
   a.NG = (E + 31) / 32;
   a.KS = a.NG >= 5 ? 1 : a.NG >= 3 ? 2 : 4;
   const int64_t units = (int64_t)a.NG * (H / 16) * 64;
@@ -338,7 +337,7 @@ hipError_t launch_router_stream(const uint16_t* x, const uint16_t* w_router, con
                      a.NG, static_cast<uint16_t*>(wpack), chunk_hist, nzero);
   const size_t kseg = (size_t)(H < RS_KSEG ? H : RS_KSEG);
   const size_t tile = (size_t)RS_BM * RS_KSEG * 2 + (w_sg ? (kseg * 2 + 1023) / 1024 * 1024 : 0);
-  const size_t epi = (size_t)RS_BM * RS_LD * 4 + (size_t)(a.KS - 1) * a.NG * 4096 + 8 * RS_BM * 4 + 2 * E * 4;
+  const size_t epi = (size_t)RS_BM * RS_LD * 4 + (size_t)(a.KS - 1) * a.NG * 4096 + 8 * RS_BM * 4 + 3 * E * 4;
   const size_t lds = tile > epi ? tile : epi;
   // sub-steps per block: the largest of 32, 16, 8, 4 that divides the
   // sub-step count of every segment (full segments of RS_KSEG columns, then
