@@ -1180,10 +1180,10 @@ hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st) {
 #define MOE_GEMM_CFG_128 128, 32, 2
 #endif
 #ifndef MOE_GEMM_CFG_64
-#define MOE_GEMM_CFG_64 64, 32, 2
+#define MOE_GEMM_CFG_64 64, 64, 2
 #endif
 #ifndef MOE_GEMM_CFG_32
-#define MOE_GEMM_CFG_32 32, 32, 2
+#define MOE_GEMM_CFG_32 32, 64, 2
 #endif
 // Router launch: (token-tile rows, K step, workgroups per CU).
 #ifndef MOE_ROUTER_CFG
