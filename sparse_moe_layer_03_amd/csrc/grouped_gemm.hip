@@ -1176,6 +1176,20 @@ hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st) {
 #ifndef MOE_COMBINE_CFG
 #define MOE_COMBINE_CFG 128, 32, 2
 #endif
+// Combine launch below MOE_COMBINE_SMALL_T (MOE_COMBINE_MID_T) tokens: smaller
+// token tiles, so that the gather of the o rows runs on more workgroups.
+#ifndef MOE_COMBINE_CFG_SMALL
+#define MOE_COMBINE_CFG_SMALL 32, 64, 2
+#endif
+#ifndef MOE_COMBINE_SMALL_T
+#define MOE_COMBINE_SMALL_T 4096
+#endif
+#ifndef MOE_COMBINE_CFG_MID
+#define MOE_COMBINE_CFG_MID 64, 64, 2
+#endif
+#ifndef MOE_COMBINE_MID_T
+#define MOE_COMBINE_MID_T 8192
+#endif
 #ifndef MOE_GEMM_CFG_128
 #define MOE_GEMM_CFG_128 128, 32, 2
 #endif
@@ -1314,12 +1328,22 @@ hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s
   p.o = o;
   p.w = w;
   p.s = s;
+  if (q) p.ssc0 = q->s_down;
+  if (T < MOE_COMBINE_SMALL_T) {
+    constexpr int BM = router_rows(MOE_COMBINE_CFG_SMALL);
+    const int64_t max_items = (int64_t)((T + BM - 1) / BM) * (H / 256);
+    if (q) return launch_mode<MOE_COMBINE_CFG_SMALL, SHARED_COMBINE, true>(p, max_items, st);
+    return launch_mode<MOE_COMBINE_CFG_SMALL, SHARED_COMBINE>(p, max_items, st);
+  }
+  if (T < MOE_COMBINE_MID_T) {
+    constexpr int BM = router_rows(MOE_COMBINE_CFG_MID);
+    const int64_t max_items = (int64_t)((T + BM - 1) / BM) * (H / 256);
+    if (q) return launch_mode<MOE_COMBINE_CFG_MID, SHARED_COMBINE, true>(p, max_items, st);
+    return launch_mode<MOE_COMBINE_CFG_MID, SHARED_COMBINE>(p, max_items, st);
+  }
   constexpr int BM = router_rows(MOE_COMBINE_CFG);
   const int64_t max_items = (int64_t)((T + BM - 1) / BM) * (H / 256);
-  if (q) {
-    p.ssc0 = q->s_down;
-    return launch_mode<MOE_COMBINE_CFG, SHARED_COMBINE, true>(p, max_items, st);
-  }
+  if (q) return launch_mode<MOE_COMBINE_CFG, SHARED_COMBINE, true>(p, max_items, st);
   return launch_mode<MOE_COMBINE_CFG, SHARED_COMBINE>(p, max_items, st);
 }
 

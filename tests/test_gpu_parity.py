@@ -157,6 +157,8 @@ LAYER_CASES = [
     ("full-T300", dict(wl="prefill1k", T=300)),
     ("full-T2", dict(wl="prefill1k", T=2)),
     ("full-bias-T257", dict(wl="prefill8k", T=257)),
+    # 64-row combine tiles (4096 <= T < 8192), 128-row routed tiles
+    ("full-T5000", dict(wl="prefill1k", T=5000)),
 ]
 
 
