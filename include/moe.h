@@ -159,7 +159,7 @@ int moe_forward(const uint16_t* x, const uint16_t* w_router, const float* router
  * each GPU's memory, allocated with the library's code and held until the process ends.  The call
  * allocates and frees nothing.
  *   - Sizes whose moe_workspace_size exceeds MOE_NOALLOC_WS_BYTES give MOE_ERR_WORKSPACE before
- *     anything is enqueued (at hidden 2048, 256 experts, top-8, FFN 512, shared 512: up to 1,399
+ *     anything is enqueued (at hidden 2048, 256 experts, top-8, FFN 512, shared 512: up to 1,198
  *     tokens per call).
  *   - Every call on a GPU uses that GPU's one array and leaves its contents there (no part of it has
  *     to start at zero).  Calls that overlap on one GPU (other streams, other host threads) race:

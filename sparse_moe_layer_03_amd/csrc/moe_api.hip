@@ -188,7 +188,9 @@ int moe_align_tile_rows(int T, int E, int k) {
   const int64_t avg = (int64_t)T * k / E;  // mean rows per expert
   if (avg >= MOE_TILE256_MIN_MEAN) return 256;
   if (avg >= 128) return 128;
-  if (avg >= 48) return 64;
+  // 64 from a mean of 32: with 32-row tiles, experts just above the mean take
+  // two tiles and their weights cross HBM twice
+  if (avg >= 32) return 64;
   return 32;
 }
 

@@ -39,13 +39,14 @@ def test_status_strings(L):
 
 
 def test_tile_rows_policy():
-    # mean rows per expert T*k/E: >= 192 -> 256, >= 128 -> 128, >= 48 -> 64, else 32
+    # mean rows per expert T*k/E: >= 192 -> 256, >= 128 -> 128, >= 32 -> 64, else 32
     assert moe.moe_align_tile_rows(8192, 256, 8) == 256
     assert moe.moe_align_tile_rows(32768, 256, 8) == 256
     assert moe.moe_align_tile_rows(6144, 256, 8) == 256
     assert moe.moe_align_tile_rows(6143, 256, 8) == 128
     assert moe.moe_align_tile_rows(4096, 256, 8) == 128
-    assert moe.moe_align_tile_rows(1024, 256, 8) == 32
+    assert moe.moe_align_tile_rows(1024, 256, 8) == 64
+    assert moe.moe_align_tile_rows(1023, 256, 8) == 32
     assert moe.moe_align_tile_rows(2048, 256, 8) == 64
     for T, E, k in ((8192, 256, 8), (4096, 256, 8), (2048, 256, 8), (1024, 256, 8), (16, 8, 2), (5, 3, 3)):
         assert moe.moe_align_small_tile_rows(T, E, k) == moe.moe_align_tile_rows(T, E, k)
