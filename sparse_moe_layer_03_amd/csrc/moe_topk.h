@@ -166,7 +166,12 @@ __device__ __forceinline__ uint64_t topk_key64(float v, int e, bool valid) {
 // expert in sel_e and logit in sel_v, and returns rank r's weight (0 in the
 // other sub-lanes); the weights are those of wave_topk_weights_n:
 //   w_r = exp(l_r - l_0) / sum_{r' < k} exp(l_r' - l_0), the sum in rank order.
+// KMAX: an upper bound of k (8 or 16).  A lane gives at most k winners, so
+// only the first KMAX of its sorted keys are ever its head: the pops shift
+// those alone.
+template <int KMAX = 16>
 __device__ __forceinline__ float row16_topk_weights(uint64_t (&key)[16], int k, int sub, int& sel_e, float& sel_v) {
+  static_assert(KMAX == 8 || KMAX == 16, "KMAX");
   sort_desc_u64<16>(key);
   sel_e = -1;
   sel_v = 0.0f;
@@ -175,8 +180,8 @@ __device__ __forceinline__ float row16_topk_weights(uint64_t (&key)[16], int k, 
     const uint64_t M = row16_max_u64(key[0]);
     const bool win = key[0] == M;  // keys are unique: one lane of the row
 #pragma unroll
-    for (int i = 0; i < 15; ++i) key[i] = win ? key[i + 1] : key[i];
-    key[15] = win ? 0ull : key[15];
+    for (int i = 0; i < KMAX - 1; ++i) key[i] = win ? key[i + 1] : key[i];
+    key[KMAX - 1] = win ? 0ull : key[KMAX - 1];
     const float val = float_from_order_key((uint32_t)(M >> 8));
     if (sub == r) {
       sel_e = 255 - (int)(M & 255u);

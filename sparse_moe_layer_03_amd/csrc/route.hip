@@ -298,7 +298,8 @@ __global__ __launch_bounds__(RS_NT, 1) void router_stream_kernel(RouterStreamArg
   }
   int sel_e;
   float sel_v;
-  const float wt = row16_topk_weights(key, a.k, sub, sel_e, sel_v);
+  const float wt = a.k <= 8 ? row16_topk_weights<8>(key, a.k, sub, sel_e, sel_v)
+                            : row16_topk_weights<16>(key, a.k, sub, sel_e, sel_v);
   if (tr < nrow && sub < a.k) {
     a.ids[(size_t)(row0 + tr) * a.k + sub] = sel_e;
     a.w[(size_t)(row0 + tr) * a.k + sub] = wt;
