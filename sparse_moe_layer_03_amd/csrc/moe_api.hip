@@ -61,9 +61,15 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-// Mean rows per expert from which 256-row tiles are used.
+// Mean rows per expert from which 256-row tiles (the persistent kernel) are
+// used.  Measured on the decode-config layer without router bias, forward
+// per tile height 64 / 128 / 256 rows: 2,304 tokens (mean 72) 470 / 460 /
+// 460 us, 2,560 tokens 497 / 480 / 467 us, 3,584 tokens 549 / 517 / 496 us,
+// 4,096 tokens 589 / 574 / 521 us, 6,144 tokens 781 / 709 / 602 us; below
+// a mean of 72, 64-row tiles were fastest (2,048 tokens 446 against 452 us
+// with 128 rows, 1,024 tokens 383 against 425 us).
 #ifndef MOE_TILE256_MIN_MEAN
-#define MOE_TILE256_MIN_MEAN 192
+#define MOE_TILE256_MIN_MEAN 72
 #endif
 
 int env_rows(const char* name) {
@@ -187,7 +193,6 @@ int moe_align_tile_rows(int T, int E, int k) {
   if (E < 1) return 32;
   const int64_t avg = (int64_t)T * k / E;  // mean rows per expert
   if (avg >= MOE_TILE256_MIN_MEAN) return 256;
-  if (avg >= 128) return 128;
   // 64 from a mean of 32: with 32-row tiles, experts just above the mean take
   // two tiles and their weights cross HBM twice
   if (avg >= 32) return 64;
