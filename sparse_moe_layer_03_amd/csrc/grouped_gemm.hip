@@ -721,7 +721,10 @@ __global__ __launch_bounds__(Cfg<BM>::NT, OCC) void grouped_gemm_kernel(GemmPara
 //     every row load is one whole 128-byte line;
 //   * two 64 KB stages: the loads of step k + 1 are in flight while step k
 //     is computed, and the last step of an item overlaps the first loads of
-//     the next item, which also run under the epilogue;
+//     the next item, which also run under the epilogue; or (R3, BF16 weights:
+//     every down launch, and gate/up launches below a mean of 192 rows per
+//     expert) two A stages and three B stages, the weight rows loaded two
+//     steps ahead (160 KB of LDS);
 //   * the MFMAs produce transposed output blocks, so every lane holds runs
 //     of 4 consecutive output columns of one row: the gate/up epilogue
 //     stores them as 8-byte writes straight from the accumulators (no LDS
@@ -767,6 +770,21 @@ struct DmaGeom {
   static constexpr size_t SCALES = Q ? 2 * BNB * 4 : 0;    // LDS bytes of two items' B-row scales
   static constexpr size_t LDS = 2 * (size_t)STAGE * 16 + SCALES;  // 128 KB (bf16), 98 KB (FP8)
   static_assert((size_t)DNT / 64 * (Q ? 4096 : 8192) <= (size_t)STAGE * 16, "down epilogue staging fits in one stage");
+};
+
+// LDS layout of the persistent kernel, in 16-byte chunks: two stages of A
+// and B ([A0 B0][A1 B1]; the down epilogue stages its outputs in one whole
+// stage), or (R3) two A stages and three B stages ([A0 A1][B0 B1 B2]), the
+// weight rows then loaded two K steps ahead.
+template <bool Q, bool R3>
+struct DmaLay {
+  using G = DmaGeom<Q>;
+  static constexpr int ASZ = DBM * DKCH, BSZ = BNB * G::BKCH;
+  static constexpr int TOTAL = R3 ? 2 * ASZ + 3 * BSZ : 2 * (ASZ + BSZ);
+  static constexpr size_t LDS = (size_t)TOTAL * 16 + G::SCALES;  // 160 KB (bf16, R3)
+  __device__ static constexpr int a_off(int s) { return R3 ? s * ASZ : s * (ASZ + BSZ); }
+  __device__ static constexpr int b_off(int s) { return R3 ? 2 * ASZ + s * BSZ : s * (ASZ + BSZ) + ASZ; }
+  static_assert(LDS <= 160 * 1024, "LDS per workgroup");
 };
 
 // One direct-to-LDS load: 16 bytes per lane from src into LDS at
@@ -854,11 +872,12 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
   return d;
 }
 
-template <int MODE, bool Q = false>
+template <int MODE, bool Q = false, bool R3 = false>
 __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   static_assert(MODE == GATE_UP || MODE == DOWN, "routed GEMMs only");
   using C = DCfg;
   using G = DmaGeom<Q>;
+  using L = DmaLay<Q, R3>;  // R3: weight rows two K steps ahead
   constexpr size_t EB = Q ? 1 : 2;  // bytes per weight
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -878,10 +897,10 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
   // A groups that are never loaded must not hold arbitrary bits on the first item
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int i = tid; i < 2 * G::STAGE; i += DNT) sm[i] = zero;
+  for (int i = tid; i < L::TOTAL; i += DNT) sm[i] = zero;
   __syncthreads();
-  const uint32_t lds_scales = lds0 + (uint32_t)(2 * G::STAGE * 16);
-  const float* scales = reinterpret_cast<const float*>(smem + 2 * G::STAGE * 16);  // [2][BNB]
+  const uint32_t lds_scales = lds0 + (uint32_t)(L::TOTAL * 16);
+  const float* scales = reinterpret_cast<const float*>(smem + L::TOTAL * 16);  // [2][BNB]
 
   // byte offset of this lane's B source of load q from the wave's bbase:
   // lane l fills row w*32 + q*BRPI + l/BKCH, LDS slot l%BKCH, which holds
@@ -896,10 +915,12 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   // barrier, group 1 after the MFMAs of two sub-steps.  A wave's load
   // instructions wait in issue while the CU's load path drains the other
   // waves' loads (64 KB per step), and its MFMAs queue behind them; moving
-  // one operand's loads behind some MFMAs overlaps the two.  Gate/up issues
-  // B (the expert rows, mostly L2 misses) first, down issues A first:
-  // measured, gate/up 385.6 -> 369.3 us and down 234.3 -> 225.3 us against
-  // all loads in group 0 (the other orders were slower).
+  // one operand's loads behind some MFMAs overlaps the two.  With two
+  // stages gate/up issues B (the expert rows, mostly L2 misses) first, down
+  // issues A first: measured, gate/up 385.6 -> 369.3 us and down 234.3 ->
+  // 225.3 us against all loads in group 0 (the other orders were slower).
+  // With the R3 ring group 0 is A of the next step and group 1 B of the
+  // step after, so a step waits for all but the latest B group.
   constexpr bool a_first = MODE == DOWN;
   auto issue_a = [&](const DmaItem& d, uint32_t base, int kb) {
 #pragma unroll
@@ -910,18 +931,19 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   auto issue_b = [&](const DmaItem& d, uint32_t base, int kb) {
 #pragma unroll
     for (int q = 0; q < G::BNQ; ++q)
-      dma16(d.bbase + boff[q] + (size_t)kb * DBK * EB,
-            base + (uint32_t)(DBM * DKCH + (wave * DCfg::RPW + q * G::BRPI) * G::BKCH) * 16);
+      dma16(d.bbase + boff[q] + (size_t)kb * DBK * EB, base + (uint32_t)((wave * DCfg::RPW + q * G::BRPI) * G::BKCH) * 16);
+  };
+  auto issue_scales = [&](const DmaItem& d) {
+    if constexpr (Q) {
+      if (wave == 0) dma16(d.ssrc, lds_scales + (uint32_t)d.spar * BNB * 4);
+    }
   };
   auto issue_grp = [&](const DmaItem& d, int st, int kb, int g) {
-    const uint32_t base = lds0 + (uint32_t)st * G::STAGE * 16;
     if ((g == 0) == a_first)
-      issue_a(d, base, kb);
+      issue_a(d, lds0 + (uint32_t)L::a_off(st) * 16, kb);
     else
-      issue_b(d, base, kb);
-    if constexpr (Q) {
-      if (g == 0 && kb == 0 && wave == 0) dma16(d.ssrc, lds_scales + (uint32_t)d.spar * BNB * 4);
-    }
+      issue_b(d, lds0 + (uint32_t)L::b_off(st) * 16, kb);
+    if (g == 0 && kb == 0) issue_scales(d);
   };
   auto issue = [&](const DmaItem& d, int st, int kb) {
     issue_grp(d, st, kb, 0);
@@ -938,9 +960,9 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   struct Frag {
     bf16x8 a[C::MI], b[C::NJ];
   };
-  auto read_frags = [&](Frag& f, int st, int sub) {
-    const u32x4* cA = sm + st * G::STAGE;
-    const u32x4* cB = cA + DBM * DKCH;
+  auto read_frags = [&](Frag& f, int ast, int bst, int sub) {
+    const u32x4* cA = sm + L::a_off(ast);
+    const u32x4* cB = sm + L::b_off(bst);
     const int c = 2 * sub + (lane >> 5);
 #pragma unroll
     for (int m = 0; m < C::MI; ++m) {
@@ -980,7 +1002,17 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   static_assert(SUB == 4, "the K loop below is written out for four sub-steps");
   const int nk = p.K / DBK;  // even: K is a multiple of 128
   DmaItem cur = dma_item<MODE, Q>(p, routed_item_at<DBM, MODE>(p, ri, first), wave, wm, lane, 0);
-  issue(cur, 0, 0);
+  int bs = 0;       // R3: B stage of the current K step (cycles 0, 1, 2 across items)
+  int nb_pend = 0;  // R3: B loads of the latest group, which the next step need not wait for
+  if constexpr (R3) {
+    issue_a(cur, lds0 + (uint32_t)L::a_off(0) * 16, 0);
+    issue_b(cur, lds0 + (uint32_t)L::b_off(0) * 16, 0);
+    issue_scales(cur);
+    issue_b(cur, lds0 + (uint32_t)L::b_off(1) * 16, 1);
+    nb_pend = G::BNQ;
+  } else {
+    issue(cur, 0, 0);
+  }
   for (int item = first; item < last; item += nslot) {
     const int nxt = item + nslot;
     const bool has_next = nxt < last;
@@ -1002,31 +1034,78 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     // one conditional block the compiler spilled the accumulators.)
     Frag f0, f1;
     bool pending = false;
-    for (int kb = 0; kb < nk; ++kb) {
-      const int st = kb & 1;
-      wait_vm0();
-      __syncthreads();
-      // nk is even, so the next item's step 0 goes to stage 0 = st ^ 1 too
-      auto group = [&](int g) {
+    if constexpr (R3) {
+      // Step kb: wait for A(kb) (issued one step earlier) and B(kb) (two
+      // steps earlier); B(kb + 1), the latest group, may still be in flight.
+      // Group 0 loads A(kb + 1), group 1 B(kb + 2) -- of the next item past
+      // the end of this one.  A stages alternate with kb (nk is even), B
+      // stages cycle through three.
+      for (int kb = 0; kb < nk; ++kb) {
+        const int as = kb & 1;
+        if (nb_pend >= 4)
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else if (nb_pend >= 2)
+          asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else
+          wait_vm0();
+        __syncthreads();
         if (kb + 1 < nk)
-          issue_grp(cur, st ^ 1, kb + 1, g);
+          issue_a(cur, lds0 + (uint32_t)L::a_off(as ^ 1) * 16, kb + 1);
         else if (has_next)
-          issue_grp(next, 0, 0, g);
-      };
-      group(0);
-      if (cur.live) {
-        read_frags(f0, st, 0);
-        if (pending) mma(f1);
-        read_frags(f1, st, 1);
-        mma(f0);
+          issue_a(next, lds0 + (uint32_t)L::a_off(0) * 16, 0);
+        if (cur.live) {
+          read_frags(f0, as, bs, 0);
+          if (pending) mma(f1);
+          read_frags(f1, as, bs, 1);
+          mma(f0);
+        }
+        const int bs2 = bs == 0 ? 2 : bs - 1;  // (bs + 2) % 3
+        nb_pend = 0;
+        if (kb + 2 < nk) {
+          issue_b(cur, lds0 + (uint32_t)L::b_off(bs2) * 16, kb + 2);
+          nb_pend = G::BNQ;
+        } else if (has_next) {
+          issue_b(next, lds0 + (uint32_t)L::b_off(bs2) * 16, kb + 2 - nk);
+          if (kb + 2 == nk) issue_scales(next);
+          nb_pend = G::BNQ;
+        }
+        asm volatile("" : "+s"(nb_pend));
+        if (cur.live) {
+          read_frags(f0, as, bs, 2);
+          mma(f1);
+          read_frags(f1, as, bs, 3);
+          mma(f0);
+          pending = true;
+        }
+        bs = bs == 2 ? 0 : bs + 1;
       }
-      group(1);
-      if (cur.live) {
-        read_frags(f0, st, 2);
-        mma(f1);
-        read_frags(f1, st, 3);
-        mma(f0);
-        pending = true;
+    } else {
+      for (int kb = 0; kb < nk; ++kb) {
+        const int st = kb & 1;
+        wait_vm0();
+        __syncthreads();
+        // nk is even, so the next item's step 0 goes to stage 0 = st ^ 1 too
+        auto group = [&](int g) {
+          if (kb + 1 < nk)
+            issue_grp(cur, st ^ 1, kb + 1, g);
+          else if (has_next)
+            issue_grp(next, 0, 0, g);
+        };
+        group(0);
+        if (cur.live) {
+          read_frags(f0, st, st, 0);
+          if (pending) mma(f1);
+          read_frags(f1, st, st, 1);
+          mma(f0);
+        }
+        group(1);
+        if (cur.live) {
+          read_frags(f0, st, st, 2);
+          mma(f1);
+          read_frags(f1, st, st, 3);
+          mma(f0);
+          pending = true;
+        }
       }
     }
     if (pending) mma(f1);
@@ -1077,7 +1156,8 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       // segments; each lane scales its 4 consecutive columns by their weight
       // rows' scales (in LDS since the item's first K step)
       __syncthreads();
-      char* ew = reinterpret_cast<char*>(smem) + (size_t)((nk - 1) & 1) * G::STAGE * 16 + (size_t)wave * 4096;
+      // the last step's A stage (R3: the next item's loads go to the other one and to other B stages)
+      char* ew = reinterpret_cast<char*>(smem) + (size_t)L::a_off((nk - 1) & 1) * 16 + (size_t)wave * 4096;
       const float* S = scales + cur.spar * BNB;
       int arow[4];  // the assignment of this lane's copy-out rows lane / 4 + 16 i (block m = i / 2)
 #pragma unroll
@@ -1114,7 +1194,12 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       // involves the workgroup; a wave's LDS operations complete in order, so
       // the rest needs none.  16-byte slots are XOR-swizzled by the row.
       __syncthreads();
-      char* ew = reinterpret_cast<char*>(smem) + (size_t)((nk - 1) & 1) * G::STAGE * 16 + (size_t)wave * 8192;
+      // the last step's stages: its A stage (waves 0-3) and B stage (waves 4-7), which no load in flight writes
+      const int blast = bs == 0 ? 2 : bs - 1;  // R3: the B stage of step nk - 1
+      char* ew = reinterpret_cast<char*>(smem) +
+                 (R3 ? (wave < 4 ? (size_t)L::a_off(1) * 16 + (size_t)wave * 8192
+                                 : (size_t)L::b_off(blast) * 16 + (size_t)(wave - 4) * 8192)
+                     : (size_t)((nk - 1) & 1) * G::STAGE * 16 + (size_t)wave * 8192);
       // the assignment of this lane's copy-out rows lane / 8 + 8 i (block m = i / 4)
       int arow[8];
 #pragma unroll
@@ -1180,9 +1265,10 @@ hipError_t launch_mode(const GemmParams& p, int64_t max_items, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Persistent launch: one workgroup per CU (at most one per item).
+// Persistent launch: one workgroup per CU (at most one per item).  ring3:
+// the three-stage weight ring (BF16 weights only).
 template <int MODE, bool Q = false>
-hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st) {
+hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st, bool ring3) {
   if (max_items <= 0) return hipSuccess;
   if (p.K % (2 * DBK) != 0) return hipErrorInvalidValue;
   int dev = 0, n_cu = 0;
@@ -1191,12 +1277,19 @@ hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st) {
   if (e != hipSuccess) return e;
   int64_t grid = n_cu < max_items ? n_cu : max_items;
   grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  constexpr size_t lds = DmaGeom<Q>::LDS;
-  e = hipFuncSetAttribute((const void*)grouped_gemm_dma_kernel<MODE, Q>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE, Q>), dim3((unsigned)grid), dim3(DNT), lds, st, p);
-  return hipGetLastError();
+  auto go = [&](auto R3) -> hipError_t {
+    constexpr bool r3 = decltype(R3)::value;
+    constexpr size_t lds = DmaLay<Q, r3>::LDS;
+    hipError_t e2 = hipFuncSetAttribute((const void*)grouped_gemm_dma_kernel<MODE, Q, r3>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e2 != hipSuccess) return e2;
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE, Q, r3>), dim3((unsigned)grid), dim3(DNT), lds, st, p);
+    return hipGetLastError();
+  };
+  if constexpr (!Q) {
+    if (ring3) return go(std::true_type{});
+  }
+  return go(std::false_type{});
 }
 
 // Tile configuration per tile height: (rows, K step, workgroups per CU).
@@ -1239,7 +1332,7 @@ constexpr int router_rows(int bm, int, int) { return bm; }
 constexpr int router_bk(int, int bk, int) { return bk; }
 
 template <int MODE, bool Q = false>
-hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t st) {
+hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t st, bool ring3 = false) {
   switch (BM) {
     case 32: return launch_mode<MOE_GEMM_CFG_32, MODE, Q>(p, max_items, st);
     case 64: return launch_mode<MOE_GEMM_CFG_64, MODE, Q>(p, max_items, st);
@@ -1247,7 +1340,7 @@ hipError_t launch_bm(int BM, const GemmParams& p, int64_t max_items, hipStream_t
       if constexpr (MODE == DOWN) return launch_mode<MOE_DOWN_CFG_128, MODE, Q>(p, max_items, st);
       return launch_mode<MOE_GEMM_CFG_128, MODE, Q>(p, max_items, st);
     case 256:
-      if constexpr (MODE == GATE_UP || MODE == DOWN) return launch_dma<MODE, Q>(p, max_items, st);
+      if constexpr (MODE == GATE_UP || MODE == DOWN) return launch_dma<MODE, Q>(p, max_items, st, ring3);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -1280,7 +1373,7 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const floa
 hipError_t launch_gate_up(const uint16_t* x, const void* w_gate, const void* w_up, const int32_t* sorted,
                           const int32_t* tiles, const int32_t* n_tiles, int T, int H, int k, int I, int BM,
                           int64_t max_tiles, uint16_t* h, const void* ws_gate, const void* ws_up, int I_s,
-                          uint16_t* h_s, hipStream_t st, const FP8Scales* q) {
+                          uint16_t* h_s, hipStream_t st, const FP8Scales* q, bool ring3) {
   GemmParams p = {};
   p.a = x;
   p.lda = H;
@@ -1307,12 +1400,12 @@ hipError_t launch_gate_up(const uint16_t* x, const void* w_gate, const void* w_u
     p.sc0 = q->gate, p.sc1 = q->up, p.ssc0 = q->s_gate, p.ssc1 = q->s_up;
     return launch_bm<GATE_UP, true>(BM, p, max_tiles * (I / 128) + shared_items, st);
   }
-  return launch_bm<GATE_UP>(BM, p, max_tiles * (I / 128) + shared_items, st);
+  return launch_bm<GATE_UP>(BM, p, max_tiles * (I / 128) + shared_items, st, ring3);
 }
 
 hipError_t launch_down(const uint16_t* h, const void* w_down, const int32_t* sorted, const int32_t* tiles,
                        const int32_t* n_tiles, int T, int H, int k, int I, int BM, int64_t max_tiles, uint16_t* o,
-                       hipStream_t st, const FP8Scales* q) {
+                       hipStream_t st, const FP8Scales* q, bool ring3) {
   GemmParams p = {};
   p.a = h;
   p.lda = I;
@@ -1330,7 +1423,7 @@ hipError_t launch_down(const uint16_t* h, const void* w_down, const int32_t* sor
     p.sc0 = q->down;
     return launch_bm<DOWN, true>(BM, p, max_tiles * (H / 256), st);
   }
-  return launch_bm<DOWN>(BM, p, max_tiles * (H / 256), st);
+  return launch_bm<DOWN>(BM, p, max_tiles * (H / 256), st, ring3);
 }
 
 hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s,
