@@ -63,13 +63,12 @@ int hip_status(hipError_t e, const char* what) {
 
 // Mean rows per expert from which 256-row tiles (the persistent kernel) are
 // used.  Measured on the decode-config layer without router bias, forward
-// per tile height 64 / 128 / 256 rows: 2,304 tokens (mean 72) 470 / 460 /
-// 460 us, 2,560 tokens 497 / 480 / 467 us, 3,584 tokens 549 / 517 / 496 us,
-// 4,096 tokens 589 / 574 / 521 us, 6,144 tokens 781 / 709 / 602 us; below
-// a mean of 72, 64-row tiles were fastest (2,048 tokens 446 against 452 us
-// with 128 rows, 1,024 tokens 383 against 425 us).
+// per tile height 64 / 256 rows (BF16 weights): 1,536 tokens (mean 48)
+// 406 / 425 us, 2,048 tokens (mean 64) 451 / 438 us, 2,560 tokens 497 /
+// 467 us, 4,096 tokens 589 / 521 us, 6,144 tokens 781 / 602 us (128-row
+// tiles were between the two from a mean of 64 up).
 #ifndef MOE_TILE256_MIN_MEAN
-#define MOE_TILE256_MIN_MEAN 72
+#define MOE_TILE256_MIN_MEAN 64
 #endif
 
 int env_rows(const char* name) {

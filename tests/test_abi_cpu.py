@@ -39,22 +39,22 @@ def test_status_strings(L):
 
 
 def test_tile_rows_policy():
-    # mean rows per expert T*k/E (integer): >= 72 -> 256, >= 32 -> 64, else 32
+    # mean rows per expert T*k/E (integer): >= 64 -> 256, >= 32 -> 64, else 32
     assert moe.moe_align_tile_rows(8192, 256, 8) == 256
     assert moe.moe_align_tile_rows(32768, 256, 8) == 256
     assert moe.moe_align_tile_rows(6144, 256, 8) == 256
     assert moe.moe_align_tile_rows(4096, 256, 8) == 256
-    assert moe.moe_align_tile_rows(2304, 256, 8) == 256
-    assert moe.moe_align_tile_rows(2303, 256, 8) == 64
+    assert moe.moe_align_tile_rows(2048, 256, 8) == 256
+    assert moe.moe_align_tile_rows(2047, 256, 8) == 64
     assert moe.moe_align_tile_rows(1024, 256, 8) == 64
     assert moe.moe_align_tile_rows(1023, 256, 8) == 32
-    assert moe.moe_align_tile_rows(2048, 256, 8) == 64
     for T, E, k in ((8192, 256, 8), (4096, 256, 8), (2048, 256, 8), (1024, 256, 8), (16, 8, 2), (5, 3, 3)):
         assert moe.moe_align_small_tile_rows(T, E, k) == moe.moe_align_tile_rows(T, E, k)
     # padding is at most BIG - 1 rows per used expert
     assert moe.moe_align_max_rows(8192, 256, 8) == 8192 * 8 + 256 * 255
     assert moe.moe_align_max_rows(4096, 256, 8) == 4096 * 8 + 256 * 255
-    assert moe.moe_align_max_rows(2048, 256, 8) == 2048 * 8 + 256 * 63
+    assert moe.moe_align_max_rows(2048, 256, 8) == 2048 * 8 + 256 * 255
+    assert moe.moe_align_max_rows(2047, 256, 8) == 2047 * 8 + 256 * 63
     assert moe.moe_align_max_rows(2, 256, 8) == 16 + 16 * 31
     assert moe.moe_align_max_big_tiles(8192, 256, 8) == (65536 + 256 * 255) // 256
     assert moe.moe_align_max_tiles(8192, 256, 8) == (65536 + 256 * 255) // 256

@@ -159,10 +159,10 @@ LAYER_CASES = [
     ("full-bias-T257", dict(wl="prefill8k", T=257)),
     # 64-row combine tiles (4096 <= T < 8192), 256-row routed tiles (mean 156 rows per expert)
     ("full-T5000", dict(wl="prefill1k", T=5000)),
-    # the persistent 256-row kernel at the lowest mean that takes it (72 rows per expert: most tiles
-    # hold under a third data rows), and 64-row tiles just below it
-    ("full-T2304", dict(wl="prefill1k", T=2304)),
-    ("full-T2303", dict(wl="prefill1k", T=2303)),
+    # the persistent 256-row kernel at the lowest mean that takes it (64 rows per expert: most tiles
+    # hold about a quarter data rows), and 64-row tiles just below it
+    ("full-T2048", dict(wl="prefill1k", T=2048)),
+    ("full-T2047", dict(wl="prefill1k", T=2047)),
 ]
 
 
