@@ -201,17 +201,17 @@ def test_layer_parity(torch, full_layer, label, case):
         assert torch.equal(b["y"].view(torch.int16), y.view(torch.int16))
         assert np.array_equal(fwd_ids, ids)
     # stages h (padded rows, reached through inv) and o (one row per
-    # assignment t*k + j): vs the oracle's, for tokens with the same selection
+    # assignment t*k + j): every element against the oracle's, for tokens
+    # with the same selection
     same = np.all(ids == r["ids"], axis=1)
     if same.sum() > 0:
         ro = oracle.forward(inp, want=("h", "o"))
         inv = b["inv"].cpu().numpy()
         sel = np.repeat(same, wl.k)
-        for name, got in (("h", G.y_to_f64(b["h"][torch.from_numpy(inv).long().cuda()])), ("o", G.y_to_f64(b["o"]))):
-            d = got[sel] - ro[name][sel]
-            rel = np.linalg.norm(d) / np.linalg.norm(ro[name][sel])
-            G.say(f"[{label}] {name}: rel-L2 {rel:.3e}")
-            assert rel < 1e-2
+        h_got = G.y_to_f64(b["h"][torch.from_numpy(inv).long().cuda()])
+        G.check_stage(h_got[sel], ro["h"][sel], f"{label} h")
+        G.check_stage(G.y_to_f64(b["o"])[sel], ro["o"][sel], f"{label} o",
+                      extra=G.down_rounding_bound(ro["h"][sel], ids[same], inp["w_down"]))
 
 
 # ------------------------------------------------------------ small batches
