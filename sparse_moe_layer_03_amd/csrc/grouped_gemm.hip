@@ -1040,6 +1040,10 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
       // Group 0 loads A(kb + 1), group 1 B(kb + 2) -- of the next item past
       // the end of this one.  A stages alternate with kb (nk is even), B
       // stages cycle through three.
+      // (The partial waits are inline assembly: the compiler's wait-count
+      // pass does not see the direct-to-LDS loads and may turn a builtin
+      // partial wait into a full one.  launch_dma instantiates R3 for BF16
+      // weights, BNQ = 4; the FP8 count, 2, is kept for completeness.)
       for (int kb = 0; kb < nk; ++kb) {
         const int as = kb & 1;
         if (nb_pend >= 4)
@@ -1069,7 +1073,7 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
           if (kb + 2 == nk) issue_scales(next);
           nb_pend = G::BNQ;
         }
-        asm volatile("" : "+s"(nb_pend));
+        asm volatile("" : "+s"(nb_pend));  // opaque: the compiler then does not peel the first step
         if (cur.live) {
           read_frags(f0, as, bs, 2);
           mma(f1);
