@@ -1301,12 +1301,16 @@ hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st, bo
 #define MOE_COMBINE_CFG 128, 32, 2
 #endif
 // Combine launch below MOE_COMBINE_SMALL_T (MOE_COMBINE_MID_T) tokens: smaller
-// token tiles, so that the gather of the o rows runs on more workgroups.
+// token tiles, so that the gather of the o rows runs on more workgroups.  The
+// 32-row tiles stop where they no longer fit one round of two workgroups per
+// CU at H = 2048 (64 token tiles x 8 column blocks): combine at 2,304 /
+// 3,072 / 3,584 tokens 41.0 / 46.0 / 50.0 us with 32-row tiles, 38.0 / 40.4
+// / 43.1 us with 64-row tiles.
 #ifndef MOE_COMBINE_CFG_SMALL
 #define MOE_COMBINE_CFG_SMALL 32, 64, 2
 #endif
 #ifndef MOE_COMBINE_SMALL_T
-#define MOE_COMBINE_SMALL_T 4096
+#define MOE_COMBINE_SMALL_T 2049
 #endif
 #ifndef MOE_COMBINE_CFG_MID
 #define MOE_COMBINE_CFG_MID 64, 64, 2

@@ -157,7 +157,7 @@ LAYER_CASES = [
     ("full-T300", dict(wl="prefill1k", T=300)),
     ("full-T2", dict(wl="prefill1k", T=2)),
     ("full-bias-T257", dict(wl="prefill8k", T=257)),
-    # 64-row combine tiles (4096 <= T < 8192), 256-row routed tiles (mean 156 rows per expert)
+    # 64-row combine tiles (2049 <= T < 8192), 256-row routed tiles (mean 156 rows per expert)
     ("full-T5000", dict(wl="prefill1k", T=5000)),
     # the persistent 256-row kernel at the lowest mean that takes it (64 rows per expert: most tiles
     # hold about a quarter data rows), and 64-row tiles just below it
