@@ -3,7 +3,8 @@
 Largest hidden size (8192) with the widest top-k (16 of 256 experts), a
 single expert (E = k = 1), the smallest FFN (128) without a shared expert,
 and token counts on each path: 1 (single-token kernels), a few (small-batch
-kernels) and above 32 (tiled GEMMs; 4-bit weights stop at 32).
+kernels), above 32 (tiled GEMMs; 4-bit weights stop at 32) and, at the largest
+hidden size, enough for the persistent 256-row kernel.
 """
 import pytest
 
@@ -20,6 +21,9 @@ EDGE_SHAPES = {
 }
 CASES = [(name, T, fmt) for name in EDGE_SHAPES for T in (1, 5, 40) for fmt in ("bf16", "fp8", "q4")
          if not (fmt == "q4" and T > 32)]
+# the persistent 256-row kernel at the largest hidden size (a mean of 64 rows per expert): gate/up
+# over 128 K steps, down over 2 (FFN 128), the three-stage weight ring with BF16 weights
+CASES += [("H8192-k16", 1024, "bf16"), ("H8192-k16", 1024, "fp8")]
 
 
 @pytest.fixture(scope="module")
