@@ -61,7 +61,7 @@ def gate_up_kernel_name(tile_rows):
     """The kernel that runs the gate/up launch for a tile height (as rocprofv3 names it)."""
     if tile_rows == 256:
         # the two-stage ring: at a mean of 192 rows per expert or more (the 8192-token workload)
-        return "grouped_gemm_dma_kernel<0, false, false>"
+        return "grouped_gemm_dma_kernel<0, false, false, false>"
     return f"grouped_gemm_kernel<{tile_rows}, 32, 2, 0, false>"
 
 

@@ -116,6 +116,8 @@ struct GemmParams {
   const float* sc1;
   const float* ssc0;
   const float* ssc1;
+  int b_stream;  // persistent kernel, BF16, three-stage ring: an expert's only tile loads its weight rows
+                 // with the non-temporal hint
 };
 
 // 16-byte chunk swizzles of an LDS row of KCH chunks.  Any 16 consecutive rows
@@ -137,6 +139,7 @@ struct Item {
   int expert;
   int row0;  // first padded row or first token; -1: no item
   int nb;    // column block
+  int tile;  // routed launches: index in the tile table (-1: dense)
 };
 
 // Routed launches (GATE_UP, DOWN): item count and item by index.  Routed
@@ -160,8 +163,10 @@ __device__ __forceinline__ Item routed_item_at(const GemmParams& p, const Routed
   Item it;
   it.kind = (MODE == DOWN) ? K_DOWN : K_GU;
   it.expert = 0;
+  it.tile = -1;
   if (item < r.n_routed) {
     const int tile = item / r.nb_per;
+    it.tile = tile;
     it.dense = false;
     it.nb = item % r.nb_per;
     it.expert = p.tiles[2 * tile];
@@ -797,6 +802,12 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
                : "memory", "m0");
 }
+// The same with the non-temporal hint: the bytes are not kept in the caches
+// for later readers.
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_base), "v"(src)
+               : "memory", "m0");
+}
 
 // wait until every vector-memory access of this wave has completed
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
@@ -811,10 +822,11 @@ struct DmaItem {
   uint32_t aon;               // bit q: A group q holds a data row
   int live;                   // this wave's 64 rows hold data
   int nm;                     // 32-row blocks of this wave that hold data (padding rows are last)
+  int bnt;                    // B rows loaded with the non-temporal hint (no other item reads them)
   int orow[DCfg::MI];         // this lane's epilogue rows (block m): assignment (down), or >= 0 if stored
 };
 
-template <int MODE, bool Q>
+template <int MODE, bool Q, bool NT>
 __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, int wave, int wm, int lane,
                                             int spar) {
   constexpr size_t EB = Q ? 1 : 2;  // bytes per weight
@@ -862,6 +874,16 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
     d.nm += __builtin_amdgcn_readfirstlane((int)lv);
   }
   d.live = d.nm > 0;
+  // an expert's only tile: no other item of the launch reads these weight
+  // rows, so they are loaded past the caches, which then keep the token
+  // rows, h and o that this and the next launches read again
+  d.bnt = 0;
+  if (NT && !it.dense) {
+    const int ntl = p.n_tiles[0];
+    const bool shared_w = (it.tile > 0 && p.tiles[2 * (it.tile - 1)] == it.expert) ||
+                          (it.tile + 1 < ntl && p.tiles[2 * (it.tile + 1)] == it.expert);
+    d.bnt = __builtin_amdgcn_readfirstlane(shared_w ? 0 : 1);
+  }
   // the epilogue's rows, read here so that the epilogue issues no load (a
   // load there would wait behind the next item's loads already in flight)
 #pragma unroll
@@ -872,9 +894,10 @@ __device__ __forceinline__ DmaItem dma_item(const GemmParams& p, const Item it, 
   return d;
 }
 
-template <int MODE, bool Q = false, bool R3 = false>
+template <int MODE, bool Q = false, bool R3 = false, bool NT = false>
 __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) {
   static_assert(MODE == GATE_UP || MODE == DOWN, "routed GEMMs only");
+  static_assert(!NT || (R3 && !Q), "non-temporal weight loads only with the BF16 three-stage ring");
   using C = DCfg;
   using G = DmaGeom<Q>;
   using L = DmaLay<Q, R3>;  // R3: weight rows two K steps ahead
@@ -929,9 +952,17 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
         dma16(d.asrc[q] + kb * DBK, base + (uint32_t)(wave * DCfg::RPW + q * DRPI) * DKCH * 16);
   };
   auto issue_b = [&](const DmaItem& d, uint32_t base, int kb) {
+    if (NT && d.bnt) {
 #pragma unroll
-    for (int q = 0; q < G::BNQ; ++q)
-      dma16(d.bbase + boff[q] + (size_t)kb * DBK * EB, base + (uint32_t)((wave * DCfg::RPW + q * G::BRPI) * G::BKCH) * 16);
+      for (int q = 0; q < G::BNQ; ++q)
+        dma16_nt(d.bbase + boff[q] + (size_t)kb * DBK * EB,
+                 base + (uint32_t)((wave * DCfg::RPW + q * G::BRPI) * G::BKCH) * 16);
+    } else {
+#pragma unroll
+      for (int q = 0; q < G::BNQ; ++q)
+        dma16(d.bbase + boff[q] + (size_t)kb * DBK * EB,
+              base + (uint32_t)((wave * DCfg::RPW + q * G::BRPI) * G::BKCH) * 16);
+    }
   };
   auto issue_scales = [&](const DmaItem& d) {
     if constexpr (Q) {
@@ -1001,7 +1032,7 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
   constexpr int SUB = DBK / 16;
   static_assert(SUB == 4, "the K loop below is written out for four sub-steps");
   const int nk = p.K / DBK;  // even: K is a multiple of 128
-  DmaItem cur = dma_item<MODE, Q>(p, routed_item_at<DBM, MODE>(p, ri, first), wave, wm, lane, 0);
+  DmaItem cur = dma_item<MODE, Q, NT>(p, routed_item_at<DBM, MODE>(p, ri, first), wave, wm, lane, 0);
   int bs = 0;       // R3: B stage of the current K step (cycles 0, 1, 2 across items)
   int nb_pend = 0;  // R3: B loads of the latest group, which the next step need not wait for
   if constexpr (R3) {
@@ -1017,7 +1048,7 @@ __global__ __launch_bounds__(DNT, 1) void grouped_gemm_dma_kernel(GemmParams p) 
     const int nxt = item + nslot;
     const bool has_next = nxt < last;
     DmaItem next = cur;
-    if (has_next) next = dma_item<MODE, Q>(p, routed_item_at<DBM, MODE>(p, ri, nxt), wave, wm, lane, cur.spar ^ 1);
+    if (has_next) next = dma_item<MODE, Q, NT>(p, routed_item_at<DBM, MODE>(p, ri, nxt), wave, wm, lane, cur.spar ^ 1);
 #pragma unroll
     for (int m = 0; m < C::MI; ++m)
 #pragma unroll
@@ -1270,7 +1301,8 @@ hipError_t launch_mode(const GemmParams& p, int64_t max_items, hipStream_t st) {
 }
 
 // Persistent launch: one workgroup per CU (at most one per item).  ring3:
-// the three-stage weight ring (BF16 weights only).
+// the three-stage weight ring (BF16 weights only); p.b_stream: with it, the
+// non-temporal weight loads of single-tile experts (ignored without ring3).
 template <int MODE, bool Q = false>
 hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st, bool ring3) {
   if (max_items <= 0) return hipSuccess;
@@ -1281,19 +1313,20 @@ hipError_t launch_dma(const GemmParams& p, int64_t max_items, hipStream_t st, bo
   if (e != hipSuccess) return e;
   int64_t grid = n_cu < max_items ? n_cu : max_items;
   grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  auto go = [&](auto R3) -> hipError_t {
-    constexpr bool r3 = decltype(R3)::value;
+  auto go = [&](auto R3, auto NT) -> hipError_t {
+    constexpr bool r3 = decltype(R3)::value, nt = decltype(NT)::value;
     constexpr size_t lds = DmaLay<Q, r3>::LDS;
-    hipError_t e2 = hipFuncSetAttribute((const void*)grouped_gemm_dma_kernel<MODE, Q, r3>,
+    hipError_t e2 = hipFuncSetAttribute((const void*)grouped_gemm_dma_kernel<MODE, Q, r3, nt>,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e2 != hipSuccess) return e2;
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE, Q, r3>), dim3((unsigned)grid), dim3(DNT), lds, st, p);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<MODE, Q, r3, nt>), dim3((unsigned)grid), dim3(DNT), lds, st, p);
     return hipGetLastError();
   };
   if constexpr (!Q) {
-    if (ring3) return go(std::true_type{});
+    if (ring3 && p.b_stream) return go(std::true_type{}, std::true_type{});
+    if (ring3) return go(std::true_type{}, std::false_type{});
   }
-  return go(std::false_type{});
+  return go(std::false_type{}, std::false_type{});
 }
 
 // Tile configuration per tile height: (rows, K step, workgroups per CU).
@@ -1381,8 +1414,9 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, const floa
 hipError_t launch_gate_up(const uint16_t* x, const void* w_gate, const void* w_up, const int32_t* sorted,
                           const int32_t* tiles, const int32_t* n_tiles, int T, int H, int k, int I, int BM,
                           int64_t max_tiles, uint16_t* h, const void* ws_gate, const void* ws_up, int I_s,
-                          uint16_t* h_s, hipStream_t st, const FP8Scales* q, bool ring3) {
+                          uint16_t* h_s, hipStream_t st, const FP8Scales* q, bool ring3, bool stream_w) {
   GemmParams p = {};
+  p.b_stream = stream_w ? 1 : 0;
   p.a = x;
   p.lda = H;
   p.K = H;
@@ -1413,8 +1447,9 @@ hipError_t launch_gate_up(const uint16_t* x, const void* w_gate, const void* w_u
 
 hipError_t launch_down(const uint16_t* h, const void* w_down, const int32_t* sorted, const int32_t* tiles,
                        const int32_t* n_tiles, int T, int H, int k, int I, int BM, int64_t max_tiles, uint16_t* o,
-                       hipStream_t st, const FP8Scales* q, bool ring3) {
+                       hipStream_t st, const FP8Scales* q, bool ring3, bool stream_w) {
   GemmParams p = {};
+  p.b_stream = stream_w ? 1 : 0;
   p.a = h;
   p.lda = I;
   p.K = I;

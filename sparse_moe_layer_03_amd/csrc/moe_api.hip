@@ -106,6 +106,7 @@ int check_ffn_shapes(int I, int I_s) {
 struct Layout {
   int BIG, SMALL;
   bool ring3_gate_up;  // the gate/up launch's persistent kernel with the three-stage weight ring
+  bool stream_w;       // the persistent launches load single-tile experts' weight rows non-temporally
   int64_t max_rows, max_big, max_small, max_tiles;
   size_t off_ids, off_w, off_s, off_counts, off_padoff, off_sorted, off_inv, off_tiles, off_ntiles,
       off_scratch, off_h, off_hs, off_o, total;
@@ -137,6 +138,7 @@ Layout layout(int T, int H, int E, int k, int I, int I_s) {
   L.BIG = moe_align_tile_rows(T, E, k);
   L.SMALL = moe_align_small_tile_rows(T, E, k);
   L.ring3_gate_up = ring3_gate_up(T, E, k);
+  L.stream_w = stream_weights(T, E, k);
   const int64_t nA = (int64_t)T * k;
   L.max_rows = max_rows_for(nA, E, L.SMALL);
   L.max_big = max_big_for(nA, E, L.BIG, L.SMALL);
@@ -319,7 +321,7 @@ hipError_t launch_routed_gate_up(const uint16_t* x, const void* w_gate, const vo
                                  uint16_t* h, const void* ws_gate, const void* ws_up, int I_s, uint16_t* h_s,
                                  const Layout& L, hipStream_t st, const FP8Scales* q = nullptr) {
   hipError_t e = launch_gate_up(x, w_gate, w_up, sorted, tiles, n_tiles, T, H, k, I, L.BIG, L.max_big, h, ws_gate,
-                                ws_up, I_s, h_s, st, q, L.ring3_gate_up);
+                                ws_up, I_s, h_s, st, q, L.ring3_gate_up, L.stream_w);
   if (e != hipSuccess || L.SMALL == L.BIG) return e;
   return launch_gate_up(x, w_gate, w_up, sorted, tiles + 2 * L.max_big, n_tiles + 1, T, H, k, I, L.SMALL, L.max_small,
                         h, nullptr, nullptr, 0, nullptr, st, q);
@@ -328,7 +330,8 @@ hipError_t launch_routed_gate_up(const uint16_t* x, const void* w_gate, const vo
 hipError_t launch_routed_down(const uint16_t* h, const void* w_down, const int32_t* sorted, const int32_t* tiles,
                               const int32_t* n_tiles, int T, int H, int k, int I, uint16_t* o, const Layout& L,
                               hipStream_t st, const FP8Scales* q = nullptr) {
-  hipError_t e = launch_down(h, w_down, sorted, tiles, n_tiles, T, H, k, I, L.BIG, L.max_big, o, st, q);
+  hipError_t e =
+      launch_down(h, w_down, sorted, tiles, n_tiles, T, H, k, I, L.BIG, L.max_big, o, st, q, true, L.stream_w);
   if (e != hipSuccess || L.SMALL == L.BIG) return e;
   return launch_down(h, w_down, sorted, tiles + 2 * L.max_big, n_tiles + 1, T, H, k, I, L.SMALL, L.max_small, o, st,
                      q);

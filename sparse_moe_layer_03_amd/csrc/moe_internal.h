@@ -223,16 +223,24 @@ struct FP8Scales {
 };
 // ring3: with 256-row tiles and BF16 weights, the persistent kernel loads the
 // weight rows two K steps ahead (three weight stages); see ring3_gate_up.
+// stream_w: with 256-row tiles and BF16 weights, the weight rows of an
+// expert's only tile are loaded with the non-temporal hint; see stream_weights.
 hipError_t launch_gate_up(const uint16_t* x, const void* w_gate, const void* w_up, const int32_t* sorted,
                           const int32_t* tiles, const int32_t* n_tiles, int T, int H, int k, int I, int BM,
                           int64_t max_tiles, uint16_t* h, const void* ws_gate, const void* ws_up, int I_s,
-                          uint16_t* h_s, hipStream_t st, const FP8Scales* q = nullptr, bool ring3 = false);
+                          uint16_t* h_s, hipStream_t st, const FP8Scales* q = nullptr, bool ring3 = false,
+                          bool stream_w = false);
 hipError_t launch_down(const uint16_t* h, const void* w_down, const int32_t* sorted, const int32_t* tiles,
                        const int32_t* n_tiles, int T, int H, int k, int I, int BM, int64_t max_tiles, uint16_t* o,
-                       hipStream_t st, const FP8Scales* q = nullptr, bool ring3 = true);
+                       hipStream_t st, const FP8Scales* q = nullptr, bool ring3 = true, bool stream_w = false);
 // Whether the gate/up launch takes the three-stage weight ring: below a mean
 // of 192 rows per expert (tiles partly filled, the launch streams weights).
 inline bool ring3_gate_up(int T, int E, int k) { return E > 0 && (int64_t)T * k / E < 192; }
+// Whether the persistent routed launches load single-tile experts' weight
+// rows with the non-temporal hint: below a mean of 192 rows per expert, where
+// the token rows, h and o that later launches read again then stay in the
+// Infinity Cache (at larger means o outgrows it and the hint only costs).
+inline bool stream_weights(int T, int E, int k) { return E > 0 && (int64_t)T * k / E < 192; }
 hipError_t launch_combine(const uint16_t* o, const float* w, const uint16_t* h_s,
                           const void* ws_down, const float* s, int T, int H, int k, int I_s, uint16_t* y,
                           hipStream_t st, const FP8Scales* q = nullptr);
